@@ -1,0 +1,192 @@
+"""CPU oracle for the KDA hot path -- TEST INFRASTRUCTURE ONLY.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline leg of
+``bench.py`` may import this package.  The product path (the HIP library and
+its Python binding) never imports, links or executes anything here, and this
+package never imports the product.
+
+The arithmetic lives in ``kda_oracle.c`` (plain C, fp64, token by token,
+compiled with gcc); this module only compiles it, marshals numpy arrays and
+composes its steps in the method's order:
+
+    prefill:  conv+act (q, k, v)  ->  L2(q), L2(k)  ->  beta = sigmoid,
+              gate = sigmoid  ->  recurrence  ->  y, final state, conv cache
+    decode:   one more prefill token per row, state and conv cache in place
+
+Function citations are in ``kda_oracle.c``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+SRC = os.path.join(HERE, "kda_oracle.c")
+LIB = os.path.join(HERE, "libkda_oracle.so")
+
+ACT_NONE, ACT_SILU = 0, 1
+L2_EPS = 1e-6  # KDA_L2_EPS reading (value not printed on the pages; 1e-6 as the tiny fp32 workload states)
+
+_D = ctypes.POINTER(ctypes.c_double)
+_I = ctypes.POINTER(ctypes.c_int32)
+
+
+def build(src=SRC, out=LIB, extra=()):
+    """Compile the oracle with gcc (OpenMP over independent heads)."""
+    cmd = ["gcc", "-O2", "-fopenmp", "-fPIC", "-shared", "-std=c11", *extra, src, "-o", out, "-lm"]
+    subprocess.run(cmd, check=True)
+    return out
+
+
+def _f64(a):
+    if a is None:
+        return None
+    if hasattr(a, "detach"):  # torch tensor -> exact fp64 copy
+        a = a.detach().to("cpu").double().numpy()
+    return np.ascontiguousarray(a, dtype=np.float64)
+
+
+def _i32(a):
+    if a is None:
+        return None
+    if hasattr(a, "detach"):
+        a = a.detach().to("cpu").numpy()
+    return np.ascontiguousarray(a, dtype=np.int32)
+
+
+def _p(a, t=_D):
+    return None if a is None else a.ctypes.data_as(t)
+
+
+class Oracle:
+    """Handle on one compiled oracle library (the default one, or a test build)."""
+
+    def __init__(self, path=LIB):
+        if not os.path.exists(path):
+            if path != LIB:
+                raise FileNotFoundError(path)
+            build()
+        self.lib = ctypes.CDLL(path)
+        L = self.lib
+        L.kda_oracle_num_threads.restype = ctypes.c_int
+        L.kda_oracle_conv.argtypes = [ctypes.c_int, _I, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                      _D, _D, _D, _D, ctypes.c_long, _D]
+        L.kda_oracle_l2norm.argtypes = [ctypes.c_long, ctypes.c_int, ctypes.c_double, _D]
+        L.kda_oracle_sigmoid.argtypes = [ctypes.c_long, _D, _D]
+        L.kda_oracle_recurrence.argtypes = [ctypes.c_int, _I, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                            _D, _D, _D, _D, _D, _D, ctypes.c_double, _D, _D, _D]
+        L.kda_oracle_decode_step.argtypes = [ctypes.c_int, _I, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                             ctypes.c_int, ctypes.c_double, ctypes.c_double,
+                                             _D, _D, _D, _D, _D, _D, _D, _D, _D, _D]
+
+    def num_threads(self):
+        return int(self.lib.kda_oracle_num_threads())
+
+    # ---- single steps --------------------------------------------------
+    def conv(self, x, w, cu, act=ACT_SILU, cache_in=None):
+        """x [T, C], w [C, K], cu [N+1], cache_in None or [N, K-1, C].
+        Returns (y [T, C], cache_out [N, K-1, C])."""
+        x, w, cu, cache_in = _f64(x), _f64(w), _i32(cu), _f64(cache_in)
+        T, C = x.shape
+        K = w.shape[1]
+        N = cu.shape[0] - 1
+        y = np.zeros((T, C))
+        cache_out = np.zeros((N, max(K - 1, 0), C))
+        self.lib.kda_oracle_conv(N, _p(cu, _I), C, K, act, _p(x), _p(w), _p(cache_in),
+                                 _p(cache_out) if K > 1 else None, (K - 1) * C, _p(y))
+        return y, cache_out
+
+    def l2norm(self, x, eps=L2_EPS):
+        x = _f64(x).copy()
+        d = x.shape[-1]
+        self.lib.kda_oracle_l2norm(x.size // d, d, eps, _p(x))
+        return x
+
+    def sigmoid(self, x):
+        x = _f64(x)
+        y = np.empty_like(x)
+        self.lib.kda_oracle_sigmoid(x.size, _p(x), _p(y))
+        return y
+
+    def recurrence(self, q, k, v, la, beta, gate, cu, scale=1.0, s0=None):
+        """Prepared operands (normalised q, k; post-sigmoid beta and gate).
+        q, k, la [T, H, dk]; v [T, H, dv]; beta [T, H]; gate None or [T, H, dv];
+        s0 None or [N, H, dk, dv].  Returns (y [T, H, dv], S [N, H, dk, dv])."""
+        q, k, v, la, beta, gate, s0 = map(_f64, (q, k, v, la, beta, gate, s0))
+        cu = _i32(cu)
+        T, H, dk = q.shape
+        dv = v.shape[2]
+        N = cu.shape[0] - 1
+        y = np.zeros((T, H, dv))
+        S = np.zeros((N, H, dk, dv))
+        self.lib.kda_oracle_recurrence(N, _p(cu, _I), H, dk, dv, _p(q), _p(k), _p(v), _p(la),
+                                       _p(beta), _p(gate), float(scale), _p(s0), _p(y), _p(S))
+        return y, S
+
+    # ---- composed paths ----------------------------------------------------
+    def prologue(self, inp, act=ACT_SILU, eps=L2_EPS, cache_in=None):
+        """Conv + act + L2 + gates on raw prefill inputs (dict from kda_inputs).
+        cache_in: None = the dict's conv_cache, or an explicit [N, 3, K-1, H*d]."""
+        H, d, K = inp["H"], inp["d"], inp["K"]
+        T = inp["T"]
+        cu = inp["cu_seqlens"]
+        w = _f64(inp["conv_w"])
+        cache = _f64(inp["conv_cache"] if cache_in is None else cache_in)
+        outs, caches = [], []
+        for X, key in enumerate(("q_raw", "k_raw", "v_raw")):
+            y, c = self.conv(_f64(inp[key]).reshape(T, H * d), w[X], cu, act,
+                             cache[:, X] if K > 1 else None)
+            outs.append(y.reshape(T, H, d))
+            caches.append(c)
+        q = self.l2norm(outs[0], eps)
+        k = self.l2norm(outs[1], eps)
+        v = outs[2]
+        beta = self.sigmoid(inp["beta_logit"])
+        gate = self.sigmoid(inp["gate_logit"]) if inp.get("gate_logit") is not None else None
+        cache_out = np.stack(caches, axis=1) if K > 1 else np.zeros((inp["N"], 3, 0, H * d))
+        return dict(q=q, k=k, v=v, beta=beta, gate=gate, conv_cache=cache_out)
+
+    def prefill(self, inp, act=ACT_SILU, eps=L2_EPS, scale=1.0, s0=None, cache_in=None):
+        """Full prefill on raw inputs.  Returns dict with y, final_state,
+        conv_cache and the prologue intermediates q, k, v, beta, gate."""
+        pro = self.prologue(inp, act, eps, cache_in)
+        y, S = self.recurrence(pro["q"], pro["k"], pro["v"], inp["log_alpha"], pro["beta"],
+                               pro["gate"], inp["cu_seqlens"], scale,
+                               inp["initial_state"] if s0 is None else s0)
+        pro.update(y=y, final_state=S)
+        return pro
+
+    def decode_step(self, state, conv_cache, conv_w, step, slot_idx=None, act=ACT_SILU,
+                    eps=L2_EPS, scale=1.0):
+        """One decode step.  ``state`` [n_slots, H, d, d] and ``conv_cache``
+        [n_slots, 3, K-1, H*d] must be float64 numpy arrays; both are
+        updated in place.  ``step`` holds q_raw, k_raw, v_raw, log_alpha,
+        beta_logit, gate_logit for [batch, H, d].  Returns y [batch, H, d]."""
+        assert state.dtype == np.float64 and state.flags.c_contiguous
+        assert conv_cache.dtype == np.float64 and conv_cache.flags.c_contiguous
+        q, k, v = _f64(step["q_raw"]), _f64(step["k_raw"]), _f64(step["v_raw"])
+        la, bl = _f64(step["log_alpha"]), _f64(step["beta_logit"])
+        gl = _f64(step.get("gate_logit"))
+        w = _f64(conv_w)
+        B, H, d = q.shape
+        K = w.shape[2]
+        si = _i32(slot_idx)
+        y = np.zeros((B, H, d))
+        self.lib.kda_oracle_decode_step(B, _p(si, _I), H, d, K, act, eps, float(scale),
+                                        _p(q), _p(k), _p(v), _p(w), _p(conv_cache), _p(state),
+                                        _p(la), _p(bl), _p(gl), _p(y))
+        return y
+
+
+_default = None
+
+
+def get():
+    """The default oracle (compiled on first use if no build is present)."""
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default

@@ -1,0 +1,231 @@
+/*
+ * KDA CPU oracle -- TEST INFRASTRUCTURE, NOT PART OF THE PRODUCT PATH.
+ *
+ * Only the test suite, the package's smoke check and the benchmark's CPU
+ * baseline leg may load this library.  It shares no code, header or constant
+ * with the HIP implementation; the two meet only through seeded inputs.
+ *
+ * What it computes, in fp64, token by token, exactly as the method is defined
+ * (page names below are the titles of the public pages this follows):
+ *
+ *  - Kimi Delta Attention per head, the gated delta rule with per-channel
+ *    decay ("recurrent KDA state" in the implementation list of the forum post
+ *    "Experimental Native Vulkan Backend for Kimi K3"; the fp32 recurrent KDA
+ *    step of the "metrale_model_arch::kimi_k3" API docs, Constants):
+ *        S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *        o_t = scale * S_t^T q_t,          y_t = o_t (.) gate_t
+ *    S is dk x dv (row index = key channel), alpha_t = exp(log_alpha_t).
+ *  - the independent short causal depthwise convolutions on q, k and v
+ *    (forum post, implementation list), each followed by an activation
+ *    (SiLU by default, or none);
+ *  - L2 normalisation of q and k over the key channels with the epsilon the
+ *    kimi_k3 API docs call KDA_L2_EPS (Constants), as x / sqrt(sum x^2 + eps);
+ *  - beta = sigmoid(beta_logit) per (token, head) and the output gate
+ *    sigmoid(gate_logit) per (token, head, value channel) ("KDA output
+ *    gating", forum post, implementation list);
+ *  - the decode step as conv update, then recurrent step (kimi_k3 API docs,
+ *    Functions: kda_decode_token): one more prefill token that reads and
+ *    rewrites the per-sequence conv cache and recurrent state in place (the
+ *    docs' struct KdaState keeps both as fp32 read-modify-write buffers; fp64
+ *    here).
+ *
+ * Readings taken where the pages are silent: conv tap K-1 multiplies the
+ * current token, no conv bias, zero history at a sequence start unless a
+ * cache is given, and the conv never crosses sequences; the output scale is
+ * an explicit argument; nothing (no RMSNorm) follows the output gate.
+ *
+ * Layouts are row-major, last index fastest.  The ctypes prototypes live in
+ * oracle/__init__.py, the only caller.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
+
+int kda_oracle_num_threads(void) {
+#ifdef _OPENMP
+    return omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
+
+static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
+
+static double activation(int act, double x) {
+    /* act 1 = SiLU x*sigmoid(x); act 0 = identity */
+    return act == 1 ? x * sigmoid(x) : x;
+}
+
+/*
+ * Causal depthwise convolution of one stream over a packed batch.
+ *   x        [T][C] raw inputs, sequences packed by cu_seqlens [n_seqs+1]
+ *   w        [C][K] taps; y_t[c] = act( sum_j w[c][j] * x_{t-K+1+j}[c] )
+ *   cache_in NULL or [n_seqs] x (K-1) x C at stride cache_stride between
+ *            sequences: the K-1 raw inputs that precede each sequence,
+ *            oldest first; NULL means zeros
+ *   cache_out NULL or same layout: the last K-1 raw inputs of each sequence
+ *            (reaching back into cache_in when the sequence is shorter)
+ * cache_out may alias cache_in.
+ */
+void kda_oracle_conv(int n_seqs, const int32_t *cu, int C, int K, int act,
+                     const double *x, const double *w,
+                     const double *cache_in, double *cache_out, long cache_stride,
+                     double *y) {
+    for (int n = 0; n < n_seqs; ++n) {
+        const long start = cu[n], end = cu[n + 1];
+        const double *cin = cache_in ? cache_in + (long)n * cache_stride : NULL;
+        /* history value of channel c at absolute token position tau */
+#define XS(tau, c)                                                          \
+    ((tau) >= start ? x[(long)(tau) * C + (c)]                              \
+     : (cin && (start - (tau)) <= K - 1 ? cin[(long)((K - 1) - (start - (tau))) * C + (c)] \
+        : 0.0))
+#pragma omp parallel for schedule(static)
+        for (int c = 0; c < C; ++c) {
+            for (long t = start; t < end; ++t) {
+                double acc = 0.0;
+                for (int j = 0; j < K; ++j) acc += w[(long)c * K + j] * XS(t - K + 1 + j, c);
+                y[t * C + c] = activation(act, acc);
+            }
+        }
+        if (cache_out && K > 1) {
+            double *tmp = (double *)malloc(sizeof(double) * (size_t)(K - 1) * (size_t)C);
+            for (int j = 0; j < K - 1; ++j)
+                for (int c = 0; c < C; ++c) tmp[(long)j * C + c] = XS(end - (K - 1) + j, c);
+            memcpy(cache_out + (long)n * cache_stride, tmp, sizeof(double) * (size_t)(K - 1) * (size_t)C);
+            free(tmp);
+        }
+#undef XS
+    }
+}
+
+/* x[r][0..d) <- x / sqrt(sum x^2 + eps), for each of `rows` rows (in place) */
+void kda_oracle_l2norm(long rows, int d, double eps, double *x) {
+#pragma omp parallel for schedule(static)
+    for (long r = 0; r < rows; ++r) {
+        double ss = 0.0;
+        for (int c = 0; c < d; ++c) ss += x[r * d + c] * x[r * d + c];
+        const double inv = 1.0 / sqrt(ss + eps);
+        for (int c = 0; c < d; ++c) x[r * d + c] *= inv;
+    }
+}
+
+/* y[i] = sigmoid(x[i]) */
+void kda_oracle_sigmoid(long n, const double *x, double *y) {
+    for (long i = 0; i < n; ++i) y[i] = sigmoid(x[i]);
+}
+
+/*
+ * One token of the recurrence on a dk x dv state S (row-major, in place):
+ *   D  = Diag(alpha) S                     (alpha = exp(la))
+ *   S' = D - beta k (k^T D) + beta k v^T   = (I - beta k k^T) D + beta k v^T
+ *   o  = scale S'^T q;  y = o (.) g  (g NULL: no gate)
+ */
+static void token_step(double *S, int dk, int dv, const double *q, const double *k,
+                       const double *v, const double *la, double beta, const double *g,
+                       double scale, double *kTD, double *y) {
+    for (int i = 0; i < dk; ++i) {
+        const double a = exp(la[i]);
+        for (int j = 0; j < dv; ++j) S[(long)i * dv + j] *= a;
+    }
+    for (int j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < dk; ++i) acc += k[i] * S[(long)i * dv + j];
+        kTD[j] = acc;
+    }
+    for (int i = 0; i < dk; ++i)
+        for (int j = 0; j < dv; ++j)
+            S[(long)i * dv + j] += beta * k[i] * (v[j] - kTD[j]);
+    for (int j = 0; j < dv; ++j) {
+        double acc = 0.0;
+        for (int i = 0; i < dk; ++i) acc += S[(long)i * dv + j] * q[i];
+        y[j] = scale * acc * (g ? g[j] : 1.0);
+    }
+}
+
+/*
+ * The recurrence over a packed batch, on already-prepared operands:
+ *   q, k [T][H][dk] (normalised), v [T][H][dv], la [T][H][dk] (log alpha),
+ *   beta [T][H], gate NULL or [T][H][dv] (post-sigmoid),
+ *   s0 NULL (zeros) or [n_seqs][H][dk][dv];  y [T][H][dv];
+ *   s_final NULL or [n_seqs][H][dk][dv] (may alias s0).
+ * Sequences and heads are independent and run in parallel; within one
+ * (sequence, head) the tokens run strictly in order.
+ */
+void kda_oracle_recurrence(int n_seqs, const int32_t *cu, int H, int dk, int dv,
+                           const double *q, const double *k, const double *v,
+                           const double *la, const double *beta, const double *gate,
+                           double scale, const double *s0, double *y, double *s_final) {
+    const long SS = (long)dk * dv;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int n = 0; n < n_seqs; ++n) {
+        for (int h = 0; h < H; ++h) {
+            double *S = (double *)malloc(sizeof(double) * (size_t)SS);
+            double *kTD = (double *)malloc(sizeof(double) * (size_t)dv);
+            if (s0) memcpy(S, s0 + ((long)n * H + h) * SS, sizeof(double) * (size_t)SS);
+            else memset(S, 0, sizeof(double) * (size_t)SS);
+            for (long t = cu[n]; t < cu[n + 1]; ++t) {
+                const long th = t * H + h;
+                token_step(S, dk, dv, q + th * dk, k + th * dk, v + th * dv, la + th * dk,
+                           beta[th], gate ? gate + th * dv : NULL, scale, kTD, y + th * dv);
+            }
+            if (s_final) memcpy(s_final + ((long)n * H + h) * SS, S, sizeof(double) * (size_t)SS);
+            free(kTD);
+            free(S);
+        }
+    }
+}
+
+/*
+ * One decode step for `batch` rows (metrale kimi_k3 docs, kda_decode_token:
+ * conv update, then recurrent step).  Row b works on slot s = slot_idx[b]
+ * (identity when slot_idx is NULL; slots must be distinct):
+ *   q_raw, k_raw, v_raw [batch][H][d] pre-conv inputs, la [batch][H][d],
+ *   beta_logit [batch][H], gate_logit NULL or [batch][H][d];
+ *   conv_w [3][H*d][K]; conv_cache [n_slots][3][K-1][H*d] and
+ *   state [n_slots][H][d][d] are read and rewritten in place;  y [batch][H][d].
+ * It is exactly one more prefill token for each row's sequence.
+ */
+void kda_oracle_decode_step(int batch, const int32_t *slot_idx, int H, int d, int K, int act,
+                            double eps, double scale, const double *q_raw, const double *k_raw,
+                            const double *v_raw, const double *conv_w, double *conv_cache,
+                            double *state, const double *la, const double *beta_logit,
+                            const double *gate_logit, double *y) {
+    const int C = H * d;
+    const long cstride = 3L * (K - 1) * C;
+    const int32_t cu1[2] = {0, 1};
+    double *xq = (double *)malloc(sizeof(double) * (size_t)C);
+    double *xk = (double *)malloc(sizeof(double) * (size_t)C);
+    double *xv = (double *)malloc(sizeof(double) * (size_t)C);
+    for (int b = 0; b < batch; ++b) {
+        const long s = slot_idx ? slot_idx[b] : b;
+        double *cache = conv_cache + s * cstride;
+        const double *raw[3] = {q_raw + (long)b * C, k_raw + (long)b * C, v_raw + (long)b * C};
+        double *out[3] = {xq, xk, xv};
+        for (int X = 0; X < 3; ++X)
+            kda_oracle_conv(1, cu1, C, K, act, raw[X], conv_w + (long)X * C * K,
+                            K > 1 ? cache + (long)X * (K - 1) * C : NULL,
+                            K > 1 ? cache + (long)X * (K - 1) * C : NULL, cstride, out[X]);
+        kda_oracle_l2norm(H, d, eps, xq);
+        kda_oracle_l2norm(H, d, eps, xk);
+#pragma omp parallel for schedule(static)
+        for (int h = 0; h < H; ++h) {
+            double *kTD = (double *)malloc(sizeof(double) * (size_t)d);
+            double *g = (double *)malloc(sizeof(double) * (size_t)d);
+            const long bh = (long)b * H + h;
+            if (gate_logit)
+                for (int j = 0; j < d; ++j) g[j] = sigmoid(gate_logit[bh * d + j]);
+            token_step(state + (s * H + h) * (long)d * d, d, d, xq + (long)h * d, xk + (long)h * d,
+                       xv + (long)h * d, la + bh * d, sigmoid(beta_logit[bh]),
+                       gate_logit ? g : NULL, scale, kTD, y + bh * d);
+            free(g);
+            free(kTD);
+        }
+    }
+    free(xv);
+    free(xk);
+    free(xq);
+}
