@@ -1,0 +1,198 @@
+/*
+ * kda.h -- C ABI of libkda.so: Kimi Delta Attention (KDA) prefill and decode
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * KDA is the gated delta rule with per-channel decay behind Kimi K3's
+ * linear-attention layers.  Per head, with a dk x dv state S (row = key
+ * channel):
+ *     S_t = (I - beta_t k_t k_t^T) Diag(alpha_t) S_{t-1} + beta_t k_t v_t^T
+ *     o_t = scale * S_t^T q_t,        y_t = o_t (.) sigmoid(gate_logit_t)
+ * where q, k, v come out of independent short causal depthwise convolutions
+ * ("independent Q/K/V short convolutions", "recurrent KDA state", "KDA output
+ * gating": implementation list of the forum post "Experimental Native Vulkan
+ * Backend for Kimi K3"), q and k are L2-normalised with KDA_L2_EPS
+ * ("metrale_model_arch::kimi_k3" API docs, Constants), alpha_t =
+ * exp(log_alpha_t) per key channel and beta_t = sigmoid(beta_logit_t).
+ *
+ * Entry points (one GPU, caller-owned memory, asynchronous on `stream`):
+ *   kda_prologue        short conv + activation + L2(q, k) + sigmoid gates
+ *   kda_chunk_forward   chunked prefill over packed variable-length sequences
+ *                       with fp32 initial/final state (= kda_chunk_prepare
+ *                       followed by kda_chunk_scan, also exported)
+ *   kda_decode_step     one token for a batch of resident states: conv update
+ *                       then recurrent step (kimi_k3 API docs, Functions:
+ *                       kda_decode_token)
+ *
+ * Conventions shared by every entry point
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *     never allocates, frees or keeps them, and keeps no state between calls
+ *     except a per-device "is this a gfx950" flag.
+ *   - Calls only enqueue kernels on `stream` (a hipStream_t; NULL = the null
+ *     stream) and return; results are ready once the caller synchronises.
+ *   - Arguments are checked on the host before anything is launched.  On any
+ *     error nothing is launched and nothing is written; the return value
+ *     says why and kda_last_error_detail() gives a sentence (per thread).
+ *     Unsupported inputs are rejected, never approximated.
+ *   - Device-side values are not inspected: NaN/Inf propagate; out-of-range
+ *     slot indices or log_alpha > 0 are undefined behaviour.
+ *   - Layouts are row-major (last index fastest).  Tokens of all sequences
+ *     are packed ("THD": [total_tokens, H, d]); sequence n owns tokens
+ *     cu_seqlens[n] .. cu_seqlens[n+1]-1 (int32, cu_seqlens[0] = 0,
+ *     non-decreasing; empty sequences are allowed).
+ *   - Every tensor pointer must be 16-byte aligned.
+ *   - dk = dv = d.  kda_prologue and kda_decode_step accept d in
+ *     {4, 8, 16, 32, 64, 128}; the chunk path accepts d = 128 and bf16 only.
+ *   - Conv weights: [3][H*d][conv_k] fp32, stream order q, k, v; tap
+ *     conv_k-1 multiplies the current token; no bias.  Conv cache:
+ *     [n][3][conv_k-1][H*d] fp32, the conv_k-1 raw inputs that precede the
+ *     next token of sequence/slot n, oldest first.  Both the conv cache and
+ *     the recurrent state are fp32 read-modify-write buffers, as the kimi_k3
+ *     API docs describe its per-sequence KdaState.
+ *   - Recurrent state: [n][H][d][d] fp32, S[key channel][value channel].
+ *   - Thread-safe; calls on different streams may overlap as long as they
+ *     do not write the same buffers.
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KDA_OK = 0,
+    KDA_ERR_NULL = 1,        /* a required pointer is NULL */
+    KDA_ERR_SHAPE = 2,       /* a size is <= 0 / inconsistent (e.g. total_tokens != cu_seqlens[n]) */
+    KDA_ERR_DTYPE = 3,       /* dtype not one of kda_dtype */
+    KDA_ERR_UNSUPPORTED = 4, /* valid but not implemented here (d, conv_k, dtype on the chunk path,
+                                device architecture other than gfx950) */
+    KDA_ERR_SEQLENS = 5,     /* cu_seqlens[0] != 0 or decreasing */
+    KDA_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than kda_chunk_workspace_bytes() */
+    KDA_ERR_ALIGN = 7,       /* a tensor pointer is not 16-byte aligned */
+    KDA_ERR_HIP = 8          /* the HIP runtime reported an error (see kda_last_error_detail) */
+} kda_status;
+
+typedef enum { KDA_F32 = 0, KDA_BF16 = 1 } kda_dtype;
+typedef enum { KDA_ACT_NONE = 0, KDA_ACT_SILU = 1 } kda_act;
+
+/* Geometry and scalars shared by all calls.  The pages give production KDA
+ * geometry as head dim 128 and conv kernel 4 (kimi_k3 API docs, struct
+ * KdaConfig); they do not print KDA_L2_EPS's value (1e-6 is used by the
+ * workloads here).  `scale` multiplies o_t (1.0 reproduces the bare
+ * recurrence; dk^-0.5 is the usual attention scaling). */
+typedef struct {
+    int32_t H;       /* heads (> 0) */
+    int32_t d;       /* head dim, dk = dv = d */
+    int32_t conv_k;  /* short-conv kernel size, 1..4 */
+    int32_t act;     /* kda_act applied after each conv */
+    float l2_eps;    /* epsilon inside the L2 norm: x / sqrt(sum x^2 + eps), >= 0 */
+    float scale;     /* output scale */
+} kda_geom;
+
+/*
+ * kda_prologue: per token of each sequence,
+ *   x~ = act(conv(x)) for x in {q, k, v};  q^ = L2(q~), k^ = L2(k~), v^ = v~;
+ *   beta = sigmoid(beta_logit);  gate = sigmoid(gate_logit).
+ * The conv reads history from conv_cache_in at a sequence start (zeros if
+ * NULL) and never crosses sequences.
+ *   n_seqs >= 1, total_tokens >= 0, cu_seqlens_dev / cu_seqlens_host: the same
+ *     [n_seqs+1] int32 offsets, on device and on host (host copy validated).
+ *   in_dtype: dtype of q_raw, k_raw, v_raw, beta_logit, gate_logit and of the
+ *     outputs q_out, k_out, v_out, gate_out.
+ *   q_raw, k_raw, v_raw [T][H][d]; conv_w [3][H*d][conv_k] fp32;
+ *   conv_cache_in NULL or [n_seqs][3][conv_k-1][H*d] fp32;
+ *   conv_cache_out NULL (skip) or same shape -- the last conv_k-1 raw inputs
+ *     of each sequence (reaching into conv_cache_in for short sequences);
+ *     it may alias conv_cache_in;
+ *   beta_logit [T][H]; gate_logit NULL or [T][H][d] (then gate_out unused);
+ *   q_out, k_out, v_out [T][H][d]; beta_out [T][H] fp32; gate_out [T][H][d].
+ */
+kda_status kda_prologue(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
+                        const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host,
+                        kda_dtype in_dtype, const void *q_raw, const void *k_raw,
+                        const void *v_raw, const float *conv_w, const float *conv_cache_in,
+                        float *conv_cache_out, const void *beta_logit, const void *gate_logit,
+                        void *q_out, void *k_out, void *v_out, float *beta_out, void *gate_out,
+                        void *stream);
+
+/*
+ * Chunked prefill (d = 128, bf16, chunk = 64 tokens).  Inputs are the
+ * prologue's outputs plus the per-channel log decay.  Each sequence is cut
+ * into 64-token chunks from its own start (the last one may be shorter);
+ * within a chunk the recurrence is evaluated in its WY/UT form (cumulative
+ * log-decay, unit-lower-triangular inverse, bf16 matrix-core products with
+ * fp32 accumulation) and the fp32 state is carried from chunk to chunk.
+ * The result equals the token-by-token recurrence up to rounding.
+ *
+ *   q, k [T][H][128] bf16 (L2-normalised), v [T][H][128] bf16,
+ *   log_alpha [T][H][128] bf16, <= 0; the chunk form multiplies by
+ *     exp(+-cumulative log decay) within a chunk, so the sum of |log_alpha|
+ *     over any 64 consecutive tokens of a channel must stay below 80
+ *     (e.g. log_alpha >= -1.25 per token); beyond that results overflow;
+ *   beta [T][H] fp32 (post-sigmoid), gate NULL or [T][H][128] bf16 (post-sigmoid);
+ *   initial_state NULL (zeros) or [n_seqs][H][128][128] fp32;
+ *   final_state NULL (skip) or same shape, may alias initial_state;
+ *   out [T][H][128] bf16 = scale * o (.) gate;
+ *   workspace: device memory of at least kda_chunk_workspace_bytes(...) bytes,
+ *     16-byte aligned; its contents are scratch (only kda_chunk_scan reads
+ *     what kda_chunk_prepare wrote there).
+ */
+size_t kda_chunk_workspace_bytes(const kda_geom *geom, int32_t n_seqs,
+                                 const int32_t *cu_seqlens_host);
+
+kda_status kda_chunk_forward(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
+                             const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host,
+                             kda_dtype in_dtype, const void *q, const void *k, const void *v,
+                             const void *log_alpha, const float *beta, const void *gate,
+                             const float *initial_state, float *final_state, void *out,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+/* The two stages of kda_chunk_forward, exported so callers can time or
+ * overlap them.  kda_chunk_prepare builds every chunk's WY/UT operands
+ * (parallel over chunks and heads) into the workspace; kda_chunk_scan then
+ * carries the state through each sequence's chunks in order and writes the
+ * output and the final state.  Arguments mean what they mean above; the
+ * workspace must be passed unchanged between the two. */
+kda_status kda_chunk_prepare(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
+                             const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host,
+                             kda_dtype in_dtype, const void *q, const void *k, const void *v,
+                             const void *log_alpha, const float *beta,
+                             void *workspace, size_t workspace_bytes, void *stream);
+
+kda_status kda_chunk_scan(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
+                          const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host,
+                          kda_dtype in_dtype, const void *gate, const float *initial_state,
+                          float *final_state, void *out, void *workspace, size_t workspace_bytes,
+                          void *stream);
+
+/*
+ * kda_decode_step: one token for each of `batch` rows, fused: conv-cache
+ * shift and conv, activation, L2(q, k), sigmoid gates, then one step of the
+ * recurrence on the row's resident state, read and written once.
+ *   slot_idx_dev NULL (row b uses slot b, needs batch <= n_slots) or
+ *     [batch] int32 distinct slot numbers in [0, n_slots);
+ *   in_dtype: dtype of q_raw, k_raw, v_raw [batch][H][d], log_alpha
+ *     [batch][H][d], beta_logit [batch][H], gate_logit NULL or [batch][H][d];
+ *   conv_w [3][H*d][conv_k] fp32; conv_cache [n_slots][3][conv_k-1][H*d] fp32
+ *     and state [n_slots][H][d][d] fp32 are updated in place;
+ *   out [batch][H][d] in out_dtype (fp32 keeps the step's fp32 accuracy).
+ */
+kda_status kda_decode_step(const kda_geom *geom, int32_t batch, const int32_t *slot_idx_dev,
+                           int32_t n_slots, kda_dtype in_dtype, const void *q_raw,
+                           const void *k_raw, const void *v_raw, const float *conv_w,
+                           float *conv_cache, float *state, const void *log_alpha,
+                           const void *beta_logit, const void *gate_logit, kda_dtype out_dtype,
+                           void *out, void *stream);
+
+/* Short name of a status code (static string). */
+const char *kda_status_str(kda_status s);
+/* Sentence describing the last error returned on the calling thread ("" if none). */
+const char *kda_last_error_detail(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KDA_H */

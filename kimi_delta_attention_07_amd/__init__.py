@@ -1,0 +1,24 @@
+"""Kimi Delta Attention (KDA) on AMD Instinct MI355X (gfx950).
+
+The work runs in libkda.so (hand-written HIP kernels behind the C ABI of
+include/kda.h); this package is its thin Python binding:
+
+    prologue(...)       short conv + activation + L2(q, k) + sigmoid gates
+    chunk_forward(...)  chunked prefill over packed varlen sequences
+    decode_step(...)    one token for a batch of resident fp32 states
+
+Build the library with ``python -m kimi_delta_attention_07_amd.build``.
+"""
+from ._lib import (  # noqa: F401
+    CHUNK,
+    EXPORTS,
+    KdaError,
+    chunk_forward,
+    chunk_prepare,
+    chunk_scan,
+    chunk_workspace,
+    chunk_workspace_bytes,
+    decode_step,
+    load,
+    prologue,
+)

@@ -1,0 +1,191 @@
+"""ctypes binding of libkda.so (declared in include/kda.h).
+
+Argument marshalling only: every step of the path runs in the HIP library.
+PyTorch provides device memory and the current stream.  If the library is
+not built this module raises on first use; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(PKG, "libkda.so")
+
+KDA_F32, KDA_BF16 = 0, 1
+ACT = {"none": 0, "silu": 1}
+CHUNK = 64
+STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE", 4: "KDA_ERR_UNSUPPORTED",
+          5: "KDA_ERR_SEQLENS", 6: "KDA_ERR_WORKSPACE", 7: "KDA_ERR_ALIGN", 8: "KDA_ERR_HIP"}
+EXPORTS = ("kda_prologue", "kda_chunk_workspace_bytes", "kda_chunk_forward", "kda_chunk_prepare",
+           "kda_chunk_scan", "kda_decode_step", "kda_status_str", "kda_last_error_detail")
+
+
+class KdaError(RuntimeError):
+    def __init__(self, code, detail):
+        super().__init__(f"{STATUS.get(code, code)}: {detail}")
+        self.code = code
+        self.detail = detail
+
+
+class Geom(ctypes.Structure):
+    _fields_ = [("H", ctypes.c_int32), ("d", ctypes.c_int32), ("conv_k", ctypes.c_int32),
+                ("act", ctypes.c_int32), ("l2_eps", ctypes.c_float), ("scale", ctypes.c_float)]
+
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int32
+_lib = None
+
+
+def load(path=LIB_PATH):
+    """Load libkda.so and declare its prototypes (raises if it is missing)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m kimi_delta_attention_07_amd.build`")
+    L = ctypes.CDLL(path)
+    G = ctypes.POINTER(Geom)
+    L.kda_prologue.argtypes = [G, _I, _I, _P, _P, _I] + [_P] * 13 + [_P]
+    L.kda_prologue.restype = _I
+    L.kda_chunk_workspace_bytes.argtypes = [G, _I, _P]
+    L.kda_chunk_workspace_bytes.restype = ctypes.c_size_t
+    L.kda_chunk_forward.argtypes = [G, _I, _I, _P, _P, _I] + [_P] * 10 + [ctypes.c_size_t, _P]
+    L.kda_chunk_forward.restype = _I
+    L.kda_chunk_prepare.argtypes = [G, _I, _I, _P, _P, _I] + [_P] * 6 + [ctypes.c_size_t, _P]
+    L.kda_chunk_prepare.restype = _I
+    L.kda_chunk_scan.argtypes = [G, _I, _I, _P, _P, _I] + [_P] * 5 + [ctypes.c_size_t, _P]
+    L.kda_chunk_scan.restype = _I
+    L.kda_decode_step.argtypes = [G, _I, _P, _I, _I] + [_P] * 9 + [_I, _P, _P]
+    L.kda_decode_step.restype = _I
+    L.kda_status_str.argtypes = [_I]
+    L.kda_status_str.restype = ctypes.c_char_p
+    L.kda_last_error_detail.argtypes = []
+    L.kda_last_error_detail.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(code):
+    if code != 0:
+        raise KdaError(code, load().kda_last_error_detail().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libkda must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype(t):
+    if t.dtype == torch.float32:
+        return KDA_F32
+    if t.dtype == torch.bfloat16:
+        return KDA_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _stream(t):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def geom(H, d, conv_k, act="silu", eps=1e-6, scale=1.0):
+    return Geom(H, d, conv_k, ACT[act] if isinstance(act, str) else int(act), float(eps), float(scale))
+
+
+def _host_cu(cu_seqlens, cu_seqlens_host):
+    if cu_seqlens_host is None:
+        cu_seqlens_host = cu_seqlens.to("cpu")
+    h = cu_seqlens_host.to(torch.int32).contiguous()
+    return h, ctypes.cast(h.data_ptr(), ctypes.c_void_p)
+
+
+def prologue(q_raw, k_raw, v_raw, conv_w, cu_seqlens, beta_logit, gate_logit=None, conv_cache_in=None,
+             conv_cache_out=None, *, act="silu", eps=1e-6, cu_seqlens_host=None, outs=None):
+    """Short conv + activation + L2(q, k) + sigmoid gates.  Returns
+    dict(q, k, v, beta, gate) (allocated unless ``outs`` supplies them)."""
+    T, H, d = q_raw.shape
+    K = conv_w.shape[2]
+    n = cu_seqlens.numel() - 1
+    hcu, hptr = _host_cu(cu_seqlens, cu_seqlens_host)
+    if outs is None:
+        outs = dict(q=torch.empty_like(q_raw), k=torch.empty_like(k_raw), v=torch.empty_like(v_raw),
+                    beta=torch.empty((T, H), dtype=torch.float32, device=q_raw.device),
+                    gate=torch.empty_like(gate_logit) if gate_logit is not None else None)
+    g = geom(H, d, K, act, eps)
+    _check(load().kda_prologue(ctypes.byref(g), n, T, _ptr(cu_seqlens), hptr, _dtype(q_raw), _ptr(q_raw),
+                               _ptr(k_raw), _ptr(v_raw), _ptr(conv_w), _ptr(conv_cache_in), _ptr(conv_cache_out),
+                               _ptr(beta_logit), _ptr(gate_logit), _ptr(outs["q"]), _ptr(outs["k"]),
+                               _ptr(outs["v"]), _ptr(outs["beta"]), _ptr(outs["gate"]), _stream(q_raw)))
+    return outs
+
+
+def chunk_workspace_bytes(H, d, cu_seqlens_host):
+    h = cu_seqlens_host.to("cpu", torch.int32).contiguous()
+    g = geom(H, d, 4)
+    return int(load().kda_chunk_workspace_bytes(ctypes.byref(g), h.numel() - 1,
+                                                ctypes.cast(h.data_ptr(), ctypes.c_void_p)))
+
+
+def chunk_workspace(H, d, cu_seqlens_host, device):
+    return torch.empty(chunk_workspace_bytes(H, d, cu_seqlens_host), dtype=torch.uint8, device=device)
+
+
+def chunk_forward(q, k, v, log_alpha, beta, gate, cu_seqlens, initial_state=None, *, final_state=None,
+                  out=None, scale=1.0, workspace=None, cu_seqlens_host=None, want_final_state=True):
+    """Chunked prefill (d = 128, bf16).  Returns (out, final_state)."""
+    T, H, d = q.shape
+    n = cu_seqlens.numel() - 1
+    hcu, hptr = _host_cu(cu_seqlens, cu_seqlens_host)
+    if workspace is None:
+        workspace = chunk_workspace(H, d, hcu, q.device)
+    if out is None:
+        out = torch.empty_like(v)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((n, H, d, d), dtype=torch.float32, device=q.device)
+    g = geom(H, d, 4, scale=scale)
+    _check(load().kda_chunk_forward(ctypes.byref(g), n, T, _ptr(cu_seqlens), hptr, _dtype(q), _ptr(q), _ptr(k),
+                                    _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(gate), _ptr(initial_state),
+                                    _ptr(final_state), _ptr(out), _ptr(workspace), workspace.numel(), _stream(q)))
+    return out, final_state
+
+
+def chunk_prepare(q, k, v, log_alpha, beta, cu_seqlens, workspace, *, cu_seqlens_host=None):
+    T, H, d = q.shape
+    n = cu_seqlens.numel() - 1
+    hcu, hptr = _host_cu(cu_seqlens, cu_seqlens_host)
+    g = geom(H, d, 4)
+    _check(load().kda_chunk_prepare(ctypes.byref(g), n, T, _ptr(cu_seqlens), hptr, _dtype(q), _ptr(q), _ptr(k),
+                                    _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(workspace), workspace.numel(),
+                                    _stream(q)))
+
+
+def chunk_scan(gate, cu_seqlens, workspace, out, initial_state=None, final_state=None, *, H, d=128, scale=1.0,
+               cu_seqlens_host=None):
+    T = out.shape[0]
+    n = cu_seqlens.numel() - 1
+    hcu, hptr = _host_cu(cu_seqlens, cu_seqlens_host)
+    g = geom(H, d, 4, scale=scale)
+    _check(load().kda_chunk_scan(ctypes.byref(g), n, T, _ptr(cu_seqlens), hptr, _dtype(out), _ptr(gate),
+                                 _ptr(initial_state), _ptr(final_state), _ptr(out), _ptr(workspace),
+                                 workspace.numel(), _stream(out)))
+
+
+def decode_step(q_raw, k_raw, v_raw, conv_w, conv_cache, state, log_alpha, beta_logit, gate_logit=None,
+                slot_idx=None, *, act="silu", eps=1e-6, scale=1.0, out=None, out_dtype=torch.float32):
+    """One decode token per row; state and conv_cache updated in place.  Returns out [B, H, d]."""
+    B, H, d = q_raw.shape
+    K = conv_w.shape[2]
+    if out is None:
+        out = torch.empty((B, H, d), dtype=out_dtype, device=q_raw.device)
+    g = geom(H, d, K, act, eps, scale)
+    _check(load().kda_decode_step(ctypes.byref(g), B, _ptr(slot_idx), state.shape[0], _dtype(q_raw), _ptr(q_raw),
+                                  _ptr(k_raw), _ptr(v_raw), _ptr(conv_w), _ptr(conv_cache), _ptr(state),
+                                  _ptr(log_alpha), _ptr(beta_logit), _ptr(gate_logit), _dtype(out), _ptr(out),
+                                  _stream(q_raw)))
+    return out

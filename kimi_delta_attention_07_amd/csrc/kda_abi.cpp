@@ -1,0 +1,335 @@
+// C ABI of libkda.so (declared in include/kda.h): argument validation on the
+// host, chunk planning, kernel dispatch and error reporting.  Every check runs
+// before the first HIP call, so an invalid call launches nothing, writes
+// nothing and touches no device.
+#include "../../include/kda.h"
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "kda_internal.h"
+
+namespace {
+
+thread_local std::string g_detail;
+
+kda_status fail(kda_status s, const char *fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_detail = buf;
+    return s;
+}
+
+kda_status ok() {
+    g_detail.clear();
+    return KDA_OK;
+}
+
+bool aligned16(const void *p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool is_pow2_dim(int d) { return d == 4 || d == 8 || d == 16 || d == 32 || d == 64 || d == 128; }
+
+kda_status check_geom(const kda_geom *g, bool chunk_path) {
+    if (!g) return fail(KDA_ERR_NULL, "geom is NULL");
+    if (g->H <= 0) return fail(KDA_ERR_SHAPE, "H = %d must be > 0", g->H);
+    if (g->d <= 0) return fail(KDA_ERR_SHAPE, "d = %d must be > 0", g->d);
+    if (chunk_path) {
+        if (g->d != kda::kHeadDim)
+            return fail(KDA_ERR_UNSUPPORTED, "the chunk path supports d = 128 only (got %d)", g->d);
+    } else if (!is_pow2_dim(g->d)) {
+        return fail(KDA_ERR_UNSUPPORTED, "d = %d not in {4, 8, 16, 32, 64, 128}", g->d);
+    }
+    if (g->conv_k < 1 || g->conv_k > 4)
+        return fail(KDA_ERR_UNSUPPORTED, "conv_k = %d not in [1, 4]", g->conv_k);
+    if (g->act != KDA_ACT_NONE && g->act != KDA_ACT_SILU)
+        return fail(KDA_ERR_UNSUPPORTED, "act = %d is not a kda_act", g->act);
+    if (!(g->l2_eps >= 0.0f)) return fail(KDA_ERR_SHAPE, "l2_eps must be >= 0");
+    if ((long)g->H * g->d > (1L << 24)) return fail(KDA_ERR_SHAPE, "H * d too large");
+    return KDA_OK;
+}
+
+// cu_seqlens (host copy): [0] == 0, non-decreasing, last == total_tokens.
+kda_status check_seqlens(int32_t n_seqs, int32_t total_tokens, const int32_t *cu_host, long *n_chunks) {
+    if (n_seqs <= 0) return fail(KDA_ERR_SHAPE, "n_seqs = %d must be > 0", n_seqs);
+    if (total_tokens < 0) return fail(KDA_ERR_SHAPE, "total_tokens = %d must be >= 0", total_tokens);
+    if (!cu_host) return fail(KDA_ERR_NULL, "cu_seqlens_host is NULL");
+    if (cu_host[0] != 0) return fail(KDA_ERR_SEQLENS, "cu_seqlens[0] = %d, expected 0", cu_host[0]);
+    long chunks = 0;
+    for (int32_t n = 0; n < n_seqs; ++n) {
+        if (cu_host[n + 1] < cu_host[n])
+            return fail(KDA_ERR_SEQLENS, "cu_seqlens decreases at %d (%d -> %d)", n, cu_host[n], cu_host[n + 1]);
+        chunks += (cu_host[n + 1] - cu_host[n] + kda::kChunk - 1) / kda::kChunk;
+    }
+    if (cu_host[n_seqs] != total_tokens)
+        return fail(KDA_ERR_SHAPE, "total_tokens = %d but cu_seqlens[%d] = %d", total_tokens, n_seqs,
+                    cu_host[n_seqs]);
+    if (n_chunks) *n_chunks = chunks;
+    return KDA_OK;
+}
+
+kda_status check_dtype(kda_dtype t) {
+    if (t != KDA_F32 && t != KDA_BF16) return fail(KDA_ERR_DTYPE, "dtype %d is not a kda_dtype", (int)t);
+    return KDA_OK;
+}
+
+struct Ptr {
+    const void *p;
+    const char *name;
+};
+
+kda_status check_required(std::initializer_list<Ptr> ps) {
+    for (const Ptr &x : ps)
+        if (!x.p) return fail(KDA_ERR_NULL, "%s is NULL", x.name);
+    return KDA_OK;
+}
+
+kda_status check_aligned(std::initializer_list<Ptr> ps) {
+    for (const Ptr &x : ps)
+        if (x.p && !aligned16(x.p)) return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", x.name);
+    return KDA_OK;
+}
+
+// gfx950 check of the current device, cached per device ordinal.
+std::atomic<int> g_arch_ok[64];
+
+kda_status check_device() {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(KDA_ERR_UNSUPPORTED, "device ordinal %d out of range", dev);
+    int st = g_arch_ok[dev].load(std::memory_order_relaxed);
+    if (st == 0) {
+        hipDeviceProp_t prop;
+        e = hipGetDeviceProperties(&prop, dev);
+        if (e != hipSuccess) return fail(KDA_ERR_HIP, "hipGetDeviceProperties: %s", hipGetErrorString(e));
+        st = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 2;
+        g_arch_ok[dev].store(st, std::memory_order_relaxed);
+        if (st == 2) return fail(KDA_ERR_UNSUPPORTED, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+    }
+    if (st == 2) return fail(KDA_ERR_UNSUPPORTED, "device %d is not gfx950", dev);
+    return KDA_OK;
+}
+
+kda_status launched(hipError_t e, const char *what) {
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "%s launch: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+#define KDA_TRY(x)                         \
+    do {                                   \
+        kda_status _s = (x);               \
+        if (_s != KDA_OK) return _s;       \
+    } while (0)
+
+// Checks shared by the chunk entry points; fills n_chunks.
+kda_status check_chunk_common(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
+                              const int32_t *cu_dev, const int32_t *cu_host, kda_dtype in_dtype,
+                              void *workspace, size_t workspace_bytes, long *n_chunks) {
+    KDA_TRY(check_geom(geom, true));
+    KDA_TRY(check_seqlens(n_seqs, total_tokens, cu_host, n_chunks));
+    KDA_TRY(check_dtype(in_dtype));
+    if (in_dtype != KDA_BF16) return fail(KDA_ERR_UNSUPPORTED, "the chunk path takes bf16 inputs only");
+    KDA_TRY(check_required({{cu_dev, "cu_seqlens_dev"}, {workspace, "workspace"}}));
+    KDA_TRY(check_aligned({{workspace, "workspace"}}));
+    const size_t need = kda::chunk_workspace_bytes(geom->H, n_seqs, *n_chunks);
+    if (workspace_bytes < need)
+        return fail(KDA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    if ((long)n_seqs * geom->H * kda::kTilesV > 0x7fffffffL) return fail(KDA_ERR_SHAPE, "too many sequences x heads");
+    return KDA_OK;
+}
+
+kda::ChunkParams chunk_params(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens, long n_chunks,
+                              const int32_t *cu_dev, void *workspace) {
+    kda::ChunkParams p{};
+    p.T = total_tokens;
+    p.H = geom->H;
+    p.n_seqs = n_seqs;
+    p.n_chunks = (int)n_chunks;
+    p.scale = geom->scale;
+    p.cu = cu_dev;
+    kda::chunk_workspace_carve(workspace, geom->H, n_seqs, n_chunks, p);
+    return p;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *kda_status_str(kda_status s) {
+    switch (s) {
+        case KDA_OK: return "KDA_OK";
+        case KDA_ERR_NULL: return "KDA_ERR_NULL";
+        case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE";
+        case KDA_ERR_DTYPE: return "KDA_ERR_DTYPE";
+        case KDA_ERR_UNSUPPORTED: return "KDA_ERR_UNSUPPORTED";
+        case KDA_ERR_SEQLENS: return "KDA_ERR_SEQLENS";
+        case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
+        case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN";
+        case KDA_ERR_HIP: return "KDA_ERR_HIP";
+    }
+    return "KDA_ERR_UNKNOWN";
+}
+
+const char *kda_last_error_detail(void) { return g_detail.c_str(); }
+
+kda_status kda_prologue(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
+                        const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host, kda_dtype in_dtype,
+                        const void *q_raw, const void *k_raw, const void *v_raw, const float *conv_w,
+                        const float *conv_cache_in, float *conv_cache_out, const void *beta_logit,
+                        const void *gate_logit, void *q_out, void *k_out, void *v_out, float *beta_out,
+                        void *gate_out, void *stream) {
+    KDA_TRY(check_geom(geom, false));
+    KDA_TRY(check_seqlens(n_seqs, total_tokens, cu_seqlens_host, nullptr));
+    KDA_TRY(check_dtype(in_dtype));
+    KDA_TRY(check_required({{cu_seqlens_dev, "cu_seqlens_dev"}, {q_raw, "q_raw"}, {k_raw, "k_raw"},
+                            {v_raw, "v_raw"}, {conv_w, "conv_w"}, {beta_logit, "beta_logit"},
+                            {q_out, "q_out"}, {k_out, "k_out"}, {v_out, "v_out"}, {beta_out, "beta_out"}}));
+    if (gate_logit && !gate_out) return fail(KDA_ERR_NULL, "gate_out is NULL while gate_logit is given");
+    KDA_TRY(check_aligned({{q_raw, "q_raw"}, {k_raw, "k_raw"}, {v_raw, "v_raw"}, {conv_w, "conv_w"},
+                           {conv_cache_in, "conv_cache_in"}, {conv_cache_out, "conv_cache_out"},
+                           {beta_logit, "beta_logit"}, {gate_logit, "gate_logit"}, {q_out, "q_out"},
+                           {k_out, "k_out"}, {v_out, "v_out"}, {beta_out, "beta_out"}, {gate_out, "gate_out"}}));
+    KDA_TRY(check_device());
+    kda::PrologueParams p{};
+    p.T = total_tokens;
+    p.H = geom->H;
+    p.d = geom->d;
+    p.K = geom->conv_k;
+    p.act = geom->act;
+    p.n_seqs = n_seqs;
+    p.eps = geom->l2_eps;
+    p.cu = cu_seqlens_dev;
+    p.q_raw = q_raw;
+    p.k_raw = k_raw;
+    p.v_raw = v_raw;
+    p.beta_logit = beta_logit;
+    p.gate_logit = gate_logit;
+    p.conv_w = conv_w;
+    p.cache_in = geom->conv_k > 1 ? conv_cache_in : nullptr;
+    p.cache_out = geom->conv_k > 1 ? conv_cache_out : nullptr;
+    p.q_out = q_out;
+    p.k_out = k_out;
+    p.v_out = v_out;
+    p.gate_out = gate_logit ? gate_out : nullptr;
+    p.beta_out = beta_out;
+    return launched(kda::launch_prologue(p, (int)in_dtype, (hipStream_t)stream), "prologue");
+}
+
+size_t kda_chunk_workspace_bytes(const kda_geom *geom, int32_t n_seqs, const int32_t *cu_seqlens_host) {
+    if (check_geom(geom, true) != KDA_OK) return 0;
+    if (n_seqs <= 0 || !cu_seqlens_host) return 0;
+    long n_chunks = 0;
+    if (check_seqlens(n_seqs, cu_seqlens_host[n_seqs], cu_seqlens_host, &n_chunks) != KDA_OK) return 0;
+    return kda::chunk_workspace_bytes(geom->H, n_seqs, n_chunks);
+}
+
+kda_status kda_chunk_prepare(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
+                             const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host, kda_dtype in_dtype,
+                             const void *q, const void *k, const void *v, const void *log_alpha,
+                             const float *beta, void *workspace, size_t workspace_bytes, void *stream) {
+    long n_chunks = 0;
+    KDA_TRY(check_chunk_common(geom, n_seqs, total_tokens, cu_seqlens_dev, cu_seqlens_host, in_dtype, workspace,
+                               workspace_bytes, &n_chunks));
+    KDA_TRY(check_required({{q, "q"}, {k, "k"}, {v, "v"}, {log_alpha, "log_alpha"}, {beta, "beta"}}));
+    KDA_TRY(check_aligned({{q, "q"}, {k, "k"}, {v, "v"}, {log_alpha, "log_alpha"}, {beta, "beta"}}));
+    KDA_TRY(check_device());
+    kda::ChunkParams p = chunk_params(geom, n_seqs, total_tokens, n_chunks, cu_seqlens_dev, workspace);
+    p.q = static_cast<const uint16_t *>(q);
+    p.k = static_cast<const uint16_t *>(k);
+    p.v = static_cast<const uint16_t *>(v);
+    p.log_alpha = static_cast<const uint16_t *>(log_alpha);
+    p.beta = beta;
+    return launched(kda::launch_chunk_prepare(p, (hipStream_t)stream), "chunk prepare");
+}
+
+kda_status kda_chunk_scan(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
+                          const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host, kda_dtype in_dtype,
+                          const void *gate, const float *initial_state, float *final_state, void *out,
+                          void *workspace, size_t workspace_bytes, void *stream) {
+    long n_chunks = 0;
+    KDA_TRY(check_chunk_common(geom, n_seqs, total_tokens, cu_seqlens_dev, cu_seqlens_host, in_dtype, workspace,
+                               workspace_bytes, &n_chunks));
+    if (total_tokens > 0) KDA_TRY(check_required({{out, "out"}}));
+    KDA_TRY(check_aligned({{gate, "gate"}, {initial_state, "initial_state"}, {final_state, "final_state"},
+                           {out, "out"}}));
+    KDA_TRY(check_device());
+    kda::ChunkParams p = chunk_params(geom, n_seqs, total_tokens, n_chunks, cu_seqlens_dev, workspace);
+    p.gate = static_cast<const uint16_t *>(gate);
+    p.s0 = initial_state;
+    p.s_final = final_state;
+    p.out = static_cast<uint16_t *>(out);
+    return launched(kda::launch_chunk_scan(p, (hipStream_t)stream), "chunk scan");
+}
+
+kda_status kda_chunk_forward(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
+                             const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host, kda_dtype in_dtype,
+                             const void *q, const void *k, const void *v, const void *log_alpha,
+                             const float *beta, const void *gate, const float *initial_state, float *final_state,
+                             void *out, void *workspace, size_t workspace_bytes, void *stream) {
+    // validate everything the two stages need before launching either
+    long n_chunks = 0;
+    KDA_TRY(check_chunk_common(geom, n_seqs, total_tokens, cu_seqlens_dev, cu_seqlens_host, in_dtype, workspace,
+                               workspace_bytes, &n_chunks));
+    KDA_TRY(check_required({{q, "q"}, {k, "k"}, {v, "v"}, {log_alpha, "log_alpha"}, {beta, "beta"}}));
+    if (total_tokens > 0) KDA_TRY(check_required({{out, "out"}}));
+    KDA_TRY(check_aligned({{q, "q"}, {k, "k"}, {v, "v"}, {log_alpha, "log_alpha"}, {beta, "beta"}, {gate, "gate"},
+                           {initial_state, "initial_state"}, {final_state, "final_state"}, {out, "out"}}));
+    KDA_TRY(kda_chunk_prepare(geom, n_seqs, total_tokens, cu_seqlens_dev, cu_seqlens_host, in_dtype, q, k, v,
+                              log_alpha, beta, workspace, workspace_bytes, stream));
+    return kda_chunk_scan(geom, n_seqs, total_tokens, cu_seqlens_dev, cu_seqlens_host, in_dtype, gate,
+                          initial_state, final_state, out, workspace, workspace_bytes, stream);
+}
+
+kda_status kda_decode_step(const kda_geom *geom, int32_t batch, const int32_t *slot_idx_dev, int32_t n_slots,
+                           kda_dtype in_dtype, const void *q_raw, const void *k_raw, const void *v_raw,
+                           const float *conv_w, float *conv_cache, float *state, const void *log_alpha,
+                           const void *beta_logit, const void *gate_logit, kda_dtype out_dtype, void *out,
+                           void *stream) {
+    KDA_TRY(check_geom(geom, false));
+    if (batch <= 0) return fail(KDA_ERR_SHAPE, "batch = %d must be > 0", batch);
+    if (n_slots <= 0) return fail(KDA_ERR_SHAPE, "n_slots = %d must be > 0", n_slots);
+    if (!slot_idx_dev && batch > n_slots)
+        return fail(KDA_ERR_SHAPE, "batch = %d > n_slots = %d with identity slots", batch, n_slots);
+    if (batch > 65535 * 256 || geom->H > 65535) return fail(KDA_ERR_SHAPE, "batch or H too large for the grid");
+    KDA_TRY(check_dtype(in_dtype));
+    KDA_TRY(check_dtype(out_dtype));
+    KDA_TRY(check_required({{q_raw, "q_raw"}, {k_raw, "k_raw"}, {v_raw, "v_raw"}, {conv_w, "conv_w"},
+                            {state, "state"}, {log_alpha, "log_alpha"}, {beta_logit, "beta_logit"}, {out, "out"}}));
+    if (geom->conv_k > 1 && !conv_cache) return fail(KDA_ERR_NULL, "conv_cache is NULL with conv_k > 1");
+    KDA_TRY(check_aligned({{slot_idx_dev, "slot_idx"}, {q_raw, "q_raw"}, {k_raw, "k_raw"}, {v_raw, "v_raw"},
+                           {conv_w, "conv_w"}, {conv_cache, "conv_cache"}, {state, "state"},
+                           {log_alpha, "log_alpha"}, {beta_logit, "beta_logit"}, {gate_logit, "gate_logit"},
+                           {out, "out"}}));
+    KDA_TRY(check_device());
+    kda::DecodeParams p{};
+    p.batch = batch;
+    p.H = geom->H;
+    p.d = geom->d;
+    p.K = geom->conv_k;
+    p.act = geom->act;
+    p.n_slots = n_slots;
+    p.eps = geom->l2_eps;
+    p.scale = geom->scale;
+    p.slot_idx = slot_idx_dev;
+    p.q_raw = q_raw;
+    p.k_raw = k_raw;
+    p.v_raw = v_raw;
+    p.log_alpha = log_alpha;
+    p.beta_logit = beta_logit;
+    p.gate_logit = gate_logit;
+    p.conv_w = conv_w;
+    p.conv_cache = conv_cache;
+    p.state = state;
+    p.out = out;
+    return launched(kda::launch_decode(p, (int)in_dtype, (int)out_dtype, (hipStream_t)stream), "decode");
+}
+
+}  // extern "C"

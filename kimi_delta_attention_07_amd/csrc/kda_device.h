@@ -1,0 +1,81 @@
+// Device-side helpers for the gfx950 KDA kernels: bf16 packing, typed
+// loads/stores for the two input dtypes, wave64 reductions, gates.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+__device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint32_t(b) << 16); }
+
+// fp32 -> bf16, round to nearest even (hardware conversion on gfx950).
+__device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+__device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
+    return uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
+}
+__device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two consecutive elements of a dtype-DT array (DT 0 = fp32, 1 = bf16),
+// starting at an even element index.
+template <int DT>
+__device__ __forceinline__ float2 load2(const void *base, long idx) {
+    if constexpr (DT == 1) {
+        const uint32_t w = *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(base) + idx);
+        return make_float2(lo_bf(w), hi_bf(w));
+    } else {
+        return *reinterpret_cast<const float2 *>(static_cast<const float *>(base) + idx);
+    }
+}
+template <int DT>
+__device__ __forceinline__ void store2(void *base, long idx, float a, float b) {
+    if constexpr (DT == 1) {
+        *reinterpret_cast<uint32_t *>(static_cast<uint16_t *>(base) + idx) = pack_bf2(a, b);
+    } else {
+        *reinterpret_cast<float2 *>(static_cast<float *>(base) + idx) = make_float2(a, b);
+    }
+}
+template <int DT>
+__device__ __forceinline__ float load1(const void *base, long idx) {
+    if constexpr (DT == 1) return bf2f(static_cast<const uint16_t *>(base)[idx]);
+    else return static_cast<const float *>(base)[idx];
+}
+template <int DT>
+__device__ __forceinline__ void store1(void *base, long idx, float a) {
+    if constexpr (DT == 1) static_cast<uint16_t *>(base)[idx] = f2bf(a);
+    else static_cast<float *>(base)[idx] = a;
+}
+
+__device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + __expf(-x)); }
+__device__ __forceinline__ float activate(int act, float x) { return act == 1 ? x * sigmoidf(x) : x; }
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+__device__ __forceinline__ float group_sum(float v, int width) {
+    for (int o = width >> 1; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const u32x4 &v) { return __builtin_bit_cast(bf16x8, v); }
+
+// 8 bf16 from two groups of 4 fp32 (the MFMA output rows of two 16-row tiles).
+__device__ __forceinline__ bf16x8 pack8(const f32x4 &a, const f32x4 &b) {
+    u32x4 w;
+    w[0] = pack_bf2(a[0], a[1]);
+    w[1] = pack_bf2(a[2], a[3]);
+    w[2] = pack_bf2(b[0], b[1]);
+    w[3] = pack_bf2(b[2], b[3]);
+    return as_bf16x8(w);
+}
+
+}  // namespace kda

@@ -1,0 +1,86 @@
+// Internal interface between the C ABI (kda_abi.cpp) and the HIP kernels.
+// Parameter blocks are passed by value to the launchers; every pointer is a
+// device pointer already validated by the ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Chunk geometry of the prefill path (fixed: head dim 128, 64-token chunks).
+constexpr int kChunk = 64;
+constexpr int kHeadDim = 128;
+constexpr int kTileV = 16;                       // value columns per scan wave
+constexpr int kTilesV = kHeadDim / kTileV;       // 8 scan waves per (sequence, head)
+
+// Per-(chunk, head) record written by the prepare stage, read by the scan.
+// All operands are stored as MFMA fragments (64 lanes x 16 B each) so both
+// stages move them with whole-wave, fully coalesced 16-byte accesses.
+//   W   16 fragments (tokens m 0..3 x channel k-step s 0..3): -W = -T beta (K e^G)
+//   Qg  16 fragments (m x s):                                  Q e^G
+//   Kg  16 fragments (channel tile 0..7 x token k-step 0..1):  (K e^{G_L - G})^T
+//   P    8 fragments (m x token k-step 0..1):                  tril(Q e^G (K e^-G)^T)
+//   U   32 fragments of 64 x 4 bf16 (value tile 0..7 x m):     T beta V
+//   gL  128 fp32:                                               e^{G_L}
+constexpr size_t kFragBytes = 64 * 16;
+constexpr size_t kOffW = 0;
+constexpr size_t kOffQg = kOffW + 16 * kFragBytes;
+constexpr size_t kOffKg = kOffQg + 16 * kFragBytes;
+constexpr size_t kOffP = kOffKg + 16 * kFragBytes;
+constexpr size_t kOffU = kOffP + 8 * kFragBytes;
+constexpr size_t kOffGL = kOffU + 32 * 64 * 8;
+constexpr size_t kChunkRecordBytes = kOffGL + kHeadDim * 4;   // 74,240 B
+
+struct ChunkInfo {
+    int32_t start;  // first token (absolute, in the packed batch)
+    int32_t len;    // 1..64
+};
+
+struct PrologueParams {
+    int T, H, d, K, act, n_seqs;
+    float eps;
+    const int32_t *cu;  // [n_seqs+1]
+    const void *q_raw, *k_raw, *v_raw, *beta_logit, *gate_logit;
+    const float *conv_w, *cache_in;
+    float *cache_out;
+    void *q_out, *k_out, *v_out, *gate_out;
+    float *beta_out;
+};
+
+struct ChunkParams {
+    int T, H, n_seqs, n_chunks;
+    float scale;
+    const int32_t *cu;          // [n_seqs+1] device
+    int32_t *chunk_off;         // [n_seqs+1] in workspace
+    ChunkInfo *chunk_info;      // [n_chunks] in workspace
+    unsigned char *records;     // [n_chunks][H][kChunkRecordBytes] in workspace
+    const uint16_t *q, *k, *v, *log_alpha, *gate;   // bf16 bit patterns
+    const float *beta;
+    const float *s0;
+    float *s_final;
+    uint16_t *out;
+};
+
+struct DecodeParams {
+    int batch, H, d, K, act, n_slots;
+    float eps, scale;
+    const int32_t *slot_idx;
+    const void *q_raw, *k_raw, *v_raw, *log_alpha, *beta_logit, *gate_logit;
+    const float *conv_w;
+    float *conv_cache, *state;
+    void *out;
+};
+
+// dtype codes match kda_dtype: 0 = fp32, 1 = bf16.
+hipError_t launch_prologue(const PrologueParams &p, int dtype, hipStream_t s);
+hipError_t launch_chunk_prepare(const ChunkParams &p, hipStream_t s);
+hipError_t launch_chunk_scan(const ChunkParams &p, hipStream_t s);
+hipError_t launch_decode(const DecodeParams &p, int in_dtype, int out_dtype, hipStream_t s);
+
+// Workspace carving shared by the two chunk stages.
+size_t chunk_workspace_bytes(int H, int n_seqs, long n_chunks);
+void chunk_workspace_carve(void *ws, int H, int n_seqs, long n_chunks, ChunkParams &p);
+
+}  // namespace kda

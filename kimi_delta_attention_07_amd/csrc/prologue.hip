@@ -1,0 +1,168 @@
+// KDA prologue for gfx950: short causal depthwise conv + activation on q, k,
+// v (independently, as the implementation list of the forum post
+// "Experimental Native Vulkan Backend for Kimi K3" has it), L2 normalisation
+// of q and k with KDA_L2_EPS (kimi_k3 API docs, Constants), beta =
+// sigmoid(beta_logit) and gate = sigmoid(gate_logit).
+//
+// Memory-bound.  A wave handles one token row of one head per step (two
+// channels per lane, 256 contiguous bytes per bf16 row), so every load and
+// store of a wave is one coalesced row; tokens are independent and the L2
+// norm is a lane-group reduction with no barrier.  For head dims below 128 a
+// wave step covers 128/d tokens.  The conv reads its K-1 history rows
+// directly (they hit in L1/L2) and, before a sequence start, from the conv
+// cache; a second small kernel writes each sequence's outgoing conv cache
+// after the main kernel has read the incoming one, so the two may alias.
+#include "kda_device.h"
+#include "kda_internal.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int kSteps = 16;  // wave steps per workgroup
+
+__device__ __forceinline__ int find_seq(const int32_t *cu, int n_seqs, long t) {
+    // largest n with cu[n] <= t  (then cu[n+1] > t; empty sequences skipped)
+    int lo = 0, hi = n_seqs;  // answer in [lo, hi)
+    while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (cu[mid] <= t) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+template <int D, int DT>
+__global__ __launch_bounds__(256) void prologue_kernel(PrologueParams p) {
+    constexpr int LPT = D / 2;                  // lanes per token
+    constexpr int TPW = 64 / LPT;               // tokens per wave step
+    const int h = blockIdx.y;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int sub = lane / LPT;
+    const int c0 = 2 * (lane % LPT);
+    const int C = p.H * D;
+    const int Km1 = p.K - 1;
+
+    // this lane's conv taps: [stream][channel pair][tap]
+    float w[3][2][4];
+#pragma unroll
+    for (int X = 0; X < 3; ++X)
+#pragma unroll
+        for (int e = 0; e < 2; ++e)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                w[X][e][j] = j < p.K ? p.conv_w[((long)X * C + h * D + c0 + e) * p.K + j] : 0.0f;
+
+    const long tok_base = (long)blockIdx.x * (4 * TPW * kSteps);
+    for (int step = 0; step < kSteps; ++step) {
+        const long t = tok_base + (long)(step * 4 + wave) * TPW + sub;
+        const bool valid = t < p.T;
+        float x[3][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
+        if (valid) {
+            const int n = find_seq(p.cu, p.n_seqs, t);
+            const long start = p.cu[n];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (j < p.K) {
+                    const long tau = t - Km1 + j;
+#pragma unroll
+                    for (int X = 0; X < 3; ++X) {
+                        const void *raw = X == 0 ? p.q_raw : (X == 1 ? p.k_raw : p.v_raw);
+                        float2 v;
+                        if (tau >= start) {
+                            v = load2<DT>(raw, (tau * p.H + h) * D + c0);
+                        } else if (p.cache_in) {
+                            const float *cp = p.cache_in +
+                                (((long)n * 3 + X) * Km1 + (Km1 - (start - tau))) * C + h * D + c0;
+                            v = *reinterpret_cast<const float2 *>(cp);
+                        } else {
+                            v = make_float2(0.f, 0.f);
+                        }
+                        x[X][0] += w[X][0][j] * v.x;
+                        x[X][1] += w[X][1][j] * v.y;
+                    }
+                }
+            }
+#pragma unroll
+            for (int X = 0; X < 3; ++X) {
+                x[X][0] = activate(p.act, x[X][0]);
+                x[X][1] = activate(p.act, x[X][1]);
+            }
+        }
+        // L2 over the token's D channels (LPT lanes); every lane takes part
+        const float sq = group_sum(x[0][0] * x[0][0] + x[0][1] * x[0][1], LPT);
+        const float sk = group_sum(x[1][0] * x[1][0] + x[1][1] * x[1][1], LPT);
+        if (valid) {
+            const float rq = 1.0f / sqrtf(sq + p.eps), rk = 1.0f / sqrtf(sk + p.eps);
+            const long o = (t * p.H + h) * D + c0;
+            store2<DT>(p.q_out, o, x[0][0] * rq, x[0][1] * rq);
+            store2<DT>(p.k_out, o, x[1][0] * rk, x[1][1] * rk);
+            store2<DT>(p.v_out, o, x[2][0], x[2][1]);
+            if (p.gate_logit) {
+                const float2 gl = load2<DT>(p.gate_logit, o);
+                store2<DT>(p.gate_out, o, sigmoidf(gl.x), sigmoidf(gl.y));
+            }
+            if (c0 == 0) p.beta_out[t * p.H + h] = sigmoidf(load1<DT>(p.beta_logit, t * p.H + h));
+        }
+    }
+}
+
+// Outgoing conv cache: the last K-1 raw inputs of each sequence, reaching
+// into the incoming cache when the sequence is shorter than K-1.  Slot j takes
+// raw token end-(K-1)+j, or incoming slot j+len; slots are visited in rising
+// order so an aliased in/out buffer is read before it is overwritten.
+template <int DT>
+__global__ __launch_bounds__(256) void conv_cache_out_kernel(PrologueParams p, int nblk) {
+    const int C = p.H * p.d;
+    const int Km1 = p.K - 1;
+    const int nx = blockIdx.x / nblk;          // n * 3 + X
+    const int ch = (blockIdx.x - nx * nblk) * 256 + threadIdx.x;
+    if (ch >= C) return;
+    const int n = nx / 3, X = nx - n * 3;
+    const long start = p.cu[n], end = p.cu[n + 1], len = end - start;
+    const void *raw = X == 0 ? p.q_raw : (X == 1 ? p.k_raw : p.v_raw);
+    for (int j = 0; j < Km1; ++j) {
+        const long tau = end - Km1 + j;
+        float v;
+        if (tau >= start) v = load1<DT>(raw, tau * C + ch);
+        else v = p.cache_in ? p.cache_in[((long)nx * Km1 + (j + len)) * C + ch] : 0.0f;
+        p.cache_out[((long)nx * Km1 + j) * C + ch] = v;
+    }
+}
+
+template <int D, int DT>
+hipError_t launch_pd(const PrologueParams &p, hipStream_t s) {
+    constexpr int TPW = 64 / (D / 2);
+    const long per_block = 4L * TPW * kSteps;
+    if (p.T > 0) {
+        dim3 grid((unsigned)((p.T + per_block - 1) / per_block), p.H);
+        hipLaunchKernelGGL((prologue_kernel<D, DT>), grid, dim3(256), 0, s, p);
+    }
+    if (p.cache_out && p.K > 1) {
+        const int nblk = (p.H * D + 255) / 256;
+        hipLaunchKernelGGL((conv_cache_out_kernel<DT>), dim3((unsigned)(nblk * 3 * p.n_seqs)),
+                           dim3(256), 0, s, p, nblk);
+    }
+    return hipGetLastError();
+}
+
+template <int DT>
+hipError_t launch_p(const PrologueParams &p, hipStream_t s) {
+    switch (p.d) {
+        case 4: return launch_pd<4, DT>(p, s);
+        case 8: return launch_pd<8, DT>(p, s);
+        case 16: return launch_pd<16, DT>(p, s);
+        case 32: return launch_pd<32, DT>(p, s);
+        case 64: return launch_pd<64, DT>(p, s);
+        case 128: return launch_pd<128, DT>(p, s);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_prologue(const PrologueParams &p, int dtype, hipStream_t s) {
+    return dtype == 1 ? launch_p<1>(p, s) : launch_p<0>(p, s);
+}
+
+}  // namespace kda

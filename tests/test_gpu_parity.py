@@ -1,0 +1,286 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on the
+same seeded inputs.
+
+Bars (from the method's stated accuracy targets):
+  fp32 decode path ........ max |gpu - oracle| <= 1e-5
+  bf16 chunked prefill .... |gpu - oracle| <= 2e-2 + 1e-2 |oracle| per element,
+                            on the output y and on the final state
+  bf16 prologue outputs ... one bf16 rounding: <= 2^-8 |oracle| + 1e-5
+Reduced sizes span several 64-token chunks and ragged tails; the full-size
+workloads run on the GPU exactly as the benchmark launches them and are
+compared on every output the oracle can afford (all heads for T=4096,
+sampled heads / sequences for T=65536 and the packed varlen batch).
+"""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs as ki
+import kimi_delta_attention_07_amd as kda
+import oracle
+from kda_testlib import (assert_bf16_rounding, assert_chunk_close, assert_fp32_close, gpu_prefill, np64,
+                         slice_heads, slice_seqs, to_dev)
+
+pytestmark = pytest.mark.gpu
+ORC = oracle.get()
+
+
+def _step_dev(step, dev="cuda"):
+    return {k: v.to(dev) for k, v in step.items()}
+
+
+def run_decode(dec, steps=None, out_dtype=torch.float32):
+    """GPU and oracle decode over the given steps; returns per-step errors."""
+    st = dec["state"].double().numpy().copy()
+    ca = dec["conv_cache"].double().numpy().copy()
+    gst, gca, cw = dec["state"].cuda(), dec["conv_cache"].cuda(), dec["conv_w"].cuda()
+    si = dec["slot_idx"]
+    gsi = si.cuda() if si is not None else None
+    errs = []
+    for step in (dec["steps"] if steps is None else steps):
+        want = ORC.decode_step(st, ca, dec["conv_w"], step, slot_idx=si)
+        s = _step_dev(step)
+        got = kda.decode_step(s["q_raw"], s["k_raw"], s["v_raw"], cw, gca, gst, s["log_alpha"], s["beta_logit"],
+                              s["gate_logit"], gsi, out_dtype=out_dtype)
+        errs.append((got, want))
+    torch.cuda.synchronize()
+    return errs, (gst, st), (gca, ca)
+
+
+# ----------------------------------------------------------------------------
+# decode
+# ----------------------------------------------------------------------------
+def test_decode_tiny_fp32():
+    """Tiny workload: B=1, T=16, H=2, d=4, K=2, fp32, zero state: 16 decode steps."""
+    dec = ki.config_decode(0)
+    errs, (gst, st), (gca, ca) = run_decode(dec)
+    for t, (got, want) in enumerate(errs):
+        assert_fp32_close(got, want, f"y step {t}")
+    assert_fp32_close(gst, st, "state")
+    assert_fp32_close(gca, ca, "conv cache", 0.0)
+    # token-by-token decode equals the oracle's prefill of the same tokens
+    ref = ORC.prefill(ki.config_prefill(0))
+    assert_fp32_close(torch.cat([g for g, _ in errs]), ref["y"], "decode vs prefill y")
+
+
+def test_decode_batched_full():
+    """256 slots x 1 token, H=32, d=128, K=4, 64 consecutive steps, state in place."""
+    dec = ki.config_decode(2)
+    errs, (gst, st), (gca, ca) = run_decode(dec)
+    worst = max(assert_fp32_close(got, want, f"y step {t}") for t, (got, want) in enumerate(errs))
+    assert_fp32_close(gst, st, "state after 64 steps")
+    assert_fp32_close(gca, ca, "conv cache after 64 steps", 0.0)
+    print(f"decode 256x64: worst |y err| {worst:.2e}")
+
+
+@pytest.mark.parametrize("d", [8, 16, 32, 64, 128])
+def test_decode_slot_map_and_dims(d):
+    dec = ki.decode_inputs(40 + d, 5, H=3, d=d, K=3, steps=3, n_slots=9, slot_perm=True, state_std=0.1)
+    before = dec["state"].clone()
+    errs, (gst, st), (gca, ca) = run_decode(dec)
+    for t, (got, want) in enumerate(errs):
+        assert_fp32_close(got, want, f"y step {t}")
+    assert_fp32_close(gst, st, "state")
+    untouched = sorted(set(range(9)) - set(dec["slot_idx"].tolist()))
+    assert torch.equal(gst.cpu()[untouched], before[untouched])
+
+
+def test_decode_bf16_output_and_no_gate():
+    dec = ki.decode_inputs(50, 4, H=2, d=128, K=4, steps=2)
+    for s in dec["steps"]:
+        s["gate_logit"] = None
+    st = dec["state"].double().numpy().copy()
+    ca = dec["conv_cache"].double().numpy().copy()
+    gst, gca, cw = dec["state"].cuda(), dec["conv_cache"].cuda(), dec["conv_w"].cuda()
+    for step in dec["steps"]:
+        want = ORC.decode_step(st, ca, dec["conv_w"], step)
+        s = {k: (v.cuda() if v is not None else None) for k, v in step.items()}
+        got = kda.decode_step(s["q_raw"], s["k_raw"], s["v_raw"], cw, gca, gst, s["log_alpha"], s["beta_logit"],
+                              None, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        assert_bf16_rounding(got, want, "bf16 decode output")
+    assert_fp32_close(gst, st, "state")
+
+
+# ----------------------------------------------------------------------------
+# prologue
+# ----------------------------------------------------------------------------
+def _gpu_prologue(inp, alias=False):
+    g = to_dev(inp)
+    cache_out = g["conv_cache"] if alias else torch.empty_like(g["conv_cache"])
+    pro = kda.prologue(g["q_raw"], g["k_raw"], g["v_raw"], g["conv_w"], g["cu_seqlens"], g["beta_logit"],
+                       g["gate_logit"], g["conv_cache"], cache_out, cu_seqlens_host=inp["cu_seqlens"])
+    torch.cuda.synchronize()
+    return pro, cache_out
+
+
+def test_prologue_tiny_fp32():
+    inp = ki.config_prefill(0)
+    ref = ORC.prologue(inp)
+    pro, cache_out = _gpu_prologue(inp)
+    for k in ("q", "k", "v", "beta", "gate"):
+        assert_fp32_close(pro[k], ref[k], f"prologue {k}")
+    assert_fp32_close(cache_out, ref["conv_cache"], "conv cache", 0.0)
+
+
+@pytest.mark.parametrize("alias", [False, True])
+def test_prologue_bf16_varlen(alias):
+    inp = ki.prefill_inputs(60, [0, 1, 2, 3, 70, 5, 129], H=4, d=128, K=4, cache_std=1.0)
+    ref = ORC.prologue(inp)
+    pro, cache_out = _gpu_prologue(inp, alias)
+    for k in ("q", "k", "v", "gate"):
+        assert_bf16_rounding(pro[k], ref[k], f"prologue {k}")
+    assert_fp32_close(pro["beta"], ref["beta"], "beta")
+    assert_fp32_close(cache_out, ref["conv_cache"], "conv cache out", 0.0)
+
+
+@pytest.mark.parametrize("d,K,dtype", [(8, 1, torch.float32), (16, 2, torch.bfloat16), (32, 3, torch.float32),
+                                       (64, 4, torch.bfloat16)])
+def test_prologue_dims(d, K, dtype):
+    inp = ki.prefill_inputs(61, [9, 0, 40], H=3, d=d, K=K, dtype=dtype, cache_std=1.0)
+    ref = ORC.prologue(inp)
+    pro, cache_out = _gpu_prologue(inp)
+    check = assert_fp32_close if dtype == torch.float32 else assert_bf16_rounding
+    for k in ("q", "k", "v", "gate"):
+        check(pro[k], ref[k], f"prologue {k}")
+    if K > 1:
+        assert_fp32_close(cache_out, ref["conv_cache"], "conv cache", 0.0)
+
+
+# ----------------------------------------------------------------------------
+# chunked prefill, reduced sizes
+# ----------------------------------------------------------------------------
+def _check_prefill(inp, res, what, scale=1.0):
+    ref = ORC.prefill(inp, scale=scale)
+    e1 = assert_chunk_close(res["y"], ref["y"], f"{what} y")
+    e2 = assert_chunk_close(res["final_state"], ref["final_state"], f"{what} final state")
+    assert_fp32_close(res["conv_cache"], ref["conv_cache"], f"{what} conv cache", 0.0)
+    return e1, e2
+
+
+def _check_chunk_isolated(inp, res, what, scale=1.0):
+    """Oracle recurrence on the GPU prologue's (bf16) outputs: isolates the chunk kernels."""
+    pro = res["pro"]
+    y, S = ORC.recurrence(pro["q"], pro["k"], pro["v"], inp["log_alpha"], pro["beta"], pro["gate"],
+                          inp["cu_seqlens"], scale, inp["initial_state"])
+    assert_chunk_close(res["y"], y, f"{what} y (isolated)")
+    assert_chunk_close(res["final_state"], S, f"{what} final state (isolated)")
+    return float(np.abs(np64(res["y"]) - y).max()), float(np.abs(np64(res["final_state"]) - S).max())
+
+
+def test_chunk_single_sequence_reduced():
+    """T=4096 workload shape cut to T=300: 4 full chunks and a 44-token tail."""
+    inp = ki.config_prefill(1, scale_T=300)
+    res = gpu_prefill(inp)
+    e = _check_prefill(inp, res, "T=300")
+    iso = _check_chunk_isolated(inp, res, "T=300")
+    print(f"T=300: end-to-end max |err| y {e[0]:.2e} S {e[1]:.2e}; chunk-only y {iso[0]:.2e} S {iso[1]:.2e}")
+
+
+def test_chunk_varlen_edges():
+    inp = ki.prefill_inputs(70, [0, 1, 63, 64, 65, 130, 0, 200], H=4, d=128, K=4, cache_std=1.0)
+    res = gpu_prefill(inp)
+    _check_prefill(inp, res, "varlen edges")
+    _check_chunk_isolated(inp, res, "varlen edges")
+    S = np64(res["final_state"])
+    for n in (0, 6):   # empty sequences pass their state through exactly
+        assert np.array_equal(S[n], inp["initial_state"][n].double().numpy())
+
+
+def test_chunk_zero_state_alias_scale():
+    inp = ki.prefill_inputs(71, [77, 150], H=2, d=128, K=4, state_std=None)
+    g = to_dev(inp)
+    pro = kda.prologue(g["q_raw"], g["k_raw"], g["v_raw"], g["conv_w"], g["cu_seqlens"], g["beta_logit"],
+                       g["gate_logit"], cu_seqlens_host=inp["cu_seqlens"])
+    scale = 128 ** -0.5
+    # initial_state None means zeros
+    y0, S0 = kda.chunk_forward(pro["q"], pro["k"], pro["v"], g["log_alpha"], pro["beta"], pro["gate"],
+                               g["cu_seqlens"], None, scale=scale, cu_seqlens_host=inp["cu_seqlens"])
+    # final_state aliasing initial_state
+    st = torch.zeros(2, 2, 128, 128, device="cuda")
+    y1, S1 = kda.chunk_forward(pro["q"], pro["k"], pro["v"], g["log_alpha"], pro["beta"], pro["gate"],
+                               g["cu_seqlens"], st, final_state=st, scale=scale, cu_seqlens_host=inp["cu_seqlens"])
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(S0, st)
+    ref = ORC.prefill(inp, scale=scale)
+    assert_chunk_close(y0, ref["y"], "scaled y")
+    assert_chunk_close(S0, ref["final_state"], "final state")
+
+
+def test_chunk_no_gate_deterministic():
+    inp = ki.prefill_inputs(72, [190], H=2, d=128, K=4)
+    g = to_dev(inp)
+    pro = kda.prologue(g["q_raw"], g["k_raw"], g["v_raw"], g["conv_w"], g["cu_seqlens"], g["beta_logit"], None,
+                       cu_seqlens_host=inp["cu_seqlens"])
+    outs = [kda.chunk_forward(pro["q"], pro["k"], pro["v"], g["log_alpha"], pro["beta"], None, g["cu_seqlens"],
+                              g["initial_state"], cu_seqlens_host=inp["cu_seqlens"]) for _ in range(2)]
+    torch.cuda.synchronize()
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    y, S = ORC.recurrence(pro["q"], pro["k"], pro["v"], inp["log_alpha"], pro["beta"], None, inp["cu_seqlens"],
+                          1.0, inp["initial_state"])
+    assert_chunk_close(outs[0][0], y, "ungated y")
+    assert_chunk_close(outs[0][1], S, "ungated S")
+
+
+def test_chunk_continuation():
+    """prefill(T) == prefill(T1) then prefill(T - T1) from its final state and conv cache."""
+    inp = ki.prefill_inputs(73, [260], H=2, d=128, K=4, cache_std=1.0)
+    whole = gpu_prefill(inp)
+    T1 = 100
+    a = dict(inp, T=T1, lengths=[T1], cu_seqlens=torch.tensor([0, T1], dtype=torch.int32))
+    b = dict(inp, T=260 - T1, lengths=[260 - T1], cu_seqlens=torch.tensor([0, 260 - T1], dtype=torch.int32))
+    for k in ("q_raw", "k_raw", "v_raw", "beta_logit", "log_alpha", "gate_logit"):
+        a[k], b[k] = inp[k][:T1].contiguous(), inp[k][T1:].contiguous()
+    ra = gpu_prefill(a)
+    b["initial_state"], b["conv_cache"] = ra["final_state"].cpu(), ra["conv_cache"].cpu()
+    rb = gpu_prefill(b)
+    ref = ORC.prefill(inp)
+    assert_chunk_close(torch.cat([ra["y"], rb["y"]]), ref["y"], "split y")
+    assert_chunk_close(rb["final_state"], ref["final_state"], "split final state")
+    assert torch.equal(rb["conv_cache"], whole["conv_cache"])
+
+
+# ----------------------------------------------------------------------------
+# full-size workloads (the benchmark's launch configuration)
+# ----------------------------------------------------------------------------
+def test_prefill_T4096_full():
+    """T=4096, H=32, d=128: every output against the oracle."""
+    inp = ki.config_prefill(1)
+    res = gpu_prefill(inp)
+    e = _check_prefill(inp, res, "T=4096")
+    print(f"T=4096 full: max |err| y {e[0]:.2e} final state {e[1]:.2e}")
+
+
+def test_prefill_varlen_full_sampled():
+    """32 packed sequences (lengths U[256, 8192]); oracle on sampled sequences x heads."""
+    inp = ki.config_prefill(3)
+    res = gpu_prefill(inp)
+    lens = inp["lengths"]
+    seqs = sorted({0, int(np.argmax(lens)), int(np.argmin(lens)), 17})
+    heads = [0, 13, 31]
+    sub = slice_heads(slice_seqs(inp, seqs), heads)
+    ref = ORC.prefill(sub)
+    cu = inp["cu_seqlens"].tolist()
+    y = torch.cat([res["y"][cu[n]:cu[n + 1]] for n in seqs])[:, heads]
+    S = res["final_state"][seqs][:, heads]
+    e1 = assert_chunk_close(y, ref["y"], "varlen y")
+    e2 = assert_chunk_close(S, ref["final_state"], "varlen final state")
+    print(f"varlen T={inp['T']}: sampled max |err| y {e1:.2e} S {e2:.2e}")
+
+
+def test_prefill_T65536_full_sampled_and_decode_tail():
+    """T=65536 with slow decay (1024 chunks); oracle on two heads; then 128
+    decode tokens from the GPU's final state and conv cache (fp32 bar)."""
+    inp = ki.config_prefill(4)
+    res = gpu_prefill(inp)
+    heads = [0, 31]
+    ref = ORC.prefill(slice_heads(inp, heads))
+    e1 = assert_chunk_close(res["y"][:, heads], ref["y"], "T=65536 y")
+    e2 = assert_chunk_close(res["final_state"][:, heads], ref["final_state"], "T=65536 final state")
+    print(f"T=65536: sampled max |err| y {e1:.2e} S {e2:.2e}")
+    dec = dict(state=res["final_state"].cpu(), conv_cache=res["conv_cache"].cpu(), conv_w=inp["conv_w"],
+               slot_idx=None, steps=inp["tail"])
+    errs, (gst, st), _ = run_decode(dec)
+    worst = max(assert_fp32_close(got, want, f"tail y step {t}") for t, (got, want) in enumerate(errs))
+    assert_fp32_close(gst, st, "tail state")
+    print(f"decode tail 128 steps: worst |y err| {worst:.2e}")
