@@ -1,0 +1,235 @@
+"""Benchmark of the KDA hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W]
+
+Headline: chunked prefill of one 4096-token sequence (H=32, dk=dv=128, conv
+kernel 4, 64-token chunks, bf16 inputs, fp32 state).  One step is the whole
+prefill path over one batch already resident in HBM: kda_prologue (short
+conv + SiLU + L2 + sigmoid gates, writing the outgoing conv cache) then
+kda_chunk_forward (kda_chunk_prepare + kda_chunk_scan) with initial and final
+fp32 state.  Two input sets alternate between steps so the 256 MB Infinity
+Cache cannot hold one step's inputs for the next.  value = prefill tokens/s.
+
+The metric's second half, decode, is measured in the same run on the batched
+decode workload (256 resident fp32 states x 1 token, 64 consecutive
+kda_decode_step calls with distinct inputs) and reported under "decode".
+
+Every kernel is timed with HIP events on the stream it is launched on; the
+roofline object is for the kernel that takes the longest, with the algorithmic
+bytes of that kernel's own inputs and outputs.  The oracle (CPU, fp64) is
+timed on the same prefill workload as "cpu_baseline".  Prints ONE JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "KDA prefill tokens/s (%MFMA peak) + decode tokens/s (%HBM BW), H=32 d=128"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
+
+H, D, K, CHUNK = 32, 128, 4, 64
+# Algorithmic bytes per token (all 32 heads, bf16 activations) of each stage's
+# compulsory inputs and outputs.
+PROLOGUE_B_PER_TOK = 3 * 8192 + 64 + 8192 + 3 * 8192 + 128 + 8192           # 65,728
+PREPARE_B_PER_TOK = 3 * 8192 + 8192 + 128 + 74240 * H // CHUNK                # 70,016
+SCAN_B_PER_TOK = 74240 * H // CHUNK + 8192 + 8192                              # 53,504
+PATH_B_PER_TOK = 5 * 8192 + 64 + 8192                                          # 49,216 (q,k,v,log-a,gate,beta in; y out)
+STATE_B = H * D * D * 4                                                        # one sequence's fp32 state
+CONV_CACHE_B = 3 * (K - 1) * H * D * 4
+FLOP_PER_TOK = 4_496_032                                                       # useful chunked-form flops (H=32)
+DECODE_B_PER_ROW = 2 * STATE_B + 2 * CONV_CACHE_B + 3 * 8192 + 8192 + 64 + 8192 + 16384   # 4,546,624
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-reps", type=int, default=3, help="timed passes of 64 decode steps")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
+    ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def prefill_sets(torch, ki, dev, n_sets=2):
+    sets = []
+    for i in range(n_sets):
+        inp = ki.prefill_inputs(1 + 100 * i, [4096], H=H, d=D, K=K)
+        g = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in inp.items()}
+        g["pro"] = dict(q=torch.empty_like(g["q_raw"]), k=torch.empty_like(g["k_raw"]), v=torch.empty_like(g["v_raw"]),
+                        beta=torch.empty(4096, H, dtype=torch.float32, device=dev),
+                        gate=torch.empty_like(g["gate_logit"]))
+        g["cache_out"] = torch.empty_like(g["conv_cache"])
+        g["y"] = torch.empty_like(g["v_raw"])
+        g["final_state"] = torch.empty_like(g["initial_state"])
+        g["cu_host"] = inp["cu_seqlens"]
+        sets.append(g)
+    return sets
+
+
+def run_prefill_step(kda, g, ws, ev=None):
+    """prologue -> chunk_prepare -> chunk_scan; ev: 4 events recorded between them."""
+    if ev:
+        ev[0].record()
+    kda.prologue(g["q_raw"], g["k_raw"], g["v_raw"], g["conv_w"], g["cu_seqlens"], g["beta_logit"], g["gate_logit"],
+                 g["conv_cache"], g["cache_out"], cu_seqlens_host=g["cu_host"], outs=g["pro"])
+    if ev:
+        ev[1].record()
+    p = g["pro"]
+    kda.chunk_prepare(p["q"], p["k"], p["v"], g["log_alpha"], p["beta"], g["cu_seqlens"], ws,
+                      cu_seqlens_host=g["cu_host"])
+    if ev:
+        ev[2].record()
+    kda.chunk_scan(p["gate"], g["cu_seqlens"], ws, g["y"], g["initial_state"], g["final_state"], H=H,
+                   cu_seqlens_host=g["cu_host"])
+    if ev:
+        ev[3].record()
+
+
+def bench_prefill(torch, kda, ki, args, dev):
+    sets = prefill_sets(torch, ki, dev)
+    ws = kda.chunk_workspace(H, D, sets[0]["cu_host"], dev)
+    for i in range(args.warmup):
+        run_prefill_step(kda, sets[i % 2], ws)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    start.record()
+    for i in range(args.steps):
+        run_prefill_step(kda, sets[i % 2], ws, evs[i])
+    stop.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    total_ms = start.elapsed_time(stop)
+    per = {"prologue": 0.0, "chunk_prepare": 0.0, "chunk_scan": 0.0}
+    for e in evs:
+        per["prologue"] += e[0].elapsed_time(e[1])
+        per["chunk_prepare"] += e[1].elapsed_time(e[2])
+        per["chunk_scan"] += e[2].elapsed_time(e[3])
+    per = {k: v / args.steps for k, v in per.items()}
+    return dict(ms_per_step=total_ms / args.steps, wall_s=wall, per_kernel_ms=per)
+
+
+def bench_decode(torch, kda, ki, args, dev):
+    dec = ki.config_decode(2)
+    state, cache, cw = dec["state"].to(dev), dec["conv_cache"].to(dev), dec["conv_w"].to(dev)
+    steps = [{k: v.to(dev) for k, v in s.items()} for s in dec["steps"]]
+    out = torch.empty(256, H, D, dtype=torch.float32, device=dev)
+
+    def one(s):
+        kda.decode_step(s["q_raw"], s["k_raw"], s["v_raw"], cw, cache, state, s["log_alpha"], s["beta_logit"],
+                        s["gate_logit"], out=out)
+
+    for s in steps[:8]:
+        one(s)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(args.decode_reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for s in steps:
+            one(s)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) / len(steps))
+    ms = sorted(times)[len(times) // 2]
+    gbs = 256 * DECODE_B_PER_ROW / (ms * 1e-3) / 1e9
+    return {"workload": "batched decode: 256 resident fp32 states x 1 token, H=32 d=128 conv 4, 64 steps",
+            "value": 256 / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "bytes_per_launch": 256 * DECODE_B_PER_ROW}}
+
+
+def copy_bandwidth(torch, dev):
+    a = torch.empty(1 << 28, dtype=torch.float32, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(5):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    ms = s.elapsed_time(e) / 5
+    return 2 * a.numel() * 4 / (ms * 1e-3) / 1e9
+
+
+def cpu_baseline(ki, seconds):
+    import oracle
+
+    orc = oracle.get()
+    inp = ki.config_prefill(1)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        orc.prefill(inp)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or reps >= 50:
+            break
+    cores = min(orc.num_threads(), H)
+    return {"value": reps * 4096 / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": f"the full T=4096 H=32 prefill workload, fp64 oracle, {reps} run(s) in {el:.1f} s "
+                      f"on {cores} OpenMP threads (heads in parallel)"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this single-GPU build "
+              "(heads and sequences are independent, so N GPUs would each run this kernel on their share).",
+              file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    import kda_inputs as ki
+    import kimi_delta_attention_07_amd as kda
+
+    kda.load()
+    dev = torch.device("cuda:0")
+    pre = bench_prefill(torch, kda, ki, args, dev)
+    ms = pre["ms_per_step"]
+    tok_s = 4096 / (ms * 1e-3)
+    per = pre["per_kernel_ms"]
+    bytes_per_launch = {"prologue": 4096 * PROLOGUE_B_PER_TOK + 2 * CONV_CACHE_B // 1 + 3 * H * D * K * 4,
+                        "chunk_prepare": 4096 * PREPARE_B_PER_TOK,
+                        "chunk_scan": 4096 * SCAN_B_PER_TOK + 2 * STATE_B}
+    dom = max(per, key=per.get)
+    ach = bytes_per_launch[dom] / (per[dom] * 1e-3) / 1e9
+    path_bytes = 4096 * PATH_B_PER_TOK + 2 * STATE_B + 2 * CONV_CACHE_B
+    res = {
+        "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "chunked prefill, 1 sequence x 4096 tokens, H=32 dk=dv=128, conv 4, chunk 64, "
+                               "bf16 inputs, fp32 initial/final state", "global_batch": 1, "seq_len": 4096,
+                   "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": dom,
+                     "bytes_per_launch": bytes_per_launch[dom]},
+        "prefill": {"per_kernel_ms": per,
+                    "mfma_frac": FLOP_PER_TOK * 4096 / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
+                    "path_hbm_frac": path_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "path_roofline_floor_us": path_bytes / (HBM_PEAK_GBS * 1e9) * 1e6},
+    }
+    if not args.no_decode:
+        res["decode"] = bench_decode(torch, kda, ki, args, dev)
+    res["copy_gbs"] = copy_bandwidth(torch, dev)
+    if not args.no_cpu:
+        res["cpu_baseline"] = cpu_baseline(ki, args.cpu_seconds)
+    print(json.dumps(res))
+
+
+if __name__ == "__main__":
+    main()

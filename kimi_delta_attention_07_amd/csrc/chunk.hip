@@ -14,17 +14,18 @@
 // start, so every product is an MFMA contraction over channels.
 //
 // Two stages:
-//  prepare  grid (chunks, heads), 256 threads.  Everything that does not
+//  prepare  grid chunks x heads (heads fastest), 256 threads.  Everything that does not
 //           depend on S: G, the exponentials, A and P (bf16 MFMA, fp32 acc),
 //           the 64x64 unit-lower-triangular inverse (fp32, LDS, blocked by
 //           16), W and U~.
 //           Results go to the workspace as ready-made MFMA fragments.
-//  scan     grid (sequences x heads x 8 value tiles), one wave each.  Walks a
-//           sequence's chunks in order; the 128 x 16 fp32 state tile stays in
-//           the wave's accumulator registers the whole time.  Per chunk:
-//           54 MFMAs (U, O, the state update) and one pass over the chunk's
-//           fragments.  Blocks are numbered so that the eight tiles of one
-//           (sequence, head) land on the same XCD and share its L2.
+//  scan     grid (sequences x heads x 8 value tiles), two waves each.  Walks
+//           a sequence's chunks in order; the 128 x 16 fp32 state tile stays
+//           in the chain wave's accumulator registers the whole time (32
+//           MFMAs per chunk on the serial path) while a second wave forms the
+//           chunk's output (22 MFMAs) one chunk behind.  Blocks are numbered
+//           so that the eight tiles of one (sequence, head) land on the same
+//           XCD and share its L2.
 //
 // MFMA used: v_mfma_f32_16x16x32_bf16.  Fragment convention (checked on the
 // device): lane l holds row (l % 16) of A / column (l % 16) of B with k
@@ -83,6 +84,12 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t *cu, int n_seqs
     if (tid == 0) chunk_off[n_seqs] = carry;
 }
 
+// Record of (chunk, head): head-major, so one head's chunks are contiguous and
+// the sequential scan of a head walks forward through memory.
+__device__ __forceinline__ unsigned char *record(const ChunkParams &p, long cid, int h) {
+    return p.records + ((long)h * p.n_chunks + cid) * (long)kChunkRecordBytes;
+}
+
 // A chunk record as the kernels may use it: the table is built on the device
 // from cu_seqlens_dev while grids are sized from the host copy; should the two
 // ever disagree, out-of-range entries become empty chunks instead of stray
@@ -125,37 +132,52 @@ __device__ __forceinline__ bf16x8 lds_frag(const unsigned char *lds, int off_byt
 
 __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsPrepare];
-    const int cid = blockIdx.x, h = blockIdx.y;
+    // heads vary fastest: concurrent blocks read adjacent heads of one chunk
+    const int h = blockIdx.x % p.H, cid = blockIdx.x / p.H;
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c16 = l & 15;
     const int H = p.H;
     const ChunkInfo ci = load_chunk(p, cid);
     const long tok0 = ci.start;
     const int len = ci.len;
-    unsigned char *rec = p.records + ((long)cid * H + h) * kChunkRecordBytes;
+    unsigned char *rec = record(p, cid, h);
 
     float *A = reinterpret_cast<float *>(lds + kOffA);
     uint16_t *Tm = reinterpret_cast<uint16_t *>(lds + kOffTm);
     float *beta_s = reinterpret_cast<float *>(lds + kOffBeta);
     float *tot = reinterpret_cast<float *>(lds + kOffTm);   // [4][128], dead before T is written
 
-    if (tid < 64) beta_s[tid] = tid < len ? p.beta[(tok0 + tid) * H + h] : 0.0f;
 
     // ---- phase 1: cumulative log decay and decayed operands ----------------
-    // wave w: tokens 16w..16w+15; lane l: channels 2l, 2l+1
+    // wave w: tokens 16w..16w+15; lane l: channels 2l, 2l+1.  All of this
+    // lane's loads (log alpha, q, k, v rows) are issued before any is used.
+    uint32_t ula[16], uq[16], uk[16], uv[16];
+#pragma unroll
+    for (int ii = 0; ii < 16; ++ii) {
+        const long o = ((tok0 + max(0, min(16 * w + ii, len - 1))) * H + h) * kHeadDim + 2 * l;
+        ula[ii] = *reinterpret_cast<const uint32_t *>(p.log_alpha + o);
+    }
+#pragma unroll
+    for (int ii = 0; ii < 16; ++ii) {
+        const long o = ((tok0 + max(0, min(16 * w + ii, len - 1))) * H + h) * kHeadDim + 2 * l;
+        uq[ii] = *reinterpret_cast<const uint32_t *>(p.q + o);
+        uk[ii] = *reinterpret_cast<const uint32_t *>(p.k + o);
+        uv[ii] = *reinterpret_cast<const uint32_t *>(p.v + o);
+    }
+    // Token indices are clamped into the chunk so that loads are unconditional
+    // (and issued together); rows past the chunk's end are zeroed afterwards.
+    if (tid < 64) {
+        const float b = p.beta[(tok0 + max(0, min(tid, len - 1))) * H + h];
+        beta_s[tid] = tid < len ? b : 0.0f;
+    }
     float2 G[16];
     {
         float2 run = make_float2(0.f, 0.f);
 #pragma unroll
         for (int ii = 0; ii < 16; ++ii) {
-            const int tk = 16 * w + ii;
-            float2 la = make_float2(0.f, 0.f);
-            if (tk < len) {
-                const uint32_t u = *reinterpret_cast<const uint32_t *>(
-                    p.log_alpha + ((tok0 + tk) * H + h) * kHeadDim + 2 * l);
-                la = make_float2(lo_bf(u), hi_bf(u));
+            if (16 * w + ii < len) {
+                run.x += lo_bf(ula[ii]);
+                run.y += hi_bf(ula[ii]);
             }
-            run.x += la.x;
-            run.y += la.y;
             G[ii] = run;
         }
         tot[w * 128 + 2 * l] = run.x;
@@ -187,13 +209,9 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
         const float gx = G[ii].x + off.x, gy = G[ii].y + off.y;
         float2 q2 = make_float2(0.f, 0.f), k2 = q2, v2 = q2;
         if (tk < len) {
-            const long o = ((tok0 + tk) * H + h) * kHeadDim + 2 * l;
-            const uint32_t uq = *reinterpret_cast<const uint32_t *>(p.q + o);
-            const uint32_t uk = *reinterpret_cast<const uint32_t *>(p.k + o);
-            const uint32_t uv = *reinterpret_cast<const uint32_t *>(p.v + o);
-            q2 = make_float2(lo_bf(uq), hi_bf(uq));
-            k2 = make_float2(lo_bf(uk), hi_bf(uk));
-            v2 = make_float2(lo_bf(uv), hi_bf(uv));
+            q2 = make_float2(lo_bf(uq[ii]), hi_bf(uq[ii]));
+            k2 = make_float2(lo_bf(uk[ii]), hi_bf(uk[ii]));
+            v2 = make_float2(lo_bf(uv[ii]), hi_bf(uv[ii]));
         }
         const float ex = __expf(gx), ey = __expf(gy);
         const float ix = __expf(-gx), iy = __expf(-gy);
@@ -406,11 +424,70 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
 // ---------------------------------------------------------------------------
 // scan
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ bf16x8 rec_frag(const unsigned char *rec, size_t off, int idx, int l) {
-    return as_bf16x8(*reinterpret_cast<const u32x4 *>(rec + off + ((size_t)idx * 64 + l) * 16));
+__device__ __forceinline__ const u32x4 *frag_ptr(const unsigned char *rec, size_t off, int idx, int l) {
+    return reinterpret_cast<const u32x4 *>(rec + off + ((size_t)idx * 64 + l) * 16);
 }
 
-__global__ __launch_bounds__(64) void scan_kernel(ChunkParams p) {
+// Operands of the state chain for one chunk and one 16-column tile.
+struct ChainOperands {
+    u32x4 W[16];    // -W fragments, index m * 4 + s
+    u32x4 Kg[16];   // (K e^{G_L - G})^T fragments, index mm * 2 + s'
+    f32x4 gl[8];    // e^{G_L} for rows 16 mm + 4 g .. + 3
+    u32x2 U[4];     // U~ tile fragments (4 bf16), index m
+};
+__device__ __forceinline__ void load_chain(ChainOperands &o, const unsigned char *rec, int l, int g, int tile) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        o.U[m] = *reinterpret_cast<const u32x2 *>(rec + kOffU + ((tile * 4 + m) * 64 + l) * 8);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o.W[i] = *frag_ptr(rec, kOffW, i, l);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o.Kg[i] = *frag_ptr(rec, kOffKg, i, l);
+#pragma unroll
+    for (int mm = 0; mm < 8; ++mm)
+        o.gl[mm] = *reinterpret_cast<const f32x4 *>(rec + kOffGL + (16 * mm + 4 * g) * 4);
+}
+
+// Operands of the output for one chunk and one tile.
+struct OutOperands {
+    u32x4 Q[16];    // Q e^G fragments, index m * 4 + s
+    u32x4 P[6];     // P fragments (m, s' <= m / 2): 0:(0,0) 1:(1,0) 2:(2,0) 3:(2,1) 4:(3,0) 5:(3,1)
+    u32x4 gate[2];  // 8 bf16 gate values of token (l >> 1) + 32 j, columns 8 (l & 1) ..
+};
+// Gate and output move in row layout: lane l owns 16 contiguous bytes (8
+// columns) of token (l >> 1) + 32 j.  Token indices are clamped so the load
+// is unconditional; rows past the chunk's end are never stored.
+__device__ __forceinline__ long row_elem(const ChunkParams &p, const ChunkInfo &ci, int tk, int h, int tile, int l) {
+    return ((long)(ci.start + max(0, min(tk, ci.len - 1))) * p.H + h) * kHeadDim + tile * kTileV + 8 * (l & 1);
+}
+__device__ __forceinline__ void load_out(OutOperands &o, const ChunkParams &p, const unsigned char *rec,
+                                         const ChunkInfo &ci, int h, int tile, int l) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o.Q[i] = *frag_ptr(rec, kOffQg, i, l);
+    const int idx[6] = {0, 2, 4, 5, 6, 7};   // fragment m * 2 + s'
+#pragma unroll
+    for (int i = 0; i < 6; ++i) o.P[i] = *frag_ptr(rec, kOffP, idx[i], l);
+    if (p.gate) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+            o.gate[j] = *reinterpret_cast<const u32x4 *>(p.gate + row_elem(p, ci, (l >> 1) + 32 * j, h, tile, l));
+    }
+}
+
+// Two waves per (sequence, head, 16-column tile), on different SIMDs:
+//   wave 0, the state chain: per chunk U = U~ - W S and
+//     S <- Diag(e^{G_L}) S + (K e^{G_L - G})^T U  (32 MFMAs); the 128 x 16
+//     fp32 state stays in its accumulator registers for the whole sequence;
+//   wave 1, the output, one chunk behind: O = (Q e^G) S + P U (22 MFMAs) and
+//     y = scale O (.) gate, with S and U of that chunk handed over through
+//     LDS as ready bf16 B-operand fragments (double-buffered).
+// Each wave loads the next chunk's operands while working on the current one.
+// One barrier per chunk keeps the two in step.  Blocks are numbered so that
+// the eight tiles of one (sequence, head) land on the same XCD.
+__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) void scan_kernel(ChunkParams p) {
+    constexpr int kOS = 20;                           // fp32 row stride of the output tile
+    __shared__ __attribute__((aligned(16))) u32x4 xfer[2][6][64];   // [slot][Sb0..3, Ub0..1][lane]
+    __shared__ __attribute__((aligned(16))) float O_lds[64 * kOS];
     const int H = p.H;
     const int total = p.n_seqs * H * kTilesV;   // a multiple of 8
     const int per_xcd = total / 8;
@@ -419,86 +496,143 @@ __global__ __launch_bounds__(64) void scan_kernel(ChunkParams p) {
     const int tile = u % kTilesV;
     const int h = (u / kTilesV) % H;
     const int n = u / (kTilesV * H);
-    const int l = threadIdx.x, g = l >> 4, c16 = l & 15;
-    const int col = tile * kTileV + c16;
-
-    // state tile S[128][16] as 8 C-layout tiles: rows 16 mm + 4 g + r
-    f32x4 S[8];
-    const long sbase = ((long)n * H + h) * kHeadDim * kHeadDim;
-#pragma unroll
-    for (int mm = 0; mm < 8; ++mm)
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-            S[mm][r] = p.s0 ? p.s0[sbase + (16 * mm + 4 * g + r) * kHeadDim + col] : 0.0f;
-
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int l = threadIdx.x & 63, g = l >> 4, c16 = l & 15;
     const int c_begin = max(0, p.chunk_off[n]), c_end = min(p.n_chunks, p.chunk_off[n + 1]);
-    for (int cid = c_begin; cid < c_end; ++cid) {
-        const unsigned char *rec = p.records + ((long)cid * H + h) * kChunkRecordBytes;
-        const ChunkInfo ci = load_chunk(p, cid);
+    const int nch = max(0, c_end - c_begin);
 
-        bf16x8 Sb[4];
-#pragma unroll
-        for (int s = 0; s < 4; ++s) Sb[s] = pack8(S[2 * s], S[2 * s + 1]);
-
-        // U = U~ + (-W) S
-        f32x4 U[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            const u32x2 uw = *reinterpret_cast<const u32x2 *>(rec + kOffU + ((tile * 4 + m) * 64 + l) * 8);
-            U[m][0] = lo_bf(uw[0]);
-            U[m][1] = hi_bf(uw[0]);
-            U[m][2] = lo_bf(uw[1]);
-            U[m][3] = hi_bf(uw[1]);
-        }
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int s = 0; s < 4; ++s) U[m] = mfma16(rec_frag(rec, kOffW, m * 4 + s, l), Sb[s], U[m]);
-
-        // O = (Q e^G) S + P U
-        f32x4 O[4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m) {
-            O[m] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int s = 0; s < 4; ++s) O[m] = mfma16(rec_frag(rec, kOffQg, m * 4 + s, l), Sb[s], O[m]);
-        }
-        bf16x8 Ub[2];
-        Ub[0] = pack8(U[0], U[1]);
-        Ub[1] = pack8(U[2], U[3]);
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int sp = 0; sp <= m / 2; ++sp) O[m] = mfma16(rec_frag(rec, kOffP, m * 2 + sp, l), Ub[sp], O[m]);
-
-        // S <- Diag(e^{G_L}) S + (K e^{G_L - G})^T U
-#pragma unroll
-        for (int mm = 0; mm < 8; ++mm) {
-            const f32x4 gl = *reinterpret_cast<const f32x4 *>(rec + kOffGL + (16 * mm + 4 * g) * 4);
-            S[mm] *= gl;
-#pragma unroll
-            for (int sp = 0; sp < 2; ++sp) S[mm] = mfma16(rec_frag(rec, kOffKg, mm * 2 + sp, l), Ub[sp], S[mm]);
-        }
-
-        // y = scale O (.) gate
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int tk = 16 * m + 4 * g + r;
-                if (tk < ci.len) {
-                    const long o = ((long)(ci.start + tk) * H + h) * kHeadDim + col;
-                    float y = p.scale * O[m][r];
-                    if (p.gate) y *= bf2f(p.gate[o]);
-                    p.out[o] = f2bf(y);
-                }
-            }
-    }
-    if (p.s_final) {
+    if (wave == 0) {
+        // ---------------- state chain ----------------
+        const int col = tile * kTileV + c16;
+        f32x4 S[8];
+        const long sbase = ((long)n * H + h) * kHeadDim * kHeadDim;
 #pragma unroll
         for (int mm = 0; mm < 8; ++mm)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) p.s_final[sbase + (16 * mm + 4 * g + r) * kHeadDim + col] = S[mm][r];
+            for (int r = 0; r < 4; ++r)
+                S[mm][r] = p.s0 ? p.s0[sbase + (16 * mm + 4 * g + r) * kHeadDim + col] : 0.0f;
+        // two chunks of operands in flight: o[0] holds even chunks, o[1] odd
+        ChainOperands o0, o1;
+        auto rec_of = [&](int i) { return (const unsigned char *)record(p, c_begin + i, h); };
+        if (nch > 0) load_chain(o0, rec_of(0), l, g, tile);
+        if (nch > 1) load_chain(o1, rec_of(1), l, g, tile);
+        auto step = [&](int i, ChainOperands &o) {
+            bf16x8 Sb[4];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) {
+                Sb[s] = pack8(S[2 * s], S[2 * s + 1]);
+                xfer[i & 1][s][l] = __builtin_bit_cast(u32x4, Sb[s]);
+            }
+            f32x4 U[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                U[m][0] = lo_bf(o.U[m][0]);
+                U[m][1] = hi_bf(o.U[m][0]);
+                U[m][2] = lo_bf(o.U[m][1]);
+                U[m][3] = hi_bf(o.U[m][1]);
+            }
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) U[m] = mfma16(as_bf16x8(o.W[m * 4 + s]), Sb[s], U[m]);
+            bf16x8 Ub[2];
+            Ub[0] = pack8(U[0], U[1]);
+            Ub[1] = pack8(U[2], U[3]);
+            xfer[i & 1][4][l] = __builtin_bit_cast(u32x4, Ub[0]);
+            xfer[i & 1][5][l] = __builtin_bit_cast(u32x4, Ub[1]);
+#pragma unroll
+            for (int mm = 0; mm < 8; ++mm) S[mm] *= o.gl[mm];
+#pragma unroll
+            for (int sp = 0; sp < 2; ++sp)
+#pragma unroll
+                for (int mm = 0; mm < 8; ++mm) S[mm] = mfma16(as_bf16x8(o.Kg[mm * 2 + sp]), Ub[sp], S[mm]);
+            if (i + 2 < nch) load_chain(o, rec_of(i + 2), l, g, tile);
+        };
+        for (int i = 0; i <= nch; i += 2) {
+            if (i < nch) step(i, o0);
+            __syncthreads();
+            if (i + 1 <= nch) {
+                if (i + 1 < nch) step(i + 1, o1);
+                __syncthreads();
+            }
+        }
+        if (p.s_final) {
+#pragma unroll
+            for (int mm = 0; mm < 8; ++mm)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) p.s_final[sbase + (16 * mm + 4 * g + r) * kHeadDim + col] = S[mm][r];
+        }
+    } else {
+        // ---------------- output, one chunk behind ----------------
+        const bool gated = p.gate != nullptr;
+        auto rec_of = [&](int i) { return (const unsigned char *)record(p, c_begin + i, h); };
+        OutOperands o0, o1;
+        if (nch > 0) load_out(o0, p, rec_of(0), load_chunk(p, c_begin), h, tile, l);
+        if (nch > 1) load_out(o1, p, rec_of(1), load_chunk(p, c_begin + 1), h, tile, l);
+        auto step = [&](int j, OutOperands &o) {
+            const ChunkInfo ci = load_chunk(p, c_begin + j);
+            bf16x8 Sb[4], Ub[2];
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Sb[s] = __builtin_bit_cast(bf16x8, xfer[j & 1][s][l]);
+            Ub[0] = __builtin_bit_cast(bf16x8, xfer[j & 1][4][l]);
+            Ub[1] = __builtin_bit_cast(bf16x8, xfer[j & 1][5][l]);
+            f32x4 O[4];
+#pragma unroll
+            for (int m = 0; m < 4; ++m) O[m] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) O[m] = mfma16(as_bf16x8(o.Q[m * 4 + s]), Sb[s], O[m]);
+            O[0] = mfma16(as_bf16x8(o.P[0]), Ub[0], O[0]);
+            O[1] = mfma16(as_bf16x8(o.P[1]), Ub[0], O[1]);
+            O[2] = mfma16(as_bf16x8(o.P[2]), Ub[0], O[2]);
+            O[3] = mfma16(as_bf16x8(o.P[4]), Ub[0], O[3]);
+            O[2] = mfma16(as_bf16x8(o.P[3]), Ub[1], O[2]);
+            O[3] = mfma16(as_bf16x8(o.P[5]), Ub[1], O[3]);
+            const u32x4 gcur[2] = {o.gate[0], o.gate[1]};
+            if (j + 2 < nch) load_out(o, p, rec_of(j + 2), load_chunk(p, c_begin + j + 2), h, tile, l);
+            // y = scale O (.) gate, transposed to row layout through this wave's LDS tile
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) O_lds[(16 * m + 4 * g + r) * kOS + c16] = O[m][r];
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_s_waitcnt(0xc07f);   // lgkmcnt(0): this wave's LDS writes are done
+            f32x4 yr[2][2];
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                const float *row = O_lds + ((l >> 1) + 32 * jj) * kOS + 8 * (l & 1);
+                yr[jj][0] = *reinterpret_cast<const f32x4 *>(row);
+                yr[jj][1] = *reinterpret_cast<const f32x4 *>(row + 4);
+            }
+            __builtin_amdgcn_s_waitcnt(0xc07f);
+            __builtin_amdgcn_wave_barrier();
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj) {
+                u32x4 yo;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    float a = p.scale * yr[jj][q >> 1][2 * (q & 1)];
+                    float bb = p.scale * yr[jj][q >> 1][2 * (q & 1) + 1];
+                    if (gated) {
+                        a *= lo_bf(gcur[jj][q]);
+                        bb *= hi_bf(gcur[jj][q]);
+                    }
+                    yo[q] = pack_bf2(a, bb);
+                }
+                const int tk = (l >> 1) + 32 * jj;
+                if (tk < ci.len) *reinterpret_cast<u32x4 *>(p.out + row_elem(p, ci, tk, h, tile, l)) = yo;
+            }
+        };
+        // iteration i handles chunk i - 1 (chunks alternate between o0 and o1)
+        for (int i = 0; i <= nch; i += 2) {
+            if (i >= 1) step(i - 1, o1);
+            __syncthreads();
+            if (i + 1 <= nch) {
+                step(i, o0);
+                __syncthreads();
+            }
+        }
     }
 }
 
@@ -525,13 +659,13 @@ hipError_t launch_chunk_prepare(const ChunkParams &p, hipStream_t s) {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p.cu, p.n_seqs, p.n_chunks, p.chunk_off,
                        p.chunk_info);
     if (p.n_chunks > 0)
-        hipLaunchKernelGGL(prepare_kernel, dim3((unsigned)p.n_chunks, (unsigned)p.H), dim3(256), 0, s, p);
+        hipLaunchKernelGGL(prepare_kernel, dim3((unsigned)((long)p.n_chunks * p.H)), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_chunk_scan(const ChunkParams &p, hipStream_t s) {
     const unsigned blocks = (unsigned)(p.n_seqs * p.H * kTilesV);
-    if (blocks > 0) hipLaunchKernelGGL(scan_kernel, dim3(blocks), dim3(64), 0, s, p);
+    if (blocks > 0) hipLaunchKernelGGL(scan_kernel, dim3(blocks), dim3(128), 0, s, p);
     return hipGetLastError();
 }
 

@@ -17,8 +17,13 @@ __device__ __forceinline__ float bf2f(uint16_t b) { return __uint_as_float(uint3
 // fp32 -> bf16, round to nearest even (hardware conversion on gfx950).
 __device__ __forceinline__ uint16_t f2bf(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+
+// two fp32 -> packed bf16x2 (one v_cvt_pk_bf16_f32, round to nearest even)
 __device__ __forceinline__ uint32_t pack_bf2(float lo, float hi) {
-    return uint32_t(f2bf(lo)) | (uint32_t(f2bf(hi)) << 16);
+    const f32x2_t v = {lo, hi};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
 }
 __device__ __forceinline__ float lo_bf(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
@@ -33,6 +38,21 @@ __device__ __forceinline__ float2 load2(const void *base, long idx) {
     } else {
         return *reinterpret_cast<const float2 *>(static_cast<const float *>(base) + idx);
     }
+}
+// Raw bits of two consecutive elements (bf16: one word in .x; fp32: .x, .y),
+// so a load can stay in flight until unpack2() at the point of use.
+template <int DT>
+__device__ __forceinline__ uint2 load_raw2(const void *base, long idx) {
+    if constexpr (DT == 1) {
+        return make_uint2(*reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(base) + idx), 0u);
+    } else {
+        return *reinterpret_cast<const uint2 *>(static_cast<const float *>(base) + idx);
+    }
+}
+template <int DT>
+__device__ __forceinline__ float2 unpack2(uint2 r) {
+    if constexpr (DT == 1) return make_float2(lo_bf(r.x), hi_bf(r.x));
+    else return make_float2(__uint_as_float(r.x), __uint_as_float(r.y));
 }
 template <int DT>
 __device__ __forceinline__ void store2(void *base, long idx, float a, float b) {
@@ -53,8 +73,28 @@ __device__ __forceinline__ void store1(void *base, long idx, float a) {
     else static_cast<float *>(base)[idx] = a;
 }
 
-__device__ __forceinline__ float sigmoidf(float x) { return 1.0f / (1.0f + __expf(-x)); }
+// Gates in the bf16 paths: hardware exp2 and reciprocal (about 1 ulp each),
+// well inside one bf16 rounding of the result.
+__device__ __forceinline__ float sigmoidf(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 __device__ __forceinline__ float activate(int act, float x) { return act == 1 ? x * sigmoidf(x) : x; }
+
+// Sum over all 64 lanes, result in every lane: DPP within 16-lane rows, then
+// the four row sums through readlane (no LDS round trips).
+template <int CTRL>
+__device__ __forceinline__ float dpp_shift(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float wave_sum(float v) {
+    v += dpp_shift<0xB1>(v);    // quad_perm [1,0,3,2]
+    v += dpp_shift<0x4E>(v);    // quad_perm [2,3,0,1]
+    v += dpp_shift<0x141>(v);   // row_half_mirror
+    v += dpp_shift<0x140>(v);   // row_mirror
+    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
+    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
+    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
+    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
+    return (r0 + r1) + (r2 + r3);
+}
 
 // Sum over aligned groups of `width` lanes (width a power of two <= 64).
 __device__ __forceinline__ float group_sum(float v, int width) {

@@ -55,7 +55,7 @@ struct ChunkParams {
     const int32_t *cu;          // [n_seqs+1] device
     int32_t *chunk_off;         // [n_seqs+1] in workspace
     ChunkInfo *chunk_info;      // [n_chunks] in workspace
-    unsigned char *records;     // [n_chunks][H][kChunkRecordBytes] in workspace
+    unsigned char *records;     // [H][n_chunks][kChunkRecordBytes] in workspace
     const uint16_t *q, *k, *v, *log_alpha, *gate;   // bf16 bit patterns
     const float *beta;
     const float *s0;
