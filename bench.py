@@ -47,6 +47,33 @@ FLOP_PER_TOK = 4_496_032                                                       #
 DECODE_B_PER_ROW = 2 * STATE_B + 2 * CONV_CACHE_B + 3 * 8192 + 8192 + 64 + 8192 + 16384   # 4,546,624
 
 
+# bench timing slot -> kernel whose counters profiles/traffic.json holds
+TRAFFIC_KERNEL = {"prologue": "prologue128_kernel<4, 1>", "chunk_prepare": "prepare_kernel",
+                  "chunk_scan": "scan_kernel", "decode": "decode_kernel<128, 1, 0>"}
+KERNEL_SOURCES = {"prologue128_kernel<4, 1>": ["prologue.hip"], "prepare_kernel": ["chunk.hip"],
+                  "scan_kernel": ["chunk.hip"], "decode_kernel<128, 1, 0>": ["decode.hip"]}
+
+
+def measured_traffic(slot):
+    """HBM bytes per launch measured by rocprofv3 (FETCH_SIZE, WRITE_SIZE, both
+    calibrated against a 1 GiB copy) and kept in profiles/traffic.json, or None
+    when that file is missing or the kernel's sources changed since."""
+    import hashlib
+
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    name = TRAFFIC_KERNEL.get(slot)
+    if not name or not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get("kernels", {}).get(name)
+    if not rec:
+        return None
+    h = hashlib.sha256()
+    for fn in KERNEL_SOURCES[name] + ["kda_device.h", "kda_internal.h"]:
+        with open(os.path.join(ROOT, "kimi_delta_attention_07_amd", "csrc", fn), "rb") as f:
+            h.update(f.read())
+    return rec["bytes_per_launch"] if h.hexdigest()[:16] == rec["src_sha"] else None
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -147,7 +174,7 @@ def bench_decode(torch, kda, ki, args, dev):
     return {"workload": "batched decode: 256 resident fp32 states x 1 token, H=32 d=128 conv 4, 64 steps",
             "value": 256 / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("decode"),
                          "bytes_per_launch": 256 * DECODE_B_PER_ROW}}
 
 
@@ -216,7 +243,7 @@ def main():
                                "bf16 inputs, fp32 initial/final state", "global_batch": 1, "seq_len": 4096,
                    "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ach / HBM_PEAK_GBS, "traffic": None, "kernel": dom,
+                     "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(dom), "kernel": dom,
                      "bytes_per_launch": bytes_per_launch[dom]},
         "prefill": {"per_kernel_ms": per,
                     "mfma_frac": FLOP_PER_TOK * 4096 / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
