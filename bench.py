@@ -4,11 +4,13 @@
 
 Headline: chunked prefill of one 4096-token sequence (H=32, dk=dv=128, conv
 kernel 4, 64-token chunks, bf16 inputs, fp32 state).  One step is the whole
-prefill path over one batch already resident in HBM: kda_prologue (short
-conv + SiLU + L2 + sigmoid gates, writing the outgoing conv cache) then
-kda_chunk_forward (kda_chunk_prepare + kda_chunk_scan) with initial and final
-fp32 state.  Two input sets alternate between steps so the 256 MB Infinity
-Cache cannot hold one step's inputs for the next.  value = prefill tokens/s.
+prefill path over one batch already resident in HBM, from raw inputs to the
+gated output, the final fp32 state and the outgoing conv cache: kda_prefill
+(kda_prefill_prepare: short conv + SiLU + L2 + sigmoid(beta) fused into the
+chunk preparation; kda_prefill_scan: state pass + sigmoid output gate).
+`--path unfused` times kda_prologue + kda_chunk_forward instead.  Two input
+sets alternate between steps so the 256 MB Infinity Cache cannot hold one
+step's inputs for the next.  value = prefill tokens/s.
 
 The metric's second half, decode, is measured in the same run on the batched
 decode workload (256 resident fp32 states x 1 token, 64 consecutive
@@ -41,6 +43,7 @@ PROLOGUE_B_PER_TOK = 3 * 8192 + 64 + 8192 + 3 * 8192 + 128 + 8192           # 65
 PREPARE_B_PER_TOK = 3 * 8192 + 8192 + 128 + 74240 * H // CHUNK                # 70,016
 SCAN_B_PER_TOK = 74240 * H // CHUNK + 8192 + 8192                              # 53,504
 PATH_B_PER_TOK = 5 * 8192 + 64 + 8192                                          # 49,216 (q,k,v,log-a,gate,beta in; y out)
+FUSED_PREPARE_B_PER_TOK = 3 * 8192 + 8192 + 64 + 74240 * H // CHUNK          # 69,952 (raw q,k,v, log-a, beta logit in; record out)
 STATE_B = H * D * D * 4                                                        # one sequence's fp32 state
 CONV_CACHE_B = 3 * (K - 1) * H * D * 4
 FLOP_PER_TOK = 4_496_032                                                       # useful chunked-form flops (H=32)
@@ -48,10 +51,12 @@ DECODE_B_PER_ROW = 2 * STATE_B + 2 * CONV_CACHE_B + 3 * 8192 + 8192 + 64 + 8192 
 
 
 # bench timing slot -> kernel whose counters profiles/traffic.json holds
-TRAFFIC_KERNEL = {"prologue": "prologue128_kernel<4, 1>", "chunk_prepare": "prepare_kernel",
-                  "chunk_scan": "scan_kernel", "decode": "decode_kernel<128, 1, 0>"}
-KERNEL_SOURCES = {"prologue128_kernel<4, 1>": ["prologue.hip"], "prepare_kernel": ["chunk.hip"],
-                  "scan_kernel": ["chunk.hip"], "decode_kernel<128, 1, 0>": ["decode.hip"]}
+TRAFFIC_KERNEL = {"prologue": "prologue128_kernel<4, 1>", "chunk_prepare": "prepare_kernel<false>",
+                  "chunk_scan": "scan_kernel", "prefill_prepare": "prepare_kernel<true>",
+                  "prefill_scan": "scan_kernel", "decode": "decode_kernel<128, 1, 0>"}
+KERNEL_SOURCES = {"prologue128_kernel<4, 1>": ["prologue.hip"], "prepare_kernel<false>": ["chunk.hip"],
+                  "prepare_kernel<true>": ["chunk.hip"], "scan_kernel": ["chunk.hip"],
+                  "decode_kernel<128, 1, 0>": ["decode.hip"]}
 
 
 def measured_traffic(slot):
@@ -83,6 +88,7 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--path", choices=("fused", "unfused"), default="fused")
     return ap.parse_args()
 
 
@@ -100,6 +106,20 @@ def prefill_sets(torch, ki, dev, n_sets=2):
         g["cu_host"] = inp["cu_seqlens"]
         sets.append(g)
     return sets
+
+
+def run_fused_step(kda, g, ws, ev=None):
+    """kda_prefill_prepare -> kda_prefill_scan; ev: 3 events recorded around them."""
+    if ev:
+        ev[0].record()
+    kda.prefill_prepare(g["q_raw"], g["k_raw"], g["v_raw"], g["conv_w"], g["log_alpha"], g["beta_logit"],
+                        g["cu_seqlens"], ws, g["conv_cache"], g["cache_out"], cu_seqlens_host=g["cu_host"])
+    if ev:
+        ev[1].record()
+    kda.prefill_scan(g["gate_logit"], g["cu_seqlens"], ws, g["y"], g["initial_state"], g["final_state"], H=H,
+                     cu_seqlens_host=g["cu_host"])
+    if ev:
+        ev[2].record()
 
 
 def run_prefill_step(kda, g, ws, ev=None):
@@ -124,25 +144,27 @@ def run_prefill_step(kda, g, ws, ev=None):
 def bench_prefill(torch, kda, ki, args, dev):
     sets = prefill_sets(torch, ki, dev)
     ws = kda.chunk_workspace(H, D, sets[0]["cu_host"], dev)
+    fused = args.path == "fused"
+    step = run_fused_step if fused else run_prefill_step
+    slots = ["prefill_prepare", "prefill_scan"] if fused else ["prologue", "chunk_prepare", "chunk_scan"]
     for i in range(args.warmup):
-        run_prefill_step(kda, sets[i % 2], ws)
+        step(kda, sets[i % 2], ws)
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(slots) + 1)] for _ in range(args.steps)]
     start, stop = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     start.record()
     for i in range(args.steps):
-        run_prefill_step(kda, sets[i % 2], ws, evs[i])
+        step(kda, sets[i % 2], ws, evs[i])
     stop.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     total_ms = start.elapsed_time(stop)
-    per = {"prologue": 0.0, "chunk_prepare": 0.0, "chunk_scan": 0.0}
+    per = {k: 0.0 for k in slots}
     for e in evs:
-        per["prologue"] += e[0].elapsed_time(e[1])
-        per["chunk_prepare"] += e[1].elapsed_time(e[2])
-        per["chunk_scan"] += e[2].elapsed_time(e[3])
+        for j, k in enumerate(slots):
+            per[k] += e[j].elapsed_time(e[j + 1])
     per = {k: v / args.steps for k, v in per.items()}
     return dict(ms_per_step=total_ms / args.steps, wall_s=wall, per_kernel_ms=per)
 
@@ -229,9 +251,11 @@ def main():
     ms = pre["ms_per_step"]
     tok_s = 4096 / (ms * 1e-3)
     per = pre["per_kernel_ms"]
-    bytes_per_launch = {"prologue": 4096 * PROLOGUE_B_PER_TOK + 2 * CONV_CACHE_B // 1 + 3 * H * D * K * 4,
+    bytes_per_launch = {"prologue": 4096 * PROLOGUE_B_PER_TOK + 2 * CONV_CACHE_B + 3 * H * D * K * 4,
                         "chunk_prepare": 4096 * PREPARE_B_PER_TOK,
-                        "chunk_scan": 4096 * SCAN_B_PER_TOK + 2 * STATE_B}
+                        "chunk_scan": 4096 * SCAN_B_PER_TOK + 2 * STATE_B,
+                        "prefill_prepare": 4096 * FUSED_PREPARE_B_PER_TOK + 2 * CONV_CACHE_B + 3 * H * D * K * 4,
+                        "prefill_scan": 4096 * SCAN_B_PER_TOK + 2 * STATE_B}
     dom = max(per, key=per.get)
     ach = bytes_per_launch[dom] / (per[dom] * 1e-3) / 1e9
     path_bytes = 4096 * PATH_B_PER_TOK + 2 * STATE_B + 2 * CONV_CACHE_B
@@ -241,7 +265,8 @@ def main():
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "chunked prefill, 1 sequence x 4096 tokens, H=32 dk=dv=128, conv 4, chunk 64, "
                                "bf16 inputs, fp32 initial/final state", "global_batch": 1, "seq_len": 4096,
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU", "path": "kda_prefill (fused)" if args.path == "fused"
+                   else "kda_prologue + kda_chunk_forward"},
         "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(dom), "kernel": dom,
                      "bytes_per_launch": bytes_per_launch[dom]},

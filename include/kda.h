@@ -19,6 +19,8 @@
  *   kda_chunk_forward   chunked prefill over packed variable-length sequences
  *                       with fp32 initial/final state (= kda_chunk_prepare
  *                       followed by kda_chunk_scan, also exported)
+ *   kda_prefill         the same prefill from raw inputs in two fused stages
+ *                       (= kda_prefill_prepare + kda_prefill_scan)
  *   kda_decode_step     one token for a batch of resident states: conv update
  *                       then recurrent step (kimi_k3 API docs, Functions:
  *                       kda_decode_token)
@@ -167,6 +169,43 @@ kda_status kda_chunk_scan(const kda_geom *geom, int32_t n_seqs, int32_t total_to
                           kda_dtype in_dtype, const void *gate, const float *initial_state,
                           float *final_state, void *out, void *workspace, size_t workspace_bytes,
                           void *stream);
+
+/*
+ * Fused prefill: the whole path from raw inputs in two stages, with no
+ * intermediate q^, k^, v^, beta or gate tensors.  kda_prefill_prepare applies
+ * the short conv + activation + L2(q, k) + sigmoid(beta) inside the chunk
+ * preparation (reading the incoming conv cache at sequence starts) and then
+ * writes the outgoing conv cache; kda_prefill_scan carries the state and
+ * applies sigmoid(gate_logit) to the output.  kda_prefill runs both.  The
+ * result equals kda_prologue followed by kda_chunk_forward, except that q^,
+ * k^, v^ are never rounded to bf16 in between.
+ *   geom: d = 128, conv_k in [1, 4]; in_dtype must be KDA_BF16;
+ *   q_raw, k_raw, v_raw [T][H][128] bf16 (pre-conv); conv_w [3][H*128][conv_k]
+ *   fp32; conv_cache_in NULL (zeros) or [n_seqs][3][conv_k-1][H*128] fp32;
+ *   conv_cache_out NULL (skip) or same shape, may alias conv_cache_in;
+ *   log_alpha [T][H][128] bf16 (same contract as kda_chunk_forward);
+ *   beta_logit [T][H] bf16; gate_logit NULL (no gate) or [T][H][128] bf16;
+ *   initial_state, final_state, out, workspace: as for kda_chunk_forward (the
+ *   workspace size is kda_chunk_workspace_bytes()).
+ */
+kda_status kda_prefill(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
+                       const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host, kda_dtype in_dtype,
+                       const void *q_raw, const void *k_raw, const void *v_raw, const float *conv_w,
+                       const float *conv_cache_in, float *conv_cache_out, const void *log_alpha,
+                       const void *beta_logit, const void *gate_logit, const float *initial_state,
+                       float *final_state, void *out, void *workspace, size_t workspace_bytes, void *stream);
+
+kda_status kda_prefill_prepare(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
+                               const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host,
+                               kda_dtype in_dtype, const void *q_raw, const void *k_raw, const void *v_raw,
+                               const float *conv_w, const float *conv_cache_in, float *conv_cache_out,
+                               const void *log_alpha, const void *beta_logit, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+kda_status kda_prefill_scan(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
+                            const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host, kda_dtype in_dtype,
+                            const void *gate_logit, const float *initial_state, float *final_state, void *out,
+                            void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * kda_decode_step: one token for each of `batch` rows, fused: conv-cache

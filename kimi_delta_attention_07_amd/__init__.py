@@ -5,6 +5,7 @@ include/kda.h); this package is its thin Python binding:
 
     prologue(...)       short conv + activation + L2(q, k) + sigmoid gates
     chunk_forward(...)  chunked prefill over packed varlen sequences
+    prefill(...)        the same from raw inputs, prologue fused into the chunk path
     decode_step(...)    one token for a batch of resident fp32 states
 
 Build the library with ``python -m kimi_delta_attention_07_amd.build``.
@@ -20,5 +21,8 @@ from ._lib import (  # noqa: F401
     chunk_workspace_bytes,
     decode_step,
     load,
+    prefill,
+    prefill_prepare,
+    prefill_scan,
     prologue,
 )

@@ -20,7 +20,8 @@ CHUNK = 64
 STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE", 4: "KDA_ERR_UNSUPPORTED",
           5: "KDA_ERR_SEQLENS", 6: "KDA_ERR_WORKSPACE", 7: "KDA_ERR_ALIGN", 8: "KDA_ERR_HIP"}
 EXPORTS = ("kda_prologue", "kda_chunk_workspace_bytes", "kda_chunk_forward", "kda_chunk_prepare",
-           "kda_chunk_scan", "kda_decode_step", "kda_status_str", "kda_last_error_detail")
+           "kda_chunk_scan", "kda_prefill", "kda_prefill_prepare", "kda_prefill_scan", "kda_decode_step",
+           "kda_status_str", "kda_last_error_detail")
 
 
 class KdaError(RuntimeError):
@@ -59,6 +60,12 @@ def load(path=LIB_PATH):
     L.kda_chunk_prepare.restype = _I
     L.kda_chunk_scan.argtypes = [G, _I, _I, _P, _P, _I] + [_P] * 5 + [ctypes.c_size_t, _P]
     L.kda_chunk_scan.restype = _I
+    L.kda_prefill.argtypes = [G, _I, _I, _P, _P, _I] + [_P] * 13 + [ctypes.c_size_t, _P]
+    L.kda_prefill.restype = _I
+    L.kda_prefill_prepare.argtypes = [G, _I, _I, _P, _P, _I] + [_P] * 9 + [ctypes.c_size_t, _P]
+    L.kda_prefill_prepare.restype = _I
+    L.kda_prefill_scan.argtypes = [G, _I, _I, _P, _P, _I] + [_P] * 5 + [ctypes.c_size_t, _P]
+    L.kda_prefill_scan.restype = _I
     L.kda_decode_step.argtypes = [G, _I, _P, _I, _I] + [_P] * 9 + [_I, _P, _P]
     L.kda_decode_step.restype = _I
     L.kda_status_str.argtypes = [_I]
@@ -174,6 +181,52 @@ def chunk_scan(gate, cu_seqlens, workspace, out, initial_state=None, final_state
     _check(load().kda_chunk_scan(ctypes.byref(g), n, T, _ptr(cu_seqlens), hptr, _dtype(out), _ptr(gate),
                                  _ptr(initial_state), _ptr(final_state), _ptr(out), _ptr(workspace),
                                  workspace.numel(), _stream(out)))
+
+
+def prefill(q_raw, k_raw, v_raw, conv_w, log_alpha, beta_logit, gate_logit, cu_seqlens, initial_state=None,
+            conv_cache_in=None, conv_cache_out=None, *, final_state=None, out=None, act="silu", eps=1e-6,
+            scale=1.0, workspace=None, cu_seqlens_host=None, want_final_state=True):
+    """Fused prefill from raw inputs (d = 128, bf16).  Returns (out, final_state)."""
+    T, H, d = q_raw.shape
+    K = conv_w.shape[2]
+    n = cu_seqlens.numel() - 1
+    hcu, hptr = _host_cu(cu_seqlens, cu_seqlens_host)
+    if workspace is None:
+        workspace = chunk_workspace(H, d, hcu, q_raw.device)
+    if out is None:
+        out = torch.empty_like(v_raw)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((n, H, d, d), dtype=torch.float32, device=q_raw.device)
+    g = geom(H, d, K, act, eps, scale)
+    _check(load().kda_prefill(ctypes.byref(g), n, T, _ptr(cu_seqlens), hptr, _dtype(q_raw), _ptr(q_raw),
+                              _ptr(k_raw), _ptr(v_raw), _ptr(conv_w), _ptr(conv_cache_in), _ptr(conv_cache_out),
+                              _ptr(log_alpha), _ptr(beta_logit), _ptr(gate_logit), _ptr(initial_state),
+                              _ptr(final_state), _ptr(out), _ptr(workspace), workspace.numel(), _stream(q_raw)))
+    return out, final_state
+
+
+def prefill_prepare(q_raw, k_raw, v_raw, conv_w, log_alpha, beta_logit, cu_seqlens, workspace, conv_cache_in=None,
+                    conv_cache_out=None, *, act="silu", eps=1e-6, cu_seqlens_host=None):
+    T, H, d = q_raw.shape
+    K = conv_w.shape[2]
+    n = cu_seqlens.numel() - 1
+    hcu, hptr = _host_cu(cu_seqlens, cu_seqlens_host)
+    g = geom(H, d, K, act, eps)
+    _check(load().kda_prefill_prepare(ctypes.byref(g), n, T, _ptr(cu_seqlens), hptr, _dtype(q_raw), _ptr(q_raw),
+                                      _ptr(k_raw), _ptr(v_raw), _ptr(conv_w), _ptr(conv_cache_in),
+                                      _ptr(conv_cache_out), _ptr(log_alpha), _ptr(beta_logit), _ptr(workspace),
+                                      workspace.numel(), _stream(q_raw)))
+
+
+def prefill_scan(gate_logit, cu_seqlens, workspace, out, initial_state=None, final_state=None, *, H, d=128,
+                 K=4, scale=1.0, cu_seqlens_host=None):
+    T = out.shape[0]
+    n = cu_seqlens.numel() - 1
+    hcu, hptr = _host_cu(cu_seqlens, cu_seqlens_host)
+    g = geom(H, d, K, scale=scale)
+    _check(load().kda_prefill_scan(ctypes.byref(g), n, T, _ptr(cu_seqlens), hptr, _dtype(out), _ptr(gate_logit),
+                                   _ptr(initial_state), _ptr(final_state), _ptr(out), _ptr(workspace),
+                                   workspace.numel(), _stream(out)))
 
 
 def decode_step(q_raw, k_raw, v_raw, conv_w, conv_cache, state, log_alpha, beta_logit, gate_logit=None,

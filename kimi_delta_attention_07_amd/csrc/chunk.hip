@@ -74,6 +74,8 @@ __global__ __launch_bounds__(256) void plan_kernel(const int32_t *cu, int n_seqs
                 ChunkInfo ci;
                 ci.start = start + kChunk * c;
                 ci.len = min(kChunk, len - kChunk * c);
+                ci.seq = n;
+                ci.first = c == 0;
                 info[excl + c] = ci;
             }
         }
@@ -96,9 +98,12 @@ __device__ __forceinline__ unsigned char *record(const ChunkParams &p, long cid,
 // memory accesses.
 __device__ __forceinline__ ChunkInfo load_chunk(const ChunkParams &p, int cid) {
     ChunkInfo ci = p.chunk_info[cid];
-    if (ci.start < 0 || ci.len < 0 || ci.len > kChunk || ci.start > p.T - ci.len) {
+    if (ci.start < 0 || ci.len < 0 || ci.len > kChunk || ci.start > p.T - ci.len || ci.seq < 0 ||
+        ci.seq >= p.n_seqs) {
         ci.start = 0;
         ci.len = 0;
+        ci.seq = 0;
+        ci.first = 0;
     }
     return ci;
 }
@@ -130,6 +135,13 @@ __device__ __forceinline__ bf16x8 lds_frag(const unsigned char *lds, int off_byt
     return as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + off_bytes));
 }
 
+// FUSED: q, k, v, beta come raw (pre-conv bf16 rows, beta logits) and this
+// kernel applies the short causal conv (K <= 4 taps, zero-padded to 4 so the
+// register window is indexed statically), the activation, the L2 norm of q
+// and k (a DPP wave reduction per token: lanes hold the token's channels) and
+// the sigmoid of beta.  The conv reads the 3 rows before the chunk from the
+// same sequence, or from the incoming conv cache at a sequence start.
+template <bool FUSED>
 __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsPrepare];
     // heads vary fastest: concurrent blocks read adjacent heads of one chunk
@@ -150,24 +162,69 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
     // ---- phase 1: cumulative log decay and decayed operands ----------------
     // wave w: tokens 16w..16w+15; lane l: channels 2l, 2l+1.  All of this
     // lane's loads (log alpha, q, k, v rows) are issued before any is used.
-    uint32_t ula[16], uq[16], uk[16], uv[16];
+    uint32_t ula[16];
 #pragma unroll
     for (int ii = 0; ii < 16; ++ii) {
         const long o = ((tok0 + max(0, min(16 * w + ii, len - 1))) * H + h) * kHeadDim + 2 * l;
         ula[ii] = *reinterpret_cast<const uint32_t *>(p.log_alpha + o);
     }
+    // unfused: the prologue's rows q^, k^, v^ of this wave's 16 tokens;
+    // fused: the raw rows of tokens 16w-3 .. 16w+15 (conv window)
+    constexpr int NR = FUSED ? 19 : 16;
+    constexpr int R0 = FUSED ? 3 : 0;
+    uint32_t uq[NR], uk[NR], uv[NR];
+    const uint16_t *sq = FUSED ? p.q_raw : p.q, *sk = FUSED ? p.k_raw : p.k, *sv = FUSED ? p.v_raw : p.v;
 #pragma unroll
-    for (int ii = 0; ii < 16; ++ii) {
-        const long o = ((tok0 + max(0, min(16 * w + ii, len - 1))) * H + h) * kHeadDim + 2 * l;
-        uq[ii] = *reinterpret_cast<const uint32_t *>(p.q + o);
-        uk[ii] = *reinterpret_cast<const uint32_t *>(p.k + o);
-        uv[ii] = *reinterpret_cast<const uint32_t *>(p.v + o);
+    for (int r = 0; r < NR; ++r) {
+        long t = tok0 + 16 * w - R0 + r;
+        t = FUSED ? (t < 0 ? 0 : (t >= p.T ? p.T - 1 : t)) : tok0 + max(0, min(16 * w + r, len - 1));
+        const long o = (t * H + h) * kHeadDim + 2 * l;
+        uq[r] = *reinterpret_cast<const uint32_t *>(sq + o);
+        uk[r] = *reinterpret_cast<const uint32_t *>(sk + o);
+        uv[r] = *reinterpret_cast<const uint32_t *>(sv + o);
     }
     // Token indices are clamped into the chunk so that loads are unconditional
     // (and issued together); rows past the chunk's end are zeroed afterwards.
     if (tid < 64) {
-        const float b = p.beta[(tok0 + max(0, min(tid, len - 1))) * H + h];
+        const long ob = (tok0 + max(0, min(tid, len - 1))) * H + h;
+        const float b = FUSED ? sigmoidf(bf2f(p.beta_logit[ob])) : p.beta[ob];
         beta_s[tid] = tid < len ? b : 0.0f;
+    }
+    // fused: conv taps (zero-padded to 4 on the old side) and, for the first
+    // chunk of a sequence, the 3 rows before it from the incoming conv cache
+    float wc[3][2][4];
+    float2 halo[3][3];
+    if constexpr (FUSED) {
+        const int C = H * kHeadDim, Km1 = p.K - 1;
+#pragma unroll
+        for (int X = 0; X < 3; ++X)
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int jj = j - (4 - p.K);
+                    wc[X][e][j] = jj >= 0 ? p.conv_w[((long)X * C + h * kHeadDim + 2 * l + e) * p.K + jj] : 0.0f;
+                }
+#pragma unroll
+        for (int r = 0; r < 3; ++r) {
+            halo[0][r] = make_float2(lo_bf(uq[r]), hi_bf(uq[r]));
+            halo[1][r] = make_float2(lo_bf(uk[r]), hi_bf(uk[r]));
+            halo[2][r] = make_float2(lo_bf(uv[r]), hi_bf(uv[r]));
+        }
+        if (w == 0 && ci.first) {   // rows before a sequence start: conv cache or zeros
+#pragma unroll
+            for (int r = 0; r < 3; ++r) {
+                const int idx = r - (3 - Km1);   // cache slot of row tok0-3+r
+#pragma unroll
+                for (int X = 0; X < 3; ++X) {
+                    float2 v = make_float2(0.f, 0.f);
+                    if (idx >= 0 && p.cache_in)
+                        v = *reinterpret_cast<const float2 *>(
+                            p.cache_in + (((long)ci.seq * 3 + X) * Km1 + idx) * C + h * kHeadDim + 2 * l);
+                    halo[X][r] = v;
+                }
+            }
+        }
     }
     float2 G[16];
     {
@@ -208,7 +265,31 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
         const int tk = 16 * w + ii;
         const float gx = G[ii].x + off.x, gy = G[ii].y + off.y;
         float2 q2 = make_float2(0.f, 0.f), k2 = q2, v2 = q2;
-        if (tk < len) {
+        if constexpr (FUSED) {
+            // conv over rows ii .. ii+3 of the window (row ii+3 is token tk)
+            float x[3][2];
+#pragma unroll
+            for (int X = 0; X < 3; ++X) {
+                const uint32_t *u = X == 0 ? uq : (X == 1 ? uk : uv);
+                float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    const int r = ii + j;
+                    const float2 v = r < 3 ? halo[X][r] : make_float2(lo_bf(u[r]), hi_bf(u[r]));
+                    a0 += wc[X][0][j] * v.x;
+                    a1 += wc[X][1][j] * v.y;
+                }
+                x[X][0] = activate(p.act, a0);
+                x[X][1] = activate(p.act, a1);
+            }
+            const float rq = __builtin_amdgcn_rsqf(wave_sum(x[0][0] * x[0][0] + x[0][1] * x[0][1]) + p.eps);
+            const float rk = __builtin_amdgcn_rsqf(wave_sum(x[1][0] * x[1][0] + x[1][1] * x[1][1]) + p.eps);
+            if (tk < len) {
+                q2 = make_float2(x[0][0] * rq, x[0][1] * rq);
+                k2 = make_float2(x[1][0] * rk, x[1][1] * rk);
+                v2 = make_float2(x[2][0], x[2][1]);
+            }
+        } else if (tk < len) {
             q2 = make_float2(lo_bf(uq[ii]), hi_bf(uq[ii]));
             k2 = make_float2(lo_bf(uk[ii]), hi_bf(uk[ii]));
             v2 = make_float2(lo_bf(uv[ii]), hi_bf(uv[ii]));
@@ -566,11 +647,21 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // ---------------- output, one chunk behind ----------------
         const bool gated = p.gate != nullptr;
         auto rec_of = [&](int i) { return (const unsigned char *)record(p, c_begin + i, h); };
+        // chunk j of this sequence covers tokens seq_start + 64 j .. (no table load per chunk:
+        // a load the gate addresses depend on would drain every prefetch before it)
+        const int seq_start = min(max(p.cu[n], 0), p.T);
+        const int seq_len = max(0, min(p.cu[n + 1], p.T) - seq_start);
+        auto chunk_of = [&](int j) {
+            ChunkInfo ci;
+            ci.len = max(0, min(kChunk, seq_len - kChunk * j));
+            ci.start = ci.len > 0 ? seq_start + kChunk * j : 0;   // empty: any in-range row
+            return ci;
+        };
         OutOperands o0, o1;
-        if (nch > 0) load_out(o0, p, rec_of(0), load_chunk(p, c_begin), h, tile, l);
-        if (nch > 1) load_out(o1, p, rec_of(1), load_chunk(p, c_begin + 1), h, tile, l);
+        if (nch > 0) load_out(o0, p, rec_of(0), chunk_of(0), h, tile, l);
+        if (nch > 1) load_out(o1, p, rec_of(1), chunk_of(1), h, tile, l);
         auto step = [&](int j, OutOperands &o) {
-            const ChunkInfo ci = load_chunk(p, c_begin + j);
+            const ChunkInfo ci = chunk_of(j);
             bf16x8 Sb[4], Ub[2];
 #pragma unroll
             for (int s = 0; s < 4; ++s) Sb[s] = __builtin_bit_cast(bf16x8, xfer[j & 1][s][l]);
@@ -590,7 +681,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             O[2] = mfma16(as_bf16x8(o.P[3]), Ub[1], O[2]);
             O[3] = mfma16(as_bf16x8(o.P[5]), Ub[1], O[3]);
             const u32x4 gcur[2] = {o.gate[0], o.gate[1]};
-            if (j + 2 < nch) load_out(o, p, rec_of(j + 2), load_chunk(p, c_begin + j + 2), h, tile, l);
+            if (j + 2 < nch) load_out(o, p, rec_of(j + 2), chunk_of(j + 2), h, tile, l);
             // y = scale O (.) gate, transposed to row layout through this wave's LDS tile
 #pragma unroll
             for (int m = 0; m < 4; ++m)
@@ -615,8 +706,9 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                     float a = p.scale * yr[jj][q >> 1][2 * (q & 1)];
                     float bb = p.scale * yr[jj][q >> 1][2 * (q & 1) + 1];
                     if (gated) {
-                        a *= lo_bf(gcur[jj][q]);
-                        bb *= hi_bf(gcur[jj][q]);
+                        const float g0 = lo_bf(gcur[jj][q]), g1 = hi_bf(gcur[jj][q]);
+                        a *= p.gate_is_logit ? sigmoidf(g0) : g0;
+                        bb *= p.gate_is_logit ? sigmoidf(g1) : g1;
                     }
                     yo[q] = pack_bf2(a, bb);
                 }
@@ -659,7 +751,15 @@ hipError_t launch_chunk_prepare(const ChunkParams &p, hipStream_t s) {
     hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p.cu, p.n_seqs, p.n_chunks, p.chunk_off,
                        p.chunk_info);
     if (p.n_chunks > 0)
-        hipLaunchKernelGGL(prepare_kernel, dim3((unsigned)((long)p.n_chunks * p.H)), dim3(256), 0, s, p);
+        hipLaunchKernelGGL(prepare_kernel<false>, dim3((unsigned)((long)p.n_chunks * p.H)), dim3(256), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_prefill_prepare(const ChunkParams &p, hipStream_t s) {
+    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p.cu, p.n_seqs, p.n_chunks, p.chunk_off,
+                       p.chunk_info);
+    if (p.n_chunks > 0)
+        hipLaunchKernelGGL(prepare_kernel<true>, dim3((unsigned)((long)p.n_chunks * p.H)), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

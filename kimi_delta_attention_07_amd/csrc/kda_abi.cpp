@@ -288,6 +288,90 @@ kda_status kda_chunk_forward(const kda_geom *geom, int32_t n_seqs, int32_t total
                           initial_state, final_state, out, workspace, workspace_bytes, stream);
 }
 
+kda_status kda_prefill_prepare(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
+                               const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host, kda_dtype in_dtype,
+                               const void *q_raw, const void *k_raw, const void *v_raw, const float *conv_w,
+                               const float *conv_cache_in, float *conv_cache_out, const void *log_alpha,
+                               const void *beta_logit, void *workspace, size_t workspace_bytes, void *stream) {
+    long n_chunks = 0;
+    KDA_TRY(check_chunk_common(geom, n_seqs, total_tokens, cu_seqlens_dev, cu_seqlens_host, in_dtype, workspace,
+                               workspace_bytes, &n_chunks));
+    KDA_TRY(check_required({{q_raw, "q_raw"}, {k_raw, "k_raw"}, {v_raw, "v_raw"}, {conv_w, "conv_w"},
+                            {log_alpha, "log_alpha"}, {beta_logit, "beta_logit"}}));
+    KDA_TRY(check_aligned({{q_raw, "q_raw"}, {k_raw, "k_raw"}, {v_raw, "v_raw"}, {conv_w, "conv_w"},
+                           {conv_cache_in, "conv_cache_in"}, {conv_cache_out, "conv_cache_out"},
+                           {log_alpha, "log_alpha"}, {beta_logit, "beta_logit"}}));
+    KDA_TRY(check_device());
+    kda::ChunkParams p = chunk_params(geom, n_seqs, total_tokens, n_chunks, cu_seqlens_dev, workspace);
+    p.K = geom->conv_k;
+    p.act = geom->act;
+    p.eps = geom->l2_eps;
+    p.q_raw = static_cast<const uint16_t *>(q_raw);
+    p.k_raw = static_cast<const uint16_t *>(k_raw);
+    p.v_raw = static_cast<const uint16_t *>(v_raw);
+    p.log_alpha = static_cast<const uint16_t *>(log_alpha);
+    p.beta_logit = static_cast<const uint16_t *>(beta_logit);
+    p.conv_w = conv_w;
+    p.cache_in = geom->conv_k > 1 ? conv_cache_in : nullptr;
+    KDA_TRY(launched(kda::launch_prefill_prepare(p, (hipStream_t)stream), "prefill prepare"));
+    // outgoing conv cache, after the prepare kernel has read the incoming one
+    kda::PrologueParams c{};
+    c.T = total_tokens;
+    c.H = geom->H;
+    c.d = geom->d;
+    c.K = geom->conv_k;
+    c.n_seqs = n_seqs;
+    c.cu = cu_seqlens_dev;
+    c.q_raw = q_raw;
+    c.k_raw = k_raw;
+    c.v_raw = v_raw;
+    c.cache_in = geom->conv_k > 1 ? conv_cache_in : nullptr;
+    c.cache_out = geom->conv_k > 1 ? conv_cache_out : nullptr;
+    return launched(kda::launch_conv_cache_out(c, (int)in_dtype, (hipStream_t)stream), "conv cache out");
+}
+
+kda_status kda_prefill_scan(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
+                            const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host, kda_dtype in_dtype,
+                            const void *gate_logit, const float *initial_state, float *final_state, void *out,
+                            void *workspace, size_t workspace_bytes, void *stream) {
+    long n_chunks = 0;
+    KDA_TRY(check_chunk_common(geom, n_seqs, total_tokens, cu_seqlens_dev, cu_seqlens_host, in_dtype, workspace,
+                               workspace_bytes, &n_chunks));
+    if (total_tokens > 0) KDA_TRY(check_required({{out, "out"}}));
+    KDA_TRY(check_aligned({{gate_logit, "gate_logit"}, {initial_state, "initial_state"},
+                           {final_state, "final_state"}, {out, "out"}}));
+    KDA_TRY(check_device());
+    kda::ChunkParams p = chunk_params(geom, n_seqs, total_tokens, n_chunks, cu_seqlens_dev, workspace);
+    p.gate = static_cast<const uint16_t *>(gate_logit);
+    p.gate_is_logit = 1;
+    p.s0 = initial_state;
+    p.s_final = final_state;
+    p.out = static_cast<uint16_t *>(out);
+    return launched(kda::launch_chunk_scan(p, (hipStream_t)stream), "prefill scan");
+}
+
+kda_status kda_prefill(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens, const int32_t *cu_seqlens_dev,
+                       const int32_t *cu_seqlens_host, kda_dtype in_dtype, const void *q_raw, const void *k_raw,
+                       const void *v_raw, const float *conv_w, const float *conv_cache_in, float *conv_cache_out,
+                       const void *log_alpha, const void *beta_logit, const void *gate_logit,
+                       const float *initial_state, float *final_state, void *out, void *workspace,
+                       size_t workspace_bytes, void *stream) {
+    // validate what both stages need before launching either
+    long n_chunks = 0;
+    KDA_TRY(check_chunk_common(geom, n_seqs, total_tokens, cu_seqlens_dev, cu_seqlens_host, in_dtype, workspace,
+                               workspace_bytes, &n_chunks));
+    KDA_TRY(check_required({{q_raw, "q_raw"}, {k_raw, "k_raw"}, {v_raw, "v_raw"}, {conv_w, "conv_w"},
+                            {log_alpha, "log_alpha"}, {beta_logit, "beta_logit"}}));
+    if (total_tokens > 0) KDA_TRY(check_required({{out, "out"}}));
+    KDA_TRY(check_aligned({{gate_logit, "gate_logit"}, {initial_state, "initial_state"},
+                           {final_state, "final_state"}, {out, "out"}}));
+    KDA_TRY(kda_prefill_prepare(geom, n_seqs, total_tokens, cu_seqlens_dev, cu_seqlens_host, in_dtype, q_raw, k_raw,
+                                v_raw, conv_w, conv_cache_in, conv_cache_out, log_alpha, beta_logit, workspace,
+                                workspace_bytes, stream));
+    return kda_prefill_scan(geom, n_seqs, total_tokens, cu_seqlens_dev, cu_seqlens_host, in_dtype, gate_logit,
+                            initial_state, final_state, out, workspace, workspace_bytes, stream);
+}
+
 kda_status kda_decode_step(const kda_geom *geom, int32_t batch, const int32_t *slot_idx_dev, int32_t n_slots,
                            kda_dtype in_dtype, const void *q_raw, const void *k_raw, const void *v_raw,
                            const float *conv_w, float *conv_cache, float *state, const void *log_alpha,

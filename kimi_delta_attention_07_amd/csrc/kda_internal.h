@@ -36,6 +36,8 @@ constexpr size_t kChunkRecordBytes = kOffGL + kHeadDim * 4;   // 74,240 B
 struct ChunkInfo {
     int32_t start;  // first token (absolute, in the packed batch)
     int32_t len;    // 1..64
+    int32_t seq;    // sequence index
+    int32_t first;  // 1 for the first chunk of its sequence
 };
 
 struct PrologueParams {
@@ -52,6 +54,13 @@ struct PrologueParams {
 struct ChunkParams {
     int T, H, n_seqs, n_chunks;
     float scale;
+    // fused prefill only: raw inputs of the short conv, read by the prepare
+    // kernel, and raw gate logits (sigmoid applied by the scan)
+    int K, act;
+    float eps;
+    const uint16_t *q_raw, *k_raw, *v_raw, *beta_logit;
+    const float *conv_w, *cache_in;
+    int gate_is_logit;
     const int32_t *cu;          // [n_seqs+1] device
     int32_t *chunk_off;         // [n_seqs+1] in workspace
     ChunkInfo *chunk_info;      // [n_chunks] in workspace
@@ -76,6 +85,8 @@ struct DecodeParams {
 // dtype codes match kda_dtype: 0 = fp32, 1 = bf16.
 hipError_t launch_prologue(const PrologueParams &p, int dtype, hipStream_t s);
 hipError_t launch_chunk_prepare(const ChunkParams &p, hipStream_t s);
+hipError_t launch_prefill_prepare(const ChunkParams &p, hipStream_t s);   // fused conv/L2/gates
+hipError_t launch_conv_cache_out(const PrologueParams &p, int dtype, hipStream_t s);
 hipError_t launch_chunk_scan(const ChunkParams &p, hipStream_t s);
 hipError_t launch_decode(const DecodeParams &p, int in_dtype, int out_dtype, hipStream_t s);
 

@@ -291,6 +291,16 @@ hipError_t launch_p(const PrologueParams &p, hipStream_t s) {
 
 }  // namespace
 
+hipError_t launch_conv_cache_out(const PrologueParams &p, int dtype, hipStream_t s) {
+    if (p.cache_out && p.K > 1) {
+        const int nblk = (p.H * p.d + 255) / 256;
+        const dim3 grid((unsigned)(nblk * 3 * p.n_seqs));
+        if (dtype == 1) hipLaunchKernelGGL((conv_cache_out_kernel<1>), grid, dim3(256), 0, s, p, nblk);
+        else hipLaunchKernelGGL((conv_cache_out_kernel<0>), grid, dim3(256), 0, s, p, nblk);
+    }
+    return hipGetLastError();
+}
+
 hipError_t launch_prologue(const PrologueParams &p, int dtype, hipStream_t s) {
     return dtype == 1 ? launch_p<1>(p, s) : launch_p<0>(p, s);
 }

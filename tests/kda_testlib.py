@@ -34,6 +34,17 @@ def gpu_prefill(inp, dev="cuda", scale=1.0, with_cache=True):
     return dict(y=y, final_state=S, conv_cache=cache_out, pro=pro)
 
 
+def gpu_prefill_fused(inp, dev="cuda", scale=1.0, alias_cache=False, gated=True):
+    """kda_prefill (fused prologue) on the GPU."""
+    g = to_dev(inp, dev)
+    cache_out = g["conv_cache"] if alias_cache else torch.empty_like(g["conv_cache"])
+    y, S = kda.prefill(g["q_raw"], g["k_raw"], g["v_raw"], g["conv_w"], g["log_alpha"], g["beta_logit"],
+                       g["gate_logit"] if gated else None, g["cu_seqlens"], g["initial_state"], g["conv_cache"],
+                       cache_out, scale=scale, cu_seqlens_host=inp["cu_seqlens"])
+    torch.cuda.synchronize()
+    return dict(y=y, final_state=S, conv_cache=cache_out)
+
+
 def np64(t):
     return t.detach().double().cpu().numpy()
 

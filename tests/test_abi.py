@@ -154,7 +154,7 @@ def test_chunk_workspace_bytes(L):
     t, hp = _cu([0, 100, 100, 228])
     n_chunks = 2 + 0 + 2
     al = lambda x: (x + 255) // 256 * 256
-    want = al(4 * 4) + al(8 * n_chunks) + n_chunks * 32 * 74240
+    want = al(4 * 4) + al(16 * n_chunks) + n_chunks * 32 * 74240
     assert L.kda_chunk_workspace_bytes(_geom(H=32), 3, hp) == want
     assert L.kda_chunk_workspace_bytes(_geom(H=32, d=64), 3, hp) == 0
     assert L.kda_chunk_workspace_bytes(None, 3, hp) == 0
@@ -184,3 +184,28 @@ def test_chunk_rejects(L):
     p = list(FAKE[:9])
     p[6] = ctypes.c_void_p(0x10002)   # initial_state misaligned
     assert chunk_forward(L, ptrs=p) == ALIGN
+
+
+def prefill(L, geom=None, dtype=1, ws=FAKE[16], ws_bytes=1 << 40, ptrs=None, cu_vals=(0, 100, 228)):
+    t, hp = _cu(list(cu_vals))
+    p = list(FAKE[:12]) if ptrs is None else ptrs
+    return L.kda_prefill(geom if geom is not None else _geom(), len(cu_vals) - 1, cu_vals[-1], FAKE[15], hp,
+                         dtype, *p, ws, ws_bytes, None)
+
+
+def test_prefill_rejects(L):
+    assert prefill(L, geom=_geom(d=64)) == UNSUP
+    assert prefill(L, geom=_geom(K=5)) == UNSUP
+    assert prefill(L, dtype=0) == UNSUP
+    assert prefill(L, ws_bytes=10) == WORKSPACE
+    assert prefill(L, cu_vals=(2, 100, 228)) == SEQLENS
+    for i, name in ((0, "q_raw"), (3, "conv_w"), (6, "log_alpha"), (7, "beta_logit"), (11, "out")):
+        p = list(FAKE[:12])
+        p[i] = None
+        assert prefill(L, ptrs=p) == NULL, name
+    p = list(FAKE[:12])
+    p[4] = ctypes.c_void_p(0x10004)   # conv_cache_in misaligned
+    assert prefill(L, ptrs=p) == ALIGN
+    p = list(FAKE[:12])
+    p[8] = ctypes.c_void_p(0x10006)   # gate_logit misaligned
+    assert prefill(L, ptrs=p) == ALIGN

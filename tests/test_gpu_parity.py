@@ -18,8 +18,8 @@ import torch
 import kda_inputs as ki
 import kimi_delta_attention_07_amd as kda
 import oracle
-from kda_testlib import (assert_bf16_rounding, assert_chunk_close, assert_fp32_close, gpu_prefill, np64,
-                         slice_heads, slice_seqs, to_dev)
+from kda_testlib import (assert_bf16_rounding, assert_chunk_close, assert_fp32_close, gpu_prefill,
+                         gpu_prefill_fused, np64, slice_heads, slice_seqs, to_dev)
 
 pytestmark = pytest.mark.gpu
 ORC = oracle.get()
@@ -238,6 +238,48 @@ def test_chunk_continuation():
     assert_chunk_close(torch.cat([ra["y"], rb["y"]]), ref["y"], "split y")
     assert_chunk_close(rb["final_state"], ref["final_state"], "split final state")
     assert torch.equal(rb["conv_cache"], whole["conv_cache"])
+
+
+# ----------------------------------------------------------------------------
+# fused prefill (prologue inside the chunk path)
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("K", [4, 2, 1])
+def test_prefill_fused_varlen_edges(K):
+    inp = ki.prefill_inputs(80 + K, [0, 1, 2, 3, 63, 64, 65, 130, 0, 200], H=4, d=128, K=K, cache_std=1.0)
+    res = gpu_prefill_fused(inp)
+    ref = ORC.prefill(inp)
+    e1 = assert_chunk_close(res["y"], ref["y"], f"fused K={K} y")
+    e2 = assert_chunk_close(res["final_state"], ref["final_state"], f"fused K={K} final state")
+    assert_fp32_close(res["conv_cache"], ref["conv_cache"], "fused conv cache", 0.0)
+    S = np64(res["final_state"])
+    for n in (0, 8):   # empty sequences pass their state through exactly
+        assert np.array_equal(S[n], inp["initial_state"][n].double().numpy())
+    print(f"fused K={K}: max |err| y {e1:.2e} S {e2:.2e}")
+
+
+def test_prefill_fused_alias_nogate_scale_and_matches_unfused():
+    inp = ki.prefill_inputs(90, [150, 77], H=2, d=128, K=4, cache_std=1.0)
+    scale = 128 ** -0.5
+    res = gpu_prefill_fused(inp, scale=scale, alias_cache=True, gated=False)
+    ref = ORC.prefill(dict(inp, gate_logit=None), scale=scale)
+    assert_chunk_close(res["y"], ref["y"], "fused ungated y")
+    assert_chunk_close(res["final_state"], ref["final_state"], "fused final state")
+    assert_fp32_close(res["conv_cache"], ref["conv_cache"], "aliased conv cache", 0.0)
+    a = gpu_prefill_fused(inp)
+    b = gpu_prefill(inp)   # unfused path on the same inputs: close (fused skips one bf16 rounding)
+    assert_chunk_close(a["y"], np64(b["y"]), "fused vs unfused y")
+    c = gpu_prefill_fused(inp)
+    assert torch.equal(a["y"], c["y"]) and torch.equal(a["final_state"], c["final_state"])
+
+
+def test_prefill_fused_T4096_full():
+    inp = ki.config_prefill(1)
+    res = gpu_prefill_fused(inp)
+    ref = ORC.prefill(inp)
+    e1 = assert_chunk_close(res["y"], ref["y"], "fused T=4096 y")
+    e2 = assert_chunk_close(res["final_state"], ref["final_state"], "fused T=4096 final state")
+    assert_fp32_close(res["conv_cache"], ref["conv_cache"], "fused T=4096 conv cache", 0.0)
+    print(f"fused T=4096 full: max |err| y {e1:.2e} S {e2:.2e}")
 
 
 # ----------------------------------------------------------------------------
