@@ -536,23 +536,32 @@ struct OutOperands {
     u32x4 gate[2];  // 8 bf16 gate values of token (l >> 1) + 32 j, columns 8 (l & 1) ..
 };
 // Gate and output move in row layout: lane l owns 16 contiguous bytes (8
-// columns) of token (l >> 1) + 32 j.  Token indices are clamped so the load
-// is unconditional; rows past the chunk's end are never stored.
-__device__ __forceinline__ long row_elem(const ChunkParams &p, const ChunkInfo &ci, int tk, int h, int tile, int l) {
-    return ((long)(ci.start + max(0, min(tk, ci.len - 1))) * p.H + h) * kHeadDim + tile * kTileV + 8 * (l & 1);
+// columns) of token (l >> 1) + 32 j of the chunk.  Both go through a buffer
+// resource that spans exactly the chunk's rows, so rows past its end load as
+// 0 and are not stored, without a branch.
+__device__ __forceinline__ uint32_t row_byte(const ChunkParams &p, int tk, int h, int tile, int l) {
+    return (uint32_t)((((long)tk * p.H + h) * kHeadDim + tile * kTileV + 8 * (l & 1)) * 2);
 }
-__device__ __forceinline__ void load_out(OutOperands &o, const ChunkParams &p, const unsigned char *rec,
-                                         const ChunkInfo &ci, int h, int tile, int l) {
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rows(const ChunkParams &p, const uint16_t *base,
+                                                             const ChunkInfo &ci) {
+    const int start = __builtin_amdgcn_readfirstlane(ci.start), len = __builtin_amdgcn_readfirstlane(ci.len);
+    return buffer_rsrc(base + (long)start * p.H * kHeadDim, (uint32_t)len * p.H * kHeadDim * 2);
+}
+// The output's operands of one chunk: fragments first (used by the MFMAs),
+// the gate apart (used last, so it can be refilled after its use).
+__device__ __forceinline__ void load_out_frags(OutOperands &o, const unsigned char *rec, int l) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) o.Q[i] = *frag_ptr(rec, kOffQg, i, l);
     const int idx[6] = {0, 2, 4, 5, 6, 7};   // fragment m * 2 + s'
 #pragma unroll
     for (int i = 0; i < 6; ++i) o.P[i] = *frag_ptr(rec, kOffP, idx[i], l);
-    if (p.gate) {
+}
+__device__ __forceinline__ void load_out_gate(OutOperands &o, const ChunkParams &p, const ChunkInfo &ci, int h,
+                                              int tile, int l) {
+    const __amdgpu_buffer_rsrc_t rs = chunk_rows(p, p.gate, ci);
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            o.gate[j] = *reinterpret_cast<const u32x4 *>(p.gate + row_elem(p, ci, (l >> 1) + 32 * j, h, tile, l));
-    }
+    for (int j = 0; j < 2; ++j)
+        o.gate[j] = __builtin_amdgcn_raw_buffer_load_b128(rs, row_byte(p, (l >> 1) + 32 * j, h, tile, l), 0, 0);
 }
 
 // Two waves per (sequence, head, 16-column tile), on different SIMDs:
@@ -562,9 +571,13 @@ __device__ __forceinline__ void load_out(OutOperands &o, const ChunkParams &p, c
 //   wave 1, the output, one chunk behind: O = (Q e^G) S + P U (22 MFMAs) and
 //     y = scale O (.) gate, with S and U of that chunk handed over through
 //     LDS as ready bf16 B-operand fragments (double-buffered).
-// Each wave loads the next chunk's operands while working on the current one.
-// One barrier per chunk keeps the two in step.  Blocks are numbered so that
-// the eight tiles of one (sequence, head) land on the same XCD.
+// Each wave keeps two chunks of operands in registers and refills a buffer
+// right after using it.  Every path issues the same loads (the refill index
+// is clamped to the last chunk, masked rows go through buffer resources), so
+// a wave waits only for the buffer it is about to use, never for all of its
+// loads.  One barrier per chunk keeps the two waves in step.  Blocks are
+// numbered so that the eight tiles of one (sequence, head) land on the same XCD.
+template <bool GATED>
 __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) void scan_kernel(ChunkParams p) {
     constexpr int kOS = 20;                           // fp32 row stride of the output tile
     __shared__ __attribute__((aligned(16))) u32x4 xfer[2][6][64];   // [slot][Sb0..3, Ub0..1][lane]
@@ -579,24 +592,44 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int n = u / (kTilesV * H);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int l = threadIdx.x & 63, g = l >> 4, c16 = l & 15;
-    const int c_begin = max(0, p.chunk_off[n]), c_end = min(p.n_chunks, p.chunk_off[n + 1]);
+    // block-uniform values live in scalar registers (buffer resources built
+    // from them need no per-lane loop)
+    const int c_begin = __builtin_amdgcn_readfirstlane(max(0, p.chunk_off[n]));
+    const int c_end = __builtin_amdgcn_readfirstlane(min(p.n_chunks, p.chunk_off[n + 1]));
     const int nch = max(0, c_end - c_begin);
+    const int col = tile * kTileV + c16;
+    const long sbase = ((long)n * H + h) * kHeadDim * kHeadDim;
+    // refills past the last chunk reload the last chunk (in bounds, unused)
+    auto rec_of = [&](int i) { return (const unsigned char *)record(p, c_begin + min(i, nch - 1), h); };
+
+    if (nch == 0) {   // empty sequence: the state passes through unchanged
+        if (wave == 0 && p.s_final) {
+#pragma unroll
+            for (int mm = 0; mm < 8; ++mm)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const long e = sbase + (16 * mm + 4 * g + r) * kHeadDim + col;
+                    p.s_final[e] = p.s0 ? p.s0[e] : 0.0f;
+                }
+        }
+        return;
+    }
 
     if (wave == 0) {
         // ---------------- state chain ----------------
-        const int col = tile * kTileV + c16;
         f32x4 S[8];
-        const long sbase = ((long)n * H + h) * kHeadDim * kHeadDim;
+        if (p.s0) {
 #pragma unroll
-        for (int mm = 0; mm < 8; ++mm)
+            for (int mm = 0; mm < 8; ++mm)
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                S[mm][r] = p.s0 ? p.s0[sbase + (16 * mm + 4 * g + r) * kHeadDim + col] : 0.0f;
-        // two chunks of operands in flight: o[0] holds even chunks, o[1] odd
+                for (int r = 0; r < 4; ++r) S[mm][r] = p.s0[sbase + (16 * mm + 4 * g + r) * kHeadDim + col];
+        } else {
+#pragma unroll
+            for (int mm = 0; mm < 8; ++mm) S[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
         ChainOperands o0, o1;
-        auto rec_of = [&](int i) { return (const unsigned char *)record(p, c_begin + i, h); };
-        if (nch > 0) load_chain(o0, rec_of(0), l, g, tile);
-        if (nch > 1) load_chain(o1, rec_of(1), l, g, tile);
+        load_chain(o0, rec_of(0), l, g, tile);
+        load_chain(o1, rec_of(1), l, g, tile);
         auto step = [&](int i, ChainOperands &o) {
             bf16x8 Sb[4];
 #pragma unroll
@@ -627,16 +660,22 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             for (int sp = 0; sp < 2; ++sp)
 #pragma unroll
                 for (int mm = 0; mm < 8; ++mm) S[mm] = mfma16(as_bf16x8(o.Kg[mm * 2 + sp]), Ub[sp], S[mm]);
-            if (i + 2 < nch) load_chain(o, rec_of(i + 2), l, g, tile);
+            load_chain(o, rec_of(i + 2), l, g, tile);
         };
-        for (int i = 0; i <= nch; i += 2) {
-            if (i < nch) step(i, o0);
+        // barriers: one after each chunk, one more while the output wave
+        // finishes the last chunk (nch + 1, as in the output wave)
+        int i = 0;
+        for (; i + 1 < nch; i += 2) {
+            step(i, o0);
             __syncthreads();
-            if (i + 1 <= nch) {
-                if (i + 1 < nch) step(i + 1, o1);
-                __syncthreads();
-            }
+            step(i + 1, o1);
+            __syncthreads();
         }
+        if (i < nch) {
+            step(i, o0);
+            __syncthreads();
+        }
+        __syncthreads();
         if (p.s_final) {
 #pragma unroll
             for (int mm = 0; mm < 8; ++mm)
@@ -645,21 +684,22 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         }
     } else {
         // ---------------- output, one chunk behind ----------------
-        const bool gated = p.gate != nullptr;
-        auto rec_of = [&](int i) { return (const unsigned char *)record(p, c_begin + i, h); };
         // chunk j of this sequence covers tokens seq_start + 64 j .. (no table load per chunk:
         // a load the gate addresses depend on would drain every prefetch before it)
-        const int seq_start = min(max(p.cu[n], 0), p.T);
-        const int seq_len = max(0, min(p.cu[n + 1], p.T) - seq_start);
+        const int seq_start = __builtin_amdgcn_readfirstlane(min(max(p.cu[n], 0), p.T));
+        const int seq_len = __builtin_amdgcn_readfirstlane(max(0, min(p.cu[n + 1], p.T) - seq_start));
         auto chunk_of = [&](int j) {
             ChunkInfo ci;
+            j = min(j, nch - 1);
             ci.len = max(0, min(kChunk, seq_len - kChunk * j));
-            ci.start = ci.len > 0 ? seq_start + kChunk * j : 0;   // empty: any in-range row
+            ci.start = ci.len > 0 ? seq_start + kChunk * j : 0;
             return ci;
         };
         OutOperands o0, o1;
-        if (nch > 0) load_out(o0, p, rec_of(0), chunk_of(0), h, tile, l);
-        if (nch > 1) load_out(o1, p, rec_of(1), chunk_of(1), h, tile, l);
+        load_out_frags(o0, rec_of(0), l);
+        if constexpr (GATED) load_out_gate(o0, p, chunk_of(0), h, tile, l);
+        load_out_frags(o1, rec_of(1), l);
+        if constexpr (GATED) load_out_gate(o1, p, chunk_of(1), h, tile, l);
         auto step = [&](int j, OutOperands &o) {
             const ChunkInfo ci = chunk_of(j);
             bf16x8 Sb[4], Ub[2];
@@ -680,8 +720,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             O[3] = mfma16(as_bf16x8(o.P[4]), Ub[0], O[3]);
             O[2] = mfma16(as_bf16x8(o.P[3]), Ub[1], O[2]);
             O[3] = mfma16(as_bf16x8(o.P[5]), Ub[1], O[3]);
-            const u32x4 gcur[2] = {o.gate[0], o.gate[1]};
-            if (j + 2 < nch) load_out(o, p, rec_of(j + 2), chunk_of(j + 2), h, tile, l);
+            load_out_frags(o, rec_of(j + 2), l);
             // y = scale O (.) gate, transposed to row layout through this wave's LDS tile
 #pragma unroll
             for (int m = 0; m < 4; ++m)
@@ -698,6 +737,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             }
             __builtin_amdgcn_s_waitcnt(0xc07f);
             __builtin_amdgcn_wave_barrier();
+            const __amdgpu_buffer_rsrc_t rs = chunk_rows(p, p.out, ci);
 #pragma unroll
             for (int jj = 0; jj < 2; ++jj) {
                 u32x4 yo;
@@ -705,25 +745,28 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                 for (int q = 0; q < 4; ++q) {
                     float a = p.scale * yr[jj][q >> 1][2 * (q & 1)];
                     float bb = p.scale * yr[jj][q >> 1][2 * (q & 1) + 1];
-                    if (gated) {
-                        const float g0 = lo_bf(gcur[jj][q]), g1 = hi_bf(gcur[jj][q]);
+                    if constexpr (GATED) {
+                        const float g0 = lo_bf(o.gate[jj][q]), g1 = hi_bf(o.gate[jj][q]);
                         a *= p.gate_is_logit ? sigmoidf(g0) : g0;
                         bb *= p.gate_is_logit ? sigmoidf(g1) : g1;
                     }
                     yo[q] = pack_bf2(a, bb);
                 }
-                const int tk = (l >> 1) + 32 * jj;
-                if (tk < ci.len) *reinterpret_cast<u32x4 *>(p.out + row_elem(p, ci, tk, h, tile, l)) = yo;
+                __builtin_amdgcn_raw_buffer_store_b128(yo, rs, row_byte(p, (l >> 1) + 32 * jj, h, tile, l), 0, 0);
             }
+            if constexpr (GATED) load_out_gate(o, p, chunk_of(j + 2), h, tile, l);
         };
-        // iteration i handles chunk i - 1 (chunks alternate between o0 and o1)
-        for (int i = 0; i <= nch; i += 2) {
-            if (i >= 1) step(i - 1, o1);
+        __syncthreads();   // chunk 0 of the chain
+        int j = 0;
+        for (; j + 1 < nch; j += 2) {
+            step(j, o0);
             __syncthreads();
-            if (i + 1 <= nch) {
-                step(i, o0);
-                __syncthreads();
-            }
+            step(j + 1, o1);
+            __syncthreads();
+        }
+        if (j < nch) {
+            step(j, o0);
+            __syncthreads();
         }
     }
 }
@@ -765,7 +808,9 @@ hipError_t launch_prefill_prepare(const ChunkParams &p, hipStream_t s) {
 
 hipError_t launch_chunk_scan(const ChunkParams &p, hipStream_t s) {
     const unsigned blocks = (unsigned)(p.n_seqs * p.H * kTilesV);
-    if (blocks > 0) hipLaunchKernelGGL(scan_kernel, dim3(blocks), dim3(128), 0, s, p);
+    if (blocks == 0) return hipGetLastError();
+    if (p.gate) hipLaunchKernelGGL(scan_kernel<true>, dim3(blocks), dim3(128), 0, s, p);
+    else hipLaunchKernelGGL(scan_kernel<false>, dim3(blocks), dim3(128), 0, s, p);
     return hipGetLastError();
 }
 

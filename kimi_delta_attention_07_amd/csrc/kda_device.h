@@ -102,6 +102,13 @@ __device__ __forceinline__ float group_sum(float v, int width) {
     return v;
 }
 
+// Raw buffer resource over `bytes` bytes from `base` (gfx9 format word):
+// offsets at or past `bytes` load as 0 and are dropped by stores, so a
+// row-masked access is issued by every lane without a branch.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void *base, uint32_t bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes, 0x00020000);
+}
+
 __device__ __forceinline__ f32x4 mfma16(const bf16x8 &a, const bf16x8 &b, const f32x4 &c) {
     return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
