@@ -97,6 +97,22 @@ __device__ __forceinline__ unsigned char *record(const ChunkParams &p, long cid,
 // ever disagree, out-of-range entries become empty chunks instead of stray
 // memory accesses.
 __device__ __forceinline__ ChunkInfo load_chunk(const ChunkParams &p, int cid) {
+    if (p.plan_in_args) {
+        // the sequence holding chunk cid: the last n with plan_off[n] <= cid
+        // (empty sequences share their offset with the next one)
+        int lo = 0, hi = p.n_seqs - 1;
+        while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;
+            if (p.plan_off[mid] <= cid) lo = mid;
+            else hi = mid - 1;
+        }
+        ChunkInfo ci;
+        ci.seq = lo;
+        ci.first = cid == p.plan_off[lo];
+        ci.start = p.plan_cu[lo] + kChunk * (cid - p.plan_off[lo]);
+        ci.len = max(0, min(kChunk, p.plan_cu[lo + 1] - ci.start));
+        return ci;
+    }
     ChunkInfo ci = p.chunk_info[cid];
     if (ci.start < 0 || ci.len < 0 || ci.len > kChunk || ci.start > p.T - ci.len || ci.seq < 0 ||
         ci.seq >= p.n_seqs) {
@@ -594,8 +610,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     const int l = threadIdx.x & 63, g = l >> 4, c16 = l & 15;
     // block-uniform values live in scalar registers (buffer resources built
     // from them need no per-lane loop)
-    const int c_begin = __builtin_amdgcn_readfirstlane(max(0, p.chunk_off[n]));
-    const int c_end = __builtin_amdgcn_readfirstlane(min(p.n_chunks, p.chunk_off[n + 1]));
+    const int off0 = p.plan_in_args ? p.plan_off[n] : p.chunk_off[n];
+    const int off1 = p.plan_in_args ? p.plan_off[n + 1] : p.chunk_off[n + 1];
+    const int c_begin = __builtin_amdgcn_readfirstlane(max(0, off0));
+    const int c_end = __builtin_amdgcn_readfirstlane(min(p.n_chunks, off1));
     const int nch = max(0, c_end - c_begin);
     const int col = tile * kTileV + c16;
     const long sbase = ((long)n * H + h) * kHeadDim * kHeadDim;
@@ -686,8 +704,10 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         // ---------------- output, one chunk behind ----------------
         // chunk j of this sequence covers tokens seq_start + 64 j .. (no table load per chunk:
         // a load the gate addresses depend on would drain every prefetch before it)
-        const int seq_start = __builtin_amdgcn_readfirstlane(min(max(p.cu[n], 0), p.T));
-        const int seq_len = __builtin_amdgcn_readfirstlane(max(0, min(p.cu[n + 1], p.T) - seq_start));
+        const int cu0 = p.plan_in_args ? p.plan_cu[n] : p.cu[n];
+        const int cu1 = p.plan_in_args ? p.plan_cu[n + 1] : p.cu[n + 1];
+        const int seq_start = __builtin_amdgcn_readfirstlane(min(max(cu0, 0), p.T));
+        const int seq_len = __builtin_amdgcn_readfirstlane(max(0, min(cu1, p.T) - seq_start));
         auto chunk_of = [&](int j) {
             ChunkInfo ci;
             j = min(j, nch - 1);
@@ -791,16 +811,18 @@ void chunk_workspace_carve(void *ws, int H, int n_seqs, long n_chunks, ChunkPara
 }
 
 hipError_t launch_chunk_prepare(const ChunkParams &p, hipStream_t s) {
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p.cu, p.n_seqs, p.n_chunks, p.chunk_off,
-                       p.chunk_info);
+    if (!p.plan_in_args)
+        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p.cu, p.n_seqs, p.n_chunks, p.chunk_off,
+                           p.chunk_info);
     if (p.n_chunks > 0)
         hipLaunchKernelGGL(prepare_kernel<false>, dim3((unsigned)((long)p.n_chunks * p.H)), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
 hipError_t launch_prefill_prepare(const ChunkParams &p, hipStream_t s) {
-    hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p.cu, p.n_seqs, p.n_chunks, p.chunk_off,
-                       p.chunk_info);
+    if (!p.plan_in_args)
+        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p.cu, p.n_seqs, p.n_chunks, p.chunk_off,
+                           p.chunk_info);
     if (p.n_chunks > 0)
         hipLaunchKernelGGL(prepare_kernel<true>, dim3((unsigned)((long)p.n_chunks * p.H)), dim3(256), 0, s, p);
     return hipGetLastError();

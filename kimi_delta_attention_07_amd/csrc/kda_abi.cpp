@@ -147,7 +147,7 @@ kda_status check_chunk_common(const kda_geom *geom, int32_t n_seqs, int32_t tota
 }
 
 kda::ChunkParams chunk_params(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens, long n_chunks,
-                              const int32_t *cu_dev, void *workspace) {
+                              const int32_t *cu_dev, const int32_t *cu_host, void *workspace) {
     kda::ChunkParams p{};
     p.T = total_tokens;
     p.H = geom->H;
@@ -156,6 +156,15 @@ kda::ChunkParams chunk_params(const kda_geom *geom, int32_t n_seqs, int32_t tota
     p.scale = geom->scale;
     p.cu = cu_dev;
     kda::chunk_workspace_carve(workspace, geom->H, n_seqs, n_chunks, p);
+    if (n_seqs <= kda::kPlanSeqs) {   // chunk table in the kernel arguments (cu_host is validated)
+        p.plan_in_args = 1;
+        int32_t off = 0;
+        for (int n = 0; n <= n_seqs; ++n) {
+            p.plan_cu[n] = cu_host[n];
+            p.plan_off[n] = off;
+            if (n < n_seqs) off += (cu_host[n + 1] - cu_host[n] + kda::kChunk - 1) / kda::kChunk;
+        }
+    }
     return p;
 }
 
@@ -241,7 +250,7 @@ kda_status kda_chunk_prepare(const kda_geom *geom, int32_t n_seqs, int32_t total
     KDA_TRY(check_required({{q, "q"}, {k, "k"}, {v, "v"}, {log_alpha, "log_alpha"}, {beta, "beta"}}));
     KDA_TRY(check_aligned({{q, "q"}, {k, "k"}, {v, "v"}, {log_alpha, "log_alpha"}, {beta, "beta"}}));
     KDA_TRY(check_device());
-    kda::ChunkParams p = chunk_params(geom, n_seqs, total_tokens, n_chunks, cu_seqlens_dev, workspace);
+    kda::ChunkParams p = chunk_params(geom, n_seqs, total_tokens, n_chunks, cu_seqlens_dev, cu_seqlens_host, workspace);
     p.q = static_cast<const uint16_t *>(q);
     p.k = static_cast<const uint16_t *>(k);
     p.v = static_cast<const uint16_t *>(v);
@@ -261,7 +270,7 @@ kda_status kda_chunk_scan(const kda_geom *geom, int32_t n_seqs, int32_t total_to
     KDA_TRY(check_aligned({{gate, "gate"}, {initial_state, "initial_state"}, {final_state, "final_state"},
                            {out, "out"}}));
     KDA_TRY(check_device());
-    kda::ChunkParams p = chunk_params(geom, n_seqs, total_tokens, n_chunks, cu_seqlens_dev, workspace);
+    kda::ChunkParams p = chunk_params(geom, n_seqs, total_tokens, n_chunks, cu_seqlens_dev, cu_seqlens_host, workspace);
     p.gate = static_cast<const uint16_t *>(gate);
     p.s0 = initial_state;
     p.s_final = final_state;
@@ -302,7 +311,7 @@ kda_status kda_prefill_prepare(const kda_geom *geom, int32_t n_seqs, int32_t tot
                            {conv_cache_in, "conv_cache_in"}, {conv_cache_out, "conv_cache_out"},
                            {log_alpha, "log_alpha"}, {beta_logit, "beta_logit"}}));
     KDA_TRY(check_device());
-    kda::ChunkParams p = chunk_params(geom, n_seqs, total_tokens, n_chunks, cu_seqlens_dev, workspace);
+    kda::ChunkParams p = chunk_params(geom, n_seqs, total_tokens, n_chunks, cu_seqlens_dev, cu_seqlens_host, workspace);
     p.K = geom->conv_k;
     p.act = geom->act;
     p.eps = geom->l2_eps;
@@ -341,7 +350,7 @@ kda_status kda_prefill_scan(const kda_geom *geom, int32_t n_seqs, int32_t total_
     KDA_TRY(check_aligned({{gate_logit, "gate_logit"}, {initial_state, "initial_state"},
                            {final_state, "final_state"}, {out, "out"}}));
     KDA_TRY(check_device());
-    kda::ChunkParams p = chunk_params(geom, n_seqs, total_tokens, n_chunks, cu_seqlens_dev, workspace);
+    kda::ChunkParams p = chunk_params(geom, n_seqs, total_tokens, n_chunks, cu_seqlens_dev, cu_seqlens_host, workspace);
     p.gate = static_cast<const uint16_t *>(gate_logit);
     p.gate_is_logit = 1;
     p.s0 = initial_state;

@@ -51,6 +51,10 @@ struct PrologueParams {
     float *beta_out;
 };
 
+// Batches of up to kPlanSeqs sequences carry their chunk table in the kernel
+// arguments (built on the host from cu_seqlens_host), so no table kernel runs.
+constexpr int kPlanSeqs = 128;
+
 struct ChunkParams {
     int T, H, n_seqs, n_chunks;
     float scale;
@@ -70,6 +74,10 @@ struct ChunkParams {
     const float *s0;
     float *s_final;
     uint16_t *out;
+    // small batches: first chunk of each sequence and cu_seqlens, [n_seqs+1]
+    int plan_in_args;
+    int32_t plan_off[kPlanSeqs + 1];
+    int32_t plan_cu[kPlanSeqs + 1];
 };
 
 struct DecodeParams {

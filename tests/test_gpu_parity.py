@@ -257,6 +257,23 @@ def test_prefill_fused_varlen_edges(K):
     print(f"fused K={K}: max |err| y {e1:.2e} S {e2:.2e}")
 
 
+def test_prefill_many_sequences():
+    """150 short sequences (0..90 tokens, empty ones included): more than the
+    128 whose chunk table travels in the kernel arguments, so the table is
+    built on the device; both the fused and the unfused path."""
+    g = torch.Generator().manual_seed(95)
+    lens = torch.randint(0, 91, (150,), generator=g).tolist()
+    lens[3] = lens[77] = 0
+    inp = ki.prefill_inputs(95, lens, H=2, d=128, K=4, cache_std=1.0)
+    ref = ORC.prefill(inp)
+    for name, res in (("fused", gpu_prefill_fused(inp)), ("unfused", gpu_prefill(inp))):
+        assert_chunk_close(res["y"], ref["y"], f"150 seqs {name} y")
+        assert_chunk_close(res["final_state"], ref["final_state"], f"150 seqs {name} final state")
+        assert_fp32_close(res["conv_cache"], ref["conv_cache"], f"150 seqs {name} conv cache", 0.0)
+        S = np64(res["final_state"])
+        assert np.array_equal(S[3], inp["initial_state"][3].double().numpy())
+
+
 def test_prefill_fused_alias_nogate_scale_and_matches_unfused():
     inp = ki.prefill_inputs(90, [150, 77], H=2, d=128, K=4, cache_std=1.0)
     scale = 128 ** -0.5
