@@ -516,6 +516,34 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
             *reinterpret_cast<u32x2 *>(rec + kOffU + (((2 * w + 1) * 4 + m) * 64 + l) * 8) = o1;
         }
     }
+
+    // ---- outgoing conv cache (fused): this head's channels of the last K-1
+    // input rows, written by the sequence's last chunk.  One thread walks the
+    // rows of a channel in ascending order, so an output that aliases the
+    // incoming cache reads each old row before it is overwritten.
+    if constexpr (FUSED) {
+        if (p.cache_out && len > 0) {
+            const int seq_lo = p.plan_in_args ? p.plan_cu[ci.seq] : p.cu[ci.seq];
+            const int seq_hi = p.plan_in_args ? p.plan_cu[ci.seq + 1] : p.cu[ci.seq + 1];
+            if (tok0 + len == seq_hi) {
+                const int Km1 = p.K - 1, C = H * kHeadDim;
+                const long L = seq_hi - seq_lo;
+                for (int idx = tid; idx < 3 * kHeadDim; idx += 256) {
+                    const int X = idx / kHeadDim;
+                    const long ch = (long)h * kHeadDim + idx % kHeadDim;
+                    const uint16_t *raw = X == 0 ? p.q_raw : (X == 1 ? p.k_raw : p.v_raw);
+                    const long row0 = ((long)ci.seq * 3 + X) * Km1;
+                    for (int j = 0; j < Km1; ++j) {
+                        const long tau = seq_hi - Km1 + j;
+                        float v;
+                        if (tau >= seq_lo) v = bf2f(raw[tau * C + ch]);
+                        else v = p.cache_in ? p.cache_in[(row0 + j + L) * C + ch] : 0.0f;
+                        p.cache_out[(row0 + j) * C + ch] = v;
+                    }
+                }
+            }
+        }
+    }
 }
 
 // ---------------------------------------------------------------------------

@@ -322,7 +322,24 @@ kda_status kda_prefill_prepare(const kda_geom *geom, int32_t n_seqs, int32_t tot
     p.beta_logit = static_cast<const uint16_t *>(beta_logit);
     p.conv_w = conv_w;
     p.cache_in = geom->conv_k > 1 ? conv_cache_in : nullptr;
+    // The prepare kernel writes the outgoing conv cache itself (from each
+    // sequence's last chunk) unless that could race with a read of the
+    // incoming one: in place, a sequence of several chunks has its cache read
+    // by its first chunk's blocks; out of place, an empty sequence has no
+    // chunk to copy its cache through.
+    bool fold = false;
+    if (conv_cache_out && geom->conv_k > 1) {
+        bool any_empty = false, any_multi = false;
+        for (int n = 0; n < n_seqs; ++n) {
+            const int len = cu_seqlens_host[n + 1] - cu_seqlens_host[n];
+            any_empty |= len == 0;
+            any_multi |= len > kda::kChunk;
+        }
+        fold = conv_cache_out == conv_cache_in ? !any_multi : !any_empty;
+    }
+    p.cache_out = fold ? conv_cache_out : nullptr;
     KDA_TRY(launched(kda::launch_prefill_prepare(p, (hipStream_t)stream), "prefill prepare"));
+    if (fold || !conv_cache_out || geom->conv_k <= 1) return KDA_OK;
     // outgoing conv cache, after the prepare kernel has read the incoming one
     kda::PrologueParams c{};
     c.T = total_tokens;

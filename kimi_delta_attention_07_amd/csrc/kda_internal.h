@@ -64,6 +64,7 @@ struct ChunkParams {
     float eps;
     const uint16_t *q_raw, *k_raw, *v_raw, *beta_logit;
     const float *conv_w, *cache_in;
+    float *cache_out;           // written by each sequence's last chunk when set
     int gate_is_logit;
     const int32_t *cu;          // [n_seqs+1] device
     int32_t *chunk_off;         // [n_seqs+1] in workspace

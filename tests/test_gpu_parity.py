@@ -257,6 +257,20 @@ def test_prefill_fused_varlen_edges(K):
     print(f"fused K={K}: max |err| y {e1:.2e} S {e2:.2e}")
 
 
+@pytest.mark.parametrize("lens,alias", [([1, 2, 3, 63, 64, 65, 130, 200], False),
+                                        ([0, 1, 2, 5, 64, 30, 0], True)])
+def test_prefill_fused_conv_cache_out(lens, alias):
+    """Outgoing conv cache written by the prepare kernel itself: out of place
+    with no empty sequence, and in place with every sequence within one chunk
+    (short sequences keep part of the incoming cache)."""
+    inp = ki.prefill_inputs(96 + alias, lens, H=3, d=128, K=4, cache_std=1.0)
+    res = gpu_prefill_fused(inp, alias_cache=alias)
+    ref = ORC.prefill(inp)
+    assert_chunk_close(res["y"], ref["y"], "y")
+    assert_chunk_close(res["final_state"], ref["final_state"], "final state")
+    assert_fp32_close(res["conv_cache"], ref["conv_cache"], "conv cache", 0.0)
+
+
 def test_prefill_many_sequences():
     """150 short sequences (0..90 tokens, empty ones included): more than the
     128 whose chunk table travels in the kernel arguments, so the table is
