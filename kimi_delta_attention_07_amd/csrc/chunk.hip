@@ -114,6 +114,10 @@ __device__ __forceinline__ ChunkInfo load_chunk(const ChunkParams &p, int cid) {
         return ci;
     }
     ChunkInfo ci = p.chunk_info[cid];
+    ci.start = __builtin_amdgcn_readfirstlane(ci.start);
+    ci.len = __builtin_amdgcn_readfirstlane(ci.len);
+    ci.seq = __builtin_amdgcn_readfirstlane(ci.seq);
+    ci.first = __builtin_amdgcn_readfirstlane(ci.first);
     if (ci.start < 0 || ci.len < 0 || ci.len > kChunk || ci.start > p.T - ci.len || ci.seq < 0 ||
         ci.seq >= p.n_seqs) {
         ci.start = 0;
@@ -157,12 +161,13 @@ __device__ __forceinline__ bf16x8 lds_frag(const unsigned char *lds, int off_byt
 // and k (a DPP wave reduction per token: lanes hold the token's channels) and
 // the sigmoid of beta.  The conv reads the 3 rows before the chunk from the
 // same sequence, or from the incoming conv cache at a sequence start.
-template <bool FUSED>
+template <bool FUSED, int KC>   // KC: conv taps (fused; the unfused instance ignores it)
 __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsPrepare];
     // heads vary fastest: concurrent blocks read adjacent heads of one chunk
     const int h = blockIdx.x % p.H, cid = blockIdx.x / p.H;
-    const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, g = l >> 4, c16 = l & 15;
+    const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);   // wave-uniform: scalar branches and addresses
     const int H = p.H;
     const ChunkInfo ci = load_chunk(p, cid);
     const long tok0 = ci.start;
@@ -176,13 +181,67 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
 
 
     // ---- phase 1: cumulative log decay and decayed operands ----------------
-    // wave w: tokens 16w..16w+15; lane l: channels 2l, 2l+1.  All of this
-    // lane's loads (log alpha, q, k, v rows) are issued before any is used.
+    // wave w: tokens 16w..16w+15; lane l: channels 2l, 2l+1.  Every wave
+    // issues the same loads, in order of first use, so each wait covers only
+    // what the next step needs: (fused) conv taps and incoming-cache rows,
+    // then log alpha and beta, then the q, k, v rows token by token.
+    float wc[3][2][4];     // fused: taps, zero-padded on the old side to 4
+    float2 halo[3][3];     // fused: the 3 rows before this wave's tokens
+    if constexpr (FUSED) {
+        const long C = (long)H * kHeadDim;
+#pragma unroll
+        for (int X = 0; X < 3; ++X)
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const float *src = p.conv_w + (X * C + h * kHeadDim + 2 * l + e) * KC;
+                if constexpr (KC == 4) {
+                    const f32x4 t = *reinterpret_cast<const f32x4 *>(src);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) wc[X][e][j] = t[j];
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) wc[X][e][j] = j >= 4 - KC ? src[j - (4 - KC)] : 0.0f;
+                }
+            }
+        // At a sequence start the rows before it come from the incoming conv
+        // cache (zeros where it has none).  Every wave issues these loads; the
+        // resource is empty unless this is wave 0 of a sequence's first chunk.
+        constexpr int Km1 = KC - 1;
+        if constexpr (Km1 > 0) {
+            const bool fetch = w == 0 && ci.first && p.cache_in;
+            const __amdgpu_buffer_rsrc_t rs =
+                buffer_rsrc(p.cache_in + (long)ci.seq * 3 * Km1 * C, fetch ? (uint32_t)(3 * Km1 * C * 4) : 0u);
+#pragma unroll
+            for (int r = 0; r < 3; ++r)
+#pragma unroll
+                for (int X = 0; X < 3; ++X) {
+                    const int slot = r - (3 - Km1);   // cache row of token tok0 - 3 + r
+                    if (slot >= 0) {
+                        const uint32_t off = (uint32_t)(((X * Km1 + slot) * C + h * kHeadDim + 2 * l) * 4);
+                        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+                        halo[X][r] = make_float2(__uint_as_float(v[0]), __uint_as_float(v[1]));
+                    } else {
+                        halo[X][r] = make_float2(0.f, 0.f);
+                    }
+                }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 3; ++r)
+#pragma unroll
+                for (int X = 0; X < 3; ++X) halo[X][r] = make_float2(0.f, 0.f);
+        }
+    }
     uint32_t ula[16];
 #pragma unroll
     for (int ii = 0; ii < 16; ++ii) {
         const long o = ((tok0 + max(0, min(16 * w + ii, len - 1))) * H + h) * kHeadDim + 2 * l;
         ula[ii] = *reinterpret_cast<const uint32_t *>(p.log_alpha + o);
+    }
+    // beta of this wave's tokens (lane l & 15 holds token 16 w + (l & 15))
+    float braw;
+    {
+        const long ob = (tok0 + max(0, min(16 * w + (l & 15), len - 1))) * H + h;
+        braw = FUSED ? bf2f(p.beta_logit[ob]) : p.beta[ob];
     }
     // unfused: the prologue's rows q^, k^, v^ of this wave's 16 tokens;
     // fused: the raw rows of tokens 16w-3 .. 16w+15 (conv window)
@@ -199,62 +258,25 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
         uk[r] = *reinterpret_cast<const uint32_t *>(sk + o);
         uv[r] = *reinterpret_cast<const uint32_t *>(sv + o);
     }
-    // Token indices are clamped into the chunk so that loads are unconditional
-    // (and issued together); rows past the chunk's end are zeroed afterwards.
-    if (tid < 64) {
-        const long ob = (tok0 + max(0, min(tid, len - 1))) * H + h;
-        const float b = FUSED ? sigmoidf(bf2f(p.beta_logit[ob])) : p.beta[ob];
-        beta_s[tid] = tid < len ? b : 0.0f;
-    }
-    // fused: conv taps (zero-padded to 4 on the old side) and, for the first
-    // chunk of a sequence, the 3 rows before it from the incoming conv cache
-    float wc[3][2][4];
-    float2 halo[3][3];
-    if constexpr (FUSED) {
-        const int C = H * kHeadDim, Km1 = p.K - 1;
-#pragma unroll
-        for (int X = 0; X < 3; ++X)
-#pragma unroll
-            for (int e = 0; e < 2; ++e)
-#pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    const int jj = j - (4 - p.K);
-                    wc[X][e][j] = jj >= 0 ? p.conv_w[((long)X * C + h * kHeadDim + 2 * l + e) * p.K + jj] : 0.0f;
-                }
-#pragma unroll
-        for (int r = 0; r < 3; ++r) {
-            halo[0][r] = make_float2(lo_bf(uq[r]), hi_bf(uq[r]));
-            halo[1][r] = make_float2(lo_bf(uk[r]), hi_bf(uk[r]));
-            halo[2][r] = make_float2(lo_bf(uv[r]), hi_bf(uv[r]));
-        }
-        if (w == 0 && ci.first) {   // rows before a sequence start: conv cache or zeros
-#pragma unroll
-            for (int r = 0; r < 3; ++r) {
-                const int idx = r - (3 - Km1);   // cache slot of row tok0-3+r
-#pragma unroll
-                for (int X = 0; X < 3; ++X) {
-                    float2 v = make_float2(0.f, 0.f);
-                    if (idx >= 0 && p.cache_in)
-                        v = *reinterpret_cast<const float2 *>(
-                            p.cache_in + (((long)ci.seq * 3 + X) * Km1 + idx) * C + h * kHeadDim + 2 * l);
-                    halo[X][r] = v;
-                }
-            }
-        }
-    }
+    // G in log2 units (log2 e folded into the sum), so decays are plain exp2
+    constexpr float kLog2e = 1.4426950408889634f;
     float2 G[16];
     {
         float2 run = make_float2(0.f, 0.f);
 #pragma unroll
         for (int ii = 0; ii < 16; ++ii) {
-            if (16 * w + ii < len) {
-                run.x += lo_bf(ula[ii]);
-                run.y += hi_bf(ula[ii]);
-            }
+            const bool in = 16 * w + ii < len;   // rows past the end keep G at G_L
+            run.x += in ? kLog2e * lo_bf(ula[ii]) : 0.0f;
+            run.y += in ? kLog2e * hi_bf(ula[ii]) : 0.0f;
             G[ii] = run;
         }
         tot[w * 128 + 2 * l] = run.x;
         tot[w * 128 + 2 * l + 1] = run.y;
+    }
+    {   // lanes l, l + 16, l + 32, l + 48 store the same value (no branch around the load)
+        const float b = FUSED ? sigmoidf(braw) : braw;
+        const int tk = 16 * w + (l & 15);
+        beta_s[tk] = tk < len ? b : 0.0f;
     }
     __syncthreads();
     float2 GL = make_float2(0.f, 0.f), off = make_float2(0.f, 0.f);
@@ -268,14 +290,23 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
         GL.x += a;
         GL.y += b;
     }
-    if (w == 0) {
-        float2 gl = make_float2(__expf(GL.x), __expf(GL.y));
-        *reinterpret_cast<float2 *>(rec + kOffGL + 8 * l) = gl;
+    const float2 egl = make_float2(__builtin_amdgcn_exp2f(GL.x), __builtin_amdgcn_exp2f(GL.y));   // e^{G_L}
+    if (w == 0) *reinterpret_cast<float2 *>(rec + kOffGL + 8 * l) = egl;
+    if constexpr (FUSED) {
+        if (!(w == 0 && ci.first)) {   // otherwise halo holds the incoming cache rows
+#pragma unroll
+            for (int r = 0; r < 3; ++r) {
+                halo[0][r] = make_float2(lo_bf(uq[r]), hi_bf(uq[r]));
+                halo[1][r] = make_float2(lo_bf(uk[r]), hi_bf(uk[r]));
+                halo[2][r] = make_float2(lo_bf(uv[r]), hi_bf(uv[r]));
+            }
+        }
     }
     // Operands of phase 3, packed to bf16 now so few registers stay live:
     // pk[0] = beta k^ e^G, pk[1] = beta v^, pk[2] = k^ e^{G_L - G}; per channel
-    // e (0, 1) the 16 tokens of this wave, two per 32-bit word.
+    // e (0, 1) the 16 tokens of this wave, two per 32-bit word (even token low).
     uint32_t pk[3][2][8];
+    float prev[3][2];
 #pragma unroll
     for (int ii = 0; ii < 16; ++ii) {
         const int tk = 16 * w + ii;
@@ -289,7 +320,7 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
                 const uint32_t *u = X == 0 ? uq : (X == 1 ? uk : uv);
                 float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
+                for (int j = 4 - KC; j < 4; ++j) {
                     const int r = ii + j;
                     const float2 v = r < 3 ? halo[X][r] : make_float2(lo_bf(u[r]), hi_bf(u[r]));
                     a0 += wc[X][0][j] * v.x;
@@ -310,23 +341,22 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
             k2 = make_float2(lo_bf(uk[ii]), hi_bf(uk[ii]));
             v2 = make_float2(lo_bf(uv[ii]), hi_bf(uv[ii]));
         }
-        const float ex = __expf(gx), ey = __expf(gy);
-        const float ix = __expf(-gx), iy = __expf(-gy);
-        const float hx = __expf(GL.x - gx), hy = __expf(GL.y - gy);
+        const float ex = __builtin_amdgcn_exp2f(gx), ey = __builtin_amdgcn_exp2f(gy);     // e^{G}
+        const float ix = __builtin_amdgcn_exp2f(-gx), iy = __builtin_amdgcn_exp2f(-gy);   // e^{-G}
         const float bt = beta_s[tk];
         const int e = tk * kRowA + 2 * l;
-        reinterpret_cast<uint32_t *>(lds + kOffKd)[e / 2] = pack_bf2(k2.x * ex, k2.y * ey);
+        const float kx = k2.x * ex, ky = k2.y * ey;
+        reinterpret_cast<uint32_t *>(lds + kOffKd)[e / 2] = pack_bf2(kx, ky);
         reinterpret_cast<uint32_t *>(lds + kOffKi)[e / 2] = pack_bf2(k2.x * ix, k2.y * iy);
         reinterpret_cast<uint32_t *>(lds + kOffQs)[e / 2] = pack_bf2(q2.x * ex, q2.y * ey);
-        const uint32_t vals[3][2] = {{f2bf(bt * k2.x * ex), f2bf(bt * k2.y * ey)},
-                                     {f2bf(bt * v2.x), f2bf(bt * v2.y)},
-                                     {f2bf(k2.x * hx), f2bf(k2.y * hy)}};
+        const float cur[3][2] = {{bt * kx, bt * ky}, {bt * v2.x, bt * v2.y},
+                                 {k2.x * (egl.x * ix), k2.y * (egl.y * iy)}};
 #pragma unroll
         for (int a = 0; a < 3; ++a)
 #pragma unroll
             for (int c = 0; c < 2; ++c) {
-                if (ii % 2 == 0) pk[a][c][ii / 2] = vals[a][c];
-                else pk[a][c][ii / 2] |= vals[a][c] << 16;
+                if (ii % 2 == 0) prev[a][c] = cur[a][c];
+                else pk[a][c][ii / 2] = pack_bf2(prev[a][c], cur[a][c]);
             }
     }
     __syncthreads();
@@ -843,7 +873,7 @@ hipError_t launch_chunk_prepare(const ChunkParams &p, hipStream_t s) {
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p.cu, p.n_seqs, p.n_chunks, p.chunk_off,
                            p.chunk_info);
     if (p.n_chunks > 0)
-        hipLaunchKernelGGL(prepare_kernel<false>, dim3((unsigned)((long)p.n_chunks * p.H)), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((prepare_kernel<false, 4>), dim3((unsigned)((long)p.n_chunks * p.H)), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 
@@ -851,8 +881,15 @@ hipError_t launch_prefill_prepare(const ChunkParams &p, hipStream_t s) {
     if (!p.plan_in_args)
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p.cu, p.n_seqs, p.n_chunks, p.chunk_off,
                            p.chunk_info);
-    if (p.n_chunks > 0)
-        hipLaunchKernelGGL(prepare_kernel<true>, dim3((unsigned)((long)p.n_chunks * p.H)), dim3(256), 0, s, p);
+    if (p.n_chunks > 0) {
+        const dim3 grid((unsigned)((long)p.n_chunks * p.H));
+        switch (p.K) {
+            case 1: hipLaunchKernelGGL((prepare_kernel<true, 1>), grid, dim3(256), 0, s, p); break;
+            case 2: hipLaunchKernelGGL((prepare_kernel<true, 2>), grid, dim3(256), 0, s, p); break;
+            case 3: hipLaunchKernelGGL((prepare_kernel<true, 3>), grid, dim3(256), 0, s, p); break;
+            default: hipLaunchKernelGGL((prepare_kernel<true, 4>), grid, dim3(256), 0, s, p); break;
+        }
+    }
     return hipGetLastError();
 }
 
