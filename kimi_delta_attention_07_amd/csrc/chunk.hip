@@ -149,7 +149,15 @@ constexpr int kOffBeta = kOffTm + 64 * kRowT * 2;         // fp32 [64]
 constexpr int kLdsPrepare = kOffBeta + 64 * 4;            // 81,152 B: two workgroups per CU
 static_assert(3 * 64 * kRowA * 2 <= kRegionR, "phase-1 tiles must fit region R");
 static_assert(4 * 128 * 4 <= 64 * kRowT * 2, "cumsum totals alias the T tile");
-static_assert(4 * 16 * 16 * 4 <= 64 * kRowT * 2, "inverse scratch aliases the T tile");
+
+// A (fp32 [64][64]) keeps the 16-byte column groups of row i XORed with
+// (i & 15): sixteen rows read at the same columns land in sixteen different
+// bank groups.
+__device__ __forceinline__ int aix(int i, int j) { return i * 64 + ((((j >> 2) ^ i) & 15) << 2) + (j & 3); }
+
+__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4 &c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
 
 __device__ __forceinline__ bf16x8 lds_frag(const unsigned char *lds, int off_bytes) {
     return as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + off_bytes));
@@ -376,7 +384,7 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int i = 16 * I + 4 * g + r;
-                if (j < i) A[i * 64 + j] = beta_s[i] * acc[r];
+                if (j < i) A[aix(i, j)] = beta_s[i] * acc[r];
             }
         }
     }
@@ -454,58 +462,77 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
         *reinterpret_cast<u32x4 *>(rec + kOffKg + ((mm * 2 + sp) * 64 + l) * 16) = v;
     }
     // Blocked inverse of the unit-lower-triangular I + A (A strictly lower,
-    // only its strictly-lower entries are valid), overwriting A with T:
+    // only its strictly-lower entries are valid):
     //   T_II = (I + A_II)^-1 by forward substitution (wave I, lane = column),
-    //   T_IJ = -T_II sum_{K=J}^{I-1} A_IK T_KJ for I > J (wave J, row block I).
+    //        written over A_II, which nothing reads afterwards;
+    //   T_Iw = -T_II sum_{K=w}^{I-1} A_IK T_Kw for I > w: wave w sweeps its
+    //        column block down with fp32 MFMAs (16x16x4), holding T_Kw in
+    //        registers.  The contraction index of step kk is 4 (l >> 4) + kk,
+    //        so an accumulator's C layout (rows 4g + r, column c16) is the B
+    //        operand of the next product as it stands, and an A operand is one
+    //        16-byte LDS read (row c16, columns 4g .. 4g + 3).
+    // T goes to the bf16 tile Tm straight from registers.
     {
-        float *Ad = A + (16 * w) * 64 + 16 * w;
         if (l < 16) {
             float x[16];
 #pragma unroll
             for (int i = 0; i < 16; ++i) {
                 float acc = (i == l) ? 1.0f : 0.0f;
 #pragma unroll
-                for (int k = 0; k < i; ++k) acc -= Ad[i * 64 + k] * x[k];
+                for (int k = 0; k < i; ++k) acc -= A[aix(16 * w + i, 16 * w + k)] * x[k];
                 x[i] = acc;
             }
 #pragma unroll
-            for (int i = 0; i < 16; ++i) Ad[i * 64 + l] = x[i];
+            for (int i = 0; i < 16; ++i) A[aix(16 * w + i, 16 * w + l)] = x[i];
         }
     }
-    __syncthreads();
-    float *Msc = reinterpret_cast<float *>(lds + kOffTm);   // [4][16][16] scratch, dead T tile
-    for (int I = 1; I < 4; ++I) {
-        f32x4 M = {0.f, 0.f, 0.f, 0.f};
-        if (w < I) {
-            for (int K = w; K < I; ++K) {
+    __syncthreads();   // all diagonal inverses
+    {
+        auto a_row4 = [&](int i, int j4) {   // A[i][4 j4 .. 4 j4 + 3]
+            return *reinterpret_cast<const f32x4 *>(A + i * 64 + (((j4 ^ i) & 15) << 2));
+        };
+        f32x4 Tc[4];   // Tc[K] = T_Kw in C layout, K >= w
 #pragma unroll
-                for (int k = 0; k < 16; ++k) {
-                    const float t_kc = A[(16 * K + k) * 64 + 16 * w + c16];
+        for (int K = 0; K < 4; ++K) {
+            Tc[K] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (K == w) {
 #pragma unroll
-                    for (int r = 0; r < 4; ++r) M[r] += A[(16 * I + 4 * g + r) * 64 + 16 * K + k] * t_kc;
+                for (int r = 0; r < 4; ++r) Tc[K][r] = A[aix(16 * K + 4 * g + r, 16 * K + c16)];
+            }
+        }
+#pragma unroll
+        for (int I = 1; I < 4; ++I) {
+            if (I > w) {
+                f32x4 M = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int K = 0; K < I; ++K) {
+                    if (K >= w) {
+                        const f32x4 a4 = a_row4(16 * I + c16, 4 * K + g);
+#pragma unroll
+                        for (int kk = 0; kk < 4; ++kk) M = mfma_f32(a4[kk], Tc[K][kk], M);
+                    }
                 }
+                const f32x4 t4 = a_row4(16 * I + c16, 4 * I + g);   // T_II[c16][4g ..]
+                f32x4 Tn = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) Tn = mfma_f32(t4[kk], M[kk], Tn);
+                Tc[I] = -Tn;
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) Msc[(w * 16 + 4 * g + r) * 16 + c16] = M[r];
         }
-        __syncthreads();   // row block I of A fully read; M visible
-        if (w < I) {
-            f32x4 Tn = {0.f, 0.f, 0.f, 0.f};
+        // bf16 T: this wave's column block (diagonal and below); wave 3 also
+        // zeroes the two blocks above the diagonal that phase 5 reads, (0, 1)
+        // and (2, 3)
 #pragma unroll
-            for (int m = 0; m < 16; ++m) {
-                const float mv = Msc[(w * 16 + m) * 16 + c16];
+        for (int I = 0; I < 4; ++I)
+            if (I >= w) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) Tn[r] -= A[(16 * I + 4 * g + r) * 64 + 16 * I + m] * mv;
+                for (int r = 0; r < 4; ++r) Tm[(16 * I + 4 * g + r) * kRowT + 16 * w + c16] = f2bf(Tc[I][r]);
             }
-#pragma unroll
-            for (int r = 0; r < 4; ++r) A[(16 * I + 4 * g + r) * 64 + 16 * w + c16] = Tn[r];
+        if (w == 3) {
+            const u32x2 z = {0u, 0u};
+            *reinterpret_cast<u32x2 *>(Tm + (l >> 2) * kRowT + 16 + 4 * (l & 3)) = z;
+            *reinterpret_cast<u32x2 *>(Tm + (32 + (l >> 2)) * kRowT + 48 + 4 * (l & 3)) = z;
         }
-        __syncthreads();
-    }
-    // T to bf16, zero above the block diagonal
-    for (int idx = tid; idx < 64 * 64; idx += 256) {
-        const int i = idx >> 6, j = idx & 63;
-        Tm[i * kRowT + j] = f2bf((j >> 4) <= (i >> 4) ? A[idx] : 0.0f);
     }
     __syncthreads();
 
