@@ -371,36 +371,44 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
 
     // ---- phase 2: A (row block I = w) and P^T (column block I = 3 - w) -----
     {
+        // the row block's K e^G fragments serve every column block J
         const int I = w;
-        for (int J = 0; J <= I; ++J) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        bf16x8 a[4];
 #pragma unroll
-            for (int s = 0; s < 4; ++s) {
-                const bf16x8 a = lds_frag(lds, kOffKd + ((16 * I + c16) * kRowA + 32 * s + 8 * g) * 2);
-                const bf16x8 b = lds_frag(lds, kOffKi + ((16 * J + c16) * kRowA + 32 * s + 8 * g) * 2);
-                acc = mfma16(a, b, acc);
-            }
-            const int j = 16 * J + c16;
+        for (int s = 0; s < 4; ++s) a[s] = lds_frag(lds, kOffKd + ((16 * I + c16) * kRowA + 32 * s + 8 * g) * 2);
+        float bi[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int i = 16 * I + 4 * g + r;
-                if (j < i) A[aix(i, j)] = beta_s[i] * acc[r];
+        for (int r = 0; r < 4; ++r) bi[r] = beta_s[16 * I + 4 * g + r];
+#pragma unroll
+        for (int J = 0; J < 4; ++J) {
+            if (J <= I) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+                    acc = mfma16(a[s], lds_frag(lds, kOffKi + ((16 * J + c16) * kRowA + 32 * s + 8 * g) * 2), acc);
+                const int j = 16 * J + c16;
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int i = 16 * I + 4 * g + r;
+                    if (j < i) A[aix(i, j)] = bi[r] * acc[r];
+                }
             }
         }
     }
     {
+        // the column block's Q e^G fragments serve every row block J
         const int I = 3 - w;
+        bf16x8 b[4];
+#pragma unroll
+        for (int s = 0; s < 4; ++s) b[s] = lds_frag(lds, kOffQs + ((16 * I + c16) * kRowA + 32 * s + 8 * g) * 2);
         f32x4 blk[4];
 #pragma unroll
         for (int J = 0; J < 4; ++J) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             if (J <= I) {
 #pragma unroll
-                for (int s = 0; s < 4; ++s) {
-                    const bf16x8 a = lds_frag(lds, kOffKi + ((16 * J + c16) * kRowA + 32 * s + 8 * g) * 2);
-                    const bf16x8 b = lds_frag(lds, kOffQs + ((16 * I + c16) * kRowA + 32 * s + 8 * g) * 2);
-                    acc = mfma16(a, b, acc);
-                }
+                for (int s = 0; s < 4; ++s)
+                    acc = mfma16(lds_frag(lds, kOffKi + ((16 * J + c16) * kRowA + 32 * s + 8 * g) * 2), b[s], acc);
                 const int i = 16 * I + c16;
 #pragma unroll
                 for (int r = 0; r < 4; ++r)
