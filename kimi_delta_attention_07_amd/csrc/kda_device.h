@@ -78,22 +78,22 @@ __device__ __forceinline__ void store1(void *base, long idx, float a) {
 __device__ __forceinline__ float sigmoidf(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 __device__ __forceinline__ float activate(int act, float x) { return act == 1 ? x * sigmoidf(x) : x; }
 
-// Sum over all 64 lanes, result in every lane: DPP within 16-lane rows, then
-// the four row sums through readlane (no LDS round trips).
-template <int CTRL>
+// Sum over all 64 lanes, result in every lane (no LDS round trips): DPP
+// within 16-lane rows, then the GFX9 row broadcasts carry row sums into
+// rows 1 and 3 (row_bcast:15) and rows 2-3 (row_bcast:31), leaving the total
+// in row 3, read once.  Rows masked off by a DPP step keep their value.
+template <int CTRL, int ROWS = 0xf>
 __device__ __forceinline__ float dpp_shift(float v) {
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xf, 0xf, false));
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xf, false));
 }
 __device__ __forceinline__ float wave_sum(float v) {
-    v += dpp_shift<0xB1>(v);    // quad_perm [1,0,3,2]
-    v += dpp_shift<0x4E>(v);    // quad_perm [2,3,0,1]
-    v += dpp_shift<0x141>(v);   // row_half_mirror
-    v += dpp_shift<0x140>(v);   // row_mirror
-    const float r0 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 0));
-    const float r1 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 16));
-    const float r2 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 32));
-    const float r3 = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 48));
-    return (r0 + r1) + (r2 + r3);
+    v += dpp_shift<0xB1>(v);          // quad_perm [1,0,3,2]
+    v += dpp_shift<0x4E>(v);          // quad_perm [2,3,0,1]
+    v += dpp_shift<0x141>(v);         // row_half_mirror
+    v += dpp_shift<0x140>(v);         // row_mirror: every lane of a row holds its row sum
+    v += dpp_shift<0x142, 0xA>(v);    // row_bcast:15 into rows 1, 3: r0 + r1, r2 + r3
+    v += dpp_shift<0x143, 0xC>(v);    // row_bcast:31 into rows 2, 3: row 3 = r0 + r1 + r2 + r3
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
 }
 
 // Sum over aligned groups of `width` lanes (width a power of two <= 64).
