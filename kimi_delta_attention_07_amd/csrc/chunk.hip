@@ -471,34 +471,59 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
     }
     // Blocked inverse of the unit-lower-triangular I + A (A strictly lower,
     // only its strictly-lower entries are valid):
-    //   T_II = (I + A_II)^-1 by forward substitution (wave I, lane = column),
-    //        written over A_II, which nothing reads afterwards;
+    //   T_II = (I + A_II)^-1 per wave (block w): with P = -A_ww, nilpotent
+    //        (P^16 = 0), (I + P)(I + P^2)(I + P^4)(I + P^8) = I + P + .. + P^15
+    //        is the inverse; six 16x16 fp32 MFMA products, written over A_II,
+    //        which nothing reads afterwards;
     //   T_Iw = -T_II sum_{K=w}^{I-1} A_IK T_Kw for I > w: wave w sweeps its
     //        column block down with fp32 MFMAs (16x16x4), holding T_Kw in
-    //        registers.  The contraction index of step kk is 4 (l >> 4) + kk,
-    //        so an accumulator's C layout (rows 4g + r, column c16) is the B
-    //        operand of the next product as it stands, and an A operand is one
-    //        16-byte LDS read (row c16, columns 4g .. 4g + 3).
-    // T goes to the bf16 tile Tm straight from registers.
+    //        registers.
+    // In every product the contraction index of MFMA step kk is 4 (l >> 4) +
+    // kk, so an accumulator's C layout (rows 4g + r, column c16) is the B
+    // operand of the next product as it stands, and an A operand is one
+    // 16-byte row read (row c16, columns 4g .. 4g + 3).  T goes to the bf16
+    // tile Tm straight from registers.
+    auto a_row4 = [&](int i, int j4) {   // A[i][4 j4 .. 4 j4 + 3]
+        return *reinterpret_cast<const f32x4 *>(A + i * 64 + (((j4 ^ i) & 15) << 2));
+    };
+    auto mm = [&](const f32x4 &xr, const f32x4 &yc) {   // X (row layout) * Y (C layout), C layout
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc = mfma_f32(xr[kk], yc[kk], acc);
+        return acc;
+    };
     {
-        if (l < 16) {
-            float x[16];
+        // per-wave scratch for C-to-row transposes: [16][20] fp32 in the dead T tile
+        float *sc = reinterpret_cast<float *>(lds + kOffTm) + w * 16 * 20;
+        auto to_rows = [&](const f32x4 &c) {
 #pragma unroll
-            for (int i = 0; i < 16; ++i) {
-                float acc = (i == l) ? 1.0f : 0.0f;
+            for (int r = 0; r < 4; ++r) sc[(4 * g + r) * 20 + c16] = c[r];
+            return *reinterpret_cast<const f32x4 *>(sc + c16 * 20 + 4 * g);
+        };
+        f32x4 Pc, Pr;   // P = -A_ww: C layout and row layout (entries j >= i are not valid in A)
+        const f32x4 arow = a_row4(16 * w + c16, 4 * w + g);
 #pragma unroll
-                for (int k = 0; k < i; ++k) acc -= A[aix(16 * w + i, 16 * w + k)] * x[k];
-                x[i] = acc;
-            }
-#pragma unroll
-            for (int i = 0; i < 16; ++i) A[aix(16 * w + i, 16 * w + l)] = x[i];
+        for (int r = 0; r < 4; ++r) {
+            const int i = 4 * g + r;
+            Pc[r] = c16 < i ? -A[aix(16 * w + i, 16 * w + c16)] : 0.0f;
+            Pr[r] = 4 * g + r < c16 ? -arow[r] : 0.0f;
         }
+        const f32x4 P2c = mm(Pr, Pc);
+        const f32x4 P2r = to_rows(P2c);
+        const f32x4 P4c = mm(P2r, P2c);
+        const f32x4 P4r = to_rows(P4c);
+        const f32x4 P8c = mm(P4r, P4c);
+        f32x4 Ic;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) Ic[r] = 4 * g + r == c16 ? 1.0f : 0.0f;
+        const f32x4 Yc = Ic + P4c + P8c + mm(P4r, P8c);   // (I + P^4)(I + P^8)
+        const f32x4 Zc = Yc + mm(P2r, Yc);                // (I + P^2) Y
+        const f32x4 Tw = Zc + mm(Pr, Zc);                 // (I + P) Z
+#pragma unroll
+        for (int r = 0; r < 4; ++r) A[aix(16 * w + 4 * g + r, 16 * w + c16)] = Tw[r];
     }
     __syncthreads();   // all diagonal inverses
     {
-        auto a_row4 = [&](int i, int j4) {   // A[i][4 j4 .. 4 j4 + 3]
-            return *reinterpret_cast<const f32x4 *>(A + i * 64 + (((j4 ^ i) & 15) << 2));
-        };
         f32x4 Tc[4];   // Tc[K] = T_Kw in C layout, K >= w
 #pragma unroll
         for (int K = 0; K < 4; ++K) {
