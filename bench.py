@@ -51,11 +51,11 @@ DECODE_B_PER_ROW = 2 * STATE_B + 2 * CONV_CACHE_B + 3 * 8192 + 8192 + 64 + 8192 
 
 
 # bench timing slot -> kernel whose counters profiles/traffic.json holds
-TRAFFIC_KERNEL = {"prologue": "prologue128_kernel<4, 1>", "chunk_prepare": "prepare_kernel<false, 4>",
-                  "chunk_scan": "scan_kernel<true>", "prefill_prepare": "prepare_kernel<true, 4>",
+TRAFFIC_KERNEL = {"prologue": "prologue128_kernel<4, 1>", "chunk_prepare": "prepare_kernel<false, 4, 0>",
+                  "chunk_scan": "scan_kernel<true>", "prefill_prepare": "prepare_kernel<true, 4, 1>",
                   "prefill_scan": "scan_kernel<true>", "decode": "decode_kernel<128, 1, 0>"}
-KERNEL_SOURCES = {"prologue128_kernel<4, 1>": ["prologue.hip"], "prepare_kernel<false, 4>": ["chunk.hip"],
-                  "prepare_kernel<true, 4>": ["chunk.hip"], "scan_kernel<true>": ["chunk.hip"],
+KERNEL_SOURCES = {"prologue128_kernel<4, 1>": ["prologue.hip"], "prepare_kernel<false, 4, 0>": ["chunk.hip"],
+                  "prepare_kernel<true, 4, 1>": ["chunk.hip"], "scan_kernel<true>": ["chunk.hip"],
                   "decode_kernel<128, 1, 0>": ["decode.hip"]}
 
 

@@ -169,7 +169,9 @@ __device__ __forceinline__ bf16x8 lds_frag(const unsigned char *lds, int off_byt
 // and k (a DPP wave reduction per token: lanes hold the token's channels) and
 // the sigmoid of beta.  The conv reads the 3 rows before the chunk from the
 // same sequence, or from the incoming conv cache at a sequence start.
-template <bool FUSED, int KC>   // KC: conv taps (fused; the unfused instance ignores it)
+// KC: conv taps, ACT: 1 = SiLU after the conv, 0 = none (both fused only; the
+// unfused instance ignores them)
+template <bool FUSED, int KC, int ACT>
 __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
     __shared__ __attribute__((aligned(16))) unsigned char lds[kLdsPrepare];
     // heads vary fastest: concurrent blocks read adjacent heads of one chunk
@@ -315,6 +317,20 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
     // e (0, 1) the 16 tokens of this wave, two per 32-bit word (even token low).
     uint32_t pk[3][2][8];
     float prev[3][2];
+    // With SiLU, the conv taps carry a factor log2 e, so the sigmoid's exp2
+    // needs no multiply: x = log2e * silu(conv).  The L2 norm cancels the
+    // factor (eps scaled by log2e^2 to match); v's products take ln 2.
+    constexpr float kLn2 = 0.6931471805599453f;
+    const float eps_n = ACT == 1 ? p.eps * (kLog2e * kLog2e) : p.eps;
+    const float v_unscale = FUSED && ACT == 1 ? kLn2 : 1.0f;
+    if constexpr (FUSED && ACT == 1) {
+#pragma unroll
+        for (int X = 0; X < 3; ++X)
+#pragma unroll
+            for (int e = 0; e < 2; ++e)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) wc[X][e][j] *= kLog2e;
+    }
 #pragma unroll
     for (int ii = 0; ii < 16; ++ii) {
         const int tk = 16 * w + ii;
@@ -334,11 +350,12 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
                     a0 += wc[X][0][j] * v.x;
                     a1 += wc[X][1][j] * v.y;
                 }
-                x[X][0] = activate(p.act, a0);
-                x[X][1] = activate(p.act, a1);
+                // with SiLU the taps carry log2 e (see below): x = log2e * silu(conv)
+                x[X][0] = ACT == 1 ? a0 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a0)) : a0;
+                x[X][1] = ACT == 1 ? a1 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a1)) : a1;
             }
-            const float rq = __builtin_amdgcn_rsqf(wave_sum(x[0][0] * x[0][0] + x[0][1] * x[0][1]) + p.eps);
-            const float rk = __builtin_amdgcn_rsqf(wave_sum(x[1][0] * x[1][0] + x[1][1] * x[1][1]) + p.eps);
+            const float rq = __builtin_amdgcn_rsqf(wave_sum(x[0][0] * x[0][0] + x[0][1] * x[0][1]) + eps_n);
+            const float rk = __builtin_amdgcn_rsqf(wave_sum(x[1][0] * x[1][0] + x[1][1] * x[1][1]) + eps_n);
             if (tk < len) {
                 q2 = make_float2(x[0][0] * rq, x[0][1] * rq);
                 k2 = make_float2(x[1][0] * rk, x[1][1] * rk);
@@ -353,12 +370,12 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
         const float ix = __builtin_amdgcn_exp2f(-gx), iy = __builtin_amdgcn_exp2f(-gy);   // e^{-G}
         const float bt = beta_s[tk];
         const int e = tk * kRowA + 2 * l;
-        const float kx = k2.x * ex, ky = k2.y * ey;
+        const float kx = k2.x * ex, ky = k2.y * ey, kix = k2.x * ix, kiy = k2.y * iy;
         reinterpret_cast<uint32_t *>(lds + kOffKd)[e / 2] = pack_bf2(kx, ky);
-        reinterpret_cast<uint32_t *>(lds + kOffKi)[e / 2] = pack_bf2(k2.x * ix, k2.y * iy);
+        reinterpret_cast<uint32_t *>(lds + kOffKi)[e / 2] = pack_bf2(kix, kiy);
         reinterpret_cast<uint32_t *>(lds + kOffQs)[e / 2] = pack_bf2(q2.x * ex, q2.y * ey);
-        const float cur[3][2] = {{bt * kx, bt * ky}, {bt * v2.x, bt * v2.y},
-                                 {k2.x * (egl.x * ix), k2.y * (egl.y * iy)}};
+        const float bv = bt * v_unscale;
+        const float cur[3][2] = {{bt * kx, bt * ky}, {bv * v2.x, bv * v2.y}, {kix * egl.x, kiy * egl.y}};
 #pragma unroll
         for (int a = 0; a < 3; ++a)
 #pragma unroll
@@ -928,12 +945,19 @@ void chunk_workspace_carve(void *ws, int H, int n_seqs, long n_chunks, ChunkPara
     (void)H;
 }
 
+template <int KC>
+void launch_fused_prepare(const ChunkParams &p, dim3 grid, hipStream_t s) {
+    if (p.act == 1) hipLaunchKernelGGL((prepare_kernel<true, KC, 1>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((prepare_kernel<true, KC, 0>), grid, dim3(256), 0, s, p);
+}
+
 hipError_t launch_chunk_prepare(const ChunkParams &p, hipStream_t s) {
     if (!p.plan_in_args)
         hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p.cu, p.n_seqs, p.n_chunks, p.chunk_off,
                            p.chunk_info);
     if (p.n_chunks > 0)
-        hipLaunchKernelGGL((prepare_kernel<false, 4>), dim3((unsigned)((long)p.n_chunks * p.H)), dim3(256), 0, s, p);
+        hipLaunchKernelGGL((prepare_kernel<false, 4, 0>), dim3((unsigned)((long)p.n_chunks * p.H)), dim3(256), 0, s,
+                           p);
     return hipGetLastError();
 }
 
@@ -944,10 +968,10 @@ hipError_t launch_prefill_prepare(const ChunkParams &p, hipStream_t s) {
     if (p.n_chunks > 0) {
         const dim3 grid((unsigned)((long)p.n_chunks * p.H));
         switch (p.K) {
-            case 1: hipLaunchKernelGGL((prepare_kernel<true, 1>), grid, dim3(256), 0, s, p); break;
-            case 2: hipLaunchKernelGGL((prepare_kernel<true, 2>), grid, dim3(256), 0, s, p); break;
-            case 3: hipLaunchKernelGGL((prepare_kernel<true, 3>), grid, dim3(256), 0, s, p); break;
-            default: hipLaunchKernelGGL((prepare_kernel<true, 4>), grid, dim3(256), 0, s, p); break;
+            case 1: launch_fused_prepare<1>(p, grid, s); break;
+            case 2: launch_fused_prepare<2>(p, grid, s); break;
+            case 3: launch_fused_prepare<3>(p, grid, s); break;
+            default: launch_fused_prepare<4>(p, grid, s); break;
         }
     }
     return hipGetLastError();
