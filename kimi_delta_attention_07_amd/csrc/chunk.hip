@@ -354,8 +354,9 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
                 x[X][0] = ACT == 1 ? a0 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a0)) : a0;
                 x[X][1] = ACT == 1 ? a1 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a1)) : a1;
             }
-            const float rq = __builtin_amdgcn_rsqf(wave_sum(x[0][0] * x[0][0] + x[0][1] * x[0][1]) + eps_n);
-            const float rk = __builtin_amdgcn_rsqf(wave_sum(x[1][0] * x[1][0] + x[1][1] * x[1][1]) + eps_n);
+            const float r = __builtin_amdgcn_rsqf(
+                wave_sum_pair(x[0][0] * x[0][0] + x[0][1] * x[0][1], x[1][0] * x[1][0] + x[1][1] * x[1][1]) + eps_n);
+            const float rq = lane_value(r, 0), rk = lane_value(r, 16);
             if (tk < len) {
                 q2 = make_float2(x[0][0] * rq, x[0][1] * rq);
                 k2 = make_float2(x[1][0] * rk, x[1][1] * rk);

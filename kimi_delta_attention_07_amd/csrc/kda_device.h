@@ -78,22 +78,40 @@ __device__ __forceinline__ void store1(void *base, long idx, float a) {
 __device__ __forceinline__ float sigmoidf(float x) { return __builtin_amdgcn_rcpf(1.0f + __expf(-x)); }
 __device__ __forceinline__ float activate(int act, float x) { return act == 1 ? x * sigmoidf(x) : x; }
 
-// Sum over all 64 lanes, result in every lane (no LDS round trips): DPP
-// within 16-lane rows, then the GFX9 row broadcasts carry row sums into
-// rows 1 and 3 (row_bcast:15) and rows 2-3 (row_bcast:31), leaving the total
-// in row 3, read once.  Rows masked off by a DPP step keep their value.
+// DPP read of another lane of the same 16-lane row (lanes a step leaves
+// unselected read 0).
 template <int CTRL, int ROWS = 0xf>
 __device__ __forceinline__ float dpp_shift(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROWS, 0xf, false));
 }
-__device__ __forceinline__ float wave_sum(float v) {
+
+// Sums of a and of b over all 64 lanes in one pass.  gfx950's
+// v_permlane16_swap trades the odd 16-lane rows of its first operand for the
+// even rows of its second, so adding its two results gives, lane by lane, a
+// summed over rows {0,1} and {2,3} in rows 0 and 2 and b likewise in rows 1
+// and 3; v_permlane32_swap of that vector with itself adds the two halves, and
+// DPP finishes within each row.  The returned vector holds the total of a in
+// rows 0 and 2 and the total of b in rows 1 and 3 (lanes 0 and 16 are read).
+// (The swap results are copied out element by element before the bit casts:
+// clang lowers __builtin_bit_cast of a vector element lvalue as a load of
+// element 0.)
+__device__ __forceinline__ float wave_sum_pair(float a, float b) {
+    const auto s16 = __builtin_amdgcn_permlane16_swap(__builtin_bit_cast(unsigned, a),
+                                                      __builtin_bit_cast(unsigned, b), false, false);
+    const unsigned a0 = s16[0], a1 = s16[1];
+    float v = __builtin_bit_cast(float, a0) + __builtin_bit_cast(float, a1);
+    const auto s32 = __builtin_amdgcn_permlane32_swap(__builtin_bit_cast(unsigned, v),
+                                                      __builtin_bit_cast(unsigned, v), false, false);
+    const unsigned b0 = s32[0], b1 = s32[1];
+    v = __builtin_bit_cast(float, b0) + __builtin_bit_cast(float, b1);
     v += dpp_shift<0xB1>(v);          // quad_perm [1,0,3,2]
     v += dpp_shift<0x4E>(v);          // quad_perm [2,3,0,1]
     v += dpp_shift<0x141>(v);         // row_half_mirror
     v += dpp_shift<0x140>(v);         // row_mirror: every lane of a row holds its row sum
-    v += dpp_shift<0x142, 0xA>(v);    // row_bcast:15 into rows 1, 3: r0 + r1, r2 + r3
-    v += dpp_shift<0x143, 0xC>(v);    // row_bcast:31 into rows 2, 3: row 3 = r0 + r1 + r2 + r3
-    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+    return v;
+}
+__device__ __forceinline__ float lane_value(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
 
 // Sum over aligned groups of `width` lanes (width a power of two <= 64).

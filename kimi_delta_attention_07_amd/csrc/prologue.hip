@@ -212,9 +212,9 @@ __global__ __launch_bounds__(256) void prologue128_kernel(PrologueParams p) {
             x[X][0] = activate(p.act, x[X][0]);
             x[X][1] = activate(p.act, x[X][1]);
         }
-        const float sq = wave_sum(x[0][0] * x[0][0] + x[0][1] * x[0][1]);
-        const float sk = wave_sum(x[1][0] * x[1][0] + x[1][1] * x[1][1]);
-        const float rq = __builtin_amdgcn_rsqf(sq + p.eps), rk = __builtin_amdgcn_rsqf(sk + p.eps);
+        const float r = __builtin_amdgcn_rsqf(
+            wave_sum_pair(x[0][0] * x[0][0] + x[0][1] * x[0][1], x[1][0] * x[1][0] + x[1][1] * x[1][1]) + p.eps);
+        const float rq = lane_value(r, 0), rk = lane_value(r, 16);
         const long o = (t * p.H + h) * D + c0;
         store2<DT>(p.q_out, o, x[0][0] * rq, x[0][1] * rq);
         store2<DT>(p.k_out, o, x[1][0] * rk, x[1][1] * rk);
