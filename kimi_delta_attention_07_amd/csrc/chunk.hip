@@ -241,11 +241,23 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
                 for (int X = 0; X < 3; ++X) halo[X][r] = make_float2(0.f, 0.f);
         }
     }
+    // Token rows (log alpha and q, k, v) are read through buffer resources
+    // that start at the first row this block reads (up to 3 before the chunk
+    // for the conv window) and end with the chunk's last token: rows past the
+    // end, and the missing rows before token 0, load as 0, so the later steps
+    // need no masks for them (and never see another sequence's values).
+    constexpr int R0 = FUSED ? 3 : 0;
+    const long row0 = tok0 - R0 < 0 ? 0 : tok0 - R0;
+    const uint32_t rows_bytes = (uint32_t)((tok0 + len - row0) * H * kHeadDim * 2);
+    const long rows_base = (row0 * H + h) * kHeadDim;
+    auto row_off = [&](int t_rel) {   // t_rel: token index relative to tok0
+        return (uint32_t)(((tok0 + t_rel - row0) * H * kHeadDim + 2 * l) * 2);
+    };
     uint32_t ula[16];
+    {
+        const __amdgpu_buffer_rsrc_t rs = buffer_rsrc(p.log_alpha + rows_base, rows_bytes);
 #pragma unroll
-    for (int ii = 0; ii < 16; ++ii) {
-        const long o = ((tok0 + max(0, min(16 * w + ii, len - 1))) * H + h) * kHeadDim + 2 * l;
-        ula[ii] = *reinterpret_cast<const uint32_t *>(p.log_alpha + o);
+        for (int ii = 0; ii < 16; ++ii) ula[ii] = __builtin_amdgcn_raw_buffer_load_b32(rs, row_off(16 * w + ii), 0, 0);
     }
     // beta of this wave's tokens (lane l & 15 holds token 16 w + (l & 15))
     float braw;
@@ -256,17 +268,18 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
     // unfused: the prologue's rows q^, k^, v^ of this wave's 16 tokens;
     // fused: the raw rows of tokens 16w-3 .. 16w+15 (conv window)
     constexpr int NR = FUSED ? 19 : 16;
-    constexpr int R0 = FUSED ? 3 : 0;
     uint32_t uq[NR], uk[NR], uv[NR];
-    const uint16_t *sq = FUSED ? p.q_raw : p.q, *sk = FUSED ? p.k_raw : p.k, *sv = FUSED ? p.v_raw : p.v;
+    {
+        const __amdgpu_buffer_rsrc_t rq = buffer_rsrc((FUSED ? p.q_raw : p.q) + rows_base, rows_bytes);
+        const __amdgpu_buffer_rsrc_t rk = buffer_rsrc((FUSED ? p.k_raw : p.k) + rows_base, rows_bytes);
+        const __amdgpu_buffer_rsrc_t rv = buffer_rsrc((FUSED ? p.v_raw : p.v) + rows_base, rows_bytes);
 #pragma unroll
-    for (int r = 0; r < NR; ++r) {
-        long t = tok0 + 16 * w - R0 + r;
-        t = FUSED ? (t < 0 ? 0 : (t >= p.T ? p.T - 1 : t)) : tok0 + max(0, min(16 * w + r, len - 1));
-        const long o = (t * H + h) * kHeadDim + 2 * l;
-        uq[r] = *reinterpret_cast<const uint32_t *>(sq + o);
-        uk[r] = *reinterpret_cast<const uint32_t *>(sk + o);
-        uv[r] = *reinterpret_cast<const uint32_t *>(sv + o);
+        for (int r = 0; r < NR; ++r) {
+            const uint32_t o = row_off(16 * w - R0 + r);
+            uq[r] = __builtin_amdgcn_raw_buffer_load_b32(rq, o, 0, 0);
+            uk[r] = __builtin_amdgcn_raw_buffer_load_b32(rk, o, 0, 0);
+            uv[r] = __builtin_amdgcn_raw_buffer_load_b32(rv, o, 0, 0);
+        }
     }
     // G in log2 units (log2 e folded into the sum), so decays are plain exp2
     constexpr float kLog2e = 1.4426950408889634f;
@@ -274,10 +287,9 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
     {
         float2 run = make_float2(0.f, 0.f);
 #pragma unroll
-        for (int ii = 0; ii < 16; ++ii) {
-            const bool in = 16 * w + ii < len;   // rows past the end keep G at G_L
-            run.x += in ? kLog2e * lo_bf(ula[ii]) : 0.0f;
-            run.y += in ? kLog2e * hi_bf(ula[ii]) : 0.0f;
+        for (int ii = 0; ii < 16; ++ii) {   // rows past the end are 0: G stays at G_L
+            run.x += kLog2e * lo_bf(ula[ii]);
+            run.y += kLog2e * hi_bf(ula[ii]);
             G[ii] = run;
         }
         tot[w * 128 + 2 * l] = run.x;
@@ -356,13 +368,15 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
             }
             const float r = __builtin_amdgcn_rsqf(
                 wave_sum_pair(x[0][0] * x[0][0] + x[0][1] * x[0][1], x[1][0] * x[1][0] + x[1][1] * x[1][1]) + eps_n);
-            const float rq = lane_value(r, 0), rk = lane_value(r, 16);
-            if (tk < len) {
-                q2 = make_float2(x[0][0] * rq, x[0][1] * rq);
-                k2 = make_float2(x[1][0] * rk, x[1][1] * rk);
-                v2 = make_float2(x[2][0], x[2][1]);
-            }
-        } else if (tk < len) {
+            // tokens past the end: q, k scaled to 0 (their conv window still
+            // holds real rows); v needs nothing, every product of v carries
+            // beta = 0
+            const bool live = tk < len;
+            const float rq = live ? lane_value(r, 0) : 0.0f, rk = live ? lane_value(r, 16) : 0.0f;
+            q2 = make_float2(x[0][0] * rq, x[0][1] * rq);
+            k2 = make_float2(x[1][0] * rk, x[1][1] * rk);
+            v2 = make_float2(x[2][0], x[2][1]);
+        } else {   // rows past the end are 0
             q2 = make_float2(lo_bf(uq[ii]), hi_bf(uq[ii]));
             k2 = make_float2(lo_bf(uk[ii]), hi_bf(uk[ii]));
             v2 = make_float2(lo_bf(uv[ii]), hi_bf(uv[ii]));
@@ -404,11 +418,13 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
 #pragma unroll
                 for (int s = 0; s < 4; ++s)
                     acc = mfma16(a[s], lds_frag(lds, kOffKi + ((16 * J + c16) * kRowA + 32 * s + 8 * g) * 2), acc);
+                // every entry is written, the diagonal and above as 0 (no
+                // divergent stores; the inverse reads the blocks unmasked)
                 const int j = 16 * J + c16;
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int i = 16 * I + 4 * g + r;
-                    if (j < i) A[aix(i, j)] = bi[r] * acc[r];
+                    A[aix(i, j)] = J < I || j < i ? bi[r] * acc[r] : 0.0f;
                 }
             }
         }
@@ -487,8 +503,9 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
         v[3] = hi[1];
         *reinterpret_cast<u32x4 *>(rec + kOffKg + ((mm * 2 + sp) * 64 + l) * 16) = v;
     }
-    // Blocked inverse of the unit-lower-triangular I + A (A strictly lower,
-    // only its strictly-lower entries are valid):
+    // Blocked inverse of the unit-lower-triangular I + A (A strictly lower;
+    // the diagonal blocks hold zeros on and above their diagonals, the blocks
+    // above them are never read):
     //   T_II = (I + A_II)^-1 per wave (block w): with P = -A_ww, nilpotent
     //        (P^16 = 0), (I + P)(I + P^2)(I + P^4)(I + P^8) = I + P + .. + P^15
     //        is the inverse; six 16x16 fp32 MFMA products, written over A_II,
@@ -518,13 +535,12 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
             for (int r = 0; r < 4; ++r) sc[(4 * g + r) * 20 + c16] = c[r];
             return *reinterpret_cast<const f32x4 *>(sc + c16 * 20 + 4 * g);
         };
-        f32x4 Pc, Pr;   // P = -A_ww: C layout and row layout (entries j >= i are not valid in A)
+        f32x4 Pc, Pr;   // P = -A_ww: C layout and row layout (A_ww is 0 on and above its diagonal)
         const f32x4 arow = a_row4(16 * w + c16, 4 * w + g);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
-            const int i = 4 * g + r;
-            Pc[r] = c16 < i ? -A[aix(16 * w + i, 16 * w + c16)] : 0.0f;
-            Pr[r] = 4 * g + r < c16 ? -arow[r] : 0.0f;
+            Pc[r] = -A[aix(16 * w + 4 * g + r, 16 * w + c16)];
+            Pr[r] = -arow[r];
         }
         const f32x4 P2c = mm(Pr, Pc);
         const f32x4 P2r = to_rows(P2c);

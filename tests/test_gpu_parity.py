@@ -288,6 +288,29 @@ def test_prefill_many_sequences():
         assert np.array_equal(S[3], inp["initial_state"][3].double().numpy())
 
 
+def test_prefill_nonfinite_sequence_stays_isolated():
+    """One sequence of a packed batch holds NaN / inf in every input; its
+    neighbours' outputs, final states and conv caches still match the oracle
+    run without it (a chunk never mixes rows past its end, which here belong
+    to the poisoned sequence, into its results).  Fused and unfused paths."""
+    lens = [37, 50, 64, 10]
+    inp = ki.prefill_inputs(97, lens, H=2, d=128, K=4, cache_std=1.0)
+    cu = inp["cu_seqlens"].tolist()
+    bad = dict(inp)
+    for key, val in (("q_raw", float("nan")), ("k_raw", float("inf")), ("v_raw", float("nan")),
+                     ("log_alpha", float("nan")), ("beta_logit", float("nan")), ("gate_logit", float("-inf"))):
+        t = inp[key].clone()
+        t[cu[1]:cu[2]] = val
+        bad[key] = t
+    keep = [0, 2, 3]
+    ref = ORC.prefill(slice_seqs(inp, keep))
+    for name, res in (("fused", gpu_prefill_fused(bad)), ("unfused", gpu_prefill(bad))):
+        y, S, cc = np64(res["y"]), np64(res["final_state"]), np64(res["conv_cache"])
+        assert_chunk_close(np.concatenate([y[cu[n]:cu[n + 1]] for n in keep]), ref["y"], f"{name} y")
+        assert_chunk_close(S[keep], ref["final_state"], f"{name} final state")
+        assert_fp32_close(cc[keep], ref["conv_cache"], f"{name} conv cache", 0.0)
+
+
 def test_prefill_fused_alias_nogate_scale_and_matches_unfused():
     inp = ki.prefill_inputs(90, [150, 77], H=2, d=128, K=4, cache_std=1.0)
     scale = 128 ** -0.5
