@@ -12,6 +12,8 @@ composes its steps in the method's order:
     prefill:  conv+act (q, k, v)  ->  L2(q), L2(k)  ->  beta = sigmoid,
               gate = sigmoid  ->  recurrence  ->  y, final state, conv cache
     decode:   one more prefill token per row, state and conv cache in place
+    backward: gradients of the recurrence with respect to q, k, v, log alpha,
+              beta, gate and the initial state
 
 Function citations are in ``kda_oracle.c``.
 """
@@ -78,6 +80,9 @@ class Oracle:
         L.kda_oracle_sigmoid.argtypes = [ctypes.c_long, _D, _D]
         L.kda_oracle_recurrence.argtypes = [ctypes.c_int, _I, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                             _D, _D, _D, _D, _D, _D, ctypes.c_double, _D, _D, _D]
+        L.kda_oracle_recurrence_backward.argtypes = [ctypes.c_int, _I, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                     _D, _D, _D, _D, _D, _D, ctypes.c_double, _D, _D, _D,
+                                                     _D, _D, _D, _D, _D, _D, _D]
         L.kda_oracle_decode_step.argtypes = [ctypes.c_int, _I, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                              ctypes.c_int, ctypes.c_double, ctypes.c_double,
                                              _D, _D, _D, _D, _D, _D, _D, _D, _D, _D]
@@ -125,6 +130,25 @@ class Oracle:
         self.lib.kda_oracle_recurrence(N, _p(cu, _I), H, dk, dv, _p(q), _p(k), _p(v), _p(la),
                                        _p(beta), _p(gate), float(scale), _p(s0), _p(y), _p(S))
         return y, S
+
+    def recurrence_backward(self, q, k, v, la, beta, gate, cu, dy, ds_final=None, scale=1.0, s0=None):
+        """Gradients of recurrence(): dy [T, H, dv] on the outputs and ds_final
+        None or [N, H, dk, dv] on the final states.  Returns a dict with dq, dk,
+        dv, dla, dbeta, dgate (None without a gate) and ds0, shaped like the
+        matching inputs."""
+        q, k, v, la, beta, gate, s0, dy, ds_final = map(_f64, (q, k, v, la, beta, gate, s0, dy, ds_final))
+        cu = _i32(cu)
+        T, H, dk = q.shape
+        dv = v.shape[2]
+        N = cu.shape[0] - 1
+        out = dict(dq=np.zeros((T, H, dk)), dk=np.zeros((T, H, dk)), dv=np.zeros((T, H, dv)),
+                   dla=np.zeros((T, H, dk)), dbeta=np.zeros((T, H)),
+                   dgate=np.zeros((T, H, dv)) if gate is not None else None, ds0=np.zeros((N, H, dk, dv)))
+        self.lib.kda_oracle_recurrence_backward(
+            N, _p(cu, _I), H, dk, dv, _p(q), _p(k), _p(v), _p(la), _p(beta), _p(gate), float(scale), _p(s0),
+            _p(dy), _p(ds_final), _p(out["dq"]), _p(out["dk"]), _p(out["dv"]), _p(out["dla"]), _p(out["dbeta"]),
+            _p(out["dgate"]), _p(out["ds0"]))
+        return out
 
     # ---- composed paths ----------------------------------------------------
     def prologue(self, inp, act=ACT_SILU, eps=L2_EPS, cache_in=None):

@@ -23,6 +23,9 @@
  *  - beta = sigmoid(beta_logit) per (token, head) and the output gate
  *    sigmoid(gate_logit) per (token, head, value channel) ("KDA output
  *    gating", forum post, implementation list);
+ *  - the gradient of the recurrence with respect to q, k, v, log alpha,
+ *    beta, the gate and the initial state (reverse mode, token by token; the
+ *    k3 README's functional proxy checks gradients of a KDA layer);
  *  - the decode step as conv update, then recurrent step (kimi_k3 API docs,
  *    Functions: kda_decode_token): one more prefill token that reads and
  *    rewrites the per-sequence conv cache and recurrent state in place (the
@@ -228,4 +231,112 @@ void kda_oracle_decode_step(int batch, const int32_t *slot_idx, int H, int d, in
     free(xv);
     free(xk);
     free(xq);
+}
+
+/*
+ * Reverse-mode gradient of kda_oracle_recurrence (the chunked KDA backward
+ * that the k3 README's training proxy exercises: gradients of a KDA layer,
+ * "Functional tiny proxy"), taken token by token from the same definition:
+ *   P = Diag(alpha) S_{t-1},  w = P^T k,  u = beta (v - w),  S_t = P + k u^T,
+ *   o = scale S_t^T q,  y = o (.) g.
+ * Given dy [T][H][dv] and ds_final NULL (zeros) or [n][H][dk][dv] (the
+ * gradient arriving at each final state), walking each sequence backwards:
+ *   do = dy (.) g,  dg = dy (.) o,  dq = scale S_t do,  dS += scale q do^T,
+ *   du = dS^T k,  dk = dS u,  dbeta = du . (v - w),  dv = beta du,
+ *   dw = -beta du,  dP = dS + k dw^T,  dk += P dw,
+ *   dla_i = alpha_i sum_j dP_ij S_{t-1,ij},  dS_{t-1} = Diag(alpha) dP.
+ * The forward states S_0 .. S_L of a (sequence, head) are all kept, so this
+ * is for the small sizes the tests use.  Outputs: dq, dk_ [T][H][dk],
+ * dv_ [T][H][dv], dla [T][H][dk], dbeta [T][H], dgate [T][H][dv] (only
+ * when gate is given), ds0 [n][H][dk][dv] (the gradient of the initial state).
+ */
+void kda_oracle_recurrence_backward(int n_seqs, const int32_t *cu, int H, int dk, int dv,
+                                    const double *q, const double *k, const double *v,
+                                    const double *la, const double *beta, const double *gate,
+                                    double scale, const double *s0, const double *dy,
+                                    const double *ds_final, double *dq, double *dk_, double *dv_,
+                                    double *dla, double *dbeta, double *dgate, double *ds0) {
+    const long SS = (long)dk * dv;
+#pragma omp parallel for collapse(2) schedule(dynamic)
+    for (int n = 0; n < n_seqs; ++n) {
+        for (int h = 0; h < H; ++h) {
+            const long L = cu[n + 1] - cu[n];
+            double *St = (double *)malloc(sizeof(double) * (size_t)((L + 1) * SS));
+            double *dS = (double *)malloc(sizeof(double) * (size_t)SS);
+            double *dP = (double *)malloc(sizeof(double) * (size_t)SS);
+            double *vec = (double *)malloc(sizeof(double) * (size_t)(6 * dv));
+            double *o = vec, *dov = vec + dv, *w = vec + 2 * dv, *u = vec + 3 * dv, *du = vec + 4 * dv,
+                   *dw = vec + 5 * dv;
+            double *ytmp = (double *)malloc(sizeof(double) * (size_t)dv);
+            double *kTD = (double *)malloc(sizeof(double) * (size_t)dv);
+            if (s0) memcpy(St, s0 + ((long)n * H + h) * SS, sizeof(double) * (size_t)SS);
+            else memset(St, 0, sizeof(double) * (size_t)SS);
+            for (long s = 0; s < L; ++s) {   /* forward, keeping every state */
+                const long th = (cu[n] + s) * H + h;
+                memcpy(St + (s + 1) * SS, St + s * SS, sizeof(double) * (size_t)SS);
+                token_step(St + (s + 1) * SS, dk, dv, q + th * dk, k + th * dk, v + th * dv, la + th * dk,
+                           beta[th], gate ? gate + th * dv : NULL, scale, kTD, ytmp);
+            }
+            if (ds_final) memcpy(dS, ds_final + ((long)n * H + h) * SS, sizeof(double) * (size_t)SS);
+            else memset(dS, 0, sizeof(double) * (size_t)SS);
+            for (long s = L - 1; s >= 0; --s) {
+                const long th = (cu[n] + s) * H + h;
+                const double *Sp = St + s * SS, *Sc = St + (s + 1) * SS;
+                const double *qt = q + th * dk, *kt = k + th * dk, *vt = v + th * dv, *lat = la + th * dk;
+                const double *gt = gate ? gate + th * dv : NULL, *dyt = dy + th * dv;
+                const double bt = beta[th];
+                for (int j = 0; j < dv; ++j) {
+                    double acc = 0.0;
+                    for (int i = 0; i < dk; ++i) acc += Sc[(long)i * dv + j] * qt[i];
+                    o[j] = scale * acc;
+                    dov[j] = dyt[j] * (gt ? gt[j] : 1.0);
+                    if (gt) dgate[th * dv + j] = dyt[j] * o[j];
+                }
+                for (int i = 0; i < dk; ++i) {
+                    double acc = 0.0;
+                    for (int j = 0; j < dv; ++j) acc += Sc[(long)i * dv + j] * dov[j];
+                    dq[th * dk + i] = scale * acc;
+                }
+                for (int i = 0; i < dk; ++i)
+                    for (int j = 0; j < dv; ++j) dS[(long)i * dv + j] += scale * qt[i] * dov[j];
+                for (int j = 0; j < dv; ++j) {
+                    double aw = 0.0, ad = 0.0;
+                    for (int i = 0; i < dk; ++i) {
+                        aw += exp(lat[i]) * Sp[(long)i * dv + j] * kt[i];
+                        ad += dS[(long)i * dv + j] * kt[i];
+                    }
+                    w[j] = aw;
+                    u[j] = bt * (vt[j] - aw);
+                    du[j] = ad;
+                }
+                double db = 0.0;
+                for (int j = 0; j < dv; ++j) {
+                    db += du[j] * (vt[j] - w[j]);
+                    dv_[th * dv + j] = bt * du[j];
+                    dw[j] = -bt * du[j];
+                }
+                dbeta[th] = db;
+                for (int i = 0; i < dk; ++i) {
+                    const double a = exp(lat[i]);
+                    double acc = 0.0, accd = 0.0;
+                    for (int j = 0; j < dv; ++j) {
+                        const long e = (long)i * dv + j;
+                        acc += dS[e] * u[j] + a * Sp[e] * dw[j];
+                        dP[e] = dS[e] + kt[i] * dw[j];
+                        accd += dP[e] * Sp[e];
+                    }
+                    dk_[th * dk + i] = acc;
+                    dla[th * dk + i] = a * accd;
+                    for (int j = 0; j < dv; ++j) dS[(long)i * dv + j] = a * dP[(long)i * dv + j];
+                }
+            }
+            memcpy(ds0 + ((long)n * H + h) * SS, dS, sizeof(double) * (size_t)SS);
+            free(kTD);
+            free(ytmp);
+            free(vec);
+            free(dP);
+            free(dS);
+            free(St);
+        }
+    }
 }
