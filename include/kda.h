@@ -226,6 +226,38 @@ kda_status kda_decode_step(const kda_geom *geom, int32_t batch, const int32_t *s
                            const void *beta_logit, const void *gate_logit, kda_dtype out_dtype,
                            void *out, void *stream);
 
+/*
+ * kda_chunk_backward: gradients of kda_chunk_forward with respect to its
+ * inputs (reverse-mode differentiation of the recurrence of the Vulkan-backend
+ * forum post's "recurrent KDA state", taken through the chunked WY/UT form;
+ * the k3 README's functional tiny proxy checks such KDA-layer gradients).
+ *   geom: d = 128 (as kda_chunk_forward); in_dtype must be KDA_BF16;
+ *   q, k, v, log_alpha, beta, gate, initial_state: exactly the forward call's
+ *     inputs (gate NULL when the forward had none; initial_state NULL = zeros);
+ *   dy [T][H][128] bf16: gradient of the loss with respect to `out`;
+ *   d_final_state NULL (zeros) or [n_seqs][H][128][128] fp32: gradient with
+ *     respect to `final_state`;
+ *   outputs, fp32, caller-owned and overwritten: dq, dk, dv, dlog_alpha
+ *     [T][H][128]; dbeta [T][H]; dgate [T][H][128] (required when gate is
+ *     given, ignored otherwise); d_initial_state NULL (skip) or
+ *     [n_seqs][H][128][128];
+ *   workspace: device buffer of at least kda_chunk_backward_workspace_bytes()
+ *     bytes, 16-byte aligned, contents not needed before or after the call
+ *     (819,712 B per (chunk, head) plus the chunk table).
+ * Runs the forward's chunk quantities again (nothing from a forward call is
+ * reused) and is stream-ordered like every other entry point.  Errors as for
+ * kda_chunk_forward; nothing is launched when validation fails.
+ */
+size_t kda_chunk_backward_workspace_bytes(const kda_geom *geom, int32_t n_seqs, const int32_t *cu_seqlens_host);
+
+kda_status kda_chunk_backward(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
+                              const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host,
+                              kda_dtype in_dtype, const void *q, const void *k, const void *v,
+                              const void *log_alpha, const float *beta, const void *gate,
+                              const float *initial_state, const void *dy, const float *d_final_state,
+                              float *dq, float *dk, float *dv, float *dlog_alpha, float *dbeta, float *dgate,
+                              float *d_initial_state, void *workspace, size_t workspace_bytes, void *stream);
+
 /* Short name of a status code (static string). */
 const char *kda_status_str(kda_status s);
 /* Sentence describing the last error returned on the calling thread ("" if none). */

@@ -6,6 +6,7 @@ include/kda.h); this package is its thin Python binding:
     prologue(...)       short conv + activation + L2(q, k) + sigmoid gates
     chunk_forward(...)  chunked prefill over packed varlen sequences
     prefill(...)        the same from raw inputs, prologue fused into the chunk path
+    chunk_backward(...) gradients of chunk_forward
     decode_step(...)    one token for a batch of resident fp32 states
 
 Build the library with ``python -m kimi_delta_attention_07_amd.build``.
@@ -14,6 +15,8 @@ from ._lib import (  # noqa: F401
     CHUNK,
     EXPORTS,
     KdaError,
+    chunk_backward,
+    chunk_backward_workspace_bytes,
     chunk_forward,
     chunk_prepare,
     chunk_scan,

@@ -21,7 +21,7 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE"
           5: "KDA_ERR_SEQLENS", 6: "KDA_ERR_WORKSPACE", 7: "KDA_ERR_ALIGN", 8: "KDA_ERR_HIP"}
 EXPORTS = ("kda_prologue", "kda_chunk_workspace_bytes", "kda_chunk_forward", "kda_chunk_prepare",
            "kda_chunk_scan", "kda_prefill", "kda_prefill_prepare", "kda_prefill_scan", "kda_decode_step",
-           "kda_status_str", "kda_last_error_detail")
+           "kda_chunk_backward_workspace_bytes", "kda_chunk_backward", "kda_status_str", "kda_last_error_detail")
 
 
 class KdaError(RuntimeError):
@@ -56,6 +56,10 @@ def load(path=LIB_PATH):
     L.kda_chunk_workspace_bytes.restype = ctypes.c_size_t
     L.kda_chunk_forward.argtypes = [G, _I, _I, _P, _P, _I] + [_P] * 10 + [ctypes.c_size_t, _P]
     L.kda_chunk_forward.restype = _I
+    L.kda_chunk_backward_workspace_bytes.argtypes = [G, _I, _P]
+    L.kda_chunk_backward_workspace_bytes.restype = ctypes.c_size_t
+    L.kda_chunk_backward.argtypes = [G, _I, _I, _P, _P, _I] + [_P] * 17 + [ctypes.c_size_t, _P]
+    L.kda_chunk_backward.restype = _I
     L.kda_chunk_prepare.argtypes = [G, _I, _I, _P, _P, _I] + [_P] * 6 + [ctypes.c_size_t, _P]
     L.kda_chunk_prepare.restype = _I
     L.kda_chunk_scan.argtypes = [G, _I, _I, _P, _P, _I] + [_P] * 5 + [ctypes.c_size_t, _P]
@@ -160,6 +164,37 @@ def chunk_forward(q, k, v, log_alpha, beta, gate, cu_seqlens, initial_state=None
                                     _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(gate), _ptr(initial_state),
                                     _ptr(final_state), _ptr(out), _ptr(workspace), workspace.numel(), _stream(q)))
     return out, final_state
+
+
+def chunk_backward_workspace_bytes(H, d, cu_seqlens_host):
+    h = cu_seqlens_host.to("cpu", torch.int32).contiguous()
+    g = geom(H, d, 4)
+    return int(load().kda_chunk_backward_workspace_bytes(ctypes.byref(g), h.numel() - 1,
+                                                         ctypes.cast(h.data_ptr(), ctypes.c_void_p)))
+
+
+def chunk_backward(q, k, v, log_alpha, beta, gate, cu_seqlens, dy, initial_state=None, d_final_state=None, *,
+                   scale=1.0, workspace=None, cu_seqlens_host=None, want_d_initial_state=True):
+    """Gradients of chunk_forward (d = 128, bf16 inputs; fp32 gradients).
+    Returns a dict with dq, dk, dv, dlog_alpha, dbeta, dgate (None without a
+    gate) and d_initial_state (None when not wanted)."""
+    T, H, d = q.shape
+    n = cu_seqlens.numel() - 1
+    hcu, hptr = _host_cu(cu_seqlens, cu_seqlens_host)
+    if workspace is None:
+        workspace = torch.empty(chunk_backward_workspace_bytes(H, d, hcu), dtype=torch.uint8, device=q.device)
+    f32 = dict(dtype=torch.float32, device=q.device)
+    g_out = dict(dq=torch.empty((T, H, d), **f32), dk=torch.empty((T, H, d), **f32),
+                 dv=torch.empty((T, H, d), **f32), dlog_alpha=torch.empty((T, H, d), **f32),
+                 dbeta=torch.empty((T, H), **f32), dgate=torch.empty((T, H, d), **f32) if gate is not None else None,
+                 d_initial_state=torch.empty((n, H, d, d), **f32) if want_d_initial_state else None)
+    g = geom(H, d, 4, scale=scale)
+    _check(load().kda_chunk_backward(
+        ctypes.byref(g), n, T, _ptr(cu_seqlens), hptr, _dtype(q), _ptr(q), _ptr(k), _ptr(v), _ptr(log_alpha),
+        _ptr(beta), _ptr(gate), _ptr(initial_state), _ptr(dy), _ptr(d_final_state), _ptr(g_out["dq"]),
+        _ptr(g_out["dk"]), _ptr(g_out["dv"]), _ptr(g_out["dlog_alpha"]), _ptr(g_out["dbeta"]), _ptr(g_out["dgate"]),
+        _ptr(g_out["d_initial_state"]), _ptr(workspace), workspace.numel(), _stream(q)))
+    return g_out
 
 
 def chunk_prepare(q, k, v, log_alpha, beta, cu_seqlens, workspace, *, cu_seqlens_host=None):

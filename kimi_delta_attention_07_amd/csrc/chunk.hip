@@ -34,6 +34,7 @@
 // unchanged; the scan uses k order {4g..4g+3, 16+4g..16+4g+3} inside each
 // 32-wide k step so that the state and U accumulators (C layout) become the
 // B operand of the next product with no data movement.
+#include "kda_chunk_table.h"
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -92,41 +93,6 @@ __device__ __forceinline__ unsigned char *record(const ChunkParams &p, long cid,
     return p.records + ((long)h * p.n_chunks + cid) * (long)kChunkRecordBytes;
 }
 
-// A chunk record as the kernels may use it: the table is built on the device
-// from cu_seqlens_dev while grids are sized from the host copy; should the two
-// ever disagree, out-of-range entries become empty chunks instead of stray
-// memory accesses.
-__device__ __forceinline__ ChunkInfo load_chunk(const ChunkParams &p, int cid) {
-    if (p.plan_in_args) {
-        // the sequence holding chunk cid: the last n with plan_off[n] <= cid
-        // (empty sequences share their offset with the next one)
-        int lo = 0, hi = p.n_seqs - 1;
-        while (lo < hi) {
-            const int mid = (lo + hi + 1) >> 1;
-            if (p.plan_off[mid] <= cid) lo = mid;
-            else hi = mid - 1;
-        }
-        ChunkInfo ci;
-        ci.seq = lo;
-        ci.first = cid == p.plan_off[lo];
-        ci.start = p.plan_cu[lo] + kChunk * (cid - p.plan_off[lo]);
-        ci.len = max(0, min(kChunk, p.plan_cu[lo + 1] - ci.start));
-        return ci;
-    }
-    ChunkInfo ci = p.chunk_info[cid];
-    ci.start = __builtin_amdgcn_readfirstlane(ci.start);
-    ci.len = __builtin_amdgcn_readfirstlane(ci.len);
-    ci.seq = __builtin_amdgcn_readfirstlane(ci.seq);
-    ci.first = __builtin_amdgcn_readfirstlane(ci.first);
-    if (ci.start < 0 || ci.len < 0 || ci.len > kChunk || ci.start > p.T - ci.len || ci.seq < 0 ||
-        ci.seq >= p.n_seqs) {
-        ci.start = 0;
-        ci.len = 0;
-        ci.seq = 0;
-        ci.first = 0;
-    }
-    return ci;
-}
 
 // ---------------------------------------------------------------------------
 // prepare
@@ -966,6 +932,13 @@ template <int KC>
 void launch_fused_prepare(const ChunkParams &p, dim3 grid, hipStream_t s) {
     if (p.act == 1) hipLaunchKernelGGL((prepare_kernel<true, KC, 1>), grid, dim3(256), 0, s, p);
     else hipLaunchKernelGGL((prepare_kernel<true, KC, 0>), grid, dim3(256), 0, s, p);
+}
+
+hipError_t launch_chunk_plan(const ChunkParams &p, hipStream_t s) {
+    if (!p.plan_in_args)
+        hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(256), 0, s, p.cu, p.n_seqs, p.n_chunks, p.chunk_off,
+                           p.chunk_info);
+    return hipGetLastError();
 }
 
 hipError_t launch_chunk_prepare(const ChunkParams &p, hipStream_t s) {

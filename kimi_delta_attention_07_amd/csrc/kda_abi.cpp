@@ -172,6 +172,65 @@ kda::ChunkParams chunk_params(const kda_geom *geom, int32_t n_seqs, int32_t tota
 
 extern "C" {
 
+size_t kda_chunk_backward_workspace_bytes(const kda_geom *geom, int32_t n_seqs, const int32_t *cu_seqlens_host) {
+    if (check_geom(geom, true) != KDA_OK) return 0;
+    if (n_seqs <= 0 || !cu_seqlens_host) return 0;
+    long n_chunks = 0;
+    if (check_seqlens(n_seqs, cu_seqlens_host[n_seqs], cu_seqlens_host, &n_chunks) != KDA_OK) return 0;
+    return kda::bwd_workspace_bytes(geom->H, n_seqs, n_chunks);
+}
+
+kda_status kda_chunk_backward(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
+                              const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host, kda_dtype in_dtype,
+                              const void *q, const void *k, const void *v, const void *log_alpha, const float *beta,
+                              const void *gate, const float *initial_state, const void *dy,
+                              const float *d_final_state, float *dq, float *dk, float *dv, float *dlog_alpha,
+                              float *dbeta, float *dgate, float *d_initial_state, void *workspace,
+                              size_t workspace_bytes, void *stream) {
+    KDA_TRY(check_geom(geom, true));
+    long n_chunks = 0;
+    KDA_TRY(check_seqlens(n_seqs, total_tokens, cu_seqlens_host, &n_chunks));
+    KDA_TRY(check_dtype(in_dtype));
+    if (in_dtype != KDA_BF16) return fail(KDA_ERR_UNSUPPORTED, "the chunk path takes bf16 inputs only");
+    KDA_TRY(check_required({{cu_seqlens_dev, "cu_seqlens_dev"}, {workspace, "workspace"}}));
+    if (total_tokens > 0)
+        KDA_TRY(check_required({{q, "q"}, {k, "k"}, {v, "v"}, {log_alpha, "log_alpha"}, {beta, "beta"}, {dy, "dy"},
+                                {dq, "dq"}, {dk, "dk"}, {dv, "dv"}, {dlog_alpha, "dlog_alpha"}, {dbeta, "dbeta"}}));
+    if (gate && total_tokens > 0 && !dgate) return fail(KDA_ERR_NULL, "dgate is NULL while gate is given");
+    KDA_TRY(check_aligned({{workspace, "workspace"}, {q, "q"}, {k, "k"}, {v, "v"}, {log_alpha, "log_alpha"},
+                           {beta, "beta"}, {gate, "gate"}, {initial_state, "initial_state"}, {dy, "dy"},
+                           {d_final_state, "d_final_state"}, {dq, "dq"}, {dk, "dk"}, {dv, "dv"},
+                           {dlog_alpha, "dlog_alpha"}, {dbeta, "dbeta"}, {dgate, "dgate"},
+                           {d_initial_state, "d_initial_state"}}));
+    const size_t need = kda::bwd_workspace_bytes(geom->H, n_seqs, n_chunks);
+    if (workspace_bytes < need)
+        return fail(KDA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    if ((long)n_seqs * geom->H * kda::kTilesV > 0x7fffffffL || n_chunks * geom->H > 0x7fffffffL)
+        return fail(KDA_ERR_SHAPE, "too many sequences or chunks x heads");
+    KDA_TRY(check_device());
+    kda::BwdParams p{};
+    p.c = chunk_params(geom, n_seqs, total_tokens, n_chunks, cu_seqlens_dev, cu_seqlens_host, workspace);
+    kda::bwd_workspace_carve(workspace, geom->H, n_seqs, n_chunks, p);
+    p.c.records = nullptr;
+    p.c.q = static_cast<const uint16_t *>(q);
+    p.c.k = static_cast<const uint16_t *>(k);
+    p.c.v = static_cast<const uint16_t *>(v);
+    p.c.log_alpha = static_cast<const uint16_t *>(log_alpha);
+    p.c.beta = beta;
+    p.c.gate = static_cast<const uint16_t *>(gate);
+    p.c.s0 = initial_state;
+    p.dy = static_cast<const uint16_t *>(dy);
+    p.ds_final = d_final_state;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.dla = dlog_alpha;
+    p.dbeta = dbeta;
+    p.dgate = gate ? dgate : nullptr;
+    p.ds0 = d_initial_state;
+    return launched(kda::launch_chunk_backward(p, (hipStream_t)stream), "chunk backward");
+}
+
 const char *kda_status_str(kda_status s) {
     switch (s) {
         case KDA_OK: return "KDA_OK";

@@ -91,6 +91,26 @@ struct DecodeParams {
     void *out;
 };
 
+// Backward of the chunk path.  Per (chunk, head) the workspace holds fp32
+// row-major matrices (kBwdFloats floats; layout in backward.hip): the chunk's
+// WY quantities, its entry state S0 and U from a forward state pass, the
+// state gradient at its end, dO and dU from a backward state pass, and
+// scratch for the per-chunk gradient products.
+struct BwdParams {
+    ChunkParams c;              // geometry, chunk table, forward inputs (q, k, v, log_alpha, beta, gate, s0)
+    float *buf;                 // [n_chunks * H][kBwdFloats]
+    const uint16_t *dy;         // [T][H][128] bf16: gradient of the output
+    const float *ds_final;      // [n_seqs][H][128][128] or null: gradient of the final state
+    float *dq, *dk, *dv, *dla;  // [T][H][128]
+    float *dbeta;               // [T][H]
+    float *dgate;               // [T][H][128], null when there is no gate
+    float *ds0;                 // [n_seqs][H][128][128] or null
+};
+hipError_t launch_chunk_plan(const ChunkParams &p, hipStream_t s);
+hipError_t launch_chunk_backward(const BwdParams &p, hipStream_t s);
+size_t bwd_workspace_bytes(int H, int n_seqs, long n_chunks);
+void bwd_workspace_carve(void *ws, int H, int n_seqs, long n_chunks, BwdParams &p);
+
 // dtype codes match kda_dtype: 0 = fp32, 1 = bf16.
 hipError_t launch_prologue(const PrologueParams &p, int dtype, hipStream_t s);
 hipError_t launch_chunk_prepare(const ChunkParams &p, hipStream_t s);

@@ -209,3 +209,36 @@ def test_prefill_rejects(L):
     p = list(FAKE[:12])
     p[8] = ctypes.c_void_p(0x10006)   # gate_logit misaligned
     assert prefill(L, ptrs=p) == ALIGN
+
+
+def backward(L, geom=None, dtype=1, ws=FAKE[16], ws_bytes=1 << 40, ptrs=None, cu_vals=(0, 100, 228)):
+    t, hp = _cu(list(cu_vals))
+    p = list(FAKE[:16]) if ptrs is None else ptrs
+    return L.kda_chunk_backward(geom if geom is not None else _geom(), len(cu_vals) - 1, cu_vals[-1], FAKE[15], hp,
+                                dtype, *p, ws, ws_bytes, None)
+
+
+def test_backward_workspace_bytes(L):
+    t, hp = _cu([0, 100, 100, 228])
+    al = lambda x: (x + 255) // 256 * 256
+    assert L.kda_chunk_backward_workspace_bytes(_geom(H=2), 3, hp) == al(4 * 4) + al(16 * 4) + 4 * 2 * 819712
+    assert L.kda_chunk_backward_workspace_bytes(_geom(H=2, d=64), 3, hp) == 0
+
+
+def test_backward_rejects(L):
+    assert backward(L, geom=_geom(d=64)) == UNSUP
+    assert backward(L, dtype=0) == UNSUP
+    assert backward(L, dtype=5) == DTYPE
+    assert backward(L, ws=None) == NULL
+    assert backward(L, ws_bytes=1000) == WORKSPACE
+    assert backward(L, cu_vals=(0, 100, 50)) == SEQLENS
+    for i, name in ((0, "q"), (4, "beta"), (7, "dy"), (9, "dq"), (13, "dbeta")):
+        p = list(FAKE[:16])
+        p[i] = None
+        assert backward(L, ptrs=p) == NULL, name
+    p = list(FAKE[:16])
+    p[14] = None   # dgate missing while gate given
+    assert backward(L, ptrs=p) == NULL
+    p = list(FAKE[:16])
+    p[8] = ctypes.c_void_p(0x10004)   # d_final_state misaligned
+    assert backward(L, ptrs=p) == ALIGN
