@@ -15,6 +15,8 @@ step's inputs for the next.  value = prefill tokens/s.
 The metric's second half, decode, is measured in the same run on the batched
 decode workload (256 resident fp32 states x 1 token, 64 consecutive
 kda_decode_step calls with distinct inputs) and reported under "decode".
+The chunked backward (kda_chunk_backward) on the prefill workload's shapes is
+reported under "backward".
 
 Every kernel is timed with HIP events on the stream it is launched on; the
 roofline object is for the kernel that takes the longest, with the algorithmic
@@ -48,6 +50,12 @@ STATE_B = H * D * D * 4                                                        #
 CONV_CACHE_B = 3 * (K - 1) * H * D * 4
 FLOP_PER_TOK = 4_496_032                                                       # useful chunked-form flops (H=32)
 DECODE_B_PER_ROW = 2 * STATE_B + 2 * CONV_CACHE_B + 3 * 8192 + 8192 + 64 + 8192 + 16384   # 4,546,624
+# kda_chunk_backward: the dense fp32 products it executes per (64-token chunk,
+# head), in multiply-adds: WY quantities 4 C^2 d; forward state pass 2 C d^2;
+# backward state pass C^2 d + 3 C d^2; per-chunk gradients 8 C^2 d (+2 C^3)
+# + 6 C d^2 + ... (itemised in the design doc): 18,350,080 MACs.
+BWD_FLOP_PER_CHUNK_HEAD = 2 * 18_350_080
+FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector, TFLOP/s
 
 
 # bench timing slot -> kernel whose counters profiles/traffic.json holds
@@ -87,6 +95,8 @@ def parse():
     ap.add_argument("--decode-reps", type=int, default=3, help="timed passes of 64 decode steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
+    ap.add_argument("--no-backward", action="store_true", help="skip the chunked backward measurement")
+    ap.add_argument("--backward-steps", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--path", choices=("fused", "unfused"), default="fused")
     return ap.parse_args()
@@ -240,6 +250,45 @@ def cpu_baseline(ki, seconds):
                       f"on {cores} OpenMP threads (heads in parallel)"}
 
 
+def bench_backward(torch, kda, ki, args, dev):
+    """kda_chunk_backward on the prefill workload's shapes (T=4096, H=32):
+    the forward inputs come from the library's own prologue, dy and the
+    final-state gradient are seeded random."""
+    inp = ki.prefill_inputs(3, [4096], H=H, d=D, K=K)
+    g = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in inp.items()}
+    cu_h = inp["cu_seqlens"]
+    pro = kda.prologue(g["q_raw"], g["k_raw"], g["v_raw"], g["conv_w"], g["cu_seqlens"], g["beta_logit"],
+                       g["gate_logit"], g["conv_cache"], torch.empty_like(g["conv_cache"]), cu_seqlens_host=cu_h)
+    gen = torch.Generator().manual_seed(5)
+    dy = torch.randn(4096, H, D, generator=gen).to(torch.bfloat16).to(dev)
+    dsf = (torch.randn(1, H, D, D, generator=gen) * 0.1).to(dev)
+    ws = torch.empty(kda.chunk_backward_workspace_bytes(H, D, cu_h), dtype=torch.uint8, device=dev)
+
+    def one():
+        return kda.chunk_backward(pro["q"], pro["k"], pro["v"], g["log_alpha"], pro["beta"], pro["gate"],
+                                  g["cu_seqlens"], dy, g["initial_state"], dsf, workspace=ws, cu_seqlens_host=cu_h)
+
+    for _ in range(3):
+        one()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(args.backward_steps):
+        one()
+    b.record()
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / args.backward_steps
+    flop = (4096 // CHUNK) * H * BWD_FLOP_PER_CHUNK_HEAD
+    tf = flop / (ms * 1e-3) / 1e12
+    return {"workload": "chunked backward, 1 sequence x 4096 tokens, H=32 dk=dv=128, chunk 64, bf16 inputs and dy, "
+                        "fp32 gradients (dq, dk, dv, dlog alpha, dbeta, dgate, d initial state)",
+            "value": 4096 / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "steps": args.backward_steps,
+            "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf / FP32_PEAK_TFLOPS, "traffic": None,
+                         "kernel": "kda_chunk_backward (prep, fwd_states, bwd_states, grads)",
+                         "flop_per_launch": flop}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -284,6 +333,8 @@ def main():
     }
     if not args.no_decode:
         res["decode"] = bench_decode(torch, kda, ki, args, dev)
+    if not args.no_backward:
+        res["backward"] = bench_backward(torch, kda, ki, args, dev)
     res["copy_gbs"] = copy_bandwidth(torch, dev)
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(ki, args.cpu_seconds)

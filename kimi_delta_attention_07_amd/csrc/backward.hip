@@ -25,7 +25,7 @@
 //
 // Four kernels, all fp32 on the VALU with LDS-staged tiles:
 //   prep        chunks x heads: G, the decayed operands, A, T (forward
-//               substitution, one column per thread), W, U~, Pm
+//               substitution, one row at a time), W, U~, Pm
 //   fwd_states  sequences x heads x 8 value tiles: walks the chunks forward,
 //               writes each chunk's S0 and U
 //   bwd_states  the same grid backwards: dO, dS_L and dU per chunk, and the
@@ -59,12 +59,19 @@ __device__ __forceinline__ float *chunk_buf(const BwdParams &p, long cid, int h)
     return p.buf + (cid * p.c.H + h) * kBwdFloats;
 }
 
-// Sequence n's chunk range [c_begin, c_end), sanitised like the forward scan's.
-__device__ __forceinline__ void seq_chunks(const ChunkParams &c, int n, int &c_begin, int &c_end) {
+// Sequence n's chunk range [c_begin, c_end) and its first token and length,
+// sanitised like the forward scan's and kept in scalar registers (chunk j of
+// the sequence then starts at seq_start + 64 j: no table lookup per chunk).
+__device__ __forceinline__ void seq_chunks(const ChunkParams &c, int n, int &c_begin, int &c_end, int &seq_start,
+                                           int &seq_len) {
     const int off0 = c.plan_in_args ? c.plan_off[n] : c.chunk_off[n];
     const int off1 = c.plan_in_args ? c.plan_off[n + 1] : c.chunk_off[n + 1];
-    c_begin = max(0, off0);
-    c_end = min(c.n_chunks, off1);
+    const int cu0 = c.plan_in_args ? c.plan_cu[n] : c.cu[n];
+    const int cu1 = c.plan_in_args ? c.plan_cu[n + 1] : c.cu[n + 1];
+    c_begin = __builtin_amdgcn_readfirstlane(max(0, off0));
+    c_end = __builtin_amdgcn_readfirstlane(min(c.n_chunks, off1));
+    seq_start = __builtin_amdgcn_readfirstlane(min(max(cu0, 0), c.T));
+    seq_len = __builtin_amdgcn_readfirstlane(max(0, min(cu1, c.T) - seq_start));
 }
 
 // C[0:64][0:N] (= or +=) alpha op(A)[64][K] op(B)[K][N], by all 256 threads.
@@ -72,12 +79,13 @@ __device__ __forceinline__ void seq_chunks(const ChunkParams &c, int n, int &c_b
 //   op(B)[k][j] = TB ? B[j ldb + k] : B[k ldb + j]
 // MASK 1 keeps entries j <= i, 2 keeps j < i (the rest are written as 0, or
 // left alone when accumulating); rows >= mrows are not written.  N is 64 or
-// 128, K a multiple of 16.  The operands may be in global memory (written
-// earlier by this block: the barrier on entry orders them) or in LDS.
+// 128, K a multiple of 16; operands 16-byte aligned with lda, ldb multiples of
+// 4.  The operands may be in global memory (written earlier by this block:
+// the barrier on entry orders them) or in LDS.
 template <bool TA, bool TB, int MASK, bool ACC>
 __device__ void bmm(float *C, int ldc, const float *A, int lda, const float *B, int ldb, int N, int K, float alpha,
                     int mrows, float *sm) {
-    constexpr int LA = 65, LB = 129;   // padded LDS rows
+    constexpr int LA = 68, LB = 132;   // LDS rows, padded (multiples of 4 for 16-byte accesses)
     float *As = sm;                    // [16][LA]: As[kk][i]
     float *Bs = sm + 16 * LA;          // [16][LB]: Bs[kk][j]
     const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
@@ -88,39 +96,43 @@ __device__ void bmm(float *C, int ldc, const float *A, int lda, const float *B, 
         for (int c = 0; c < 8; ++c) acc[r][c] = 0.f;
     __syncthreads();
     for (int k0 = 0; k0 < K; k0 += 16) {
-        for (int e = tid; e < 16 * 64; e += kNT) {
-            int kk, i;
+        {   // op(A) slab [64][16]: one 16-byte load per thread
             if (TA) {
-                kk = e >> 6;
-                i = e & 63;
+                const int kk = tid >> 4, i4 = (tid & 15) * 4;
+                *reinterpret_cast<float4 *>(As + kk * LA + i4) =
+                    *reinterpret_cast<const float4 *>(A + (long)(k0 + kk) * lda + i4);
             } else {
-                i = e >> 4;
-                kk = e & 15;
+                const int i = tid >> 2, k4 = (tid & 3) * 4;
+                const float4 v = *reinterpret_cast<const float4 *>(A + (long)i * lda + k0 + k4);
+                As[k4 * LA + i] = v.x;
+                As[(k4 + 1) * LA + i] = v.y;
+                As[(k4 + 2) * LA + i] = v.z;
+                As[(k4 + 3) * LA + i] = v.w;
             }
-            As[kk * LA + i] = TA ? A[(long)(k0 + kk) * lda + i] : A[(long)i * lda + k0 + kk];
         }
-        for (int e = tid; e < 16 * N; e += kNT) {
-            int kk, j;
+        for (int e = tid; e < 4 * N; e += kNT) {   // op(B) slab [16][N]
             if (TB) {
-                j = e >> 4;
-                kk = e & 15;
+                const int j = e >> 2, k4 = (e & 3) * 4;
+                const float4 v = *reinterpret_cast<const float4 *>(B + (long)j * ldb + k0 + k4);
+                Bs[k4 * LB + j] = v.x;
+                Bs[(k4 + 1) * LB + j] = v.y;
+                Bs[(k4 + 2) * LB + j] = v.z;
+                Bs[(k4 + 3) * LB + j] = v.w;
             } else {
-                kk = e / N;
-                j = e % N;
+                const int q = N >> 2, kk = e / q, j4 = (e % q) * 4;
+                *reinterpret_cast<float4 *>(Bs + kk * LB + j4) =
+                    *reinterpret_cast<const float4 *>(B + (long)(k0 + kk) * ldb + j4);
             }
-            Bs[kk * LB + j] = TB ? B[(long)j * ldb + k0 + kk] : B[(long)(k0 + kk) * ldb + j];
         }
         __syncthreads();
 #pragma unroll 4
         for (int kk = 0; kk < 16; ++kk) {
-            float a[4], b[8];
-#pragma unroll
-            for (int r = 0; r < 4; ++r) a[r] = As[kk * LA + 4 * ty + r];
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-                b[c] = Bs[kk * LB + 4 * tx + c];
-                b[4 + c] = N > 64 ? Bs[kk * LB + 64 + 4 * tx + c] : 0.f;
-            }
+            const float4 a4 = *reinterpret_cast<const float4 *>(As + kk * LA + 4 * ty);
+            const float4 b0 = *reinterpret_cast<const float4 *>(Bs + kk * LB + 4 * tx);
+            const float4 b1 = N > 64 ? *reinterpret_cast<const float4 *>(Bs + kk * LB + 64 + 4 * tx)
+                                     : make_float4(0.f, 0.f, 0.f, 0.f);
+            const float a[4] = {a4.x, a4.y, a4.z, a4.w};
+            const float b[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
             for (int r = 0; r < 4; ++r)
 #pragma unroll
@@ -149,7 +161,7 @@ __device__ void bmm(float *C, int ldc, const float *A, int lda, const float *B, 
 
 // ---- prep: the chunk's WY quantities -----------------------------------------
 __global__ __launch_bounds__(kNT) void bwd_prep_kernel(BwdParams p) {
-    __shared__ float sm[16 * 65 + 16 * 129];
+    __shared__ __attribute__((aligned(16))) float sm[16 * 68 + 16 * 132];
     __shared__ float big[64 * 128];   // G, then A (first half) and T (second half)
     __shared__ float beta_s[64];
     const ChunkParams &c = p.c;
@@ -187,21 +199,23 @@ __global__ __launch_bounds__(kNT) void bwd_prep_kernel(BwdParams p) {
     __syncthreads();
     for (int e = tid; e < 64 * 64; e += kNT) big[e] *= beta_s[e >> 6];
     __syncthreads();
-    // T = (I + A)^-1: thread j solves column j top to bottom
+    // T = (I + A)^-1 row by row: T_ij = -sum_{j <= m < i} A_im T_mj (j < i);
+    // four threads share each column's sum
     float *Tm = big + 64 * 64;
-    if (tid < 64) {
-        const int j = tid;
-        for (int i = 0; i < 64; ++i) {
-            float t = i == j ? 1.f : 0.f;
-            if (i > j) {
-                float s = 0.f;
-                for (int m = j; m < i; ++m) s += big[i * 64 + m] * Tm[m * 64 + j];
-                t = -s;
-            }
-            Tm[i * 64 + j] = t;
+    __shared__ float part[kNT];
+    for (int e = tid; e < 64 * 64; e += kNT) Tm[e] = (e >> 6) == (e & 63) ? 1.f : 0.f;
+    __syncthreads();
+    {
+        const int j = tid & 63, q = tid >> 6;
+        for (int i = 1; i < 64; ++i) {
+            float sum = 0.f;
+            for (int m = j + q; m < i; m += 4) sum += big[i * 64 + m] * Tm[m * 64 + j];
+            part[tid] = sum;
+            __syncthreads();
+            if (q == 0 && j < i) Tm[i * 64 + j] = -(part[j] + part[64 + j] + part[128 + j] + part[192 + j]);
+            __syncthreads();
         }
     }
-    __syncthreads();
     for (int e = tid; e < 64 * 64; e += kNT) {
         B[bT + e] = Tm[e];
         B[bTB + e] = Tm[e] * beta_s[e & 63];
@@ -211,63 +225,162 @@ __global__ __launch_bounds__(kNT) void bwd_prep_kernel(BwdParams p) {
     bmm<false, true, 1, false>(B + bPm, 64, B + bQd, 128, B + bKi, 128, 64, 128, 1.f, 64, sm);    // Pm
 }
 
+constexpr int kLW = 129;   // LDS row stride of staged [64][128] operands (no bank conflicts)
+constexpr int kLP = 65;    // LDS row stride of a staged [64][64] operand
+
+// A [64][128] fp32 matrix (row-major) as eight 16-byte pieces per thread:
+// fetch() issues the loads, put() writes them to LDS rows of stride kLW.
+struct Rows64x128 {
+    float4 v[8];
+    __device__ __forceinline__ void fetch(const float *src) {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int e = threadIdx.x + k * kNT, i = e >> 5, c4 = (e & 31) * 4;
+            v[k] = *reinterpret_cast<const float4 *>(src + i * 128 + c4);
+        }
+    }
+    __device__ __forceinline__ void put(float *dst) const {
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int e = threadIdx.x + k * kNT, i = e >> 5, c4 = (e & 31) * 4;
+            dst[i * kLW + c4] = v[k].x;
+            dst[i * kLW + c4 + 1] = v[k].y;
+            dst[i * kLW + c4 + 2] = v[k].z;
+            dst[i * kLW + c4 + 3] = v[k].w;
+        }
+    }
+};
+// The same for a [64][64] matrix (four pieces per thread, LDS stride kLP).
+struct Rows64x64 {
+    float4 v[4];
+    __device__ __forceinline__ void fetch(const float *src) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int e = threadIdx.x + k * kNT, i = e >> 4, c4 = (e & 15) * 4;
+            v[k] = *reinterpret_cast<const float4 *>(src + i * 64 + c4);
+        }
+    }
+    __device__ __forceinline__ void put(float *dst) const {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int e = threadIdx.x + k * kNT, i = e >> 4, c4 = (e & 15) * 4;
+            dst[i * kLP + c4] = v[k].x;
+            dst[i * kLP + c4 + 1] = v[k].y;
+            dst[i * kLP + c4 + 2] = v[k].z;
+            dst[i * kLP + c4 + 3] = v[k].w;
+        }
+    }
+};
+
+// Block -> (sequence, head, value tile) for the state passes: the eight tiles
+// of one (sequence, head) get consecutive numbers within one XCD's share of
+// the grid (blocks are dealt to the XCDs round robin), so they share its L2.
+__device__ __forceinline__ void tile_of(const ChunkParams &c, int &n, int &h, int &tile) {
+    const int total = c.n_seqs * c.H * kTilesV, per_xcd = total / 8;
+    const int b = blockIdx.x, u = (b % 8) * per_xcd + b / 8;
+    tile = u % kTilesV;
+    h = (u / kTilesV) % c.H;
+    n = u / (kTilesV * c.H);
+}
+
 // ---- forward state pass: S0 and U of every chunk ----------------------------
+// Thread roles: (r = tid / 2, 8 columns) for the 128 x 16 state tile and
+// (ui = tid / 4, 4 columns) for the 64 x 16 U tile.  The next chunk's W and
+// Kg are fetched into registers while this chunk is computed.
 __global__ __launch_bounds__(kNT) void bwd_fwd_states_kernel(BwdParams p) {
-    __shared__ float Ss[128 * 16], Us[64 * 16];
+    __shared__ float Mw[64 * kLW], Mk[64 * kLW];
+    __shared__ __attribute__((aligned(16))) float Ss[128 * 16];
+    __shared__ __attribute__((aligned(16))) float Us[64 * 16];
     const ChunkParams &c = p.c;
     const int H = c.H, tid = threadIdx.x;
-    const int tile = blockIdx.x % kTilesV, h = (blockIdx.x / kTilesV) % H, n = blockIdx.x / (kTilesV * H);
-    int c_begin, c_end;
-    seq_chunks(c, n, c_begin, c_end);
-    const int r = tid >> 1, cb = (tid & 1) * 8;    // state row, 8 of the tile's columns
-    const int ui = tid >> 2, uc = (tid & 3) * 4;   // U row, 4 of the tile's columns
+    int n, h, tile;
+    tile_of(c, n, h, tile);
+    int c_begin, c_end, seq_start, seq_len;
+    seq_chunks(c, n, c_begin, c_end, seq_start, seq_len);
+    const int r = tid >> 1, cb = (tid & 1) * 8;
+    const int ui = tid >> 2, uc = (tid & 3) * 4;
     const int col0 = tile * kTileV;
     float S[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j)
         S[j] = c.s0 ? c.s0[(((long)n * H + h) * kHeadDim + r) * kHeadDim + col0 + cb + j] : 0.f;
+    Rows64x128 nw, nk;
+    float4 n_ut = make_float4(0.f, 0.f, 0.f, 0.f);
+    float n_gl = 0.f;
+    if (c_begin < c_end) {
+        const float *Bn = chunk_buf(p, c_begin, h);
+        nw.fetch(Bn + bW);
+        nk.fetch(Bn + bKg);
+        n_ut = *reinterpret_cast<const float4 *>(Bn + bUt + ui * 128 + col0 + uc);
+        n_gl = Bn[bGL + r];
+    }
     for (int cid = c_begin; cid < c_end; ++cid) {
         float *B = chunk_buf(p, cid, h);
+        nw.put(Mw);
+        nk.put(Mk);
+        const float4 ut = n_ut;
+        const float gl = n_gl;
+        {   // the next chunk's operands (the last chunk fetches itself again)
+            const float *Bn = chunk_buf(p, min(cid + 1, c_end - 1), h);
+            nw.fetch(Bn + bW);
+            nk.fetch(Bn + bKg);
+            n_ut = *reinterpret_cast<const float4 *>(Bn + bUt + ui * 128 + col0 + uc);
+            n_gl = Bn[bGL + r];
+        }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            B[bS0 + r * 128 + col0 + cb + j] = S[j];
-            Ss[r * 16 + cb + j] = S[j];
+        for (int j = 0; j < 8; j += 4) {
+            const float4 v = make_float4(S[j], S[j + 1], S[j + 2], S[j + 3]);
+            *reinterpret_cast<float4 *>(B + bS0 + r * 128 + col0 + cb + j) = v;
+            *reinterpret_cast<float4 *>(Ss + r * 16 + cb + j) = v;
         }
         __syncthreads();
-        float u[4];
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) u[jj] = B[bUt + ui * 128 + col0 + uc + jj];
+        float4 u = ut;
+#pragma unroll 8
         for (int k = 0; k < 128; ++k) {
-            const float w = B[bW + ui * 128 + k];
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) u[jj] -= w * Ss[k * 16 + uc + jj];
+            const float w = Mw[ui * kLW + k];
+            const float4 sv = *reinterpret_cast<const float4 *>(Ss + k * 16 + uc);
+            u.x -= w * sv.x;
+            u.y -= w * sv.y;
+            u.z -= w * sv.z;
+            u.w -= w * sv.w;
         }
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            B[bU + ui * 128 + col0 + uc + jj] = u[jj];
-            Us[ui * 16 + uc + jj] = u[jj];
-        }
+        *reinterpret_cast<float4 *>(B + bU + ui * 128 + col0 + uc) = u;
+        *reinterpret_cast<float4 *>(Us + ui * 16 + uc) = u;
         __syncthreads();
-        const float gl = B[bGL + r];
 #pragma unroll
         for (int j = 0; j < 8; ++j) S[j] *= gl;
+#pragma unroll 8
         for (int i = 0; i < 64; ++i) {
-            const float kg = B[bKg + i * 128 + r];
-#pragma unroll
-            for (int j = 0; j < 8; ++j) S[j] += kg * Us[i * 16 + cb + j];
+            const float kg = Mk[i * kLW + r];
+            const float4 a = *reinterpret_cast<const float4 *>(Us + i * 16 + cb);
+            const float4 b2 = *reinterpret_cast<const float4 *>(Us + i * 16 + cb + 4);
+            S[0] += kg * a.x;
+            S[1] += kg * a.y;
+            S[2] += kg * a.z;
+            S[3] += kg * a.w;
+            S[4] += kg * b2.x;
+            S[5] += kg * b2.y;
+            S[6] += kg * b2.z;
+            S[7] += kg * b2.w;
         }
         __syncthreads();
     }
 }
 
 // ---- backward state pass: dO, dS_L, dU of every chunk; dS of the start -------
+// All four operands of a chunk (Kg, Pm for dU; Qd, W for the dS update) are
+// staged in LDS together, the previous chunk's fetched meanwhile.
 __global__ __launch_bounds__(kNT) void bwd_bwd_states_kernel(BwdParams p) {
-    __shared__ float dSs[128 * 16], dOs[64 * 16], dUs[64 * 16];
+    __shared__ float Mk[64 * kLW], Mq[64 * kLW], Mw[64 * kLW], Mp[64 * kLP];
+    __shared__ __attribute__((aligned(16))) float dSs[128 * 16];
+    __shared__ __attribute__((aligned(16))) float dOs[64 * 16];
+    __shared__ __attribute__((aligned(16))) float dUs[64 * 16];
     const ChunkParams &c = p.c;
     const int H = c.H, tid = threadIdx.x;
-    const int tile = blockIdx.x % kTilesV, h = (blockIdx.x / kTilesV) % H, n = blockIdx.x / (kTilesV * H);
-    int c_begin, c_end;
-    seq_chunks(c, n, c_begin, c_end);
+    int n, h, tile;
+    tile_of(c, n, h, tile);
+    int c_begin, c_end, seq_start, seq_len;
+    seq_chunks(c, n, c_begin, c_end, seq_start, seq_len);
     const int r = tid >> 1, cb = (tid & 1) * 8;
     const int ui = tid >> 2, uc = (tid & 3) * 4;
     const int col0 = tile * kTileV;
@@ -275,49 +388,96 @@ __global__ __launch_bounds__(kNT) void bwd_bwd_states_kernel(BwdParams p) {
     float dS[8];
 #pragma unroll
     for (int j = 0; j < 8; ++j) dS[j] = p.ds_final ? p.ds_final[sidx + j] : 0.f;
+    Rows64x128 nk, nq, nw;
+    Rows64x64 np;
+    // dy and gate of row ui (4 bf16 each; rows past the chunk's end read as 0)
+    auto fetch_rows = [&](int cid, uint2 &ry, uint2 &rg) {
+        const int j = cid - c_begin, len = min(kChunk, seq_len - kChunk * j);
+        ry = make_uint2(0u, 0u);
+        rg = make_uint2(0x3f803f80u, 0x3f803f80u);   // bf16 1.0 without a gate
+        if (ui < len) {
+            const long e = ((long)(seq_start + kChunk * j + ui) * H + h) * kHeadDim + col0 + uc;
+            ry = *reinterpret_cast<const uint2 *>(p.dy + e);
+            if (c.gate) rg = *reinterpret_cast<const uint2 *>(c.gate + e);
+        }
+    };
+    uint2 n_dy = make_uint2(0u, 0u), n_g = n_dy;
+    float n_gl = 0.f;
+    if (c_begin < c_end) {
+        const float *Bn = chunk_buf(p, c_end - 1, h);
+        nk.fetch(Bn + bKg);
+        np.fetch(Bn + bPm);
+        nq.fetch(Bn + bQd);
+        nw.fetch(Bn + bW);
+        fetch_rows(c_end - 1, n_dy, n_g);
+        n_gl = Bn[bGL + r];
+    }
     for (int cid = c_end - 1; cid >= c_begin; --cid) {
-        const ChunkInfo ci = load_chunk(c, cid);
         float *B = chunk_buf(p, cid, h);
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            float d = 0.f;
-            if (ui < ci.len) {
-                const long e = ((long)(ci.start + ui) * H + h) * kHeadDim + col0 + uc + jj;
-                d = c.scale * bf2f(p.dy[e]) * (c.gate ? bf2f(c.gate[e]) : 1.f);
-            }
-            B[bdO + ui * 128 + col0 + uc + jj] = d;
-            dOs[ui * 16 + uc + jj] = d;
+        nk.put(Mk);
+        np.put(Mp);
+        nq.put(Mq);
+        nw.put(Mw);
+        const uint2 ry = n_dy, rg = n_g;
+        const float gl = n_gl;
+        {   // the previous chunk's operands (the first chunk fetches itself again)
+            const int pc = max(cid - 1, c_begin);
+            const float *Bn = chunk_buf(p, pc, h);
+            nk.fetch(Bn + bKg);
+            np.fetch(Bn + bPm);
+            nq.fetch(Bn + bQd);
+            nw.fetch(Bn + bW);
+            fetch_rows(pc, n_dy, n_g);
+            n_gl = Bn[bGL + r];
         }
+        const float sc = c.scale;
+        const float4 d4 = make_float4(sc * lo_bf(ry.x) * lo_bf(rg.x), sc * hi_bf(ry.x) * hi_bf(rg.x),
+                                      sc * lo_bf(ry.y) * lo_bf(rg.y), sc * hi_bf(ry.y) * hi_bf(rg.y));
+        *reinterpret_cast<float4 *>(B + bdO + ui * 128 + col0 + uc) = d4;
+        *reinterpret_cast<float4 *>(dOs + ui * 16 + uc) = d4;
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            B[bdSL + r * 128 + col0 + cb + j] = dS[j];
-            dSs[r * 16 + cb + j] = dS[j];
+        for (int j = 0; j < 8; j += 4) {
+            const float4 v = make_float4(dS[j], dS[j + 1], dS[j + 2], dS[j + 3]);
+            *reinterpret_cast<float4 *>(B + bdSL + r * 128 + col0 + cb + j) = v;
+            *reinterpret_cast<float4 *>(dSs + r * 16 + cb + j) = v;
         }
         __syncthreads();
-        float du[4] = {0.f, 0.f, 0.f, 0.f};
+        float4 du = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
         for (int m = 0; m < 64; ++m) {
-            const float pm = B[bPm + m * 64 + ui];
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) du[jj] += pm * dOs[m * 16 + uc + jj];
+            const float pm = Mp[m * kLP + ui];
+            const float4 o = *reinterpret_cast<const float4 *>(dOs + m * 16 + uc);
+            du.x += pm * o.x;
+            du.y += pm * o.y;
+            du.z += pm * o.z;
+            du.w += pm * o.w;
         }
+#pragma unroll 8
         for (int k = 0; k < 128; ++k) {
-            const float kg = B[bKg + ui * 128 + k];
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) du[jj] += kg * dSs[k * 16 + uc + jj];
+            const float kg = Mk[ui * kLW + k];
+            const float4 sv = *reinterpret_cast<const float4 *>(dSs + k * 16 + uc);
+            du.x += kg * sv.x;
+            du.y += kg * sv.y;
+            du.z += kg * sv.z;
+            du.w += kg * sv.w;
         }
-#pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-            B[bdU + ui * 128 + col0 + uc + jj] = du[jj];
-            dUs[ui * 16 + uc + jj] = du[jj];
-        }
+        *reinterpret_cast<float4 *>(B + bdU + ui * 128 + col0 + uc) = du;
+        *reinterpret_cast<float4 *>(dUs + ui * 16 + uc) = du;
         __syncthreads();
-        const float gl = B[bGL + r];
 #pragma unroll
         for (int j = 0; j < 8; ++j) dS[j] *= gl;
+#pragma unroll 4
         for (int i = 0; i < 64; ++i) {
-            const float qd = B[bQd + i * 128 + r], w = B[bW + i * 128 + r];
+            const float qd = Mq[i * kLW + r], w = Mw[i * kLW + r];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) dS[j] += qd * dOs[i * 16 + cb + j] - w * dUs[i * 16 + cb + j];
+            for (int j = 0; j < 8; j += 4) {
+                const float4 o = *reinterpret_cast<const float4 *>(dOs + i * 16 + cb + j);
+                const float4 u = *reinterpret_cast<const float4 *>(dUs + i * 16 + cb + j);
+                dS[j] += qd * o.x - w * u.x;
+                dS[j + 1] += qd * o.y - w * u.y;
+                dS[j + 2] += qd * o.z - w * u.z;
+                dS[j + 3] += qd * o.w - w * u.w;
+            }
         }
         __syncthreads();
     }
@@ -329,7 +489,7 @@ __global__ __launch_bounds__(kNT) void bwd_bwd_states_kernel(BwdParams p) {
 
 // ---- per-chunk gradients -------------------------------------------------------
 __global__ __launch_bounds__(kNT) void bwd_grads_kernel(BwdParams p) {
-    __shared__ float sm[16 * 65 + 16 * 129];
+    __shared__ __attribute__((aligned(16))) float sm[16 * 68 + 16 * 132];
     __shared__ float beta_s[64], dbeta_s[64], dGL_s[128];
     const ChunkParams &c = p.c;
     const int H = c.H, h = blockIdx.x % H, cid = blockIdx.x / H, tid = threadIdx.x;
