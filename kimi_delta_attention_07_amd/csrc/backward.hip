@@ -82,49 +82,71 @@ __device__ __forceinline__ void seq_chunks(const ChunkParams &c, int n, int &c_b
 // 128, K a multiple of 16; operands 16-byte aligned with lda, ldb multiples of
 // 4.  The operands may be in global memory (written earlier by this block:
 // the barrier on entry orders them) or in LDS.
-template <bool TA, bool TB, int MASK, bool ACC>
-__device__ void bmm(float *C, int ldc, const float *A, int lda, const float *B, int ldb, int N, int K, float alpha,
-                    int mrows, float *sm) {
+template <bool TA, bool TB, int MASK, bool ACC, int N>
+__device__ void bmm(float *C, int ldc, const float *A, int lda, const float *B, int ldb, int K, float alpha, int mrows,
+                    float *sm) {
     constexpr int LA = 68, LB = 132;   // LDS rows, padded (multiples of 4 for 16-byte accesses)
     float *As = sm;                    // [16][LA]: As[kk][i]
     float *Bs = sm + 16 * LA;          // [16][LB]: Bs[kk][j]
     const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+    // this thread's share of a 16-wide k slab: one 16-byte piece of op(A),
+    // one or two of op(B); the next slab is fetched while this one is used
+    const int ai = TA ? (tid & 15) * 4 : tid >> 2, ak = TA ? tid >> 4 : (tid & 3) * 4;
+    auto a_ptr = [&](int k0) { return TA ? A + (long)(k0 + ak) * lda + ai : A + (long)ai * lda + k0 + ak; };
+    auto b_pos = [&](int e, int &j, int &k) {
+        if (TB) {
+            j = e >> 2;
+            k = (e & 3) * 4;
+        } else {
+            const int q = N >> 2;
+            k = e / q;
+            j = (e % q) * 4;
+        }
+    };
+    auto b_ptr = [&](int k0, int e) {
+        int j, k;
+        b_pos(e, j, k);
+        return TB ? B + (long)j * ldb + k0 + k : B + (long)(k0 + k) * ldb + j;
+    };
+    float4 ra, rb0, rb1 = make_float4(0.f, 0.f, 0.f, 0.f);   // op(B): 4 N / 256 pieces per thread
+    auto put_b = [&](const float4 &v, int e) {
+        int j, k;
+        b_pos(e, j, k);
+        if (TB) {
+            Bs[k * LB + j] = v.x;
+            Bs[(k + 1) * LB + j] = v.y;
+            Bs[(k + 2) * LB + j] = v.z;
+            Bs[(k + 3) * LB + j] = v.w;
+        } else {
+            *reinterpret_cast<float4 *>(Bs + k * LB + j) = v;
+        }
+    };
     float acc[4][8];
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc[r][c] = 0.f;
-    __syncthreads();
+    __syncthreads();   // operands written earlier by this block are complete; staging is free
+    ra = *reinterpret_cast<const float4 *>(a_ptr(0));
+    rb0 = *reinterpret_cast<const float4 *>(b_ptr(0, tid));
+    if constexpr (N == 128) rb1 = *reinterpret_cast<const float4 *>(b_ptr(0, tid + kNT));
     for (int k0 = 0; k0 < K; k0 += 16) {
-        {   // op(A) slab [64][16]: one 16-byte load per thread
-            if (TA) {
-                const int kk = tid >> 4, i4 = (tid & 15) * 4;
-                *reinterpret_cast<float4 *>(As + kk * LA + i4) =
-                    *reinterpret_cast<const float4 *>(A + (long)(k0 + kk) * lda + i4);
-            } else {
-                const int i = tid >> 2, k4 = (tid & 3) * 4;
-                const float4 v = *reinterpret_cast<const float4 *>(A + (long)i * lda + k0 + k4);
-                As[k4 * LA + i] = v.x;
-                As[(k4 + 1) * LA + i] = v.y;
-                As[(k4 + 2) * LA + i] = v.z;
-                As[(k4 + 3) * LA + i] = v.w;
-            }
+        if (TA) {
+            *reinterpret_cast<float4 *>(As + ak * LA + ai) = ra;
+        } else {
+            As[ak * LA + ai] = ra.x;
+            As[(ak + 1) * LA + ai] = ra.y;
+            As[(ak + 2) * LA + ai] = ra.z;
+            As[(ak + 3) * LA + ai] = ra.w;
         }
-        for (int e = tid; e < 4 * N; e += kNT) {   // op(B) slab [16][N]
-            if (TB) {
-                const int j = e >> 2, k4 = (e & 3) * 4;
-                const float4 v = *reinterpret_cast<const float4 *>(B + (long)j * ldb + k0 + k4);
-                Bs[k4 * LB + j] = v.x;
-                Bs[(k4 + 1) * LB + j] = v.y;
-                Bs[(k4 + 2) * LB + j] = v.z;
-                Bs[(k4 + 3) * LB + j] = v.w;
-            } else {
-                const int q = N >> 2, kk = e / q, j4 = (e % q) * 4;
-                *reinterpret_cast<float4 *>(Bs + kk * LB + j4) =
-                    *reinterpret_cast<const float4 *>(B + (long)(k0 + kk) * ldb + j4);
-            }
-        }
+        put_b(rb0, tid);
+        if constexpr (N == 128) put_b(rb1, tid + kNT);
         __syncthreads();
+        if (k0 + 16 < K) {
+            ra = *reinterpret_cast<const float4 *>(a_ptr(k0 + 16));
+            rb0 = *reinterpret_cast<const float4 *>(b_ptr(k0 + 16, tid));
+            if constexpr (N == 128) rb1 = *reinterpret_cast<const float4 *>(b_ptr(k0 + 16, tid + kNT));
+        }
 #pragma unroll 4
         for (int kk = 0; kk < 16; ++kk) {
             const float4 a4 = *reinterpret_cast<const float4 *>(As + kk * LA + 4 * ty);
@@ -195,7 +217,7 @@ __global__ __launch_bounds__(kNT) void bwd_prep_kernel(BwdParams p) {
         B[bV + e] = v;
     }
     // A = tril(Kd Ki^T, -1), rows scaled by beta
-    bmm<false, true, 2, false>(big, 64, B + bKd, 128, B + bKi, 128, 64, 128, 1.f, 64, sm);
+    bmm<false, true, 2, false, 64>(big, 64, B + bKd, 128, B + bKi, 128, 128, 1.f, 64, sm);
     __syncthreads();
     for (int e = tid; e < 64 * 64; e += kNT) big[e] *= beta_s[e >> 6];
     __syncthreads();
@@ -220,9 +242,9 @@ __global__ __launch_bounds__(kNT) void bwd_prep_kernel(BwdParams p) {
         B[bT + e] = Tm[e];
         B[bTB + e] = Tm[e] * beta_s[e & 63];
     }
-    bmm<false, false, 0, false>(B + bW, 128, B + bTB, 64, B + bKd, 128, 128, 64, 1.f, 64, sm);    // W = TB Kd
-    bmm<false, false, 0, false>(B + bUt, 128, B + bTB, 64, B + bV, 128, 128, 64, 1.f, 64, sm);    // U~ = TB V
-    bmm<false, true, 1, false>(B + bPm, 64, B + bQd, 128, B + bKi, 128, 64, 128, 1.f, 64, sm);    // Pm
+    bmm<false, false, 0, false, 128>(B + bW, 128, B + bTB, 64, B + bKd, 128, 64, 1.f, 64, sm);    // W = TB Kd
+    bmm<false, false, 0, false, 128>(B + bUt, 128, B + bTB, 64, B + bV, 128, 64, 1.f, 64, sm);    // U~ = TB V
+    bmm<false, true, 1, false, 64>(B + bPm, 64, B + bQd, 128, B + bKi, 128, 128, 1.f, 64, sm);    // Pm
 }
 
 constexpr int kLW = 129;   // LDS row stride of staged [64][128] operands (no bank conflicts)
@@ -499,19 +521,19 @@ __global__ __launch_bounds__(kNT) void bwd_grads_kernel(BwdParams p) {
     float *B = chunk_buf(p, cid, h);
     if (tid < 64) beta_s[tid] = tid < len ? c.beta[(tok0 + tid) * H + h] : 0.f;
     if (p.dgate) {   // O = Qd S0 + Pm U
-        bmm<false, false, 0, false>(B + bO, 128, B + bQd, 128, B + bS0, 128, 128, 128, 1.f, 64, sm);
-        bmm<false, false, 0, true>(B + bO, 128, B + bPm, 64, B + bU, 128, 128, 64, 1.f, 64, sm);
+        bmm<false, false, 0, false, 128>(B + bO, 128, B + bQd, 128, B + bS0, 128, 128, 1.f, 64, sm);
+        bmm<false, false, 0, true, 128>(B + bO, 128, B + bPm, 64, B + bU, 128, 64, 1.f, 64, sm);
     }
-    bmm<false, true, 1, false>(B + bdPm, 64, B + bdO, 128, B + bU, 128, 64, 128, 1.f, 64, sm);       // tril(dO U^T)
-    bmm<false, true, 0, false>(B + bdQd, 128, B + bdO, 128, B + bS0, 128, 128, 128, 1.f, 64, sm);    // dO S0^T
-    bmm<false, false, 0, true>(B + bdQd, 128, B + bdPm, 64, B + bKi, 128, 128, 64, 1.f, 64, sm);     //  + dPm Ki
-    bmm<false, true, 0, false>(B + bdW, 128, B + bdU, 128, B + bS0, 128, 128, 128, -1.f, 64, sm);    // -dU S0^T
-    bmm<false, true, 0, false>(B + bdKg, 128, B + bU, 128, B + bdSL, 128, 128, 128, 1.f, 64, sm);    // U dS_L^T
-    bmm<false, true, 0, false>(B + bdTB, 64, B + bdW, 128, B + bKd, 128, 64, 128, 1.f, 64, sm);      // dW Kd^T
-    bmm<false, true, 0, true>(B + bdTB, 64, B + bdU, 128, B + bV, 128, 64, 128, 1.f, 64, sm);        //  + dU V^T
-    bmm<true, false, 0, false>(B + bdKd, 128, B + bTB, 64, B + bdW, 128, 128, 64, 1.f, 64, sm);      // TB^T dW
-    bmm<true, false, 0, false>(p.dv + (tok0 * H + h) * kHeadDim, H * kHeadDim, B + bTB, 64, B + bdU, 128, 128, 64,
-                               1.f, len, sm);                                                       // dV = TB^T dU
+    bmm<false, true, 1, false, 64>(B + bdPm, 64, B + bdO, 128, B + bU, 128, 128, 1.f, 64, sm);       // tril(dO U^T)
+    bmm<false, true, 0, false, 128>(B + bdQd, 128, B + bdO, 128, B + bS0, 128, 128, 1.f, 64, sm);    // dO S0^T
+    bmm<false, false, 0, true, 128>(B + bdQd, 128, B + bdPm, 64, B + bKi, 128, 64, 1.f, 64, sm);     //  + dPm Ki
+    bmm<false, true, 0, false, 128>(B + bdW, 128, B + bdU, 128, B + bS0, 128, 128, -1.f, 64, sm);    // -dU S0^T
+    bmm<false, true, 0, false, 128>(B + bdKg, 128, B + bU, 128, B + bdSL, 128, 128, 1.f, 64, sm);    // U dS_L^T
+    bmm<false, true, 0, false, 64>(B + bdTB, 64, B + bdW, 128, B + bKd, 128, 128, 1.f, 64, sm);      // dW Kd^T
+    bmm<false, true, 0, true, 64>(B + bdTB, 64, B + bdU, 128, B + bV, 128, 128, 1.f, 64, sm);        //  + dU V^T
+    bmm<true, false, 0, false, 128>(B + bdKd, 128, B + bTB, 64, B + bdW, 128, 64, 1.f, 64, sm);      // TB^T dW
+    bmm<true, false, 0, false, 128>(p.dv + (tok0 * H + h) * kHeadDim, H * kHeadDim, B + bTB, 64, B + bdU, 128, 64,
+                                    1.f, len, sm);                                                       // dV = TB^T dU
     __syncthreads();
     // dT = dTB diag(beta) (held in the dA slot); dbeta from TB = T diag(beta)
     for (int e = tid; e < 64 * 64; e += kNT) B[bdA + e] = B[bdTB + e] * beta_s[e & 63];
@@ -520,9 +542,9 @@ __global__ __launch_bounds__(kNT) void bwd_grads_kernel(BwdParams p) {
         for (int i = 0; i < 64; ++i) s += B[bdTB + i * 64 + tid] * B[bT + i * 64 + tid];
         dbeta_s[tid] = s;
     }
-    bmm<true, false, 0, false>(B + bX, 64, B + bT, 64, B + bdA, 64, 64, 64, 1.f, 64, sm);            // T^T dT
-    bmm<false, true, 2, false>(B + bdA, 64, B + bX, 64, B + bT, 64, 64, 64, -1.f, 64, sm);           // dA
-    bmm<false, true, 2, false>(B + bKK, 64, B + bKd, 128, B + bKi, 128, 64, 128, 1.f, 64, sm);       // tril(Kd Ki^T, -1)
+    bmm<true, false, 0, false, 64>(B + bX, 64, B + bT, 64, B + bdA, 64, 64, 1.f, 64, sm);            // T^T dT
+    bmm<false, true, 2, false, 64>(B + bdA, 64, B + bX, 64, B + bT, 64, 64, -1.f, 64, sm);           // dA
+    bmm<false, true, 2, false, 64>(B + bKK, 64, B + bKd, 128, B + bKi, 128, 128, 1.f, 64, sm);       // tril(Kd Ki^T, -1)
     __syncthreads();
     if (tid < 64) {
         float s = 0.f;
@@ -531,9 +553,9 @@ __global__ __launch_bounds__(kNT) void bwd_grads_kernel(BwdParams p) {
     }
     __syncthreads();
     for (int e = tid; e < 64 * 64; e += kNT) B[bdA + e] *= beta_s[e >> 6];                          // diag(beta) dA
-    bmm<false, false, 0, true>(B + bdKd, 128, B + bdA, 64, B + bKi, 128, 128, 64, 1.f, 64, sm);      // += (beta dA) Ki
-    bmm<true, false, 0, false>(B + bdKi, 128, B + bdA, 64, B + bKd, 128, 128, 64, 1.f, 64, sm);      // (beta dA)^T Kd
-    bmm<true, false, 0, true>(B + bdKi, 128, B + bdPm, 64, B + bQd, 128, 128, 64, 1.f, 64, sm);      //  + dPm^T Qd
+    bmm<false, false, 0, true, 128>(B + bdKd, 128, B + bdA, 64, B + bKi, 128, 64, 1.f, 64, sm);      // += (beta dA) Ki
+    bmm<true, false, 0, false, 128>(B + bdKi, 128, B + bdA, 64, B + bKd, 128, 64, 1.f, 64, sm);      // (beta dA)^T Kd
+    bmm<true, false, 0, true, 128>(B + bdKi, 128, B + bdPm, 64, B + bQd, 128, 64, 1.f, 64, sm);      //  + dPm^T Qd
     __syncthreads();
     if (tid < 128) {
         const int ch = tid;
