@@ -121,10 +121,6 @@ static_assert(4 * 128 * 4 <= 64 * kRowT * 2, "cumsum totals alias the T tile");
 // bank groups.
 __device__ __forceinline__ int aix(int i, int j) { return i * 64 + ((((j >> 2) ^ i) & 15) << 2) + (j & 3); }
 
-__device__ __forceinline__ f32x4 mfma_f32(float a, float b, const f32x4 &c) {
-    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
-}
-
 __device__ __forceinline__ bf16x8 lds_frag(const unsigned char *lds, int off_bytes) {
     return as_bf16x8(*reinterpret_cast<const u32x4 *>(lds + off_bytes));
 }
