@@ -76,6 +76,17 @@ def test_backward_varlen(seed, lengths, H, gate, s0, dsf, scale):
     assert_grads_close(run_gpu(c, scale), run_oracle(c, scale), f"seed {seed}")
 
 
+def test_backward_many_sequences():
+    """150 short sequences (0..90 tokens): more than the 128 whose chunk table
+    travels in the kernel arguments, so the backward reads the table the
+    device builds."""
+    g = torch.Generator().manual_seed(96)
+    lens = torch.randint(0, 91, (150,), generator=g).tolist()
+    lens[5] = lens[140] = 0
+    c = make_case(12, lens, 1)
+    assert_grads_close(run_gpu(c), run_oracle(c), "150 sequences")
+
+
 def test_backward_slow_decay_long():
     """Decays near 1 (log alpha = -exp(U(-8, -2))) over 16 chunks."""
     c = make_case(5, [1024], 2, la_range=(-8.0, -2.0))
