@@ -51,9 +51,11 @@ CONV_CACHE_B = 3 * (K - 1) * H * D * 4
 FLOP_PER_TOK = 4_496_032                                                       # useful chunked-form flops (H=32)
 DECODE_B_PER_ROW = 2 * STATE_B + 2 * CONV_CACHE_B + 3 * 8192 + 8192 + 64 + 8192 + 16384   # 4,546,624
 # kda_chunk_backward: the dense fp32 products it executes per (64-token chunk,
-# head), in multiply-adds: WY quantities 4 C^2 d; forward state pass 2 C d^2;
-# backward state pass C^2 d + 3 C d^2; per-chunk gradients 8 C^2 d (+2 C^3)
-# + 6 C d^2 + ... (itemised in the design doc): 18,350,080 MACs.
+# head), in multiply-adds (C = 64, d = 128): WY quantities 4 C^2 d; forward
+# state pass 2 C d^2; backward state pass C^2 d + 3 C d^2; per-chunk gradients
+# 4 C d^2 + 11 C^2 d + 2 C^3 (O 1.57, dPm 0.52, dQd 1.57, dW 1.05, dKg 1.05,
+# dTB 1.05, dKd 1.05, dV 0.52, T^T dT 0.26, dA 0.26, Kd Ki^T 0.52, dKi 1.05
+# million): 18,350,080 in all.
 BWD_FLOP_PER_CHUNK_HEAD = 2 * 18_350_080
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector, TFLOP/s
 
