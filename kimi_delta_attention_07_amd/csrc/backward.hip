@@ -23,15 +23,16 @@
 // (the forward's WY/UT form is the one in chunk.hip; see the oracle for the
 // same gradient taken token by token).
 //
-// Four kernels, all fp32 on the VALU with LDS-staged tiles:
+// Four kernels, all in fp32:
 //   prep        chunks x heads: G, the decayed operands, A, T (forward
-//               substitution, one row at a time), W, U~, Pm
+//               substitution, one row at a time), W, U~, Pm, dO, and the
+//               transposed operands of the state passes (VALU, LDS-staged)
 //   fwd_states  sequences x heads x 8 value tiles: walks the chunks forward,
-//               writes each chunk's S0 and U
-//   bwd_states  the same grid backwards: dO, dS_L and dU per chunk, and the
-//               gradient of the initial state
+//               writes each chunk's S0 and U (fp32 MFMA)
+//   bwd_states  the same grid backwards: dS_L and dU per chunk, and the
+//               gradient of the initial state (fp32 MFMA)
 //   grads       chunks x heads: the per-chunk products above, then dq, dk, dv,
-//               dlog alpha, dbeta and dgate
+//               dlog alpha, dbeta and dgate (VALU, LDS-staged)
 // Rows past a chunk's end load as zeros, which makes every padded row of
 // every operand (and so of every product) zero, and keeps G at G_L there.
 #include "kda_chunk_table.h"
@@ -54,6 +55,11 @@ constexpr long bO = bdU + kM, bdPm = bO + kM, bdQd = bdPm + kSq, bdW = bdQd + kM
 constexpr long bdTB = bdKg + kM, bdKd = bdTB + kSq, bX = bdKd + kM, bdA = bX + kSq, bKK = bdA + kSq;
 constexpr long bdKi = bKK + kSq;
 constexpr long kBwdFloats = bdKi + kM;
+// Transposed copies the state passes read as MFMA A operands ([128][64] and
+// [64][64], row-major), written by the prep kernel into slots that the
+// gradient kernel only writes (and writes in full before reading), after the
+// state passes have run.
+constexpr long bKgT = bdQd, bQdT = bdW, bWT = bdKg, bPmT = bdPm;
 
 __device__ __forceinline__ float *chunk_buf(const BwdParams &p, long cid, int h) {
     return p.buf + (cid * p.c.H + h) * kBwdFloats;
@@ -181,6 +187,21 @@ __device__ void bmm(float *C, int ldc, const float *A, int lda, const float *B, 
     }
 }
 
+// dst = src^T for a row-major [64][ncols] src (row stride lds) into a
+// row-major [ncols][64] dst, through LDS in 64 x 64 blocks (row stride 65:
+// both the row-wise writes and the column-wise reads are free of bank
+// conflicts).  src may have been written by this block (the barrier on entry
+// orders it).
+__device__ void transpose64(float *dst, const float *src, int lds, int ncols, float *st) {
+    const int tid = threadIdx.x;
+    for (int cb = 0; cb < ncols; cb += 64) {
+        __syncthreads();
+        for (int e = tid; e < 64 * 64; e += kNT) st[(e >> 6) * 65 + (e & 63)] = src[(e >> 6) * lds + cb + (e & 63)];
+        __syncthreads();
+        for (int e = tid; e < 64 * 64; e += kNT) dst[(cb + (e >> 6)) * 64 + (e & 63)] = st[(e & 63) * 65 + (e >> 6)];
+    }
+}
+
 // ---- prep: the chunk's WY quantities -----------------------------------------
 __global__ __launch_bounds__(kNT) void bwd_prep_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(16))) float sm[16 * 68 + 16 * 132];
@@ -208,6 +229,7 @@ __global__ __launch_bounds__(kNT) void bwd_prep_kernel(BwdParams p) {
         const long src = ((tok0 + i) * H + h) * kHeadDim + ch;
         const bool in = i < len;
         const float q = in ? bf2f(c.q[src]) : 0.f, k = in ? bf2f(c.k[src]) : 0.f, v = in ? bf2f(c.v[src]) : 0.f;
+        const float dy = in ? bf2f(p.dy[src]) : 0.f, gv = in && c.gate ? bf2f(c.gate[src]) : 1.f;
         const float g = big[e];
         const float eg = expf(g);
         B[bQd + e] = q * eg;
@@ -215,6 +237,7 @@ __global__ __launch_bounds__(kNT) void bwd_prep_kernel(BwdParams p) {
         B[bKi + e] = k * expf(-g);
         B[bKg + e] = k * expf(big[63 * 128 + ch] - g);
         B[bV + e] = v;
+        B[bdO + e] = c.scale * dy * gv;   // dO = scale dy (.) g
     }
     // A = tril(Kd Ki^T, -1), rows scaled by beta
     bmm<false, true, 2, false, 64>(big, 64, B + bKd, 128, B + bKi, 128, 128, 1.f, 64, sm);
@@ -245,54 +268,12 @@ __global__ __launch_bounds__(kNT) void bwd_prep_kernel(BwdParams p) {
     bmm<false, false, 0, false, 128>(B + bW, 128, B + bTB, 64, B + bKd, 128, 64, 1.f, 64, sm);    // W = TB Kd
     bmm<false, false, 0, false, 128>(B + bUt, 128, B + bTB, 64, B + bV, 128, 64, 1.f, 64, sm);    // U~ = TB V
     bmm<false, true, 1, false, 64>(B + bPm, 64, B + bQd, 128, B + bKi, 128, 128, 1.f, 64, sm);    // Pm
+    // transposed copies for the state passes (big is free again: T went out above)
+    transpose64(B + bKgT, B + bKg, 128, 128, big);
+    transpose64(B + bQdT, B + bQd, 128, 128, big);
+    transpose64(B + bWT, B + bW, 128, 128, big);
+    transpose64(B + bPmT, B + bPm, 64, 64, big);
 }
-
-constexpr int kLW = 129;   // LDS row stride of staged [64][128] operands (no bank conflicts)
-constexpr int kLP = 65;    // LDS row stride of a staged [64][64] operand
-
-// A [64][128] fp32 matrix (row-major) as eight 16-byte pieces per thread:
-// fetch() issues the loads, put() writes them to LDS rows of stride kLW.
-struct Rows64x128 {
-    float4 v[8];
-    __device__ __forceinline__ void fetch(const float *src) {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int e = threadIdx.x + k * kNT, i = e >> 5, c4 = (e & 31) * 4;
-            v[k] = *reinterpret_cast<const float4 *>(src + i * 128 + c4);
-        }
-    }
-    __device__ __forceinline__ void put(float *dst) const {
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-            const int e = threadIdx.x + k * kNT, i = e >> 5, c4 = (e & 31) * 4;
-            dst[i * kLW + c4] = v[k].x;
-            dst[i * kLW + c4 + 1] = v[k].y;
-            dst[i * kLW + c4 + 2] = v[k].z;
-            dst[i * kLW + c4 + 3] = v[k].w;
-        }
-    }
-};
-// The same for a [64][64] matrix (four pieces per thread, LDS stride kLP).
-struct Rows64x64 {
-    float4 v[4];
-    __device__ __forceinline__ void fetch(const float *src) {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int e = threadIdx.x + k * kNT, i = e >> 4, c4 = (e & 15) * 4;
-            v[k] = *reinterpret_cast<const float4 *>(src + i * 64 + c4);
-        }
-    }
-    __device__ __forceinline__ void put(float *dst) const {
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-            const int e = threadIdx.x + k * kNT, i = e >> 4, c4 = (e & 15) * 4;
-            dst[i * kLP + c4] = v[k].x;
-            dst[i * kLP + c4 + 1] = v[k].y;
-            dst[i * kLP + c4 + 2] = v[k].z;
-            dst[i * kLP + c4 + 3] = v[k].w;
-        }
-    }
-};
 
 // Block -> (sequence, head, value tile) for the state passes: the eight tiles
 // of one (sequence, head) get consecutive numbers within one XCD's share of
@@ -305,207 +286,204 @@ __device__ __forceinline__ void tile_of(const ChunkParams &c, int &n, int &h, in
     n = u / (kTilesV * c.H);
 }
 
+// The state passes run on fp32 MFMAs (16x16x4): lane l supplies A[l % 16][l / 16]
+// and B[l / 16][l % 16] of a 4-wide k step and holds D[4 (l / 16) + r][l % 16]
+// in element r.  The k step (b, r) of a contraction over rows of a C-layout
+// operand covers rows {16 b + 4 k' + r : k' = 0..3}, so element r of that
+// operand's block b, as each lane holds it, is the B operand of step (b, r),
+// and the matching A operand is one element of a 16-byte load
+// A[row][16 b + 4 (l / 16) .. + 3].  A 128 x 16 state tile is eight such
+// blocks (rows 16 mm + 4 (l / 16) + r, column l % 16).
+//
+// Four waves share each chunk step of one (sequence, head, 16-column tile).
+// Wave w forms the 16-token block w of the chunk's U (or dU), a contraction
+// over the 128 state rows, and the state rows of blocks 2w and 2w + 1, a
+// contraction over the 64 tokens; U and the state go round through LDS so that
+// every wave holds all of U and of the state as B operands of the next
+// product.  Each wave refetches an operand for the next chunk right after its
+// last use in this one (the last chunk refetches itself, so every load is
+// issued on every path).
+__device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+
 // ---- forward state pass: S0 and U of every chunk ----------------------------
-// Thread roles: (r = tid / 2, 8 columns) for the 128 x 16 state tile and
-// (ui = tid / 4, 4 columns) for the 64 x 16 U tile.  The next chunk's W and
-// Kg are fetched into registers while this chunk is computed.
+//   U = U~ - W S0,   S_L = Diag(e^{G_L}) S0 + (K e^{G_L - G})^T U
 __global__ __launch_bounds__(kNT) void bwd_fwd_states_kernel(BwdParams p) {
-    __shared__ float Mw[64 * kLW], Mk[64 * kLW];
-    __shared__ __attribute__((aligned(16))) float Ss[128 * 16];
-    __shared__ __attribute__((aligned(16))) float Us[64 * 16];
+    __shared__ f32x4 xU[4][64];
+    __shared__ f32x4 xS[8][64];
     const ChunkParams &c = p.c;
     const int H = c.H, tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, i = l & 15;
     int n, h, tile;
     tile_of(c, n, h, tile);
     int c_begin, c_end, seq_start, seq_len;
     seq_chunks(c, n, c_begin, c_end, seq_start, seq_len);
-    const int r = tid >> 1, cb = (tid & 1) * 8;
-    const int ui = tid >> 2, uc = (tid & 3) * 4;
-    const int col0 = tile * kTileV;
-    float S[8];
+    const int col = tile * kTileV + i;
+    const long sb = ((long)n * H + h) * kHeadDim * kHeadDim;
+    f32x4 S[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-        S[j] = c.s0 ? c.s0[(((long)n * H + h) * kHeadDim + r) * kHeadDim + col0 + cb + j] : 0.f;
-    Rows64x128 nw, nk;
-    float4 n_ut = make_float4(0.f, 0.f, 0.f, 0.f);
-    float n_gl = 0.f;
-    if (c_begin < c_end) {
-        const float *Bn = chunk_buf(p, c_begin, h);
-        nw.fetch(Bn + bW);
-        nk.fetch(Bn + bKg);
-        n_ut = *reinterpret_cast<const float4 *>(Bn + bUt + ui * 128 + col0 + uc);
-        n_gl = Bn[bGL + r];
-    }
+    for (int mm = 0; mm < 8; ++mm)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) S[mm][r] = c.s0 ? c.s0[sb + (16 * mm + 4 * g + r) * kHeadDim + col] : 0.f;
+    if (c_begin >= c_end) return;   // block-uniform
+    f32x4 Wr[8], Kt[2][4], gl[2], ut;
+    auto fetch_w = [&](const float *Bn) {
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) Wr[mm] = ld4(Bn + bW + (16 * w + i) * 128 + 16 * mm + 4 * g);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ut[r] = Bn[bUt + (16 * w + 4 * g + r) * 128 + col];
+    };
+    auto fetch_k = [&](const float *Bn) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+#pragma unroll
+            for (int m = 0; m < 4; ++m) Kt[j][m] = ld4(Bn + bKgT + (16 * (2 * w + j) + i) * 64 + 16 * m + 4 * g);
+            gl[j] = ld4(Bn + bGL + 16 * (2 * w + j) + 4 * g);
+        }
+    };
+    fetch_w(chunk_buf(p, c_begin, h));
+    fetch_k(chunk_buf(p, c_begin, h));
     for (int cid = c_begin; cid < c_end; ++cid) {
         float *B = chunk_buf(p, cid, h);
-        nw.put(Mw);
-        nk.put(Mk);
-        const float4 ut = n_ut;
-        const float gl = n_gl;
-        {   // the next chunk's operands (the last chunk fetches itself again)
-            const float *Bn = chunk_buf(p, min(cid + 1, c_end - 1), h);
-            nw.fetch(Bn + bW);
-            nk.fetch(Bn + bKg);
-            n_ut = *reinterpret_cast<const float4 *>(Bn + bUt + ui * 128 + col0 + uc);
-            n_gl = Bn[bGL + r];
-        }
+        const float *Bn = chunk_buf(p, min(cid + 1, c_end - 1), h);
 #pragma unroll
-        for (int j = 0; j < 8; j += 4) {
-            const float4 v = make_float4(S[j], S[j + 1], S[j + 2], S[j + 3]);
-            *reinterpret_cast<float4 *>(B + bS0 + r * 128 + col0 + cb + j) = v;
-            *reinterpret_cast<float4 *>(Ss + r * 16 + cb + j) = v;
-        }
-        __syncthreads();
-        float4 u = ut;
-#pragma unroll 8
-        for (int k = 0; k < 128; ++k) {
-            const float w = Mw[ui * kLW + k];
-            const float4 sv = *reinterpret_cast<const float4 *>(Ss + k * 16 + uc);
-            u.x -= w * sv.x;
-            u.y -= w * sv.y;
-            u.z -= w * sv.z;
-            u.w -= w * sv.w;
-        }
-        *reinterpret_cast<float4 *>(B + bU + ui * 128 + col0 + uc) = u;
-        *reinterpret_cast<float4 *>(Us + ui * 16 + uc) = u;
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) B[bS0 + (16 * (2 * w + j) + 4 * g + r) * 128 + col] = S[2 * w + j][r];
+        f32x4 u = ut;
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) u = mfma_f32(-Wr[mm][r], S[mm][r], u);
+        fetch_w(Bn);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) B[bU + (16 * w + 4 * g + r) * 128 + col] = u[r];
+        xU[w][l] = u;
+        f32x4 s2[2];
+#pragma unroll
+        for (int j = 0; j < 2; ++j) s2[j] = S[2 * w + j] * gl[j];
         __syncthreads();
 #pragma unroll
-        for (int j = 0; j < 8; ++j) S[j] *= gl;
-#pragma unroll 8
-        for (int i = 0; i < 64; ++i) {
-            const float kg = Mk[i * kLW + r];
-            const float4 a = *reinterpret_cast<const float4 *>(Us + i * 16 + cb);
-            const float4 b2 = *reinterpret_cast<const float4 *>(Us + i * 16 + cb + 4);
-            S[0] += kg * a.x;
-            S[1] += kg * a.y;
-            S[2] += kg * a.z;
-            S[3] += kg * a.w;
-            S[4] += kg * b2.x;
-            S[5] += kg * b2.y;
-            S[6] += kg * b2.z;
-            S[7] += kg * b2.w;
+        for (int m = 0; m < 4; ++m) {
+            const f32x4 um = xU[m][l];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) s2[j] = mfma_f32(Kt[j][m][r], um[r], s2[j]);
         }
+        fetch_k(Bn);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) xS[2 * w + j][l] = s2[j];
         __syncthreads();
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) S[mm] = xS[mm][l];
     }
 }
 
-// ---- backward state pass: dO, dS_L, dU of every chunk; dS of the start -------
-// All four operands of a chunk (Kg, Pm for dU; Qd, W for the dS update) are
-// staged in LDS together, the previous chunk's fetched meanwhile.
+// ---- backward state pass: dS_L and dU of every chunk; dS of the start --------
+//   dU = Pm^T dO + Kg dS_L,   dS0 = Diag(e^{G_L}) dS_L + Qd^T dO - W^T dU
+// (dO = scale dy (.) g comes from the prep kernel.)
 __global__ __launch_bounds__(kNT) void bwd_bwd_states_kernel(BwdParams p) {
-    __shared__ float Mk[64 * kLW], Mq[64 * kLW], Mw[64 * kLW], Mp[64 * kLP];
-    __shared__ __attribute__((aligned(16))) float dSs[128 * 16];
-    __shared__ __attribute__((aligned(16))) float dOs[64 * 16];
-    __shared__ __attribute__((aligned(16))) float dUs[64 * 16];
+    __shared__ f32x4 xU[4][64];
+    __shared__ f32x4 xS[8][64];
     const ChunkParams &c = p.c;
     const int H = c.H, tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, g = l >> 4, i = l & 15;
     int n, h, tile;
     tile_of(c, n, h, tile);
     int c_begin, c_end, seq_start, seq_len;
     seq_chunks(c, n, c_begin, c_end, seq_start, seq_len);
-    const int r = tid >> 1, cb = (tid & 1) * 8;
-    const int ui = tid >> 2, uc = (tid & 3) * 4;
-    const int col0 = tile * kTileV;
-    const long sidx = (((long)n * H + h) * kHeadDim + r) * kHeadDim + col0 + cb;
-    float dS[8];
+    const int col = tile * kTileV + i;
+    const long sb = ((long)n * H + h) * kHeadDim * kHeadDim;
+    f32x4 dS[8];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) dS[j] = p.ds_final ? p.ds_final[sidx + j] : 0.f;
-    Rows64x128 nk, nq, nw;
-    Rows64x64 np;
-    // dy and gate of row ui (4 bf16 each; rows past the chunk's end read as 0)
-    auto fetch_rows = [&](int cid, uint2 &ry, uint2 &rg) {
-        const int j = cid - c_begin, len = min(kChunk, seq_len - kChunk * j);
-        ry = make_uint2(0u, 0u);
-        rg = make_uint2(0x3f803f80u, 0x3f803f80u);   // bf16 1.0 without a gate
-        if (ui < len) {
-            const long e = ((long)(seq_start + kChunk * j + ui) * H + h) * kHeadDim + col0 + uc;
-            ry = *reinterpret_cast<const uint2 *>(p.dy + e);
-            if (c.gate) rg = *reinterpret_cast<const uint2 *>(c.gate + e);
-        }
-    };
-    uint2 n_dy = make_uint2(0u, 0u), n_g = n_dy;
-    float n_gl = 0.f;
-    if (c_begin < c_end) {
-        const float *Bn = chunk_buf(p, c_end - 1, h);
-        nk.fetch(Bn + bKg);
-        np.fetch(Bn + bPm);
-        nq.fetch(Bn + bQd);
-        nw.fetch(Bn + bW);
-        fetch_rows(c_end - 1, n_dy, n_g);
-        n_gl = Bn[bGL + r];
-    }
-    for (int cid = c_end - 1; cid >= c_begin; --cid) {
-        float *B = chunk_buf(p, cid, h);
-        nk.put(Mk);
-        np.put(Mp);
-        nq.put(Mq);
-        nw.put(Mw);
-        const uint2 ry = n_dy, rg = n_g;
-        const float gl = n_gl;
-        {   // the previous chunk's operands (the first chunk fetches itself again)
-            const int pc = max(cid - 1, c_begin);
-            const float *Bn = chunk_buf(p, pc, h);
-            nk.fetch(Bn + bKg);
-            np.fetch(Bn + bPm);
-            nq.fetch(Bn + bQd);
-            nw.fetch(Bn + bW);
-            fetch_rows(pc, n_dy, n_g);
-            n_gl = Bn[bGL + r];
-        }
-        const float sc = c.scale;
-        const float4 d4 = make_float4(sc * lo_bf(ry.x) * lo_bf(rg.x), sc * hi_bf(ry.x) * hi_bf(rg.x),
-                                      sc * lo_bf(ry.y) * lo_bf(rg.y), sc * hi_bf(ry.y) * hi_bf(rg.y));
-        *reinterpret_cast<float4 *>(B + bdO + ui * 128 + col0 + uc) = d4;
-        *reinterpret_cast<float4 *>(dOs + ui * 16 + uc) = d4;
+    for (int mm = 0; mm < 8; ++mm)
 #pragma unroll
-        for (int j = 0; j < 8; j += 4) {
-            const float4 v = make_float4(dS[j], dS[j + 1], dS[j + 2], dS[j + 3]);
-            *reinterpret_cast<float4 *>(B + bdSL + r * 128 + col0 + cb + j) = v;
-            *reinterpret_cast<float4 *>(dSs + r * 16 + cb + j) = v;
-        }
-        __syncthreads();
-        float4 du = make_float4(0.f, 0.f, 0.f, 0.f);
-#pragma unroll 8
-        for (int m = 0; m < 64; ++m) {
-            const float pm = Mp[m * kLP + ui];
-            const float4 o = *reinterpret_cast<const float4 *>(dOs + m * 16 + uc);
-            du.x += pm * o.x;
-            du.y += pm * o.y;
-            du.z += pm * o.z;
-            du.w += pm * o.w;
-        }
-#pragma unroll 8
-        for (int k = 0; k < 128; ++k) {
-            const float kg = Mk[ui * kLW + k];
-            const float4 sv = *reinterpret_cast<const float4 *>(dSs + k * 16 + uc);
-            du.x += kg * sv.x;
-            du.y += kg * sv.y;
-            du.z += kg * sv.z;
-            du.w += kg * sv.w;
-        }
-        *reinterpret_cast<float4 *>(B + bdU + ui * 128 + col0 + uc) = du;
-        *reinterpret_cast<float4 *>(dUs + ui * 16 + uc) = du;
-        __syncthreads();
+        for (int r = 0; r < 4; ++r)
+            dS[mm][r] = p.ds_final ? p.ds_final[sb + (16 * mm + 4 * g + r) * kHeadDim + col] : 0.f;
+    if (c_begin < c_end) {   // block-uniform
+        f32x4 Pt[4], Kr[8], Qt[2][4], Wt[2][4], gl[2], dO[4];
+        auto fetch_pk = [&](const float *Bn) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) dS[j] *= gl;
-#pragma unroll 4
-        for (int i = 0; i < 64; ++i) {
-            const float qd = Mq[i * kLW + r], w = Mw[i * kLW + r];
+            for (int m = 0; m < 4; ++m) Pt[m] = ld4(Bn + bPmT + (16 * w + i) * 64 + 16 * m + 4 * g);
 #pragma unroll
-            for (int j = 0; j < 8; j += 4) {
-                const float4 o = *reinterpret_cast<const float4 *>(dOs + i * 16 + cb + j);
-                const float4 u = *reinterpret_cast<const float4 *>(dUs + i * 16 + cb + j);
-                dS[j] += qd * o.x - w * u.x;
-                dS[j + 1] += qd * o.y - w * u.y;
-                dS[j + 2] += qd * o.z - w * u.z;
-                dS[j + 3] += qd * o.w - w * u.w;
+            for (int mm = 0; mm < 8; ++mm) Kr[mm] = ld4(Bn + bKg + (16 * w + i) * 128 + 16 * mm + 4 * g);
+        };
+        auto fetch_qo = [&](const float *Bn) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+#pragma unroll
+                for (int m = 0; m < 4; ++m) Qt[j][m] = ld4(Bn + bQdT + (16 * (2 * w + j) + i) * 64 + 16 * m + 4 * g);
+                gl[j] = ld4(Bn + bGL + 16 * (2 * w + j) + 4 * g);
             }
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) dO[m][r] = Bn[bdO + (16 * m + 4 * g + r) * 128 + col];
+        };
+        auto fetch_w = [&](const float *Bn) {
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int m = 0; m < 4; ++m) Wt[j][m] = ld4(Bn + bWT + (16 * (2 * w + j) + i) * 64 + 16 * m + 4 * g);
+        };
+        {
+            const float *B0 = chunk_buf(p, c_end - 1, h);
+            fetch_pk(B0);
+            fetch_qo(B0);
+            fetch_w(B0);
         }
-        __syncthreads();
+        for (int cid = c_end - 1; cid >= c_begin; --cid) {
+            float *B = chunk_buf(p, cid, h);
+            const float *Bn = chunk_buf(p, max(cid - 1, c_begin), h);
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) B[bdSL + (16 * (2 * w + j) + 4 * g + r) * 128 + col] = dS[2 * w + j][r];
+            f32x4 du = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) du = mfma_f32(Pt[m][r], dO[m][r], du);
+#pragma unroll
+            for (int mm = 0; mm < 8; ++mm)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) du = mfma_f32(Kr[mm][r], dS[mm][r], du);
+            fetch_pk(Bn);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) B[bdU + (16 * w + 4 * g + r) * 128 + col] = du[r];
+            xU[w][l] = du;
+            f32x4 s2[2];
+#pragma unroll
+            for (int j = 0; j < 2; ++j) {
+                s2[j] = dS[2 * w + j] * gl[j];
+#pragma unroll
+                for (int m = 0; m < 4; ++m)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) s2[j] = mfma_f32(Qt[j][m][r], dO[m][r], s2[j]);
+            }
+            fetch_qo(Bn);
+            __syncthreads();
+#pragma unroll
+            for (int m = 0; m < 4; ++m) {
+                const f32x4 um = xU[m][l];
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) s2[j] = mfma_f32(-Wt[j][m][r], um[r], s2[j]);
+            }
+            fetch_w(Bn);
+#pragma unroll
+            for (int j = 0; j < 2; ++j) xS[2 * w + j][l] = s2[j];
+            __syncthreads();
+#pragma unroll
+            for (int mm = 0; mm < 8; ++mm) dS[mm] = xS[mm][l];
+        }
     }
     if (p.ds0) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) p.ds0[sidx + j] = dS[j];
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) p.ds0[sb + (16 * (2 * w + j) + 4 * g + r) * kHeadDim + col] = dS[2 * w + j][r];
     }
 }
 
