@@ -25,8 +25,8 @@
 //
 // Four kernels, all in fp32:
 //   prep        chunks x heads: G, the decayed operands, A, T (forward
-//               substitution, one row at a time), W, U~, Pm, dO, and the
-//               transposed operands of the state passes (VALU, LDS-staged)
+//               substitution, one row at a time), -W, U~, Pm and dO (VALU,
+//               LDS-staged)
 //   fwd_states  sequences x heads x 8 value tiles: walks the chunks forward,
 //               writes each chunk's S0 and U (fp32 MFMA)
 //   bwd_states  the same grid backwards: dS_L and dU per chunk, and the
@@ -55,11 +55,8 @@ constexpr long bO = bdU + kM, bdPm = bO + kM, bdQd = bdPm + kSq, bdW = bdQd + kM
 constexpr long bdTB = bdKg + kM, bdKd = bdTB + kSq, bX = bdKd + kM, bdA = bX + kSq, bKK = bdA + kSq;
 constexpr long bdKi = bKK + kSq;
 constexpr long kBwdFloats = bdKi + kM;
-// Transposed copies the state passes read as MFMA A operands ([128][64] and
-// [64][64], row-major), written by the prep kernel into slots that the
-// gradient kernel only writes (and writes in full before reading), after the
-// state passes have run.
-constexpr long bKgT = bdQd, bQdT = bdW, bWT = bdKg, bPmT = bdPm;
+// The prep kernel stores -W (not W) in the bW slot: only the state passes
+// read it.
 
 __device__ __forceinline__ float *chunk_buf(const BwdParams &p, long cid, int h) {
     return p.buf + (cid * p.c.H + h) * kBwdFloats;
@@ -187,21 +184,6 @@ __device__ void bmm(float *C, int ldc, const float *A, int lda, const float *B, 
     }
 }
 
-// dst = src^T for a row-major [64][ncols] src (row stride lds) into a
-// row-major [ncols][64] dst, through LDS in 64 x 64 blocks (row stride 65:
-// both the row-wise writes and the column-wise reads are free of bank
-// conflicts).  src may have been written by this block (the barrier on entry
-// orders it).
-__device__ void transpose64(float *dst, const float *src, int lds, int ncols, float *st) {
-    const int tid = threadIdx.x;
-    for (int cb = 0; cb < ncols; cb += 64) {
-        __syncthreads();
-        for (int e = tid; e < 64 * 64; e += kNT) st[(e >> 6) * 65 + (e & 63)] = src[(e >> 6) * lds + cb + (e & 63)];
-        __syncthreads();
-        for (int e = tid; e < 64 * 64; e += kNT) dst[(cb + (e >> 6)) * 64 + (e & 63)] = st[(e & 63) * 65 + (e >> 6)];
-    }
-}
-
 // ---- prep: the chunk's WY quantities -----------------------------------------
 __global__ __launch_bounds__(kNT) void bwd_prep_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(16))) float sm[16 * 68 + 16 * 132];
@@ -265,14 +247,9 @@ __global__ __launch_bounds__(kNT) void bwd_prep_kernel(BwdParams p) {
         B[bT + e] = Tm[e];
         B[bTB + e] = Tm[e] * beta_s[e & 63];
     }
-    bmm<false, false, 0, false, 128>(B + bW, 128, B + bTB, 64, B + bKd, 128, 64, 1.f, 64, sm);    // W = TB Kd
+    bmm<false, false, 0, false, 128>(B + bW, 128, B + bTB, 64, B + bKd, 128, 64, -1.f, 64, sm);   // -W = -TB Kd
     bmm<false, false, 0, false, 128>(B + bUt, 128, B + bTB, 64, B + bV, 128, 64, 1.f, 64, sm);    // U~ = TB V
     bmm<false, true, 1, false, 64>(B + bPm, 64, B + bQd, 128, B + bKi, 128, 128, 1.f, 64, sm);    // Pm
-    // transposed copies for the state passes (big is free again: T went out above)
-    transpose64(B + bKgT, B + bKg, 128, 128, big);
-    transpose64(B + bQdT, B + bQd, 128, 128, big);
-    transpose64(B + bWT, B + bW, 128, 128, big);
-    transpose64(B + bPmT, B + bPm, 64, 64, big);
 }
 
 // Block -> (sequence, head, value tile) for the state passes: the eight tiles
@@ -290,9 +267,11 @@ __device__ __forceinline__ void tile_of(const ChunkParams &c, int &n, int &h, in
 // and B[l / 16][l % 16] of a 4-wide k step and holds D[4 (l / 16) + r][l % 16]
 // in element r.  The k step (b, r) of a contraction over rows of a C-layout
 // operand covers rows {16 b + 4 k' + r : k' = 0..3}, so element r of that
-// operand's block b, as each lane holds it, is the B operand of step (b, r),
-// and the matching A operand is one element of a 16-byte load
-// A[row][16 b + 4 (l / 16) .. + 3].  A 128 x 16 state tile is eight such
+// operand's block b, as each lane holds it, is the B operand of step (b, r).
+// The matching A operand is A[row][16 b + 4 (l / 16) + r]: one element of a
+// 16-byte load when A is stored row-major, or, for a transposed operand
+// (A = M^T with M row-major), M[16 b + 4 (l / 16) + r][row], which sixteen
+// lanes fetch as 64 contiguous bytes.  A 128 x 16 state tile is eight such
 // blocks (rows 16 mm + 4 (l / 16) + r, column l % 16).
 //
 // Four waves share each chunk step of one (sequence, head, 16-column tile).
@@ -300,13 +279,33 @@ __device__ __forceinline__ void tile_of(const ChunkParams &c, int &n, int &h, in
 // over the 128 state rows, and the state rows of blocks 2w and 2w + 1, a
 // contraction over the 64 tokens; U and the state go round through LDS so that
 // every wave holds all of U and of the state as B operands of the next
-// product.  Each wave refetches an operand for the next chunk right after its
-// last use in this one (the last chunk refetches itself, so every load is
-// issued on every path).
-__device__ __forceinline__ f32x4 ld4(const float *p) { return *reinterpret_cast<const f32x4 *>(p); }
+// product.  Operands are fetched two chunks ahead into two register sets used
+// in turn; each set is refilled right after its last use (past the last
+// chunk the refill fetches the last chunk again, so every load is issued on
+// every path).
+// Chunk cid's workspace as a buffer resource: 32-bit offsets from a scalar
+// base, so a load needs no 64-bit address arithmetic per lane.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t chunk_rsrc(const BwdParams &p, int cid, int h) {
+    return buffer_rsrc(chunk_buf(p, cid, h), (uint32_t)(kBwdFloats * 4));
+}
+__device__ __forceinline__ f32x4 ldv(__amdgpu_buffer_rsrc_t rs, long idx) {
+    return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(rs, (uint32_t)(idx * 4), 0, 0));
+}
+__device__ __forceinline__ float lds1(__amdgpu_buffer_rsrc_t rs, long idx) {
+    return __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs, (uint32_t)(idx * 4), 0, 0));
+}
+__device__ __forceinline__ void st1(float v, __amdgpu_buffer_rsrc_t rs, long idx) {
+    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, (uint32_t)(idx * 4), 0, 0);
+}
 
 // ---- forward state pass: S0 and U of every chunk ----------------------------
 //   U = U~ - W S0,   S_L = Diag(e^{G_L}) S0 + (K e^{G_L - G})^T U
+struct FwdOps {
+    f32x4 W[8];      // -W[16 w + i][16 mm + 4 g ..]
+    f32x4 Kt[2][4];  // Kg[16 m + 4 g + r][16 (2 w + j) + i]
+    f32x4 gl[2];     // e^{G_L} of rows 16 (2 w + j) + 4 g ..
+    f32x4 ut;        // U~[16 w + 4 g + r][col]
+};
 __global__ __launch_bounds__(kNT) void bwd_fwd_states_kernel(BwdParams p) {
     __shared__ f32x4 xU[4][64];
     __shared__ f32x4 xS[8][64];
@@ -319,69 +318,89 @@ __global__ __launch_bounds__(kNT) void bwd_fwd_states_kernel(BwdParams p) {
     seq_chunks(c, n, c_begin, c_end, seq_start, seq_len);
     const int col = tile * kTileV + i;
     const long sb = ((long)n * H + h) * kHeadDim * kHeadDim;
+    if (c_begin >= c_end) return;   // block-uniform
     f32x4 S[8];
 #pragma unroll
     for (int mm = 0; mm < 8; ++mm)
 #pragma unroll
         for (int r = 0; r < 4; ++r) S[mm][r] = c.s0 ? c.s0[sb + (16 * mm + 4 * g + r) * kHeadDim + col] : 0.f;
-    if (c_begin >= c_end) return;   // block-uniform
-    f32x4 Wr[8], Kt[2][4], gl[2], ut;
-    auto fetch_w = [&](const float *Bn) {
+    const int nch = c_end - c_begin;
+    auto rsrc = [&](int j) { return chunk_rsrc(p, c_begin + min(j, nch - 1), h); };
+    auto fetch_w = [&](FwdOps &o, __amdgpu_buffer_rsrc_t rs) {
 #pragma unroll
-        for (int mm = 0; mm < 8; ++mm) Wr[mm] = ld4(Bn + bW + (16 * w + i) * 128 + 16 * mm + 4 * g);
+        for (int mm = 0; mm < 8; ++mm) o.W[mm] = ldv(rs, bW + (16 * w + i) * 128 + 16 * mm + 4 * g);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) ut[r] = Bn[bUt + (16 * w + 4 * g + r) * 128 + col];
+        for (int r = 0; r < 4; ++r) o.ut[r] = lds1(rs, bUt + (16 * w + 4 * g + r) * 128 + col);
     };
-    auto fetch_k = [&](const float *Bn) {
+    auto fetch_k = [&](FwdOps &o, __amdgpu_buffer_rsrc_t rs) {
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
 #pragma unroll
-            for (int m = 0; m < 4; ++m) Kt[j][m] = ld4(Bn + bKgT + (16 * (2 * w + j) + i) * 64 + 16 * m + 4 * g);
-            gl[j] = ld4(Bn + bGL + 16 * (2 * w + j) + 4 * g);
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o.Kt[j][m][r] = lds1(rs, bKg + (16 * m + 4 * g + r) * 128 + 16 * (2 * w + j) + i);
+            o.gl[j] = ldv(rs, bGL + 16 * (2 * w + j) + 4 * g);
         }
     };
-    fetch_w(chunk_buf(p, c_begin, h));
-    fetch_k(chunk_buf(p, c_begin, h));
-    for (int cid = c_begin; cid < c_end; ++cid) {
-        float *B = chunk_buf(p, cid, h);
-        const float *Bn = chunk_buf(p, min(cid + 1, c_end - 1), h);
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) B[bS0 + (16 * (2 * w + j) + 4 * g + r) * 128 + col] = S[2 * w + j][r];
-        f32x4 u = ut;
+    auto step = [&](int j, FwdOps &o) {
+        const __amdgpu_buffer_rsrc_t rs = rsrc(j), rn = rsrc(j + 2);
+        f32x4 u = o.ut;
 #pragma unroll
         for (int mm = 0; mm < 8; ++mm)
 #pragma unroll
-            for (int r = 0; r < 4; ++r) u = mfma_f32(-Wr[mm][r], S[mm][r], u);
-        fetch_w(Bn);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) B[bU + (16 * w + 4 * g + r) * 128 + col] = u[r];
+            for (int r = 0; r < 4; ++r) u = mfma_f32(o.W[mm][r], S[mm][r], u);
+        fetch_w(o, rn);
         xU[w][l] = u;
         f32x4 s2[2];
 #pragma unroll
-        for (int j = 0; j < 2; ++j) s2[j] = S[2 * w + j] * gl[j];
+        for (int jj = 0; jj < 2; ++jj) s2[jj] = S[2 * w + jj] * o.gl[jj];
         __syncthreads();
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
             const f32x4 um = xU[m][l];
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
+            for (int jj = 0; jj < 2; ++jj)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) s2[j] = mfma_f32(Kt[j][m][r], um[r], s2[j]);
+                for (int r = 0; r < 4; ++r) s2[jj] = mfma_f32(o.Kt[jj][m][r], um[r], s2[jj]);
         }
-        fetch_k(Bn);
+        fetch_k(o, rn);
+        // this chunk's entry state and U, for the gradient kernel
 #pragma unroll
-        for (int j = 0; j < 2; ++j) xS[2 * w + j][l] = s2[j];
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) st1(S[2 * w + jj][r], rs, bS0 + (16 * (2 * w + jj) + 4 * g + r) * 128 + col);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st1(u[r], rs, bU + (16 * w + 4 * g + r) * 128 + col);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) xS[2 * w + jj][l] = s2[jj];
         __syncthreads();
 #pragma unroll
         for (int mm = 0; mm < 8; ++mm) S[mm] = xS[mm][l];
+    };
+    FwdOps o0, o1;
+    fetch_w(o0, rsrc(0));
+    fetch_k(o0, rsrc(0));
+    fetch_w(o1, rsrc(1));
+    fetch_k(o1, rsrc(1));
+    int j = 0;
+    for (; j + 1 < nch; j += 2) {
+        step(j, o0);
+        step(j + 1, o1);
     }
+    if (j < nch) step(j, o0);
 }
 
 // ---- backward state pass: dS_L and dU of every chunk; dS of the start --------
 //   dU = Pm^T dO + Kg dS_L,   dS0 = Diag(e^{G_L}) dS_L + Qd^T dO - W^T dU
 // (dO = scale dy (.) g comes from the prep kernel.)
+struct BwdOps {
+    f32x4 Pt[4];     // Pm[16 m + 4 g + r][16 w + i]
+    f32x4 K[8];      // Kg[16 w + i][16 mm + 4 g ..]
+    f32x4 Qt[2][4];  // Qd[16 m + 4 g + r][16 (2 w + j) + i]
+    f32x4 Wt[2][4];  // -W[16 m + 4 g + r][16 (2 w + j) + i]
+    f32x4 gl[2];
+    f32x4 dO[4];     // dO[16 m + 4 g + r][col]
+};
 __global__ __launch_bounds__(kNT) void bwd_bwd_states_kernel(BwdParams p) {
     __shared__ f32x4 xU[4][64];
     __shared__ f32x4 xS[8][64];
@@ -400,84 +419,100 @@ __global__ __launch_bounds__(kNT) void bwd_bwd_states_kernel(BwdParams p) {
 #pragma unroll
         for (int r = 0; r < 4; ++r)
             dS[mm][r] = p.ds_final ? p.ds_final[sb + (16 * mm + 4 * g + r) * kHeadDim + col] : 0.f;
-    if (c_begin < c_end) {   // block-uniform
-        f32x4 Pt[4], Kr[8], Qt[2][4], Wt[2][4], gl[2], dO[4];
-        auto fetch_pk = [&](const float *Bn) {
+    const int nch = max(0, c_end - c_begin);
+    // the j-th chunk from the end
+    auto rsrc = [&](int j) { return chunk_rsrc(p, c_end - 1 - min(j, nch - 1), h); };
+    auto fetch_pk = [&](BwdOps &o, __amdgpu_buffer_rsrc_t rs) {
 #pragma unroll
-            for (int m = 0; m < 4; ++m) Pt[m] = ld4(Bn + bPmT + (16 * w + i) * 64 + 16 * m + 4 * g);
+        for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int mm = 0; mm < 8; ++mm) Kr[mm] = ld4(Bn + bKg + (16 * w + i) * 128 + 16 * mm + 4 * g);
-        };
-        auto fetch_qo = [&](const float *Bn) {
+            for (int r = 0; r < 4; ++r) o.Pt[m][r] = lds1(rs, bPm + (16 * m + 4 * g + r) * 64 + 16 * w + i);
 #pragma unroll
-            for (int j = 0; j < 2; ++j) {
+        for (int mm = 0; mm < 8; ++mm) o.K[mm] = ldv(rs, bKg + (16 * w + i) * 128 + 16 * mm + 4 * g);
+    };
+    auto fetch_qo = [&](BwdOps &o, __amdgpu_buffer_rsrc_t rs) {
 #pragma unroll
-                for (int m = 0; m < 4; ++m) Qt[j][m] = ld4(Bn + bQdT + (16 * (2 * w + j) + i) * 64 + 16 * m + 4 * g);
-                gl[j] = ld4(Bn + bGL + 16 * (2 * w + j) + 4 * g);
-            }
-#pragma unroll
-            for (int m = 0; m < 4; ++m)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) dO[m][r] = Bn[bdO + (16 * m + 4 * g + r) * 128 + col];
-        };
-        auto fetch_w = [&](const float *Bn) {
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int m = 0; m < 4; ++m) Wt[j][m] = ld4(Bn + bWT + (16 * (2 * w + j) + i) * 64 + 16 * m + 4 * g);
-        };
-        {
-            const float *B0 = chunk_buf(p, c_end - 1, h);
-            fetch_pk(B0);
-            fetch_qo(B0);
-            fetch_w(B0);
-        }
-        for (int cid = c_end - 1; cid >= c_begin; --cid) {
-            float *B = chunk_buf(p, cid, h);
-            const float *Bn = chunk_buf(p, max(cid - 1, c_begin), h);
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) B[bdSL + (16 * (2 * w + j) + 4 * g + r) * 128 + col] = dS[2 * w + j][r];
-            f32x4 du = {0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < 2; ++j) {
 #pragma unroll
             for (int m = 0; m < 4; ++m)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) du = mfma_f32(Pt[m][r], dO[m][r], du);
-#pragma unroll
-            for (int mm = 0; mm < 8; ++mm)
-#pragma unroll
-                for (int r = 0; r < 4; ++r) du = mfma_f32(Kr[mm][r], dS[mm][r], du);
-            fetch_pk(Bn);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) B[bdU + (16 * w + 4 * g + r) * 128 + col] = du[r];
-            xU[w][l] = du;
-            f32x4 s2[2];
-#pragma unroll
-            for (int j = 0; j < 2; ++j) {
-                s2[j] = dS[2 * w + j] * gl[j];
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) s2[j] = mfma_f32(Qt[j][m][r], dO[m][r], s2[j]);
-            }
-            fetch_qo(Bn);
-            __syncthreads();
-#pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                const f32x4 um = xU[m][l];
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) s2[j] = mfma_f32(-Wt[j][m][r], um[r], s2[j]);
-            }
-            fetch_w(Bn);
-#pragma unroll
-            for (int j = 0; j < 2; ++j) xS[2 * w + j][l] = s2[j];
-            __syncthreads();
-#pragma unroll
-            for (int mm = 0; mm < 8; ++mm) dS[mm] = xS[mm][l];
+                for (int r = 0; r < 4; ++r) o.Qt[j][m][r] = lds1(rs, bQd + (16 * m + 4 * g + r) * 128 + 16 * (2 * w + j) + i);
+            o.gl[j] = ldv(rs, bGL + 16 * (2 * w + j) + 4 * g);
         }
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) o.dO[m][r] = lds1(rs, bdO + (16 * m + 4 * g + r) * 128 + col);
+    };
+    auto fetch_w = [&](BwdOps &o, __amdgpu_buffer_rsrc_t rs) {
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) o.Wt[j][m][r] = lds1(rs, bW + (16 * m + 4 * g + r) * 128 + 16 * (2 * w + j) + i);
+    };
+    auto step = [&](int j, BwdOps &o) {
+        const __amdgpu_buffer_rsrc_t rs = rsrc(j), rn = rsrc(j + 2);
+        f32x4 du = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) du = mfma_f32(o.Pt[m][r], o.dO[m][r], du);
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) du = mfma_f32(o.K[mm][r], dS[mm][r], du);
+        fetch_pk(o, rn);
+        xU[w][l] = du;
+        f32x4 s2[2];
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            s2[jj] = dS[2 * w + jj] * o.gl[jj];
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) s2[jj] = mfma_f32(o.Qt[jj][m][r], o.dO[m][r], s2[jj]);
+        }
+        fetch_qo(o, rn);
+        __syncthreads();
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+            const f32x4 um = xU[m][l];
+#pragma unroll
+            for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) s2[jj] = mfma_f32(o.Wt[jj][m][r], um[r], s2[jj]);
+        }
+        fetch_w(o, rn);
+        // this chunk's end-state gradient and dU, for the gradient kernel
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                st1(dS[2 * w + jj][r], rs, bdSL + (16 * (2 * w + jj) + 4 * g + r) * 128 + col);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) st1(du[r], rs, bdU + (16 * w + 4 * g + r) * 128 + col);
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) xS[2 * w + jj][l] = s2[jj];
+        __syncthreads();
+#pragma unroll
+        for (int mm = 0; mm < 8; ++mm) dS[mm] = xS[mm][l];
+    };
+    if (nch > 0) {   // block-uniform
+        BwdOps o0, o1;
+        fetch_pk(o0, rsrc(0));
+        fetch_qo(o0, rsrc(0));
+        fetch_w(o0, rsrc(0));
+        fetch_pk(o1, rsrc(1));
+        fetch_qo(o1, rsrc(1));
+        fetch_w(o1, rsrc(1));
+        int j = 0;
+        for (; j + 1 < nch; j += 2) {
+            step(j, o0);
+            step(j + 1, o1);
+        }
+        if (j < nch) step(j, o0);
     }
     if (p.ds0) {
 #pragma unroll
