@@ -23,9 +23,10 @@
 // (the forward's WY/UT form is the one in chunk.hip; see the oracle for the
 // same gradient taken token by token).
 //
-// Four kernels, all in fp32:
+// Five kernels, all in fp32:
+//   do          chunks x heads: dO = scale dy (.) g (elementwise)
 //   prep        chunks x heads: G, the decayed operands, A, T (forward
-//               substitution, one row at a time), -W, U~, Pm and dO (VALU,
+//               substitution, one row at a time), -W, U~, Pm (VALU,
 //               LDS-staged)
 //   fwd_states  sequences x heads x 8 value tiles: walks the chunks forward,
 //               writes each chunk's S0 and U (fp32 MFMA)
@@ -184,6 +185,33 @@ __device__ void bmm(float *C, int ldc, const float *A, int lda, const float *B, 
     }
 }
 
+// ---- dO = scale dy (.) g into every chunk's slot (zero past the chunk's end) --
+// A bandwidth-bound pass of its own, kept out of the latency-bound prep
+// kernel.  Thread: four channels of one row; rows past the chunk's end load
+// its last row (in bounds) and store zeros.
+__global__ __launch_bounds__(kNT) void bwd_do_kernel(BwdParams p) {
+    const ChunkParams &c = p.c;
+    const int H = c.H, h = blockIdx.x % H, cid = blockIdx.x / H, tid = threadIdx.x;
+    const ChunkInfo ci = load_chunk(c, cid);
+    float *B = chunk_buf(p, cid, h);
+    uint2 dy[8], gt[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int e = tid + k * kNT, i = e >> 5, c4 = (e & 31) * 4;
+        const long src = (((long)ci.start + min(i, ci.len - 1)) * H + h) * kHeadDim + c4;
+        dy[k] = *reinterpret_cast<const uint2 *>(p.dy + src);
+        gt[k] = c.gate ? *reinterpret_cast<const uint2 *>(c.gate + src) : make_uint2(0x3f803f80u, 0x3f803f80u);
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+        const int e = tid + k * kNT, i = e >> 5, c4 = (e & 31) * 4;
+        const float sc = i < ci.len ? c.scale : 0.f;
+        const float4 v = make_float4(sc * lo_bf(dy[k].x) * lo_bf(gt[k].x), sc * hi_bf(dy[k].x) * hi_bf(gt[k].x),
+                                     sc * lo_bf(dy[k].y) * lo_bf(gt[k].y), sc * hi_bf(dy[k].y) * hi_bf(gt[k].y));
+        *reinterpret_cast<float4 *>(B + bdO + i * 128 + c4) = v;
+    }
+}
+
 // ---- prep: the chunk's WY quantities -----------------------------------------
 __global__ __launch_bounds__(kNT) void bwd_prep_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(16))) float sm[16 * 68 + 16 * 132];
@@ -211,7 +239,6 @@ __global__ __launch_bounds__(kNT) void bwd_prep_kernel(BwdParams p) {
         const long src = ((tok0 + i) * H + h) * kHeadDim + ch;
         const bool in = i < len;
         const float q = in ? bf2f(c.q[src]) : 0.f, k = in ? bf2f(c.k[src]) : 0.f, v = in ? bf2f(c.v[src]) : 0.f;
-        const float dy = in ? bf2f(p.dy[src]) : 0.f, gv = in && c.gate ? bf2f(c.gate[src]) : 1.f;
         const float g = big[e];
         const float eg = expf(g);
         B[bQd + e] = q * eg;
@@ -219,7 +246,6 @@ __global__ __launch_bounds__(kNT) void bwd_prep_kernel(BwdParams p) {
         B[bKi + e] = k * expf(-g);
         B[bKg + e] = k * expf(big[63 * 128 + ch] - g);
         B[bV + e] = v;
-        B[bdO + e] = c.scale * dy * gv;   // dO = scale dy (.) g
     }
     // A = tril(Kd Ki^T, -1), rows scaled by beta
     bmm<false, true, 2, false, 64>(big, 64, B + bKd, 128, B + bKi, 128, 128, 1.f, 64, sm);
@@ -392,7 +418,7 @@ __global__ __launch_bounds__(kNT) void bwd_fwd_states_kernel(BwdParams p) {
 
 // ---- backward state pass: dS_L and dU of every chunk; dS of the start --------
 //   dU = Pm^T dO + Kg dS_L,   dS0 = Diag(e^{G_L}) dS_L + Qd^T dO - W^T dU
-// (dO = scale dy (.) g comes from the prep kernel.)
+// (dO = scale dy (.) g comes from bwd_do_kernel.)
 struct BwdOps {
     f32x4 Pt[4];     // Pm[16 m + 4 g + r][16 w + i]
     f32x4 K[8];      // Kg[16 w + i][16 mm + 4 g ..]
@@ -624,7 +650,10 @@ hipError_t launch_chunk_backward(const BwdParams &p, hipStream_t s) {
     if (e != hipSuccess) return e;
     const unsigned per_chunk = (unsigned)((long)p.c.n_chunks * p.c.H);
     const unsigned per_tile = (unsigned)(p.c.n_seqs * p.c.H * kTilesV);
-    if (per_chunk > 0) hipLaunchKernelGGL(bwd_prep_kernel, dim3(per_chunk), dim3(kNT), 0, s, p);
+    if (per_chunk > 0) {
+        hipLaunchKernelGGL(bwd_do_kernel, dim3(per_chunk), dim3(kNT), 0, s, p);
+        hipLaunchKernelGGL(bwd_prep_kernel, dim3(per_chunk), dim3(kNT), 0, s, p);
+    }
     if (per_tile > 0) {
         hipLaunchKernelGGL(bwd_fwd_states_kernel, dim3(per_tile), dim3(kNT), 0, s, p);
         hipLaunchKernelGGL(bwd_bwd_states_kernel, dim3(per_tile), dim3(kNT), 0, s, p);
