@@ -223,29 +223,56 @@ __global__ __launch_bounds__(kNT) void bwd_prep_kernel(BwdParams p) {
     const long tok0 = ci.start;
     const int len = ci.len;
     float *B = chunk_buf(p, cid, h);
+    // Loads are issued in batches ahead of the stores that use them: vmcnt
+    // counts stores too, so a load waited for behind a store would also wait
+    // for that store.  Rows past the chunk's end load its last row (in bounds)
+    // and count as zero.
     if (tid < 128) {
         float run = 0.f;
-        for (int i = 0; i < 64; ++i) {
-            run += i < len ? bf2f(c.log_alpha[((tok0 + i) * H + h) * kHeadDim + tid]) : 0.f;
-            big[i * 128 + tid] = run;
-            B[bG + i * 128 + tid] = run;
+#pragma unroll
+        for (int i0 = 0; i0 < 64; i0 += 16) {
+            uint16_t la[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) la[t] = c.log_alpha[((tok0 + min(i0 + t, len - 1)) * H + h) * kHeadDim + tid];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                run += i0 + t < len ? bf2f(la[t]) : 0.f;
+                big[(i0 + t) * 128 + tid] = run;
+                B[bG + (i0 + t) * 128 + tid] = run;
+            }
         }
         B[bGL + tid] = expf(run);
     }
     if (tid < 64) beta_s[tid] = tid < len ? c.beta[(tok0 + tid) * H + h] : 0.f;
     __syncthreads();
-    for (int e = tid; e < 64 * 128; e += kNT) {
-        const int i = e >> 7, ch = e & 127;
-        const long src = ((tok0 + i) * H + h) * kHeadDim + ch;
-        const bool in = i < len;
-        const float q = in ? bf2f(c.q[src]) : 0.f, k = in ? bf2f(c.k[src]) : 0.f, v = in ? bf2f(c.v[src]) : 0.f;
-        const float g = big[e];
-        const float eg = expf(g);
-        B[bQd + e] = q * eg;
-        B[bKd + e] = k * eg;
-        B[bKi + e] = k * expf(-g);
-        B[bKg + e] = k * expf(big[63 * 128 + ch] - g);
-        B[bV + e] = v;
+    {
+        const int ch = tid & 127;
+        const float gl = big[63 * 128 + ch];
+#pragma unroll 1
+        for (int k0 = 0; k0 < 32; k0 += 8) {   // element e = tid + 256 k: row 2 k + tid / 128
+            uint16_t rq[8], rk[8], rv[8];
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int i = 2 * (k0 + t) + (tid >> 7);
+                const long src = ((tok0 + min(i, len - 1)) * H + h) * kHeadDim + ch;
+                rq[t] = c.q[src];
+                rk[t] = c.k[src];
+                rv[t] = c.v[src];
+            }
+#pragma unroll
+            for (int t = 0; t < 8; ++t) {
+                const int e = tid + (k0 + t) * kNT, i = e >> 7;
+                const bool in = i < len;
+                const float q = in ? bf2f(rq[t]) : 0.f, k = in ? bf2f(rk[t]) : 0.f, v = in ? bf2f(rv[t]) : 0.f;
+                const float g = big[e];
+                const float eg = expf(g);
+                B[bQd + e] = q * eg;
+                B[bKd + e] = k * eg;
+                B[bKi + e] = k * expf(-g);
+                B[bKg + e] = k * expf(gl - g);
+                B[bV + e] = v;
+            }
+        }
     }
     // A = tril(Kd Ki^T, -1), rows scaled by beta
     bmm<false, true, 2, false, 64>(big, 64, B + bKd, 128, B + bKi, 128, 128, 1.f, 64, sm);
