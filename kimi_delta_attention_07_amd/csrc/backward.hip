@@ -631,24 +631,59 @@ __global__ __launch_bounds__(kNT) void bwd_grads_kernel(BwdParams p) {
         dGL_s[ch] = s + B[bGL + ch] * t;
     }
     __syncthreads();
+    // As in the prep kernel, loads go out in batches ahead of the stores that
+    // use them (vmcnt counts stores too).
     if (tid < 128) {   // dlog alpha: reverse cumulative sum of dG, plus dG_L
         const int ch = tid;
         float run = dGL_s[ch];
-        for (int i = 63; i >= 0; --i) {
-            const long e = i * 128 + ch;
-            run += B[bdQd + e] * B[bQd + e] + B[bdKd + e] * B[bKd + e] - B[bdKi + e] * B[bKi + e] -
-                   B[bdKg + e] * B[bKg + e];
-            if (i < len) p.dla[((tok0 + i) * H + h) * kHeadDim + ch] = run;
+#pragma unroll 1
+        for (int i0 = 63; i0 >= 0; i0 -= 16) {
+            float dg[16];
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const long e = (i0 - t) * 128 + ch;
+                dg[t] = B[bdQd + e] * B[bQd + e] + B[bdKd + e] * B[bKd + e] - B[bdKi + e] * B[bKi + e] -
+                        B[bdKg + e] * B[bKg + e];
+            }
+#pragma unroll
+            for (int t = 0; t < 16; ++t) {
+                const int i = i0 - t;
+                run += dg[t];
+                if (i < len) p.dla[((tok0 + i) * H + h) * kHeadDim + ch] = run;
+            }
         }
     }
-    for (int e = tid; e < 64 * 128; e += kNT) {
-        const int i = e >> 7, ch = e & 127;
-        if (i >= len) continue;
-        const long o = ((tok0 + i) * H + h) * kHeadDim + ch;
-        const float g = B[bG + e], eg = expf(g);
-        p.dq[o] = B[bdQd + e] * eg;
-        p.dk[o] = B[bdKd + e] * eg + B[bdKi + e] * expf(-g) + B[bdKg + e] * expf(B[bG + 63 * 128 + ch] - g);
-        if (p.dgate) p.dgate[o] = bf2f(p.dy[o]) * c.scale * B[bO + e];
+    {
+        const int ch = tid & 127;
+        const float gl = B[bG + 63 * 128 + ch];
+#pragma unroll 1
+        for (int k0 = 0; k0 < 32; k0 += 4) {   // element e = tid + 256 k: row 2 k + tid / 128
+            float gv[4], dqd[4], dkd[4], dki[4], dkg[4], ov[4];
+            uint16_t dyv[4];
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int e = tid + (k0 + t) * kNT, i = e >> 7;
+                gv[t] = B[bG + e];
+                dqd[t] = B[bdQd + e];
+                dkd[t] = B[bdKd + e];
+                dki[t] = B[bdKi + e];
+                dkg[t] = B[bdKg + e];
+                if (p.dgate) {
+                    ov[t] = B[bO + e];
+                    dyv[t] = p.dy[((tok0 + min(i, len - 1)) * H + h) * kHeadDim + ch];
+                }
+            }
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                const int e = tid + (k0 + t) * kNT, i = e >> 7;
+                if (i >= len) continue;
+                const long o = ((tok0 + i) * H + h) * kHeadDim + ch;
+                const float g = gv[t], eg = expf(g);
+                p.dq[o] = dqd[t] * eg;
+                p.dk[o] = dkd[t] * eg + dki[t] * expf(-g) + dkg[t] * expf(gl - g);
+                if (p.dgate) p.dgate[o] = bf2f(dyv[t]) * c.scale * ov[t];
+            }
+        }
     }
     if (tid < len) p.dbeta[(tok0 + tid) * H + h] = dbeta_s[tid];
 }
