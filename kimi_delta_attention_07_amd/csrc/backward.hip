@@ -602,9 +602,18 @@ __global__ __launch_bounds__(kNT) void bwd_grads_kernel(BwdParams p) {
                                     1.f, len, sm);                                                       // dV = TB^T dU
     __syncthreads();
     // dT = dTB diag(beta) (held in the dA slot); dbeta from TB = T diag(beta)
-    for (int e = tid; e < 64 * 64; e += kNT) B[bdA + e] = B[bdTB + e] * beta_s[e & 63];
+    // (loads in batches ahead of the stores that follow them: vmcnt counts
+    // stores too)
+    {
+        float x[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) x[t] = B[bdTB + tid + t * kNT];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) B[bdA + tid + t * kNT] = x[t] * beta_s[(tid + t * kNT) & 63];
+    }
     if (tid < 64) {
         float s = 0.f;
+#pragma unroll 16
         for (int i = 0; i < 64; ++i) s += B[bdTB + i * 64 + tid] * B[bT + i * 64 + tid];
         dbeta_s[tid] = s;
     }
@@ -614,11 +623,18 @@ __global__ __launch_bounds__(kNT) void bwd_grads_kernel(BwdParams p) {
     __syncthreads();
     if (tid < 64) {
         float s = 0.f;
+#pragma unroll 16
         for (int m = 0; m < 64; ++m) s += B[bdA + tid * 64 + m] * B[bKK + tid * 64 + m];
         dbeta_s[tid] += s;
     }
     __syncthreads();
-    for (int e = tid; e < 64 * 64; e += kNT) B[bdA + e] *= beta_s[e >> 6];                          // diag(beta) dA
+    {   // diag(beta) dA
+        float x[16];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) x[t] = B[bdA + tid + t * kNT];
+#pragma unroll
+        for (int t = 0; t < 16; ++t) B[bdA + tid + t * kNT] = x[t] * beta_s[(tid + t * kNT) >> 6];
+    }
     bmm<false, false, 0, true, 128>(B + bdKd, 128, B + bdA, 64, B + bKi, 128, 64, 1.f, 64, sm);      // += (beta dA) Ki
     bmm<true, false, 0, false, 128>(B + bdKi, 128, B + bdA, 64, B + bKd, 128, 64, 1.f, 64, sm);      // (beta dA)^T Kd
     bmm<true, false, 0, true, 128>(B + bdKi, 128, B + bdPm, 64, B + bQd, 128, 64, 1.f, 64, sm);      //  + dPm^T Qd
@@ -626,7 +642,9 @@ __global__ __launch_bounds__(kNT) void bwd_grads_kernel(BwdParams p) {
     if (tid < 128) {
         const int ch = tid;
         float s = 0.f, t = 0.f;
+#pragma unroll 16
         for (int i = 0; i < 64; ++i) s += B[bdKg + i * 128 + ch] * B[bKg + i * 128 + ch];
+#pragma unroll 16
         for (int j = 0; j < 128; ++j) t += B[bS0 + ch * 128 + j] * B[bdSL + ch * 128 + j];
         dGL_s[ch] = s + B[bGL + ch] * t;
     }
