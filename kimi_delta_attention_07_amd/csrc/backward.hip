@@ -92,7 +92,7 @@ __device__ void bmm(float *C, int ldc, const float *A, int lda, const float *B, 
     constexpr int LA = 68, LB = 132;   // LDS rows, padded (multiples of 4 for 16-byte accesses)
     float *As = sm;                    // [16][LA]: As[kk][i]
     float *Bs = sm + 16 * LA;          // [16][LB]: Bs[kk][j]
-    const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+    const int tid = threadIdx.x;
     // this thread's share of a 16-wide k slab: one 16-byte piece of op(A),
     // one or two of op(B); the next slab is fetched while this one is used
     const int ai = TA ? (tid & 15) * 4 : tid >> 2, ak = TA ? tid >> 4 : (tid & 3) * 4;
@@ -125,11 +125,14 @@ __device__ void bmm(float *C, int ldc, const float *A, int lda, const float *B, 
             *reinterpret_cast<float4 *>(Bs + k * LB + j) = v;
         }
     };
-    float acc[4][8];
+    // wave w: output rows 16 w .. 16 w + 15, N / 16 column blocks, on fp32
+    // MFMAs; lane l supplies op(A)[16 w + l % 16][k] and op(B)[k][16 nb + l % 16]
+    // for k = k0 + 4 t + l / 16 and holds C[16 w + 4 (l / 16) + r][16 nb + l % 16]
+    constexpr int NB = N / 16;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, lg = l >> 4, lc = l & 15;
+    f32x4 acc[NB];
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
-#pragma unroll
-        for (int c = 0; c < 8; ++c) acc[r][c] = 0.f;
+    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     __syncthreads();   // operands written earlier by this block are complete; staging is free
     ra = *reinterpret_cast<const float4 *>(a_ptr(0));
     rb0 = *reinterpret_cast<const float4 *>(b_ptr(0, tid));
@@ -151,35 +154,28 @@ __device__ void bmm(float *C, int ldc, const float *A, int lda, const float *B, 
             rb0 = *reinterpret_cast<const float4 *>(b_ptr(k0 + 16, tid));
             if constexpr (N == 128) rb1 = *reinterpret_cast<const float4 *>(b_ptr(k0 + 16, tid + kNT));
         }
-#pragma unroll 4
-        for (int kk = 0; kk < 16; ++kk) {
-            const float4 a4 = *reinterpret_cast<const float4 *>(As + kk * LA + 4 * ty);
-            const float4 b0 = *reinterpret_cast<const float4 *>(Bs + kk * LB + 4 * tx);
-            const float4 b1 = N > 64 ? *reinterpret_cast<const float4 *>(Bs + kk * LB + 64 + 4 * tx)
-                                     : make_float4(0.f, 0.f, 0.f, 0.f);
-            const float a[4] = {a4.x, a4.y, a4.z, a4.w};
-            const float b[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+        for (int t = 0; t < 4; ++t) {
+            const int kk = 4 * t + lg;
+            const float a = As[kk * LA + 16 * w + lc];
 #pragma unroll
-                for (int c = 0; c < 8; ++c) acc[r][c] += a[r] * b[c];
+            for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma_f32(a, Bs[kk * LB + 16 * nb + lc], acc[nb]);
         }
         __syncthreads();
     }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-        const int i = 4 * ty + r;
+        const int i = 16 * w + 4 * lg + r;
         if (i >= mrows) continue;
 #pragma unroll
-        for (int cc = 0; cc < 8; ++cc) {
-            if (cc >= 4 && N <= 64) continue;
-            const int j = cc < 4 ? 4 * tx + cc : 64 + 4 * tx + (cc - 4);
+        for (int nb = 0; nb < NB; ++nb) {
+            const int j = 16 * nb + lc;
             const bool keep = MASK == 0 || (MASK == 1 ? j <= i : j < i);
             float *dst = C + (long)i * ldc + j;
             if (ACC) {
-                if (keep) *dst += alpha * acc[r][cc];
+                if (keep) *dst += alpha * acc[nb][r];
             } else {
-                *dst = keep ? alpha * acc[r][cc] : 0.f;
+                *dst = keep ? alpha * acc[nb][r] : 0.f;
             }
         }
     }
