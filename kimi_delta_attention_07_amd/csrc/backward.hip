@@ -83,18 +83,20 @@ __device__ __forceinline__ void seq_chunks(const ChunkParams &c, int n, int &c_b
 //   op(B)[k][j] = TB ? B[j ldb + k] : B[k ldb + j]
 // MASK 1 keeps entries j <= i, 2 keeps j < i (the rest are written as 0, or
 // left alone when accumulating); rows >= mrows are not written.  N is 64 or
-// 128, K a multiple of 16; operands 16-byte aligned with lda, ldb multiples of
+// 128, K a multiple of 16 HALVES; operands 16-byte aligned with lda, ldb multiples of
 // 4.  The operands may be in global memory (written earlier by this block:
 // the barrier on entry orders them) or in LDS.
-template <bool TA, bool TB, int MASK, bool ACC, int N>
+template <bool TA, bool TB, int MASK, bool ACC, int N, int HALVES = 2>
 __device__ void bmm(float *C, int ldc, const float *A, int lda, const float *B, int ldb, int K, float alpha, int mrows,
                     float *sm) {
     constexpr int LA = 68, LB = 132;   // LDS rows, padded (multiples of 4 for 16-byte accesses)
-    float *As = sm;                    // [16][LA]: As[kk][i]
-    float *Bs = sm + 16 * LA;          // [16][LB]: Bs[kk][j]
+    constexpr int KS = 16 * HALVES;    // k slab
+    float *As = sm;                    // [KS][LA]: As[kk][i]
+    float *Bs = sm + KS * LA;          // [KS][LB]: Bs[kk][j]
     const int tid = threadIdx.x;
-    // this thread's share of a 16-wide k slab: one 16-byte piece of op(A),
-    // one or two of op(B); the next slab is fetched while this one is used
+    // The k range goes in slabs of KS = 16 HALVES, staged in LDS as halves of 16;
+    // this thread's share of a half: one 16-byte piece of op(A), one or two
+    // of op(B).  The next slab is fetched while this one is used.
     const int ai = TA ? (tid & 15) * 4 : tid >> 2, ak = TA ? tid >> 4 : (tid & 3) * 4;
     auto a_ptr = [&](int k0) { return TA ? A + (long)(k0 + ak) * lda + ai : A + (long)ai * lda + k0 + ak; };
     auto b_pos = [&](int e, int &j, int &k) {
@@ -112,10 +114,20 @@ __device__ void bmm(float *C, int ldc, const float *A, int lda, const float *B, 
         b_pos(e, j, k);
         return TB ? B + (long)j * ldb + k0 + k : B + (long)(k0 + k) * ldb + j;
     };
-    float4 ra, rb0, rb1 = make_float4(0.f, 0.f, 0.f, 0.f);   // op(B): 4 N / 256 pieces per thread
-    auto put_b = [&](const float4 &v, int e) {
+    auto put_a = [&](const float4 &v, int kb) {
+        if (TA) {
+            *reinterpret_cast<float4 *>(As + (kb + ak) * LA + ai) = v;
+        } else {
+            As[(kb + ak) * LA + ai] = v.x;
+            As[(kb + ak + 1) * LA + ai] = v.y;
+            As[(kb + ak + 2) * LA + ai] = v.z;
+            As[(kb + ak + 3) * LA + ai] = v.w;
+        }
+    };
+    auto put_b = [&](const float4 &v, int e, int kb) {
         int j, k;
         b_pos(e, j, k);
+        k += kb;
         if (TB) {
             Bs[k * LB + j] = v.x;
             Bs[(k + 1) * LB + j] = v.y;
@@ -123,6 +135,18 @@ __device__ void bmm(float *C, int ldc, const float *A, int lda, const float *B, 
             Bs[(k + 3) * LB + j] = v.w;
         } else {
             *reinterpret_cast<float4 *>(Bs + k * LB + j) = v;
+        }
+    };
+    const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 ra0, ra1 = z4, rb00, rb10 = z4, rb01 = z4, rb11 = z4;   // [half]: A piece, B pieces (second only for N = 128)
+    auto fetch = [&](int k0) {
+        ra0 = *reinterpret_cast<const float4 *>(a_ptr(k0));
+        rb00 = *reinterpret_cast<const float4 *>(b_ptr(k0, tid));
+        if constexpr (N == 128) rb01 = *reinterpret_cast<const float4 *>(b_ptr(k0, tid + kNT));
+        if constexpr (HALVES == 2) {
+            ra1 = *reinterpret_cast<const float4 *>(a_ptr(k0 + 16));
+            rb10 = *reinterpret_cast<const float4 *>(b_ptr(k0 + 16, tid));
+            if constexpr (N == 128) rb11 = *reinterpret_cast<const float4 *>(b_ptr(k0 + 16, tid + kNT));
         }
     };
     // wave w: output rows 16 w .. 16 w + 15, N / 16 column blocks, on fp32
@@ -134,28 +158,20 @@ __device__ void bmm(float *C, int ldc, const float *A, int lda, const float *B, 
 #pragma unroll
     for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     __syncthreads();   // operands written earlier by this block are complete; staging is free
-    ra = *reinterpret_cast<const float4 *>(a_ptr(0));
-    rb0 = *reinterpret_cast<const float4 *>(b_ptr(0, tid));
-    if constexpr (N == 128) rb1 = *reinterpret_cast<const float4 *>(b_ptr(0, tid + kNT));
-    for (int k0 = 0; k0 < K; k0 += 16) {
-        if (TA) {
-            *reinterpret_cast<float4 *>(As + ak * LA + ai) = ra;
-        } else {
-            As[ak * LA + ai] = ra.x;
-            As[(ak + 1) * LA + ai] = ra.y;
-            As[(ak + 2) * LA + ai] = ra.z;
-            As[(ak + 3) * LA + ai] = ra.w;
+    fetch(0);
+    for (int k0 = 0; k0 < K; k0 += KS) {
+        put_a(ra0, 0);
+        put_b(rb00, tid, 0);
+        if constexpr (N == 128) put_b(rb01, tid + kNT, 0);
+        if constexpr (HALVES == 2) {
+            put_a(ra1, 16);
+            put_b(rb10, tid, 16);
+            if constexpr (N == 128) put_b(rb11, tid + kNT, 16);
         }
-        put_b(rb0, tid);
-        if constexpr (N == 128) put_b(rb1, tid + kNT);
         __syncthreads();
-        if (k0 + 16 < K) {
-            ra = *reinterpret_cast<const float4 *>(a_ptr(k0 + 16));
-            rb0 = *reinterpret_cast<const float4 *>(b_ptr(k0 + 16, tid));
-            if constexpr (N == 128) rb1 = *reinterpret_cast<const float4 *>(b_ptr(k0 + 16, tid + kNT));
-        }
+        if (k0 + KS < K) fetch(k0 + KS);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
+        for (int t = 0; t < 4 * HALVES; ++t) {
             const int kk = 4 * t + lg;
             const float a = As[kk * LA + 16 * w + lc];
 #pragma unroll
@@ -210,7 +226,7 @@ __global__ __launch_bounds__(kNT) void bwd_do_kernel(BwdParams p) {
 
 // ---- prep: the chunk's WY quantities -----------------------------------------
 __global__ __launch_bounds__(kNT) void bwd_prep_kernel(BwdParams p) {
-    __shared__ __attribute__((aligned(16))) float sm[16 * 68 + 16 * 132];
+    __shared__ __attribute__((aligned(16))) float sm[16 * 68 + 16 * 132];   // 16-wide slabs: three blocks per CU
     __shared__ float big[64 * 128];   // G, then A (first half) and T (second half)
     __shared__ float beta_s[64];
     const ChunkParams &c = p.c;
@@ -271,7 +287,7 @@ __global__ __launch_bounds__(kNT) void bwd_prep_kernel(BwdParams p) {
         }
     }
     // A = tril(Kd Ki^T, -1), rows scaled by beta
-    bmm<false, true, 2, false, 64>(big, 64, B + bKd, 128, B + bKi, 128, 128, 1.f, 64, sm);
+    bmm<false, true, 2, false, 64, 1>(big, 64, B + bKd, 128, B + bKi, 128, 128, 1.f, 64, sm);
     __syncthreads();
     for (int e = tid; e < 64 * 64; e += kNT) big[e] *= beta_s[e >> 6];
     __syncthreads();
@@ -296,9 +312,9 @@ __global__ __launch_bounds__(kNT) void bwd_prep_kernel(BwdParams p) {
         B[bT + e] = Tm[e];
         B[bTB + e] = Tm[e] * beta_s[e & 63];
     }
-    bmm<false, false, 0, false, 128>(B + bW, 128, B + bTB, 64, B + bKd, 128, 64, -1.f, 64, sm);   // -W = -TB Kd
-    bmm<false, false, 0, false, 128>(B + bUt, 128, B + bTB, 64, B + bV, 128, 64, 1.f, 64, sm);    // U~ = TB V
-    bmm<false, true, 1, false, 64>(B + bPm, 64, B + bQd, 128, B + bKi, 128, 128, 1.f, 64, sm);    // Pm
+    bmm<false, false, 0, false, 128, 1>(B + bW, 128, B + bTB, 64, B + bKd, 128, 64, -1.f, 64, sm);   // -W = -TB Kd
+    bmm<false, false, 0, false, 128, 1>(B + bUt, 128, B + bTB, 64, B + bV, 128, 64, 1.f, 64, sm);    // U~ = TB V
+    bmm<false, true, 1, false, 64, 1>(B + bPm, 64, B + bQd, 128, B + bKi, 128, 128, 1.f, 64, sm);    // Pm
 }
 
 // Block -> (sequence, head, value tile) for the state passes: the eight tiles
@@ -573,7 +589,7 @@ __global__ __launch_bounds__(kNT) void bwd_bwd_states_kernel(BwdParams p) {
 
 // ---- per-chunk gradients -------------------------------------------------------
 __global__ __launch_bounds__(kNT) void bwd_grads_kernel(BwdParams p) {
-    __shared__ __attribute__((aligned(16))) float sm[16 * 68 + 16 * 132];
+    __shared__ __attribute__((aligned(16))) float sm[32 * 68 + 32 * 132];
     __shared__ float beta_s[64], dbeta_s[64], dGL_s[128];
     const ChunkParams &c = p.c;
     const int H = c.H, h = blockIdx.x % H, cid = blockIdx.x / H, tid = threadIdx.x;
