@@ -145,6 +145,22 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
     const long tok0 = ci.start;
     const int len = ci.len;
     unsigned char *rec = record(p, cid, h);
+    // (fused) the sequence's token range, for the outgoing conv cache at the
+    // end: read here, from the kernel arguments or through a buffer resource
+    // over the device copy (never a flat load, whose wait would cover every
+    // memory access before it), so that its use after the record stores waits
+    // for this read only, not for the stores
+    int seq_lo = 0, seq_hi = 0;
+    if constexpr (FUSED) {
+        if (p.plan_in_args) {
+            seq_lo = p.plan_cu[ci.seq];
+            seq_hi = p.plan_cu[ci.seq + 1];
+        } else {
+            const __amdgpu_buffer_rsrc_t rc = buffer_rsrc(p.cu, (uint32_t)((p.n_seqs + 1) * 4));
+            seq_lo = (int)__builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)(ci.seq * 4), 0, 0);
+            seq_hi = (int)__builtin_amdgcn_raw_buffer_load_b32(rc, (uint32_t)(ci.seq * 4 + 4), 0, 0);
+        }
+    }
 
     float *A = reinterpret_cast<float *>(lds + kOffA);
     uint16_t *Tm = reinterpret_cast<uint16_t *>(lds + kOffTm);
@@ -609,8 +625,6 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
     // incoming cache reads each old row before it is overwritten.
     if constexpr (FUSED) {
         if (p.cache_out && len > 0) {
-            const int seq_lo = p.plan_in_args ? p.plan_cu[ci.seq] : p.cu[ci.seq];
-            const int seq_hi = p.plan_in_args ? p.plan_cu[ci.seq + 1] : p.cu[ci.seq + 1];
             if (tok0 + len == seq_hi) {
                 const int Km1 = p.K - 1, C = H * kHeadDim;
                 const long L = seq_hi - seq_lo;
