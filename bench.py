@@ -16,7 +16,9 @@ The metric's second half, decode, is measured in the same run on the batched
 decode workload (256 resident fp32 states x 1 token, 64 consecutive
 kda_decode_step calls with distinct inputs) and reported under "decode".
 The chunked backward (kda_chunk_backward) on the prefill workload's shapes is
-reported under "backward".
+reported under "backward", and the packed varlen and long-context prefill
+workloads under "prefill_workloads" (informative; the headline stays the
+4096-token sequence).
 
 Every kernel is timed with HIP events on the stream it is launched on; the
 roofline object is for the kernel that takes the longest, with the algorithmic
@@ -98,6 +100,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
     ap.add_argument("--no-backward", action="store_true", help="skip the chunked backward measurement")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the varlen and long-context prefill measurements")
     ap.add_argument("--backward-steps", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--path", choices=("fused", "unfused"), default="fused")
@@ -186,6 +190,50 @@ def bench_prefill(torch, kda, ki, args, dev):
             per[k] += e[j].elapsed_time(e[j + 1])
     per = {k: v / args.steps for k, v in per.items()}
     return dict(ms_per_step=total_ms / args.steps, wall_s=wall, per_kernel_ms=per)
+
+
+def bench_prefill_workloads(torch, kda, ki, args, dev):
+    """The two other prefill workloads, timed the same way on one input set
+    each (they are far larger than the 256 MB last-level cache): packed varlen
+    (32 sequences of U[256, 8192] tokens, seed 3) and long context (one
+    65,536-token sequence with slow decay, seed 4).  Reported beside the
+    headline, with the path's HBM floor (49,216 B per token plus the fp32
+    states and conv caches in and out)."""
+    out = {}
+    cases = [("varlen", dict(seed=3, lengths=None, draw_lengths=(256, 8192, 32)),
+              "packed varlen prefill, 32 sequences of U[256, 8192] tokens"),
+             ("long_context", dict(seed=4, lengths=[65536], la_range=(-8.0, -2.0)),
+              "long-context prefill, 1 sequence x 65,536 tokens, log alpha = -exp(U(-8, -2))")]
+    for name, kw, desc in cases:
+        inp = ki.prefill_inputs(kw.pop("seed"), kw.pop("lengths"), H=H, d=D, K=K, **kw)
+        T, N = inp["T"], inp["N"]
+        g = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in inp.items()}
+        g["cache_out"] = torch.empty_like(g["conv_cache"])
+        g["y"] = torch.empty_like(g["v_raw"])
+        g["final_state"] = torch.empty_like(g["initial_state"])
+        g["cu_host"] = inp["cu_seqlens"]
+        ws = kda.chunk_workspace(H, D, g["cu_host"], dev)
+        for _ in range(2):
+            run_fused_step(kda, g, ws)
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5
+        a.record()
+        for _ in range(reps):
+            run_fused_step(kda, g, ws)
+        b.record()
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b) / reps
+        floor_b = T * PATH_B_PER_TOK + N * (2 * STATE_B + 2 * CONV_CACHE_B)
+        n_chunks = sum((int(x) + CHUNK - 1) // CHUNK for x in inp["lengths"])
+        out[name] = {"workload": desc + f" ({T} tokens), H=32 dk=dv=128, conv 4, chunk 64, bf16 inputs",
+                     "tokens": T, "sequences": N, "chunks": n_chunks, "ms_per_call": ms,
+                     "value": T / (ms * 1e-3), "unit": "tokens/s",
+                     "path_hbm_frac": floor_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                     "mfma_frac": FLOP_PER_TOK * T / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)}
+        del g, ws
+        torch.cuda.empty_cache()
+    return out
 
 
 def bench_decode(torch, kda, ki, args, dev):
@@ -333,6 +381,8 @@ def main():
                     "path_hbm_frac": path_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                     "path_roofline_floor_us": path_bytes / (HBM_PEAK_GBS * 1e9) * 1e6},
     }
+    if not args.no_workloads:
+        res["prefill_workloads"] = bench_prefill_workloads(torch, kda, ki, args, dev)
     if not args.no_decode:
         res["decode"] = bench_decode(torch, kda, ki, args, dev)
     if not args.no_backward:
