@@ -86,9 +86,8 @@ __device__ __forceinline__ void seq_chunks(const ChunkParams &c, int n, int &c_b
 // 128, K a multiple of 16 HALVES; operands 16-byte aligned with lda, ldb multiples of
 // 4.  The operands may be in global memory (written earlier by this block:
 // the barrier on entry orders them) or in LDS.
-template <bool TA, bool TB, int MASK, bool ACC, int N, int HALVES = 2>
-__device__ void bmm(float *C, int ldc, const float *A, int lda, const float *B, int ldb, int K, float alpha, int mrows,
-                    float *sm) {
+template <bool TA, bool TB, int N, int HALVES>
+__device__ void bmm_acc(f32x4 (&acc)[N / 16], const float *A, int lda, const float *B, int ldb, int K, float *sm) {
     constexpr int LA = 68, LB = 132;   // LDS rows, padded (multiples of 4 for 16-byte accesses)
     constexpr int KS = 16 * HALVES;    // k slab
     float *As = sm;                    // [KS][LA]: As[kk][i]
@@ -154,9 +153,6 @@ __device__ void bmm(float *C, int ldc, const float *A, int lda, const float *B, 
     // for k = k0 + 4 t + l / 16 and holds C[16 w + 4 (l / 16) + r][16 nb + l % 16]
     constexpr int NB = N / 16;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, lg = l >> 4, lc = l & 15;
-    f32x4 acc[NB];
-#pragma unroll
-    for (int nb = 0; nb < NB; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
     __syncthreads();   // operands written earlier by this block are complete; staging is free
     fetch(0);
     for (int k0 = 0; k0 < K; k0 += KS) {
@@ -179,6 +175,13 @@ __device__ void bmm(float *C, int ldc, const float *A, int lda, const float *B, 
         }
         __syncthreads();
     }
+}
+
+template <int MASK, bool ACC, int N>
+__device__ void bmm_store(float *C, int ldc, const f32x4 (&acc)[N / 16], float alpha, int mrows) {
+    constexpr int NB = N / 16;
+    const int tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, lg = l >> 4, lc = l & 15;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         const int i = 16 * w + 4 * lg + r;
@@ -195,6 +198,31 @@ __device__ void bmm(float *C, int ldc, const float *A, int lda, const float *B, 
             }
         }
     }
+}
+
+
+template <bool TA, bool TB, int MASK, bool ACC, int N, int HALVES = 2>
+__device__ void bmm(float *C, int ldc, const float *A, int lda, const float *B, int ldb, int K, float alpha, int mrows,
+                    float *sm) {
+    f32x4 acc[N / 16];
+#pragma unroll
+    for (int nb = 0; nb < N / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bmm_acc<TA, TB, N, HALVES>(acc, A, lda, B, ldb, K, sm);
+    bmm_store<MASK, ACC, N>(C, ldc, acc, alpha, mrows);
+}
+
+// C[0:64][0:N] = alpha (op(A1) op(B1) + op(A2) op(B2)), the two products
+// accumulated in the same registers: C is written once, not written, read
+// back and written again.
+template <bool TA1, bool TB1, bool TA2, bool TB2, int MASK, int N, int HALVES = 2>
+__device__ void bmm2(float *C, int ldc, const float *A1, int lda1, const float *B1, int ldb1, int K1, const float *A2,
+                     int lda2, const float *B2, int ldb2, int K2, float alpha, int mrows, float *sm) {
+    f32x4 acc[N / 16];
+#pragma unroll
+    for (int nb = 0; nb < N / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bmm_acc<TA1, TB1, N, HALVES>(acc, A1, lda1, B1, ldb1, K1, sm);
+    bmm_acc<TA2, TB2, N, HALVES>(acc, A2, lda2, B2, ldb2, K2, sm);
+    bmm_store<MASK, false, N>(C, ldc, acc, alpha, mrows);
 }
 
 // ---- dO = scale dy (.) g into every chunk's slot (zero past the chunk's end) --
@@ -599,16 +627,16 @@ __global__ __launch_bounds__(kNT) void bwd_grads_kernel(BwdParams p) {
     float *B = chunk_buf(p, cid, h);
     if (tid < 64) beta_s[tid] = tid < len ? c.beta[(tok0 + tid) * H + h] : 0.f;
     if (p.dgate) {   // O = Qd S0 + Pm U
-        bmm<false, false, 0, false, 128>(B + bO, 128, B + bQd, 128, B + bS0, 128, 128, 1.f, 64, sm);
-        bmm<false, false, 0, true, 128>(B + bO, 128, B + bPm, 64, B + bU, 128, 64, 1.f, 64, sm);
+        bmm2<false, false, false, false, 0, 128>(B + bO, 128, B + bQd, 128, B + bS0, 128, 128, B + bPm, 64, B + bU, 128,
+                                                 64, 1.f, 64, sm);
     }
     bmm<false, true, 1, false, 64>(B + bdPm, 64, B + bdO, 128, B + bU, 128, 128, 1.f, 64, sm);       // tril(dO U^T)
-    bmm<false, true, 0, false, 128>(B + bdQd, 128, B + bdO, 128, B + bS0, 128, 128, 1.f, 64, sm);    // dO S0^T
-    bmm<false, false, 0, true, 128>(B + bdQd, 128, B + bdPm, 64, B + bKi, 128, 64, 1.f, 64, sm);     //  + dPm Ki
+    bmm2<false, true, false, false, 0, 128>(B + bdQd, 128, B + bdO, 128, B + bS0, 128, 128, B + bdPm, 64, B + bKi, 128,
+                                            64, 1.f, 64, sm);                                        // dO S0^T + dPm Ki
     bmm<false, true, 0, false, 128>(B + bdW, 128, B + bdU, 128, B + bS0, 128, 128, -1.f, 64, sm);    // -dU S0^T
     bmm<false, true, 0, false, 128>(B + bdKg, 128, B + bU, 128, B + bdSL, 128, 128, 1.f, 64, sm);    // U dS_L^T
-    bmm<false, true, 0, false, 64>(B + bdTB, 64, B + bdW, 128, B + bKd, 128, 128, 1.f, 64, sm);      // dW Kd^T
-    bmm<false, true, 0, true, 64>(B + bdTB, 64, B + bdU, 128, B + bV, 128, 128, 1.f, 64, sm);        //  + dU V^T
+    bmm2<false, true, false, true, 0, 64>(B + bdTB, 64, B + bdW, 128, B + bKd, 128, 128, B + bdU, 128, B + bV, 128,
+                                          128, 1.f, 64, sm);                                         // dW Kd^T + dU V^T
     bmm<true, false, 0, false, 128>(B + bdKd, 128, B + bTB, 64, B + bdW, 128, 64, 1.f, 64, sm);      // TB^T dW
     bmm<true, false, 0, false, 128>(p.dv + (tok0 * H + h) * kHeadDim, H * kHeadDim, B + bTB, 64, B + bdU, 128, 64,
                                     1.f, len, sm);                                                       // dV = TB^T dU
@@ -648,8 +676,8 @@ __global__ __launch_bounds__(kNT) void bwd_grads_kernel(BwdParams p) {
         for (int t = 0; t < 16; ++t) B[bdA + tid + t * kNT] = x[t] * beta_s[(tid + t * kNT) >> 6];
     }
     bmm<false, false, 0, true, 128>(B + bdKd, 128, B + bdA, 64, B + bKi, 128, 64, 1.f, 64, sm);      // += (beta dA) Ki
-    bmm<true, false, 0, false, 128>(B + bdKi, 128, B + bdA, 64, B + bKd, 128, 64, 1.f, 64, sm);      // (beta dA)^T Kd
-    bmm<true, false, 0, true, 128>(B + bdKi, 128, B + bdPm, 64, B + bQd, 128, 64, 1.f, 64, sm);      //  + dPm^T Qd
+    bmm2<true, false, true, false, 0, 128>(B + bdKi, 128, B + bdA, 64, B + bKd, 128, 64, B + bdPm, 64, B + bQd, 128,
+                                           64, 1.f, 64, sm);                                         // (beta dA)^T Kd + dPm^T Qd
     __syncthreads();
     if (tid < 128) {
         const int ch = tid;
