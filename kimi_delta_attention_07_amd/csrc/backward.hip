@@ -52,10 +52,11 @@ constexpr long kM = 64 * 128, kSq = 64 * 64, kS = 128 * 128;
 constexpr long bG = 0, bQd = bG + kM, bKd = bQd + kM, bKi = bKd + kM, bKg = bKi + kM, bV = bKg + kM;
 constexpr long bW = bV + kM, bUt = bW + kM, bTB = bUt + kM, bT = bTB + kSq, bPm = bT + kSq, bGL = bPm + kSq;
 constexpr long bS0 = bGL + 128, bU = bS0 + kS, bdSL = bU + kM, bdO = bdSL + kS, bdU = bdO + kM;
-constexpr long bO = bdU + kM, bdPm = bO + kM, bdQd = bdPm + kSq, bdW = bdQd + kM, bdKg = bdW + kM;
-constexpr long bdTB = bdKg + kM, bdKd = bdTB + kSq, bX = bdKd + kM, bdA = bX + kSq, bKK = bdA + kSq;
+constexpr long bO = bdU + kM, bdQd = bO + kM, bdW = bdQd + kM, bdKg = bdW + kM;
+constexpr long bdTB = bdKg + kM, bdKd = bdTB + kSq, bKK = bdKd + kM;
 constexpr long bdKi = bKK + kSq;
-constexpr long kBwdFloats = bdKi + kM;
+constexpr long kBwdFloats = bdKi + kM;   // 192,640 floats (dPm, T^T dT and dA live in the gradient kernel's LDS)
+static_assert(kBwdFloats * 4 == 770560, "the workspace size documented in kda.h");
 // The prep kernel stores -W (not W) in the bW slot: only the state passes
 // read it.
 
@@ -619,6 +620,10 @@ __global__ __launch_bounds__(kNT) void bwd_bwd_states_kernel(BwdParams p) {
 __global__ __launch_bounds__(kNT) void bwd_grads_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(16))) float sm[32 * 68 + 32 * 132];
     __shared__ float beta_s[64], dbeta_s[64], dGL_s[128];
+    // intermediates that never leave the block stay in LDS: dPm, T^T dT and
+    // dT / dA (row stride 68, so the per-row dbeta sum is not one bank)
+    constexpr int kLdA = 68;
+    __shared__ __attribute__((aligned(16))) float s_dPm[64 * 64], s_X[64 * 64], s_dA[64 * kLdA];
     const ChunkParams &c = p.c;
     const int H = c.H, h = blockIdx.x % H, cid = blockIdx.x / H, tid = threadIdx.x;
     const ChunkInfo ci = load_chunk(c, cid);
@@ -630,8 +635,8 @@ __global__ __launch_bounds__(kNT) void bwd_grads_kernel(BwdParams p) {
         bmm2<false, false, false, false, 0, 128>(B + bO, 128, B + bQd, 128, B + bS0, 128, 128, B + bPm, 64, B + bU, 128,
                                                  64, 1.f, 64, sm);
     }
-    bmm<false, true, 1, false, 64>(B + bdPm, 64, B + bdO, 128, B + bU, 128, 128, 1.f, 64, sm);       // tril(dO U^T)
-    bmm2<false, true, false, false, 0, 128>(B + bdQd, 128, B + bdO, 128, B + bS0, 128, 128, B + bdPm, 64, B + bKi, 128,
+    bmm<false, true, 1, false, 64>(s_dPm, 64, B + bdO, 128, B + bU, 128, 128, 1.f, 64, sm);       // tril(dO U^T)
+    bmm2<false, true, false, false, 0, 128>(B + bdQd, 128, B + bdO, 128, B + bS0, 128, 128, s_dPm, 64, B + bKi, 128,
                                             64, 1.f, 64, sm);                                        // dO S0^T + dPm Ki
     bmm<false, true, 0, false, 128>(B + bdW, 128, B + bdU, 128, B + bS0, 128, 128, -1.f, 64, sm);    // -dU S0^T
     bmm<false, true, 0, false, 128>(B + bdKg, 128, B + bU, 128, B + bdSL, 128, 128, 1.f, 64, sm);    // U dS_L^T
@@ -649,7 +654,10 @@ __global__ __launch_bounds__(kNT) void bwd_grads_kernel(BwdParams p) {
 #pragma unroll
         for (int t = 0; t < 16; ++t) x[t] = B[bdTB + tid + t * kNT];
 #pragma unroll
-        for (int t = 0; t < 16; ++t) B[bdA + tid + t * kNT] = x[t] * beta_s[(tid + t * kNT) & 63];
+        for (int t = 0; t < 16; ++t) {
+            const int e = tid + t * kNT;
+            s_dA[(e >> 6) * kLdA + (e & 63)] = x[t] * beta_s[e & 63];
+        }
     }
     if (tid < 64) {
         float s = 0.f;
@@ -657,26 +665,27 @@ __global__ __launch_bounds__(kNT) void bwd_grads_kernel(BwdParams p) {
         for (int i = 0; i < 64; ++i) s += B[bdTB + i * 64 + tid] * B[bT + i * 64 + tid];
         dbeta_s[tid] = s;
     }
-    bmm<true, false, 0, false, 64>(B + bX, 64, B + bT, 64, B + bdA, 64, 64, 1.f, 64, sm);            // T^T dT
-    bmm<false, true, 2, false, 64>(B + bdA, 64, B + bX, 64, B + bT, 64, 64, -1.f, 64, sm);           // dA
+    bmm<true, false, 0, false, 64>(s_X, 64, B + bT, 64, s_dA, kLdA, 64, 1.f, 64, sm);            // T^T dT
+    bmm<false, true, 2, false, 64>(s_dA, kLdA, s_X, 64, B + bT, 64, 64, -1.f, 64, sm);           // dA
     bmm<false, true, 2, false, 64>(B + bKK, 64, B + bKd, 128, B + bKi, 128, 128, 1.f, 64, sm);       // tril(Kd Ki^T, -1)
     __syncthreads();
     if (tid < 64) {
         float s = 0.f;
 #pragma unroll 16
-        for (int m = 0; m < 64; ++m) s += B[bdA + tid * 64 + m] * B[bKK + tid * 64 + m];
+        for (int m = 0; m < 64; ++m) s += s_dA[tid * kLdA + m] * B[bKK + tid * 64 + m];
         dbeta_s[tid] += s;
     }
     __syncthreads();
     {   // diag(beta) dA
         float x[16];
 #pragma unroll
-        for (int t = 0; t < 16; ++t) x[t] = B[bdA + tid + t * kNT];
-#pragma unroll
-        for (int t = 0; t < 16; ++t) B[bdA + tid + t * kNT] = x[t] * beta_s[(tid + t * kNT) >> 6];
+        for (int t = 0; t < 16; ++t) {
+            const int e = tid + t * kNT;
+            s_dA[(e >> 6) * kLdA + (e & 63)] *= beta_s[e >> 6];
+        }
     }
-    bmm<false, false, 0, true, 128>(B + bdKd, 128, B + bdA, 64, B + bKi, 128, 64, 1.f, 64, sm);      // += (beta dA) Ki
-    bmm2<true, false, true, false, 0, 128>(B + bdKi, 128, B + bdA, 64, B + bKd, 128, 64, B + bdPm, 64, B + bQd, 128,
+    bmm<false, false, 0, true, 128>(B + bdKd, 128, s_dA, kLdA, B + bKi, 128, 64, 1.f, 64, sm);      // += (beta dA) Ki
+    bmm2<true, false, true, false, 0, 128>(B + bdKi, 128, s_dA, kLdA, B + bKd, 128, 64, s_dPm, 64, B + bQd, 128,
                                            64, 1.f, 64, sm);                                         // (beta dA)^T Kd + dPm^T Qd
     __syncthreads();
     if (tid < 128) {
