@@ -64,10 +64,10 @@ FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector, TFLOP/s
 
 # bench timing slot -> kernel whose counters profiles/traffic.json holds
 TRAFFIC_KERNEL = {"prologue": "prologue128_kernel<4, 1>", "chunk_prepare": "prepare_kernel<false, 4, 0>",
-                  "chunk_scan": "scan_kernel<true>", "prefill_prepare": "prepare_kernel<true, 4, 1>",
-                  "prefill_scan": "scan_kernel<true>", "decode": "decode_kernel<128, 1, 0>"}
+                  "chunk_scan": "scan_kernel<true, 1>", "prefill_prepare": "prepare_kernel<true, 4, 1>",
+                  "prefill_scan": "scan_kernel<true, 1>", "decode": "decode_kernel<128, 1, 0>"}
 KERNEL_SOURCES = {"prologue128_kernel<4, 1>": ["prologue.hip"], "prepare_kernel<false, 4, 0>": ["chunk.hip"],
-                  "prepare_kernel<true, 4, 1>": ["chunk.hip"], "scan_kernel<true>": ["chunk.hip"],
+                  "prepare_kernel<true, 4, 1>": ["chunk.hip"], "scan_kernel<true, 1>": ["chunk.hip"],
                   "decode_kernel<128, 1, 0>": ["decode.hip"]}
 
 

@@ -19,7 +19,8 @@
 //           the 64x64 unit-lower-triangular inverse (fp32, LDS, blocked by
 //           16), W and U~.
 //           Results go to the workspace as ready-made MFMA fragments.
-//  scan     grid (sequences x heads x 8 value tiles), two waves each.  Walks
+//  scan     grid (sequences x heads x 8 value tiles), two waves per tile (for
+//           batches of many heads, two tiles per block).  Walks
 //           a sequence's chunks in order; the 128 x 16 fp32 state tile stays
 //           in the chain wave's accumulator registers the whole time (32
 //           MFMAs per chunk on the serial path) while a second wave forms the
@@ -721,20 +722,32 @@ __device__ __forceinline__ void load_out_gate(OutOperands &o, const ChunkParams 
 // a wave waits only for the buffer it is about to use, never for all of its
 // loads.  One barrier per chunk keeps the two waves in step.  Blocks are
 // numbered so that the eight tiles of one (sequence, head) land on the same XCD.
-template <bool GATED>
-__global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) void scan_kernel(ChunkParams p) {
+//
+// TPB = 2 puts two adjacent tiles of one (sequence, head) in one block (waves
+// 0, 1: their chains; waves 2, 3: their outputs).  The two waves of each role
+// issue the same fragment loads at the same time, so the second is served by
+// the CU's L1 and the block pulls the chunk's shared fragments from L2 once
+// for 32 columns.  It is launched when the batch gives every CU at least two
+// tiles' work anyway; a single sequence keeps one tile per block (256 blocks).
+template <bool GATED, int TPB>
+__global__ __launch_bounds__(128 * TPB) __attribute__((amdgpu_waves_per_eu(1, 1))) void scan_kernel(ChunkParams p) {
     constexpr int kOS = 20;                           // fp32 row stride of the output tile
-    __shared__ __attribute__((aligned(16))) u32x4 xfer[2][6][64];   // [slot][Sb0..3, Ub0..1][lane]
-    __shared__ __attribute__((aligned(16))) float O_lds[64 * kOS];
+    constexpr int kUnits = kTilesV / TPB;             // blocks per (sequence, head)
+    __shared__ __attribute__((aligned(16))) u32x4 xfer_all[TPB][2][6][64];   // [tile][slot][Sb0..3, Ub0..1][lane]
+    __shared__ __attribute__((aligned(16))) float O_all[TPB][64 * kOS];
     const int H = p.H;
-    const int total = p.n_seqs * H * kTilesV;   // a multiple of 8
+    const int total = p.n_seqs * H * kUnits;    // a multiple of 8 (the launcher checks it)
     const int per_xcd = total / 8;
     const int b = blockIdx.x;
     const int u = (b % 8) * per_xcd + b / 8;    // consecutive u share an XCD
-    const int tile = u % kTilesV;
-    const int h = (u / kTilesV) % H;
-    const int n = u / (kTilesV * H);
+    const int h = (u / kUnits) % H;
+    const int n = u / (kUnits * H);
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const bool chain = wave < TPB;              // wave-uniform role
+    const int sub = chain ? wave : wave - TPB;  // which of the block's tiles
+    const int tile = (u % kUnits) * TPB + sub;
+    auto &xfer = xfer_all[sub];
+    float *O_lds = O_all[sub];
     const int l = threadIdx.x & 63, g = l >> 4, c16 = l & 15;
     // block-uniform values live in scalar registers (buffer resources built
     // from them need no per-lane loop)
@@ -749,7 +762,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     auto rec_of = [&](int i) { return (const unsigned char *)record(p, c_begin + min(i, nch - 1), h); };
 
     if (nch == 0) {   // empty sequence: the state passes through unchanged
-        if (wave == 0 && p.s_final) {
+        if (chain && p.s_final) {
 #pragma unroll
             for (int mm = 0; mm < 8; ++mm)
 #pragma unroll
@@ -761,7 +774,7 @@ __global__ __launch_bounds__(128) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         return;
     }
 
-    if (wave == 0) {
+    if (chain) {
         // ---------------- state chain ----------------
         f32x4 S[8];
         if (p.s0) {
@@ -978,10 +991,19 @@ hipError_t launch_prefill_prepare(const ChunkParams &p, hipStream_t s) {
 }
 
 hipError_t launch_chunk_scan(const ChunkParams &p, hipStream_t s) {
-    const unsigned blocks = (unsigned)(p.n_seqs * p.H * kTilesV);
-    if (blocks == 0) return hipGetLastError();
-    if (p.gate) hipLaunchKernelGGL(scan_kernel<true>, dim3(blocks), dim3(128), 0, s, p);
-    else hipLaunchKernelGGL(scan_kernel<false>, dim3(blocks), dim3(128), 0, s, p);
+    const long heads = (long)p.n_seqs * p.H;
+    if (heads == 0) return hipGetLastError();
+    // two tiles per block once the one-tile grid would put two blocks on
+    // every CU (256 CUs) and the two-tile grid still divides by 8 (XCDs)
+    if (heads * kTilesV >= 512 && heads % 2 == 0) {
+        const dim3 grid((unsigned)(heads * kTilesV / 2));
+        if (p.gate) hipLaunchKernelGGL((scan_kernel<true, 2>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((scan_kernel<false, 2>), grid, dim3(256), 0, s, p);
+    } else {
+        const dim3 grid((unsigned)(heads * kTilesV));
+        if (p.gate) hipLaunchKernelGGL((scan_kernel<true, 1>), grid, dim3(128), 0, s, p);
+        else hipLaunchKernelGGL((scan_kernel<false, 1>), grid, dim3(128), 0, s, p);
+    }
     return hipGetLastError();
 }
 
