@@ -25,9 +25,8 @@
 //
 // Five kernels, all in fp32:
 //   do          chunks x heads: dO = scale dy (.) g (elementwise)
-//   prep        chunks x heads: G, the decayed operands, A, T (forward
-//               substitution, one row at a time), -W, U~, Pm (VALU,
-//               LDS-staged)
+//   prep        chunks x heads: G, the decayed operands, A, T (blocked
+//               forward substitution), -W, U~, Pm
 //   fwd_states  sequences x heads x 8 value tiles: walks the chunks forward,
 //               writes each chunk's S0 and U (fp32 MFMA)
 //   bwd_states  the same grid backwards: dS_L and dU per chunk, and the
@@ -320,23 +319,47 @@ __global__ __launch_bounds__(kNT) void bwd_prep_kernel(BwdParams p) {
     __syncthreads();
     for (int e = tid; e < 64 * 64; e += kNT) big[e] *= beta_s[e >> 6];
     __syncthreads();
-    // T = (I + A)^-1 row by row: T_ij = -sum_{j <= m < i} A_im T_mj (j < i);
-    // four threads share each column's sum
+    // T = (I + A)^-1 by 16 x 16 blocks.  (I + A) T = I gives, for block rows
+    // I > J, T_IJ = -D_I sum_{J <= K < I} A_IK T_KJ with D_I = (I + A_II)^-1.
+    // Wave w first forms D_w by forward substitution within its diagonal
+    // block (T_ij = -sum_{j <= m < i} A_im T_mj, four lanes per column, no
+    // block barrier); the off-diagonal blocks then follow one block diagonal
+    // at a time (I - J = 1, 2, 3), each in two barrier-separated halves.
     float *Tm = big + 64 * 64;
-    __shared__ float part[kNT];
+    __shared__ float xs[3 * 256];   // sum_K A_IK T_KJ of up to three blocks
     for (int e = tid; e < 64 * 64; e += kNT) Tm[e] = (e >> 6) == (e & 63) ? 1.f : 0.f;
     __syncthreads();
     {
-        const int j = tid & 63, q = tid >> 6;
-        for (int i = 1; i < 64; ++i) {
+        const int w = tid >> 6, l = tid & 63, j = l & 15, q = l >> 4, o = 16 * w;
+        for (int ii = 1; ii < 16; ++ii) {
             float sum = 0.f;
-            for (int m = j + q; m < i; m += 4) sum += big[i * 64 + m] * Tm[m * 64 + j];
-            part[tid] = sum;
-            __syncthreads();
-            if (q == 0 && j < i) Tm[i * 64 + j] = -(part[j] + part[64 + j] + part[128 + j] + part[192 + j]);
-            __syncthreads();
+            for (int mm = j + q; mm < ii; mm += 4) sum += big[(o + ii) * 64 + o + mm] * Tm[(o + mm) * 64 + o + j];
+            sum += __shfl_xor(sum, 16, 64);
+            sum += __shfl_xor(sum, 32, 64);
+            if (q == 0 && j < ii) Tm[(o + ii) * 64 + o + j] = -sum;
         }
     }
+    for (int d = 1; d < 4; ++d) {
+        __syncthreads();
+        const int r = tid >> 4, c = tid & 15;
+        for (int J = 0; J + d < 4; ++J) {   // X = sum_{J <= K < I} A_IK T_KJ
+            const int I = J + d;
+            float x = 0.f;
+            for (int K = J; K < I; ++K)
+#pragma unroll 4
+                for (int m = 0; m < 16; ++m) x += big[(16 * I + r) * 64 + 16 * K + m] * Tm[(16 * K + m) * 64 + 16 * J + c];
+            xs[J * 256 + tid] = x;
+        }
+        __syncthreads();
+        for (int J = 0; J + d < 4; ++J) {   // T_IJ = -D_I X
+            const int I = J + d;
+            float t = 0.f;
+#pragma unroll 4
+            for (int m = 0; m < 16; ++m) t += Tm[(16 * I + r) * 64 + 16 * I + m] * xs[J * 256 + m * 16 + c];
+            Tm[(16 * I + r) * 64 + 16 * J + c] = -t;
+        }
+    }
+    __syncthreads();
     for (int e = tid; e < 64 * 64; e += kNT) {
         B[bT + e] = Tm[e];
         B[bTB + e] = Tm[e] * beta_s[e & 63];
