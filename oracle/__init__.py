@@ -78,6 +78,10 @@ class Oracle:
                                       _D, _D, _D, _D, ctypes.c_long, _D]
         L.kda_oracle_l2norm.argtypes = [ctypes.c_long, ctypes.c_int, ctypes.c_double, _D]
         L.kda_oracle_sigmoid.argtypes = [ctypes.c_long, _D, _D]
+        L.kda_oracle_conv_backward.argtypes = [ctypes.c_int, _I, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                               _D, _D, _D, ctypes.c_long, _D, _D, _D, _D]
+        L.kda_oracle_l2norm_backward.argtypes = [ctypes.c_long, ctypes.c_int, ctypes.c_double, _D, _D, _D]
+        L.kda_oracle_sigmoid_backward.argtypes = [ctypes.c_long, _D, _D, _D]
         L.kda_oracle_recurrence.argtypes = [ctypes.c_int, _I, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                             _D, _D, _D, _D, _D, _D, ctypes.c_double, _D, _D, _D]
         L.kda_oracle_recurrence_backward.argtypes = [ctypes.c_int, _I, ctypes.c_int, ctypes.c_int, ctypes.c_int,
@@ -172,6 +176,52 @@ class Oracle:
         gate = self.sigmoid(inp["gate_logit"]) if inp.get("gate_logit") is not None else None
         cache_out = np.stack(caches, axis=1) if K > 1 else np.zeros((inp["N"], 3, 0, H * d))
         return dict(q=q, k=k, v=v, beta=beta, gate=gate, conv_cache=cache_out)
+
+    def prologue_backward(self, inp, grads, act=ACT_SILU, eps=L2_EPS, cache_in=None):
+        """Gradient of prologue() with respect to the raw inputs.  ``grads``
+        holds dq, dk, dv [T, H, d], dbeta [T, H] and dgate [T, H, d] (or None):
+        the gradients reaching the prologue's outputs.  Returns dq_raw, dk_raw,
+        dv_raw [T, H, d], dconv_w [3, H*d, K], dconv_cache [N, 3, K-1, H*d] and
+        dbeta_logit [T, H], dgate_logit [T, H, d] (None without a gate)."""
+        H, d, K, T, N = inp["H"], inp["d"], inp["K"], inp["T"], inp["N"]
+        C = H * d
+        cu = _i32(inp["cu_seqlens"])
+        w = _f64(inp["conv_w"])
+        cache = _f64(inp["conv_cache"] if cache_in is None else cache_in)
+        has_cache = K > 1
+        out = dict(dconv_w=np.zeros((3, C, K)), dconv_cache=np.zeros((N, 3, max(K - 1, 0), C)))
+        for X, (key, gkey) in enumerate((("q_raw", "dq"), ("k_raw", "dk"), ("v_raw", "dv"))):
+            x = _f64(inp[key]).reshape(T, C)
+            cin = np.ascontiguousarray(cache[:, X]) if has_cache else None
+            dy = _f64(grads[gkey]).reshape(T, C)
+            if X < 2:   # q and k were L2-normalised after the conv
+                pre, _ = self.conv(x, w[X], inp["cu_seqlens"], act, cin)
+                pre = np.ascontiguousarray(pre.reshape(T * H, d))
+                dyn = np.empty_like(pre)
+                self.lib.kda_oracle_l2norm_backward(T * H, d, eps, _p(pre), _p(np.ascontiguousarray(dy.reshape(T * H, d))),
+                                                  _p(dyn))
+                dy = dyn.reshape(T, C)
+            dx = np.zeros((T, C))
+            dw = np.zeros((C, K))
+            dc = np.zeros((N, max(K - 1, 0), C)) if has_cache else None
+            self.lib.kda_oracle_conv_backward(N, _p(cu, _I), C, K, act, _p(x), _p(np.ascontiguousarray(w[X])),
+                                            _p(cin) if has_cache else None, (K - 1) * C, _p(np.ascontiguousarray(dy)),
+                                            _p(dx), _p(dw), _p(dc) if has_cache else None)
+            out["d" + key] = dx.reshape(T, H, d)
+            out["dconv_w"][X] = dw
+            if has_cache:
+                out["dconv_cache"][:, X] = dc
+        zb = _f64(inp["beta_logit"])
+        dzb = np.empty_like(zb)
+        self.lib.kda_oracle_sigmoid_backward(zb.size, _p(zb), _p(_f64(grads["dbeta"])), _p(dzb))
+        out["dbeta_logit"] = dzb
+        out["dgate_logit"] = None
+        if inp.get("gate_logit") is not None and grads.get("dgate") is not None:
+            zg = _f64(inp["gate_logit"])
+            dzg = np.empty_like(zg)
+            self.lib.kda_oracle_sigmoid_backward(zg.size, _p(zg), _p(_f64(grads["dgate"])), _p(dzg))
+            out["dgate_logit"] = dzg
+        return out
 
     def prefill(self, inp, act=ACT_SILU, eps=L2_EPS, scale=1.0, s0=None, cache_in=None):
         """Full prefill on raw inputs.  Returns dict with y, final_state,

@@ -25,7 +25,9 @@
  *    gating", forum post, implementation list);
  *  - the gradient of the recurrence with respect to q, k, v, log alpha,
  *    beta, the gate and the initial state (reverse mode, token by token; the
- *    k3 README's functional proxy checks gradients of a KDA layer);
+ *    k3 README's functional proxy checks gradients of a KDA layer), and of
+ *    the prologue (conv + activation, L2 norm, sigmoids) back to the raw
+ *    projections, the conv taps and the incoming conv cache;
  *  - the decode step as conv update, then recurrent step (kimi_k3 API docs,
  *    Functions: kda_decode_token): one more prefill token that reads and
  *    rewrites the per-sequence conv cache and recurrent state in place (the
@@ -119,6 +121,86 @@ void kda_oracle_l2norm(long rows, int d, double eps, double *x) {
 /* y[i] = sigmoid(x[i]) */
 void kda_oracle_sigmoid(long n, const double *x, double *y) {
     for (long i = 0; i < n; ++i) y[i] = sigmoid(x[i]);
+}
+
+/*
+ * Gradients of the prologue's steps (reverse mode, same conventions as the
+ * forward functions above; they are what a caller needs to carry the
+ * recurrence's gradient back to the raw projections and the conv taps).
+ *
+ * Convolution + activation: with pre_t[c] = sum_j w[c][j] x_{t-K+1+j}[c] and
+ * y_t = act(pre_t), given dy:
+ *   dpre_t = dy_t * act'(pre_t)    (SiLU: s (1 + pre (1 - s)), s = sigmoid(pre))
+ *   dx_tau[c]   += w[c][j] dpre_t[c]       for tau = t-K+1+j inside the sequence
+ *   dcache[c]   += w[c][j] dpre_t[c]       for tau before it (history slot
+ *                                          (K-1) - (start - tau)), when a cache is given
+ *   dw[c][j]    += x_tau[c] dpre_t[c]      (x_tau from the sequence or the cache)
+ * dx and dw are accumulated into (the caller zeroes them); dcache_in (NULL:
+ * skipped) has cache_in's layout and is written.  The outgoing cache copies
+ * raw inputs and is taken to receive no gradient.
+ */
+void kda_oracle_conv_backward(int n_seqs, const int32_t *cu, int C, int K, int act,
+                              const double *x, const double *w,
+                              const double *cache_in, long cache_stride,
+                              const double *dy, double *dx, double *dw, double *dcache_in) {
+    for (int n = 0; n < n_seqs; ++n) {
+        const long start = cu[n], end = cu[n + 1];
+        const double *cin = cache_in ? cache_in + (long)n * cache_stride : NULL;
+        double *dcin = dcache_in ? dcache_in + (long)n * cache_stride : NULL;
+        if (dcin)
+            for (long e = 0; e < (long)(K - 1) * C; ++e) dcin[e] = 0.0;
+#pragma omp parallel for schedule(static)
+        for (int c = 0; c < C; ++c) {
+            for (long t = start; t < end; ++t) {
+                double pre = 0.0;
+                for (int j = 0; j < K; ++j) {
+                    const long tau = t - K + 1 + j;
+                    const double xv = tau >= start ? x[tau * C + c]
+                                    : (cin ? cin[(long)((K - 1) - (start - tau)) * C + c] : 0.0);
+                    pre += w[(long)c * K + j] * xv;
+                }
+                double g = dy[t * C + c];
+                if (act == 1) {
+                    const double sg = sigmoid(pre);
+                    g *= sg * (1.0 + pre * (1.0 - sg));
+                }
+                for (int j = 0; j < K; ++j) {
+                    const long tau = t - K + 1 + j;
+                    if (tau >= start) {
+                        dx[tau * C + c] += w[(long)c * K + j] * g;
+                        dw[(long)c * K + j] += x[tau * C + c] * g;
+                    } else if (cin) {
+                        const long slot = (K - 1) - (start - tau);
+                        if (dcin) dcin[slot * C + c] += w[(long)c * K + j] * g;
+                        dw[(long)c * K + j] += cin[slot * C + c] * g;
+                    }
+                }
+            }
+        }
+    }
+}
+
+/* L2 norm: with n = sqrt(sum x^2 + eps) and y = x / n, given dy (x is the
+ * un-normalised input): dx = dy / n - x (x . dy) / n^3, for each row */
+void kda_oracle_l2norm_backward(long rows, int d, double eps, const double *x, const double *dy, double *dx) {
+#pragma omp parallel for schedule(static)
+    for (long r = 0; r < rows; ++r) {
+        double ss = 0.0, xd = 0.0;
+        for (int c = 0; c < d; ++c) {
+            ss += x[r * d + c] * x[r * d + c];
+            xd += x[r * d + c] * dy[r * d + c];
+        }
+        const double nrm = sqrt(ss + eps);
+        for (int c = 0; c < d; ++c) dx[r * d + c] = dy[r * d + c] / nrm - x[r * d + c] * xd / (nrm * nrm * nrm);
+    }
+}
+
+/* sigmoid: y = sigmoid(z), given dy: dz = dy y (1 - y) */
+void kda_oracle_sigmoid_backward(long n, const double *z, const double *dy, double *dz) {
+    for (long i = 0; i < n; ++i) {
+        const double y = sigmoid(z[i]);
+        dz[i] = dy[i] * y * (1.0 - y);
+    }
 }
 
 /*
