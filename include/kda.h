@@ -227,6 +227,43 @@ kda_status kda_decode_step(const kda_geom *geom, int32_t batch, const int32_t *s
                            void *out, void *stream);
 
 /*
+ * kda_prologue_backward: gradients of kda_prologue with respect to its
+ * inputs, given the gradients that reach its outputs (for instance those
+ * kda_chunk_backward returns).  It reverses the prologue's steps: the L2
+ * normalisation of q and k with KDA_L2_EPS (kimi_k3 API docs, Constants),
+ * the activation and the short causal depthwise conv on q, k and v (the
+ * Vulkan-backend forum post's implementation list), and the sigmoids of the
+ * beta and gate logits ("KDA output gating", same list).
+ *   geom, n_seqs, total_tokens, cu_seqlens_*, in_dtype, q_raw, k_raw, v_raw,
+ *     conv_w, conv_cache_in (NULL = zeros), beta_logit, gate_logit (NULL =
+ *     none): exactly the forward call's inputs;
+ *   dq, dk, dv [T][H][d], dbeta [T][H], dgate [T][H][d] (required when
+ *     gate_logit is given): fp32 gradients with respect to q_out, k_out,
+ *     v_out, beta_out and gate_out;
+ *   outputs, fp32, caller-owned and overwritten: dq_raw, dk_raw, dv_raw
+ *     [T][H][d]; dconv_w [3][H*d][conv_k] (summed over every token);
+ *     dconv_cache_in NULL (skip) or [n_seqs][3][conv_k-1][H*d] (the gradient
+ *     with respect to the incoming cache rows, whether or not a cache was
+ *     given); dbeta_logit [T][H]; dgate_logit [T][H][d] (with a gate);
+ *   workspace: device buffer of at least kda_prologue_backward_workspace_bytes()
+ *     bytes, 16-byte aligned (3 T H d fp32 plus the tap partial sums).
+ * The outgoing conv cache copies raw inputs and is taken to receive no
+ * gradient.  The result is deterministic (no atomics).  Errors as for
+ * kda_prologue, plus KDA_ERR_WORKSPACE; nothing is launched when validation
+ * fails.
+ */
+size_t kda_prologue_backward_workspace_bytes(const kda_geom *geom, int32_t total_tokens);
+
+kda_status kda_prologue_backward(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
+                                 const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host,
+                                 kda_dtype in_dtype, const void *q_raw, const void *k_raw, const void *v_raw,
+                                 const float *conv_w, const float *conv_cache_in, const void *beta_logit,
+                                 const void *gate_logit, const float *dq, const float *dk, const float *dv,
+                                 const float *dbeta, const float *dgate, float *dq_raw, float *dk_raw,
+                                 float *dv_raw, float *dconv_w, float *dconv_cache_in, float *dbeta_logit,
+                                 float *dgate_logit, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
  * kda_chunk_backward: gradients of kda_chunk_forward with respect to its
  * inputs (reverse-mode differentiation of the recurrence of the Vulkan-backend
  * forum post's "recurrent KDA state", taken through the chunked WY/UT form;

@@ -7,6 +7,7 @@ include/kda.h); this package is its thin Python binding:
     chunk_forward(...)  chunked prefill over packed varlen sequences
     prefill(...)        the same from raw inputs, prologue fused into the chunk path
     chunk_backward(...) gradients of chunk_forward
+    prologue_backward(...) gradients of prologue, back to the raw inputs and conv taps
     decode_step(...)    one token for a batch of resident fp32 states
 
 Build the library with ``python -m kimi_delta_attention_07_amd.build``.
@@ -28,4 +29,5 @@ from ._lib import (  # noqa: F401
     prefill_prepare,
     prefill_scan,
     prologue,
+    prologue_backward,
 )

@@ -21,7 +21,8 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE"
           5: "KDA_ERR_SEQLENS", 6: "KDA_ERR_WORKSPACE", 7: "KDA_ERR_ALIGN", 8: "KDA_ERR_HIP"}
 EXPORTS = ("kda_prologue", "kda_chunk_workspace_bytes", "kda_chunk_forward", "kda_chunk_prepare",
            "kda_chunk_scan", "kda_prefill", "kda_prefill_prepare", "kda_prefill_scan", "kda_decode_step",
-           "kda_chunk_backward_workspace_bytes", "kda_chunk_backward", "kda_status_str", "kda_last_error_detail")
+           "kda_chunk_backward_workspace_bytes", "kda_chunk_backward", "kda_prologue_backward_workspace_bytes",
+           "kda_prologue_backward", "kda_status_str", "kda_last_error_detail")
 
 
 class KdaError(RuntimeError):
@@ -60,6 +61,10 @@ def load(path=LIB_PATH):
     L.kda_chunk_backward_workspace_bytes.restype = ctypes.c_size_t
     L.kda_chunk_backward.argtypes = [G, _I, _I, _P, _P, _I] + [_P] * 17 + [ctypes.c_size_t, _P]
     L.kda_chunk_backward.restype = _I
+    L.kda_prologue_backward_workspace_bytes.argtypes = [G, _I]
+    L.kda_prologue_backward_workspace_bytes.restype = ctypes.c_size_t
+    L.kda_prologue_backward.argtypes = [G, _I, _I, _P, _P, _I] + [_P] * 20 + [ctypes.c_size_t, _P]
+    L.kda_prologue_backward.restype = _I
     L.kda_chunk_prepare.argtypes = [G, _I, _I, _P, _P, _I] + [_P] * 6 + [ctypes.c_size_t, _P]
     L.kda_chunk_prepare.restype = _I
     L.kda_chunk_scan.argtypes = [G, _I, _I, _P, _P, _I] + [_P] * 5 + [ctypes.c_size_t, _P]
@@ -134,6 +139,36 @@ def prologue(q_raw, k_raw, v_raw, conv_w, cu_seqlens, beta_logit, gate_logit=Non
                                _ptr(beta_logit), _ptr(gate_logit), _ptr(outs["q"]), _ptr(outs["k"]),
                                _ptr(outs["v"]), _ptr(outs["beta"]), _ptr(outs["gate"]), _stream(q_raw)))
     return outs
+
+
+def prologue_backward(q_raw, k_raw, v_raw, conv_w, cu_seqlens, beta_logit, gate_logit, conv_cache_in, dq, dk, dv,
+                      dbeta, dgate=None, *, act="silu", eps=1e-6, cu_seqlens_host=None, want_dconv_cache=True,
+                      workspace=None):
+    """Gradients of prologue() with respect to its inputs, given fp32
+    gradients dq, dk, dv, dbeta, dgate reaching its outputs.  Returns a dict
+    with dq_raw, dk_raw, dv_raw, dconv_w, dconv_cache (None when not wanted or
+    conv_k = 1), dbeta_logit and dgate_logit (None without a gate); fp32."""
+    T, H, d = q_raw.shape
+    K = conv_w.shape[2]
+    n = cu_seqlens.numel() - 1
+    hcu, hptr = _host_cu(cu_seqlens, cu_seqlens_host)
+    g = geom(H, d, K, act, eps)
+    if workspace is None:
+        nbytes = int(load().kda_prologue_backward_workspace_bytes(ctypes.byref(g), T))
+        workspace = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=q_raw.device)
+    f32 = dict(dtype=torch.float32, device=q_raw.device)
+    out = dict(dq_raw=torch.empty((T, H, d), **f32), dk_raw=torch.empty((T, H, d), **f32),
+               dv_raw=torch.empty((T, H, d), **f32), dconv_w=torch.empty(tuple(conv_w.shape), **f32),
+               dconv_cache=torch.empty((n, 3, K - 1, H * d), **f32) if want_dconv_cache and K > 1 else None,
+               dbeta_logit=torch.empty((T, H), **f32),
+               dgate_logit=torch.empty((T, H, d), **f32) if gate_logit is not None else None)
+    _check(load().kda_prologue_backward(
+        ctypes.byref(g), n, T, _ptr(cu_seqlens), hptr, _dtype(q_raw), _ptr(q_raw), _ptr(k_raw), _ptr(v_raw),
+        _ptr(conv_w), _ptr(conv_cache_in), _ptr(beta_logit), _ptr(gate_logit), _ptr(dq), _ptr(dk), _ptr(dv),
+        _ptr(dbeta), _ptr(dgate), _ptr(out["dq_raw"]), _ptr(out["dk_raw"]), _ptr(out["dv_raw"]),
+        _ptr(out["dconv_w"]), _ptr(out["dconv_cache"]), _ptr(out["dbeta_logit"]), _ptr(out["dgate_logit"]),
+        _ptr(workspace), workspace.numel(), _stream(q_raw)))
+    return out
 
 
 def chunk_workspace_bytes(H, d, cu_seqlens_host):

@@ -291,6 +291,72 @@ kda_status kda_prologue(const kda_geom *geom, int32_t n_seqs, int32_t total_toke
     return launched(kda::launch_prologue(p, (int)in_dtype, (hipStream_t)stream), "prologue");
 }
 
+size_t kda_prologue_backward_workspace_bytes(const kda_geom *geom, int32_t total_tokens) {
+    if (check_geom(geom, false) != KDA_OK || total_tokens < 0) return 0;
+    return kda::prologue_bwd_workspace_bytes(geom->H, geom->d, total_tokens);
+}
+
+kda_status kda_prologue_backward(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
+                                 const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host, kda_dtype in_dtype,
+                                 const void *q_raw, const void *k_raw, const void *v_raw, const float *conv_w,
+                                 const float *conv_cache_in, const void *beta_logit, const void *gate_logit,
+                                 const float *dq, const float *dk, const float *dv, const float *dbeta,
+                                 const float *dgate, float *dq_raw, float *dk_raw, float *dv_raw, float *dconv_w,
+                                 float *dconv_cache_in, float *dbeta_logit, float *dgate_logit, void *workspace,
+                                 size_t workspace_bytes, void *stream) {
+    KDA_TRY(check_geom(geom, false));
+    KDA_TRY(check_seqlens(n_seqs, total_tokens, cu_seqlens_host, nullptr));
+    KDA_TRY(check_dtype(in_dtype));
+    KDA_TRY(check_required({{cu_seqlens_dev, "cu_seqlens_dev"}, {conv_w, "conv_w"}, {dconv_w, "dconv_w"},
+                            {workspace, "workspace"}}));
+    if (total_tokens > 0)
+        KDA_TRY(check_required({{q_raw, "q_raw"}, {k_raw, "k_raw"}, {v_raw, "v_raw"}, {beta_logit, "beta_logit"},
+                                {dq, "dq"}, {dk, "dk"}, {dv, "dv"}, {dbeta, "dbeta"}, {dq_raw, "dq_raw"},
+                                {dk_raw, "dk_raw"}, {dv_raw, "dv_raw"}, {dbeta_logit, "dbeta_logit"}}));
+    if (gate_logit && total_tokens > 0 && (!dgate || !dgate_logit))
+        return fail(KDA_ERR_NULL, "dgate and dgate_logit are required when gate_logit is given");
+    KDA_TRY(check_aligned({{workspace, "workspace"}, {q_raw, "q_raw"}, {k_raw, "k_raw"}, {v_raw, "v_raw"},
+                           {conv_w, "conv_w"}, {conv_cache_in, "conv_cache_in"}, {beta_logit, "beta_logit"},
+                           {gate_logit, "gate_logit"}, {dq, "dq"}, {dk, "dk"}, {dv, "dv"}, {dbeta, "dbeta"},
+                           {dgate, "dgate"}, {dq_raw, "dq_raw"}, {dk_raw, "dk_raw"}, {dv_raw, "dv_raw"},
+                           {dconv_w, "dconv_w"}, {dconv_cache_in, "dconv_cache_in"}, {dbeta_logit, "dbeta_logit"},
+                           {dgate_logit, "dgate_logit"}}));
+    const size_t need = kda::prologue_bwd_workspace_bytes(geom->H, geom->d, total_tokens);
+    if (workspace_bytes < need)
+        return fail(KDA_ERR_WORKSPACE, "workspace of %zu bytes, %zu needed", workspace_bytes, need);
+    KDA_TRY(check_device());
+    kda::PrologueBwdParams p{};
+    p.T = total_tokens;
+    p.H = geom->H;
+    p.d = geom->d;
+    p.K = geom->conv_k;
+    p.act = geom->act;
+    p.n_seqs = n_seqs;
+    p.eps = geom->l2_eps;
+    p.cu = cu_seqlens_dev;
+    p.q_raw = q_raw;
+    p.k_raw = k_raw;
+    p.v_raw = v_raw;
+    p.conv_w = conv_w;
+    p.cache_in = geom->conv_k > 1 ? conv_cache_in : nullptr;
+    p.beta_logit = beta_logit;
+    p.gate_logit = gate_logit;
+    p.dq = dq;
+    p.dk = dk;
+    p.dv = dv;
+    p.dbeta = dbeta;
+    p.dgate = gate_logit ? dgate : nullptr;
+    p.dq_raw = dq_raw;
+    p.dk_raw = dk_raw;
+    p.dv_raw = dv_raw;
+    p.dconv_w = dconv_w;
+    p.dcache_in = geom->conv_k > 1 ? dconv_cache_in : nullptr;
+    p.dbeta_logit = dbeta_logit;
+    p.dgate_logit = gate_logit ? dgate_logit : nullptr;
+    p.workspace = workspace;
+    return launched(kda::launch_prologue_backward(p, (int)in_dtype, (hipStream_t)stream), "prologue backward");
+}
+
 size_t kda_chunk_workspace_bytes(const kda_geom *geom, int32_t n_seqs, const int32_t *cu_seqlens_host) {
     if (check_geom(geom, true) != KDA_OK) return 0;
     if (n_seqs <= 0 || !cu_seqlens_host) return 0;

@@ -106,6 +106,24 @@ struct BwdParams {
     float *dgate;               // [T][H][128], null when there is no gate
     float *ds0;                 // [n_seqs][H][128][128] or null
 };
+// Backward of the prologue (conv + activation, L2 norm, sigmoids).
+struct PrologueBwdParams {
+    int T, H, d, K, act, n_seqs;
+    float eps;
+    const int32_t *cu;                          // [n_seqs+1] device
+    const void *q_raw, *k_raw, *v_raw;          // [T][H][d] in the forward's dtype
+    const float *conv_w, *cache_in;             // [3][H*d][K]; NULL or [n_seqs][3][K-1][H*d]
+    const void *beta_logit, *gate_logit;        // [T][H]; NULL or [T][H][d]
+    const float *dq, *dk, *dv, *dbeta, *dgate;  // gradients reaching the prologue's outputs
+    float *dq_raw, *dk_raw, *dv_raw;            // [T][H][d]
+    float *dconv_w, *dcache_in;                 // [3][H*d][K]; NULL or as cache_in
+    float *dbeta_logit, *dgate_logit;           // [T][H]; NULL or [T][H][d]
+    void *workspace;                            // prologue_bwd_workspace_bytes()
+    float *dpre, *dw_part;                      // carved from the workspace by the launcher
+};
+size_t prologue_bwd_workspace_bytes(int H, int d, long T);
+hipError_t launch_prologue_backward(PrologueBwdParams p, int dtype, hipStream_t s);
+
 hipError_t launch_chunk_plan(const ChunkParams &p, hipStream_t s);
 hipError_t launch_chunk_backward(const BwdParams &p, hipStream_t s);
 size_t bwd_workspace_bytes(int H, int n_seqs, long n_chunks);

@@ -242,3 +242,40 @@ def test_backward_rejects(L):
     p = list(FAKE[:16])
     p[8] = ctypes.c_void_p(0x10004)   # d_final_state misaligned
     assert backward(L, ptrs=p) == ALIGN
+
+
+# kda_prologue_backward's 20 pointer arguments, in order:
+#   q_raw k_raw v_raw conv_w conv_cache_in beta_logit gate_logit dq dk dv dbeta dgate
+#   dq_raw dk_raw dv_raw dconv_w dconv_cache_in dbeta_logit dgate_logit workspace
+def prologue_backward(L, geom=None, dtype=1, ptrs=None, ws_bytes=1 << 40, cu_vals=(0, 100, 228)):
+    t, hp = _cu(list(cu_vals))
+    p = list(FAKE[:20]) if ptrs is None else ptrs
+    return L.kda_prologue_backward(geom if geom is not None else _geom(), len(cu_vals) - 1, cu_vals[-1], FAKE[15],
+                                   hp, dtype, *p[:19], p[19], ws_bytes, None)
+
+
+def test_prologue_backward_workspace_bytes(L):
+    # 3 T H d fp32 rows of dpre, then one partial tap sum (4 floats) per
+    # (256-token block, stream, channel)
+    assert L.kda_prologue_backward_workspace_bytes(_geom(H=2, d=8), 300) == 4 * (3 * 300 * 16) + 4 * (2 * 3 * 16 * 4)
+    assert L.kda_prologue_backward_workspace_bytes(_geom(H=2, d=12), 300) == 0
+
+
+def test_prologue_backward_rejects(L):
+    assert prologue_backward(L, geom=_geom(d=12)) == UNSUP
+    assert prologue_backward(L, geom=_geom(K=5)) == UNSUP
+    assert prologue_backward(L, dtype=5) == DTYPE
+    assert prologue_backward(L, ws_bytes=100) == WORKSPACE
+    assert prologue_backward(L, cu_vals=(0, 100, 50)) == SEQLENS
+    for i, name in ((0, "q_raw"), (3, "conv_w"), (7, "dq"), (10, "dbeta"), (12, "dq_raw"), (15, "dconv_w"),
+                    (17, "dbeta_logit"), (19, "workspace")):
+        p = list(FAKE[:20])
+        p[i] = None
+        assert prologue_backward(L, ptrs=p) == NULL, name
+    for i in (11, 18):   # dgate / dgate_logit missing while a gate is given
+        p = list(FAKE[:20])
+        p[i] = None
+        assert prologue_backward(L, ptrs=p) == NULL
+    p = list(FAKE[:20])
+    p[16] = ctypes.c_void_p(0x10008)   # dconv_cache_in misaligned
+    assert prologue_backward(L, ptrs=p) == ALIGN
