@@ -28,6 +28,7 @@ timed on the same prefill workload as "cpu_baseline".  Prints ONE JSON line.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -319,7 +320,7 @@ def bench_backward(torch, kda, ki, args, dev):
                                   g["cu_seqlens"], dy, g["initial_state"], dsf, workspace=ws, cu_seqlens_host=cu_h)
 
     for _ in range(3):
-        one()
+        grads = one()
     torch.cuda.synchronize()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
@@ -328,6 +329,28 @@ def bench_backward(torch, kda, ki, args, dev):
     b.record()
     torch.cuda.synchronize()
     ms = a.elapsed_time(b) / args.backward_steps
+    # the prologue's backward on the same shapes, from the chunk backward's gradients
+    pws = torch.empty(kda._lib.load().kda_prologue_backward_workspace_bytes(
+        ctypes.byref(kda._lib.geom(H, D, K)), 4096), dtype=torch.uint8, device=dev)
+
+    def one_pro():
+        return kda.prologue_backward(g["q_raw"], g["k_raw"], g["v_raw"], g["conv_w"], g["cu_seqlens"],
+                                     g["beta_logit"], g["gate_logit"], g["conv_cache"], grads["dq"], grads["dk"],
+                                     grads["dv"], grads["dbeta"], grads["dgate"], cu_seqlens_host=cu_h, workspace=pws)
+
+    for _ in range(3):
+        one_pro()
+    torch.cuda.synchronize()
+    a.record()
+    for _ in range(args.backward_steps):
+        one_pro()
+    b.record()
+    torch.cuda.synchronize()
+    ms_pro = a.elapsed_time(b) / args.backward_steps
+    # compulsory bytes: raw q, k, v, gate and beta logits (bf16) and the five
+    # upstream gradients (fp32) in; four fp32 gradients [T, H, d] and dbeta
+    # logits out (conv taps and caches are negligible)
+    pro_bytes = 4096 * H * D * (4 * 2 + 4 * 4 + 4 * 4) + 4096 * H * (2 + 4 + 4)
     flop = (4096 // CHUNK) * H * BWD_FLOP_PER_CHUNK_HEAD
     tf = flop / (ms * 1e-3) / 1e12
     return {"workload": "chunked backward, 1 sequence x 4096 tokens, H=32 dk=dv=128, chunk 64, bf16 inputs and dy, "
@@ -336,7 +359,13 @@ def bench_backward(torch, kda, ki, args, dev):
             "roofline": {"bound": "alu", "achieved": tf, "peak": FP32_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": tf / FP32_PEAK_TFLOPS, "traffic": None,
                          "kernel": "kda_chunk_backward (prep, fwd_states, bwd_states, grads)",
-                         "flop_per_launch": flop}}
+                         "flop_per_launch": flop},
+            "prologue_backward": {"workload": "kda_prologue_backward on the same shapes, from the chunk "
+                                              "backward's gradients to raw q, k, v, conv taps, conv cache, "
+                                              "beta and gate logits",
+                                  "ms_per_call": ms_pro, "value": 4096 / (ms_pro * 1e-3), "unit": "tokens/s",
+                                  "hbm_gbs": pro_bytes / (ms_pro * 1e-3) / 1e9,
+                                  "hbm_frac": pro_bytes / (ms_pro * 1e-3) / 1e9 / HBM_PEAK_GBS}}
 
 
 def main():
