@@ -22,7 +22,7 @@
 //   dx      (token, head) rows: gathers dx from the K taps' dpre rows of the
 //           same sequence; a small kernel does the same for the incoming
 //           cache's K-1 history rows of each sequence;
-//   dw      partial tap sums over blocks of 256 tokens, then one fixed-order
+//   dw      partial tap sums over blocks of 64 tokens, then one fixed-order
 //           sum over the blocks (deterministic, no atomics).
 #include "kda_device.h"
 #include "kda_internal.h"
@@ -31,7 +31,7 @@ namespace kda {
 
 namespace {
 
-constexpr int kBwdTokBlock = 256;   // tokens per partial sum of the tap gradient
+constexpr int kBwdTokBlock = 64;    // tokens per partial sum of the tap gradient
 
 __device__ __forceinline__ int seq_of(const int32_t *cu, int n_seqs, long t) {
     // largest n with cu[n] <= t (empty sequences share their start with the next)
@@ -66,41 +66,62 @@ __device__ __forceinline__ float act_grad(int act, float pre) {
 
 // ---- stage 1: dpre of q, k, v; sigmoid gradients ------------------------------
 // Lanes hold channel pairs of one token row (LPT = D / 2 lanes per token), as
-// in the forward prologue; the two L2 sums are lane-group reductions.
-template <int D, int DT>
+// in the forward prologue; the two L2 sums are lane-group reductions.  Every
+// load of the row (the K-row conv window, the taps, the upstream gradients,
+// the logits) is issued before any of them is used.
+template <int D, int DT, int K>
 __global__ __launch_bounds__(256) void prologue_bwd_pre_kernel(PrologueBwdParams p) {
     constexpr int LPT = D / 2, TPB = 256 / LPT;   // lanes per token, tokens per block
     const int h = blockIdx.y;
     const int sub = threadIdx.x / LPT, c0 = 2 * (threadIdx.x % LPT);
     const long t = (long)blockIdx.x * TPB + sub;
     const bool valid = t < p.T;
+    const long tc = valid ? t : p.T - 1;       // rows past the end redo the last row, unstored
     const long C = (long)p.H * D, ch = (long)h * D + c0;
-    float pre[3][2] = {{0.f, 0.f}, {0.f, 0.f}, {0.f, 0.f}};
-    if (valid) {
-        const int n = seq_of(p.cu, p.n_seqs, t);
-        const long start = p.cu[n];
-        for (int j = 0; j < p.K; ++j) {
-            const long tau = t - (p.K - 1) + j;
+    const long o = (tc * p.H + h) * D + c0;    // row-major [T][H][D] index
+    const int n = seq_of(p.cu, p.n_seqs, tc);
+    const long start = p.cu[n];
+    float2 x[3][K], w[3][K];
+    // rows whose conv window lies inside the sequence (all but its first K-1;
+    // uniform across a wave at D = 128) load without a branch per tap
+    if (tc - (K - 1) >= start) {
 #pragma unroll
-            for (int X = 0; X < 3; ++X) {
-                const float2 x = raw2<DT>(p, X, n, start, tau, ch);
-                const float2 w = make_float2(p.conv_w[((long)X * C + ch) * p.K + j],
-                                             p.conv_w[((long)X * C + ch + 1) * p.K + j]);
-                pre[X][0] += w.x * x.x;
-                pre[X][1] += w.y * x.y;
-            }
+        for (int X = 0; X < 3; ++X) {
+            const void *raw = X == 0 ? p.q_raw : (X == 1 ? p.k_raw : p.v_raw);
+#pragma unroll
+            for (int j = 0; j < K; ++j) x[X][j] = load2<DT>(raw, (tc - (K - 1) + j) * C + ch);
         }
+    } else {
+#pragma unroll
+        for (int X = 0; X < 3; ++X)
+#pragma unroll
+            for (int j = 0; j < K; ++j) x[X][j] = raw2<DT>(p, X, n, start, tc - (K - 1) + j, ch);
     }
-    const long o = (t * p.H + h) * D + c0;   // row-major [T][H][D] index
-    float2 dy[3] = {make_float2(0.f, 0.f), make_float2(0.f, 0.f), make_float2(0.f, 0.f)};
-    if (valid) {
-        dy[0] = *reinterpret_cast<const float2 *>(p.dq + o);
-        dy[1] = *reinterpret_cast<const float2 *>(p.dk + o);
-        dy[2] = *reinterpret_cast<const float2 *>(p.dv + o);
+#pragma unroll
+    for (int X = 0; X < 3; ++X)
+#pragma unroll
+        for (int j = 0; j < K; ++j)
+            w[X][j] = make_float2(p.conv_w[((long)X * C + ch) * K + j], p.conv_w[((long)X * C + ch + 1) * K + j]);
+    float2 dy[3];
+    dy[0] = *reinterpret_cast<const float2 *>(p.dq + o);
+    dy[1] = *reinterpret_cast<const float2 *>(p.dk + o);
+    dy[2] = *reinterpret_cast<const float2 *>(p.dv + o);
+    float2 zg = make_float2(0.f, 0.f), dg = zg;
+    if (p.gate_logit) {
+        zg = load2<DT>(p.gate_logit, o);
+        dg = *reinterpret_cast<const float2 *>(p.dgate + o);
     }
-    float xa[3][2];
+    const long ob = tc * p.H + h;
+    const float zb = load1<DT>(p.beta_logit, ob), db = p.dbeta[ob];
+    float pre[3][2], xa[3][2];
 #pragma unroll
     for (int X = 0; X < 3; ++X) {
+        pre[X][0] = pre[X][1] = 0.f;
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            pre[X][0] += w[X][j].x * x[X][j].x;
+            pre[X][1] += w[X][j].y * x[X][j].y;
+        }
         xa[X][0] = activate(p.act, pre[X][0]);
         xa[X][1] = activate(p.act, pre[X][1]);
     }
@@ -124,21 +145,20 @@ __global__ __launch_bounds__(256) void prologue_bwd_pre_kernel(PrologueBwdParams
         *reinterpret_cast<float2 *>(p.dpre + ((long)X * p.T + t) * C + ch) = g;
     }
     if (p.gate_logit) {
-        const float2 z = load2<DT>(p.gate_logit, o);
-        const float2 d = *reinterpret_cast<const float2 *>(p.dgate + o);
-        const float s0 = sigmoidf(z.x), s1 = sigmoidf(z.y);
-        *reinterpret_cast<float2 *>(p.dgate_logit + o) = make_float2(d.x * s0 * (1.f - s0), d.y * s1 * (1.f - s1));
+        const float s0 = sigmoidf(zg.x), s1 = sigmoidf(zg.y);
+        *reinterpret_cast<float2 *>(p.dgate_logit + o) = make_float2(dg.x * s0 * (1.f - s0), dg.y * s1 * (1.f - s1));
     }
     if (c0 == 0) {
-        const long ob = t * p.H + h;
-        const float s = sigmoidf(load1<DT>(p.beta_logit, ob));
-        p.dbeta_logit[ob] = p.dbeta[ob] * s * (1.f - s);
+        const float sb = sigmoidf(zb);
+        p.dbeta_logit[ob] = db * sb * (1.f - sb);
     }
 }
 
 // ---- stage 2: dx (raw inputs) and the incoming cache's gradient ----------------
-// thread: a channel pair of one token row of one head, all three streams
-template <int D>
+// thread: a channel pair of one token row of one head, all three streams;
+// taps of tokens past the sequence's end (or the batch's) read a clamped row
+// and count as zero
+template <int D, int K>
 __global__ __launch_bounds__(256) void prologue_bwd_dx_kernel(PrologueBwdParams p) {
     constexpr int LPT = D / 2, TPB = 256 / LPT;
     const int h = blockIdx.y;
@@ -148,16 +168,24 @@ __global__ __launch_bounds__(256) void prologue_bwd_dx_kernel(PrologueBwdParams 
     const long C = (long)p.H * D, ch = (long)h * D + c0;
     const int n = seq_of(p.cu, p.n_seqs, tau);
     const long end = min((long)p.cu[n + 1], (long)p.T);
+    float2 g[3][K], w[3][K];
+#pragma unroll
+    for (int X = 0; X < 3; ++X)
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            const long t = min(tau + (K - 1) - j, (long)p.T - 1);   // the token whose tap j reads tau
+            g[X][j] = *reinterpret_cast<const float2 *>(p.dpre + ((long)X * p.T + t) * C + ch);
+            w[X][j] = make_float2(p.conv_w[((long)X * C + ch) * K + j], p.conv_w[((long)X * C + ch + 1) * K + j]);
+        }
     float *outs[3] = {p.dq_raw, p.dk_raw, p.dv_raw};
 #pragma unroll
     for (int X = 0; X < 3; ++X) {
         float2 acc = make_float2(0.f, 0.f);
-        for (int j = 0; j < p.K; ++j) {
-            const long t = tau + (p.K - 1) - j;   // the token whose tap j reads tau
-            if (t < end) {
-                const float2 g = *reinterpret_cast<const float2 *>(p.dpre + ((long)X * p.T + t) * C + ch);
-                acc.x += p.conv_w[((long)X * C + ch) * p.K + j] * g.x;
-                acc.y += p.conv_w[((long)X * C + ch + 1) * p.K + j] * g.y;
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            if (tau + (K - 1) - j < end) {
+                acc.x += w[X][j].x * g[X][j].x;
+                acc.y += w[X][j].y * g[X][j].y;
             }
         }
         *reinterpret_cast<float2 *>(outs[X] + tau * C + ch) = acc;
@@ -186,41 +214,60 @@ __global__ __launch_bounds__(256) void prologue_bwd_dcache_kernel(PrologueBwdPar
 }
 
 // ---- stage 3: tap gradient, partial sums over token blocks, then their sum ---
-// grid (token blocks, channel blocks of 256, 3 streams); thread: one channel
-template <int DT>
+// grid (token blocks, channel blocks of 256, 3 streams); thread: one channel.
+// Tokens go in batches of 8 whose loads are all issued first.
+template <int DT, int K>
 __global__ __launch_bounds__(256) void prologue_bwd_dw_partial_kernel(PrologueBwdParams p) {
+    constexpr int B8 = 8;
     const long C = (long)p.H * p.d;
     const long c = (long)blockIdx.y * 256 + threadIdx.x;
     const int X = blockIdx.z;
     const long t0 = (long)blockIdx.x * kBwdTokBlock, t1 = min((long)p.T, t0 + kBwdTokBlock);
-    float acc[4] = {0.f, 0.f, 0.f, 0.f};
-    if (c < C) {
-        const void *raw = X == 0 ? p.q_raw : (X == 1 ? p.k_raw : p.v_raw);
-        const int Km1 = p.K - 1;
-        int n = seq_of(p.cu, p.n_seqs, t0);
-        long start = p.cu[n], end = p.cu[n + 1];
-        for (long t = t0; t < t1; ++t) {
-            while (t >= end && n + 1 < p.n_seqs) {   // next non-empty sequence (uniform across the block)
-                ++n;
-                start = p.cu[n];
-                end = p.cu[n + 1];
-            }
-            const float g = p.dpre[((long)X * p.T + t) * C + c];
+    if (c >= C) return;
+    const void *raw = X == 0 ? p.q_raw : (X == 1 ? p.k_raw : p.v_raw);
+    constexpr int Km1 = K - 1;
+    float acc[K];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                if (j < p.K) {
+    for (int j = 0; j < K; ++j) acc[j] = 0.f;
+    int n = seq_of(p.cu, p.n_seqs, t0);
+    for (long tb = t0; tb < t1; tb += B8) {
+        float gv[B8], xv[B8][K];
+        while (tb >= p.cu[n + 1] && n + 1 < p.n_seqs) ++n;   // the batch's first token's sequence (uniform)
+        if (tb - Km1 >= p.cu[n] && tb + B8 <= min(t1, (long)p.cu[n + 1])) {
+            // the whole batch and its conv windows inside one sequence: no branch per tap
+#pragma unroll
+            for (int u = 0; u < B8; ++u) {
+                gv[u] = p.dpre[((long)X * p.T + tb + u) * C + c];
+#pragma unroll
+                for (int j = 0; j < K; ++j) xv[u][j] = load1<DT>(raw, (tb + u - Km1 + j) * C + c);
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < B8; ++u) {
+                const long t = min(tb + u, t1 - 1);   // past t1: a repeated row, weighted 0 below
+                while (t >= p.cu[n + 1] && n + 1 < p.n_seqs) ++n;   // the token's sequence (uniform)
+                const long start = p.cu[n];
+                gv[u] = tb + u < t1 ? p.dpre[((long)X * p.T + t) * C + c] : 0.f;
+#pragma unroll
+                for (int j = 0; j < K; ++j) {
                     const long tau = t - Km1 + j;
-                    float x = 0.f;
-                    if (tau >= start && tau >= 0) x = load1<DT>(raw, tau * C + c);
+                    if (tau >= start && tau >= 0) xv[u][j] = load1<DT>(raw, tau * C + c);
                     else if (p.cache_in && start - tau <= Km1)
-                        x = p.cache_in[(((long)n * 3 + X) * Km1 + (Km1 - (start - tau))) * C + c];
-                    acc[j] += x * g;
+                        xv[u][j] = p.cache_in[(((long)n * 3 + X) * Km1 + (Km1 - (start - tau))) * C + c];
+                    else xv[u][j] = 0.f;
                 }
             }
         }
-        float *part = p.dw_part + (((long)blockIdx.x * 3 + X) * C + c) * 4;
-        *reinterpret_cast<float4 *>(part) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+#pragma unroll
+        for (int u = 0; u < B8; ++u)
+#pragma unroll
+            for (int j = 0; j < K; ++j) acc[j] += xv[u][j] * gv[u];
     }
+    float out[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < K; ++j) out[j] = acc[j];
+    float *part = p.dw_part + (((long)blockIdx.x * 3 + X) * C + c) * 4;
+    *reinterpret_cast<float4 *>(part) = make_float4(out[0], out[1], out[2], out[3]);
 }
 
 __global__ __launch_bounds__(256) void prologue_bwd_dw_sum_kernel(PrologueBwdParams p, int n_blocks) {
@@ -239,13 +286,27 @@ __global__ __launch_bounds__(256) void prologue_bwd_dw_sum_kernel(PrologueBwdPar
     for (int j = 0; j < p.K; ++j) p.dconv_w[e * p.K + j] = sv[j];
 }
 
-template <int D>
-void launch_pre_dx(const PrologueBwdParams &p, int dtype, hipStream_t s) {
+template <int D, int K>
+void launch_stages(const PrologueBwdParams &p, int dtype, int nb, hipStream_t s) {
     constexpr int TPB = 256 / (D / 2);
     const dim3 grid((unsigned)((p.T + TPB - 1) / TPB), (unsigned)p.H);
-    if (dtype == 1) hipLaunchKernelGGL((prologue_bwd_pre_kernel<D, 1>), grid, dim3(256), 0, s, p);
-    else hipLaunchKernelGGL((prologue_bwd_pre_kernel<D, 0>), grid, dim3(256), 0, s, p);
-    hipLaunchKernelGGL(prologue_bwd_dx_kernel<D>, grid, dim3(256), 0, s, p);
+    if (dtype == 1) hipLaunchKernelGGL((prologue_bwd_pre_kernel<D, 1, K>), grid, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((prologue_bwd_pre_kernel<D, 0, K>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((prologue_bwd_dx_kernel<D, K>), grid, dim3(256), 0, s, p);
+    const long C = (long)p.H * D;
+    const dim3 g3((unsigned)nb, (unsigned)((C + 255) / 256), 3);
+    if (dtype == 1) hipLaunchKernelGGL((prologue_bwd_dw_partial_kernel<1, K>), g3, dim3(256), 0, s, p);
+    else hipLaunchKernelGGL((prologue_bwd_dw_partial_kernel<0, K>), g3, dim3(256), 0, s, p);
+}
+
+template <int D>
+void launch_d(const PrologueBwdParams &p, int dtype, int nb, hipStream_t s) {
+    switch (p.K) {
+        case 1: launch_stages<D, 1>(p, dtype, nb, s); break;
+        case 2: launch_stages<D, 2>(p, dtype, nb, s); break;
+        case 3: launch_stages<D, 3>(p, dtype, nb, s); break;
+        default: launch_stages<D, 4>(p, dtype, nb, s); break;
+    }
 }
 
 }  // namespace
@@ -262,16 +323,13 @@ hipError_t launch_prologue_backward(PrologueBwdParams p, int dtype, hipStream_t 
     const int nb = (int)((p.T + kBwdTokBlock - 1) / kBwdTokBlock);
     if (p.T > 0) {
         switch (p.d) {
-            case 4: launch_pre_dx<4>(p, dtype, s); break;
-            case 8: launch_pre_dx<8>(p, dtype, s); break;
-            case 16: launch_pre_dx<16>(p, dtype, s); break;
-            case 32: launch_pre_dx<32>(p, dtype, s); break;
-            case 64: launch_pre_dx<64>(p, dtype, s); break;
-            default: launch_pre_dx<128>(p, dtype, s); break;
+            case 4: launch_d<4>(p, dtype, nb, s); break;
+            case 8: launch_d<8>(p, dtype, nb, s); break;
+            case 16: launch_d<16>(p, dtype, nb, s); break;
+            case 32: launch_d<32>(p, dtype, nb, s); break;
+            case 64: launch_d<64>(p, dtype, nb, s); break;
+            default: launch_d<128>(p, dtype, nb, s); break;
         }
-        const dim3 g3((unsigned)nb, (unsigned)((C + 255) / 256), 3);
-        if (dtype == 1) hipLaunchKernelGGL(prologue_bwd_dw_partial_kernel<1>, g3, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL(prologue_bwd_dw_partial_kernel<0>, g3, dim3(256), 0, s, p);
     }
     if (p.dcache_in && p.K > 1)
         hipLaunchKernelGGL(prologue_bwd_dcache_kernel, dim3((unsigned)p.n_seqs, (unsigned)(3 * (p.K - 1))), dim3(256), 0,

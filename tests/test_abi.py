@@ -256,8 +256,8 @@ def prologue_backward(L, geom=None, dtype=1, ptrs=None, ws_bytes=1 << 40, cu_val
 
 def test_prologue_backward_workspace_bytes(L):
     # 3 T H d fp32 rows of dpre, then one partial tap sum (4 floats) per
-    # (256-token block, stream, channel)
-    assert L.kda_prologue_backward_workspace_bytes(_geom(H=2, d=8), 300) == 4 * (3 * 300 * 16) + 4 * (2 * 3 * 16 * 4)
+    # (64-token block, stream, channel)
+    assert L.kda_prologue_backward_workspace_bytes(_geom(H=2, d=8), 300) == 4 * (3 * 300 * 16) + 4 * (5 * 3 * 16 * 4)
     assert L.kda_prologue_backward_workspace_bytes(_geom(H=2, d=12), 300) == 0
 
 
