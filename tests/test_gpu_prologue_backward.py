@@ -68,6 +68,16 @@ def test_prologue_backward_matches_oracle(seed, lengths, H, d, K, dtype, act, ga
     check(run_gpu(inp, grads, act), ref, f"seed {seed}")
 
 
+def test_prologue_backward_empty_batch_and_odd_heads():
+    """No tokens at all (the tap and cache gradients come out as zeros), and
+    H = 5 at d = 128 (the four-heads-per-block kernel has idle waves)."""
+    inp, grads = make(9, [0, 0], 2, 128, 4, torch.bfloat16)
+    got = run_gpu(inp, grads, "silu")
+    assert not got["dconv_w"].any() and not got["dconv_cache"].any()
+    inp, grads = make(10, [33, 0, 64], 5, 128, 4, torch.bfloat16)
+    check(run_gpu(inp, grads, "silu"), ORC.prologue_backward(inp, grads), "H=5")
+
+
 def test_prologue_backward_T4096_full():
     """The benchmark's prefill shapes: T = 4096, H = 32, d = 128, K = 4, bf16."""
     inp, grads = make(7, [4096], 32, 128, 4, torch.bfloat16)
