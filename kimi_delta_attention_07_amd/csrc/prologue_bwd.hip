@@ -58,6 +58,23 @@ __device__ __forceinline__ float2 raw2(const PrologueBwdParams &p, int X, int n,
     return *reinterpret_cast<const float2 *>(cp);
 }
 
+// The K taps of channels ch and ch + 1 of stream X (w[c][j] at (X C + c) K +
+// j): with K = 4 each channel's taps are one 16-byte load.
+template <int K>
+__device__ __forceinline__ void load_taps(const float *conv_w, long C, int X, long ch, float2 (&w)[K]) {
+    const float *a = conv_w + ((long)X * C + ch) * K, *b = a + K;
+    if constexpr (K == 4) {
+        const float4 ta = *reinterpret_cast<const float4 *>(a), tb = *reinterpret_cast<const float4 *>(b);
+        w[0] = make_float2(ta.x, tb.x);
+        w[1] = make_float2(ta.y, tb.y);
+        w[2] = make_float2(ta.z, tb.z);
+        w[3] = make_float2(ta.w, tb.w);
+    } else {
+#pragma unroll
+        for (int j = 0; j < K; ++j) w[j] = make_float2(a[j], b[j]);
+    }
+}
+
 __device__ __forceinline__ float act_grad(int act, float pre) {
     if (act != 1) return 1.0f;
     const float s = sigmoidf(pre);
@@ -98,10 +115,7 @@ __global__ __launch_bounds__(256) void prologue_bwd_pre_kernel(PrologueBwdParams
             for (int j = 0; j < K; ++j) x[X][j] = raw2<DT>(p, X, n, start, tc - (K - 1) + j, ch);
     }
 #pragma unroll
-    for (int X = 0; X < 3; ++X)
-#pragma unroll
-        for (int j = 0; j < K; ++j)
-            w[X][j] = make_float2(p.conv_w[((long)X * C + ch) * K + j], p.conv_w[((long)X * C + ch + 1) * K + j]);
+    for (int X = 0; X < 3; ++X) load_taps<K>(p.conv_w, C, X, ch, w[X]);
     float2 dy[3];
     dy[0] = *reinterpret_cast<const float2 *>(p.dq + o);
     dy[1] = *reinterpret_cast<const float2 *>(p.dk + o);
@@ -125,12 +139,28 @@ __global__ __launch_bounds__(256) void prologue_bwd_pre_kernel(PrologueBwdParams
         xa[X][0] = activate(p.act, pre[X][0]);
         xa[X][1] = activate(p.act, pre[X][1]);
     }
-    // L2 backward of q and k: every lane takes part in the group sums
+    // L2 backward of q and k: every lane takes part in the group sums (head
+    // dim 128: one token row per wave, two sums per DPP/permlane pass)
+    float sums[2][2];   // [q, k][sum x~^2, sum x~ dx^]
+    if constexpr (D == 128) {
+#pragma unroll
+        for (int X = 0; X < 2; ++X) {
+            const float v = wave_sum_pair(xa[X][0] * xa[X][0] + xa[X][1] * xa[X][1],
+                                          xa[X][0] * dy[X].x + xa[X][1] * dy[X].y);
+            sums[X][0] = lane_value(v, 0);
+            sums[X][1] = lane_value(v, 16);
+        }
+    } else {
+#pragma unroll
+        for (int X = 0; X < 2; ++X) {
+            sums[X][0] = group_sum(xa[X][0] * xa[X][0] + xa[X][1] * xa[X][1], LPT);
+            sums[X][1] = group_sum(xa[X][0] * dy[X].x + xa[X][1] * dy[X].y, LPT);
+        }
+    }
     float dxt[3][2];
 #pragma unroll
     for (int X = 0; X < 2; ++X) {
-        const float ss = group_sum(xa[X][0] * xa[X][0] + xa[X][1] * xa[X][1], LPT);
-        const float xd = group_sum(xa[X][0] * dy[X].x + xa[X][1] * dy[X].y, LPT);
+        const float ss = sums[X][0], xd = sums[X][1];
         const float inv = 1.0f / sqrtf(ss + p.eps);
         const float k3 = xd * inv * inv * inv;
         dxt[X][0] = dy[X].x * inv - xa[X][0] * k3;
@@ -175,8 +205,9 @@ __global__ __launch_bounds__(256) void prologue_bwd_dx_kernel(PrologueBwdParams 
         for (int j = 0; j < K; ++j) {
             const long t = min(tau + (K - 1) - j, (long)p.T - 1);   // the token whose tap j reads tau
             g[X][j] = *reinterpret_cast<const float2 *>(p.dpre + ((long)X * p.T + t) * C + ch);
-            w[X][j] = make_float2(p.conv_w[((long)X * C + ch) * K + j], p.conv_w[((long)X * C + ch + 1) * K + j]);
         }
+#pragma unroll
+    for (int X = 0; X < 3; ++X) load_taps<K>(p.conv_w, C, X, ch, w[X]);
     float *outs[3] = {p.dq_raw, p.dk_raw, p.dv_raw};
 #pragma unroll
     for (int X = 0; X < 3; ++X) {
@@ -211,9 +242,7 @@ __global__ __launch_bounds__(256) void prologue_bwd_dx128_kernel(PrologueBwdPara
             const long t = min(tau0 + r, (long)p.T - 1);
             g[X][r] = *reinterpret_cast<const float2 *>(p.dpre + ((long)X * p.T + t) * C + ch);
         }
-#pragma unroll
-        for (int j = 0; j < K; ++j)
-            wt[X][j] = make_float2(p.conv_w[((long)X * C + ch) * K + j], p.conv_w[((long)X * C + ch + 1) * K + j]);
+        load_taps<K>(p.conv_w, C, X, ch, wt[X]);
     }
     int n = seq_of(p.cu, p.n_seqs, min(tau0, (long)p.T - 1));
     float *outs[3] = {p.dq_raw, p.dk_raw, p.dv_raw};
