@@ -280,7 +280,7 @@ kda_status kda_prologue_backward(const kda_geom *geom, int32_t n_seqs, int32_t t
  *     [n_seqs][H][128][128];
  *   workspace: device buffer of at least kda_chunk_backward_workspace_bytes()
  *     bytes, 16-byte aligned, contents not needed before or after the call
- *     (770,560 B per (chunk, head) plus the chunk table).
+ *     (573,952 B per (chunk, head) plus the chunk table).
  * Runs the forward's chunk quantities again (nothing from a forward call is
  * reused) and is stream-ordered like every other entry point.  Errors as for
  * kda_chunk_forward; nothing is launched when validation fails.

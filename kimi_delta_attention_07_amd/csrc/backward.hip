@@ -51,11 +51,9 @@ constexpr long kM = 64 * 128, kSq = 64 * 64, kS = 128 * 128;
 constexpr long bG = 0, bQd = bG + kM, bKd = bQd + kM, bKi = bKd + kM, bKg = bKi + kM, bV = bKg + kM;
 constexpr long bW = bV + kM, bUt = bW + kM, bTB = bUt + kM, bT = bTB + kSq, bPm = bT + kSq, bGL = bPm + kSq;
 constexpr long bS0 = bGL + 128, bU = bS0 + kS, bdSL = bU + kM, bdO = bdSL + kS, bdU = bdO + kM;
-constexpr long bO = bdU + kM, bdQd = bO + kM, bdW = bdQd + kM, bdKg = bdW + kM;
-constexpr long bdTB = bdKg + kM, bdKd = bdTB + kSq, bKK = bdKd + kM;
-constexpr long bdKi = bKK + kSq;
-constexpr long kBwdFloats = bdKi + kM;   // 192,640 floats (dPm, T^T dT and dA live in the gradient kernel's LDS)
-static_assert(kBwdFloats * 4 == 770560, "the workspace size documented in kda.h");
+constexpr long bdW = bdU + kM;
+constexpr long kBwdFloats = bdW + kM;   // 143,488 floats (the gradient kernel keeps its other intermediates on chip)
+static_assert(kBwdFloats * 4 == 573952, "the workspace size documented in kda.h");
 // The prep kernel stores -W (not W) in the bW slot: only the state passes
 // read it.
 
@@ -640,142 +638,245 @@ __global__ __launch_bounds__(kNT) void bwd_bwd_states_kernel(BwdParams p) {
 }
 
 // ---- per-chunk gradients -------------------------------------------------------
-__global__ __launch_bounds__(kNT) void bwd_grads_kernel(BwdParams p) {
+// Element (nb, r) of a block product's accumulators is row 16 w + 4 (l / 16) + r,
+// column 16 nb + l % 16 (wave w, lane l): the same for every 64-row product,
+// so gradients that sum over several products stay in registers.
+// Loads go through the chunk's buffer resource: 32-bit offsets with the
+// column block in the immediate, not a 64-bit address per element.
+template <int N>
+__device__ __forceinline__ void load_acc_layout(f32x4 (&x)[N / 16], __amdgpu_buffer_rsrc_t rs, long m, int ld) {
+    const int tid = threadIdx.x, row0 = 16 * (tid >> 6) + 4 * ((tid & 63) >> 4), lc = tid & 15;
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int nb = 0; nb < N / 16; ++nb) x[nb][r] = lds1(rs, m + (row0 + r) * ld + 16 * nb + lc);
+}
+// Makes the values exist here: otherwise the compiler sinks the arithmetic
+// that produces dG past the remaining products, to its one use at the end,
+// and keeps every operand of it alive (in scratch) until then.
+__device__ __forceinline__ void materialize(f32x4 (&a)[8]) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(a[i]));
+}
+// Sum over the 16 rows a wave holds of one column block (lanes l, l ^ 16, l ^ 32, l ^ 48).
+__device__ __forceinline__ float col_sum16(float v) {
+    v += __shfl_xor(v, 16, 64);
+    return v + __shfl_xor(v, 32, 64);
+}
+
+// One block per (chunk, head).  The four gradients that sum to dk and dlog
+// alpha (dQd, dKg, dKd, dKi) are consumed where their product ends: dq and dk
+// go out from the accumulators, dG = dQd Qd + dKd Kd - dKi Ki - dKg Kg is summed
+// in registers and its reverse cumulative sum is taken from LDS.  dTB and the
+// strict lower part of Kd Ki^T are consumed the same way (dT, dbeta); dPm,
+// T^T dT and dA never leave LDS.  Only dW goes through the workspace.
+__global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void bwd_grads_kernel(BwdParams p) {
     __shared__ __attribute__((aligned(16))) float sm[32 * 68 + 32 * 132];
-    __shared__ float beta_s[64], dbeta_s[64], dGL_s[128];
-    // intermediates that never leave the block stay in LDS: dPm, T^T dT and
-    // dT / dA (row stride 68, so the per-row dbeta sum is not one bank)
-    constexpr int kLdA = 68;
-    __shared__ __attribute__((aligned(16))) float s_dPm[64 * 64], s_X[64 * 64], s_dA[64 * kLdA];
+    __shared__ float beta_s[64], kk_s[64], colq_s[4][128], colb_s[4][64];
+    constexpr int kLdA = 68;   // row stride of dA (so the per-row dbeta sum is not one bank)
+    // s_big: dPm and T^T dT while the products run, then dG [64][128]
+    __shared__ __attribute__((aligned(16))) float s_big[2 * 64 * 64], s_dA[64 * kLdA];
+    float *s_dPm = s_big, *s_X = s_big + 64 * 64;
     const ChunkParams &c = p.c;
     const int H = c.H, h = blockIdx.x % H, cid = blockIdx.x / H, tid = threadIdx.x;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, lg = l >> 4, lc = l & 15;
+    const int row0 = 16 * w + 4 * lg;
     const ChunkInfo ci = load_chunk(c, cid);
     const long tok0 = ci.start;
     const int len = ci.len;
     float *B = chunk_buf(p, cid, h);
+    const __amdgpu_buffer_rsrc_t rs_B = chunk_rsrc(p, cid, h);
     if (tid < 64) beta_s[tid] = tid < len ? c.beta[(tok0 + tid) * H + h] : 0.f;
-    if (p.dgate) {   // O = Qd S0 + Pm U
-        bmm2<false, false, false, false, 0, 128>(B + bO, 128, B + bQd, 128, B + bS0, 128, 128, B + bPm, 64, B + bU, 128,
-                                                 64, 1.f, 64, sm);
+    // G is reloaded for each use (an L2 hit) rather than held across the
+    // products, which keeps the kernel within two blocks' registers per CU
+    f32x4 G[8], acc[8], X[8], dG[8];
+    auto zero = [](f32x4 *a, int n) {
+        for (int i = 0; i < n; ++i) a[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+    };
+    // Outputs [T][H][128] go through buffer resources that end at the chunk's
+    // last token: stores of rows past it are dropped, loads of them read 0,
+    // with no branch.
+    const uint32_t out_bytes = (uint32_t)len * H * kHeadDim * 4;
+    auto out_rs = [&](float *o) { return buffer_rsrc(o + tok0 * H * kHeadDim, out_bytes); };
+    auto out_off = [&](int r, int nb) { return (uint32_t)((((row0 + r) * H + h) * kHeadDim + 16 * nb + lc) * 4); };
+    auto st_out = [&](__amdgpu_buffer_rsrc_t rs, int r, int nb, float v) {
+        __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, out_off(r, nb), 0, 0);
+    };
+    const __amdgpu_buffer_rsrc_t rs_dk = out_rs(p.dk);
+    if (p.dgate) {   // O = Qd S0 + Pm U; dgate = dy scale O
+        zero(acc, 8);
+        bmm_acc<false, false, 128, 2>(acc, B + bQd, 128, B + bS0, 128, 128, sm);
+        bmm_acc<false, false, 128, 2>(acc, B + bPm, 64, B + bU, 128, 64, sm);
+        uint16_t dyv[4][8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb)
+                dyv[r][nb] = p.dy[((tok0 + min(row0 + r, len - 1)) * H + h) * kHeadDim + 16 * nb + lc];
+        const __amdgpu_buffer_rsrc_t rs = out_rs(p.dgate);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) st_out(rs, r, nb, bf2f(dyv[r][nb]) * c.scale * acc[nb][r]);
     }
-    bmm<false, true, 1, false, 64>(s_dPm, 64, B + bdO, 128, B + bU, 128, 128, 1.f, 64, sm);       // tril(dO U^T)
-    bmm2<false, true, false, false, 0, 128>(B + bdQd, 128, B + bdO, 128, B + bS0, 128, 128, s_dPm, 64, B + bKi, 128,
-                                            64, 1.f, 64, sm);                                        // dO S0^T + dPm Ki
-    bmm<false, true, 0, false, 128>(B + bdW, 128, B + bdU, 128, B + bS0, 128, 128, -1.f, 64, sm);    // -dU S0^T
-    bmm<false, true, 0, false, 128>(B + bdKg, 128, B + bU, 128, B + bdSL, 128, 128, 1.f, 64, sm);    // U dS_L^T
-    bmm2<false, true, false, true, 0, 64>(B + bdTB, 64, B + bdW, 128, B + bKd, 128, 128, B + bdU, 128, B + bV, 128,
-                                          128, 1.f, 64, sm);                                         // dW Kd^T + dU V^T
-    bmm<true, false, 0, false, 128>(B + bdKd, 128, B + bTB, 64, B + bdW, 128, 64, 1.f, 64, sm);      // TB^T dW
-    bmm<true, false, 0, false, 128>(p.dv + (tok0 * H + h) * kHeadDim, H * kHeadDim, B + bTB, 64, B + bdU, 128, 64,
-                                    1.f, len, sm);                                                       // dV = TB^T dU
-    __syncthreads();
-    // dT = dTB diag(beta) (held in the dA slot); dbeta from TB = T diag(beta)
-    // (loads in batches ahead of the stores that follow them: vmcnt counts
-    // stores too)
+    bmm<false, true, 0, false, 128>(B + bdW, 128, B + bdU, 128, B + bS0, 128, 128, -1.f, 64, sm);   // dW = -dU S0^T
+    // dTB = dW Kd^T + dU V^T: dT = dTB diag(beta) into s_dA; dbeta gets sum_i dTB_ij T_ij
     {
-        float x[16];
+        f32x4 a4[4], t4[4];
+        zero(a4, 4);
+        bmm_acc<false, true, 64, 2>(a4, B + bdW, 128, B + bKd, 128, 128, sm);
+        bmm_acc<false, true, 64, 2>(a4, B + bdU, 128, B + bV, 128, 128, sm);
+        load_acc_layout<64>(t4, rs_B, bT, 64);
 #pragma unroll
-        for (int t = 0; t < 16; ++t) x[t] = B[bdTB + tid + t * kNT];
+        for (int nb = 0; nb < 4; ++nb) {
+            float cs = 0.f;
 #pragma unroll
-        for (int t = 0; t < 16; ++t) {
-            const int e = tid + t * kNT;
-            s_dA[(e >> 6) * kLdA + (e & 63)] = x[t] * beta_s[e & 63];
+            for (int r = 0; r < 4; ++r) {
+                s_dA[(row0 + r) * kLdA + 16 * nb + lc] = a4[nb][r] * beta_s[16 * nb + lc];
+                cs += a4[nb][r] * t4[nb][r];
+            }
+            cs = col_sum16(cs);
+            if (lg == 0) colb_s[w][16 * nb + lc] = cs;
         }
     }
-    if (tid < 64) {
-        float s = 0.f;
-#pragma unroll 16
-        for (int i = 0; i < 64; ++i) s += B[bdTB + i * 64 + tid] * B[bT + i * 64 + tid];
-        dbeta_s[tid] = s;
-    }
-    bmm<true, false, 0, false, 64>(s_X, 64, B + bT, 64, s_dA, kLdA, 64, 1.f, 64, sm);            // T^T dT
-    bmm<false, true, 2, false, 64>(s_dA, kLdA, s_X, 64, B + bT, 64, 64, -1.f, 64, sm);           // dA
-    bmm<false, true, 2, false, 64>(B + bKK, 64, B + bKd, 128, B + bKi, 128, 128, 1.f, 64, sm);       // tril(Kd Ki^T, -1)
-    __syncthreads();
-    if (tid < 64) {
-        float s = 0.f;
-#pragma unroll 16
-        for (int m = 0; m < 64; ++m) s += s_dA[tid * kLdA + m] * B[bKK + tid * 64 + m];
-        dbeta_s[tid] += s;
+    bmm<true, false, 0, false, 128>(p.dv + (tok0 * H + h) * kHeadDim, H * kHeadDim, B + bTB, 64, B + bdU, 128, 64,
+                                    1.f, len, sm);                                                     // dV = TB^T dU
+    bmm<true, false, 0, false, 64>(s_X, 64, B + bT, 64, s_dA, kLdA, 64, 1.f, 64, sm);          // T^T dT
+    bmm<false, true, 2, false, 64>(s_dA, kLdA, s_X, 64, B + bT, 64, 64, -1.f, 64, sm);         // dA
+    // tril(Kd Ki^T, -1): dbeta_i gets sum_m dA_im (Kd Ki^T)_im
+    {
+        f32x4 a4[4];
+        zero(a4, 4);
+        bmm_acc<false, true, 64, 2>(a4, B + bKd, 128, B + bKi, 128, 128, sm);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int i = row0 + r;
+            float sr = 0.f;
+#pragma unroll
+            for (int nb = 0; nb < 4; ++nb) {
+                const int j = 16 * nb + lc;
+                if (j < i) sr += a4[nb][r] * s_dA[i * kLdA + j];
+            }
+            sr += __shfl_xor(sr, 1, 64);
+            sr += __shfl_xor(sr, 2, 64);
+            sr += __shfl_xor(sr, 4, 64);
+            sr += __shfl_xor(sr, 8, 64);
+            if (lc == 0) kk_s[i] = sr;
+        }
     }
     __syncthreads();
     {   // diag(beta) dA
-        float x[16];
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
             const int e = tid + t * kNT;
             s_dA[(e >> 6) * kLdA + (e & 63)] *= beta_s[e >> 6];
         }
     }
-    bmm<false, false, 0, true, 128>(B + bdKd, 128, s_dA, kLdA, B + bKi, 128, 64, 1.f, 64, sm);      // += (beta dA) Ki
-    bmm2<true, false, true, false, 0, 128>(B + bdKi, 128, s_dA, kLdA, B + bKd, 128, 64, s_dPm, 64, B + bQd, 128,
-                                           64, 1.f, 64, sm);                                         // (beta dA)^T Kd + dPm^T Qd
-    __syncthreads();
-    if (tid < 128) {
+    bmm<false, true, 1, false, 64>(s_dPm, 64, B + bdO, 128, B + bU, 128, 128, 1.f, 64, sm);   // dPm = tril(dO U^T)
+    // The four terms of dk and dG.  dG stays in registers; dk is summed in
+    // the output itself (each lane rereads only what it wrote), since holding
+    // it as well would exceed the 256 registers of two blocks per CU.
+    auto add_dk = [&]() {   // dk += acc
+        f32x4 d[8];
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb)
+                d[nb][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_dk, out_off(r, nb), 0, 0));
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) st_out(rs_dk, r, nb, d[nb][r] + acc[nb][r]);
+    };
+    // dKd = TB^T dW + (beta dA) Ki: dk = dKd e^G, dG = dKd Kd
+    zero(acc, 8);
+    bmm_acc<true, false, 128, 2>(acc, B + bTB, 64, B + bdW, 128, 64, sm);
+    bmm_acc<false, false, 128, 2>(acc, s_dA, kLdA, B + bKi, 128, 64, sm);
+    load_acc_layout<128>(X, rs_B, bKd, 128);
+    load_acc_layout<128>(G, rs_B, bG, 128);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) dG[nb] = acc[nb] * X[nb];
+    materialize(dG);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) st_out(rs_dk, r, nb, acc[nb][r] * __expf(G[nb][r]));
+    // dKi = (beta dA)^T Kd + dPm^T Qd: dk += dKi e^-G, dG -= dKi Ki
+    zero(acc, 8);
+    bmm_acc<true, false, 128, 2>(acc, s_dA, kLdA, B + bKd, 128, 64, sm);
+    bmm_acc<true, false, 128, 2>(acc, s_dPm, 64, B + bQd, 128, 64, sm);
+    load_acc_layout<128>(X, rs_B, bKi, 128);
+    load_acc_layout<128>(G, rs_B, bG, 128);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            dG[nb][r] -= acc[nb][r] * X[nb][r];
+            acc[nb][r] *= __expf(-G[nb][r]);
+        }
+    materialize(dG);
+    add_dk();
+    // dQd = dO S0^T + dPm Ki: dq = dQd e^G, dG += dQd Qd
+    zero(acc, 8);
+    bmm_acc<false, true, 128, 2>(acc, B + bdO, 128, B + bS0, 128, 128, sm);
+    bmm_acc<false, false, 128, 2>(acc, s_dPm, 64, B + bKi, 128, 64, sm);
+    load_acc_layout<128>(X, rs_B, bQd, 128);
+    load_acc_layout<128>(G, rs_B, bG, 128);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) dG[nb] += acc[nb] * X[nb];
+    materialize(dG);
+    {
+        const __amdgpu_buffer_rsrc_t rs = out_rs(p.dq);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) st_out(rs, r, nb, acc[nb][r] * __expf(G[nb][r]));
+    }
+    // dKg = U dS_L^T: dk += dKg e^{G_L - G}, dG -= dKg Kg, and its column sums for dG_L
+    zero(acc, 8);
+    bmm_acc<false, true, 128, 2>(acc, B + bU, 128, B + bdSL, 128, 128, sm);
+    load_acc_layout<128>(X, rs_B, bKg, 128);
+    load_acc_layout<128>(G, rs_B, bG, 128);
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+        const float gl = lds1(rs_B, bG + 63 * 128 + 16 * nb + lc);
+        float cs = 0.f;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const float e = acc[nb][r] * X[nb][r];
+            dG[nb][r] -= e;
+            cs += e;
+            acc[nb][r] *= __expf(gl - G[nb][r]);
+        }
+        cs = col_sum16(cs);
+        if (lg == 0) colq_s[w][16 * nb + lc] = cs;
+    }
+    add_dk();
+    // dG to LDS (s_big is free: the last product's staging ended with a barrier)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) s_big[(row0 + r) * 128 + 16 * nb + lc] = dG[nb][r];
+    float dgl = 0.f;
+    if (tid < 128) {   // dG_L = colsum(dKg Kg) + gL rowsum(S0 dS_L)
         const int ch = tid;
-        float s = 0.f, t = 0.f;
-#pragma unroll 16
-        for (int i = 0; i < 64; ++i) s += B[bdKg + i * 128 + ch] * B[bKg + i * 128 + ch];
+        float t = 0.f;
 #pragma unroll 16
         for (int j = 0; j < 128; ++j) t += B[bS0 + ch * 128 + j] * B[bdSL + ch * 128 + j];
-        dGL_s[ch] = s + B[bGL + ch] * t;
+        dgl = ((colq_s[0][ch] + colq_s[1][ch]) + (colq_s[2][ch] + colq_s[3][ch])) + B[bGL + ch] * t;
     }
     __syncthreads();
-    // As in the prep kernel, loads go out in batches ahead of the stores that
-    // use them (vmcnt counts stores too).
     if (tid < 128) {   // dlog alpha: reverse cumulative sum of dG, plus dG_L
         const int ch = tid;
-        float run = dGL_s[ch];
-#pragma unroll 1
-        for (int i0 = 63; i0 >= 0; i0 -= 16) {
-            float dg[16];
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const long e = (i0 - t) * 128 + ch;
-                dg[t] = B[bdQd + e] * B[bQd + e] + B[bdKd + e] * B[bKd + e] - B[bdKi + e] * B[bKi + e] -
-                        B[bdKg + e] * B[bKg + e];
-            }
-#pragma unroll
-            for (int t = 0; t < 16; ++t) {
-                const int i = i0 - t;
-                run += dg[t];
-                if (i < len) p.dla[((tok0 + i) * H + h) * kHeadDim + ch] = run;
-            }
+        float run = dgl;
+#pragma unroll 8
+        for (int i = 63; i >= 0; --i) {
+            run += s_big[i * 128 + ch];
+            if (i < len) p.dla[((tok0 + i) * H + h) * kHeadDim + ch] = run;
         }
     }
-    {
-        const int ch = tid & 127;
-        const float gl = B[bG + 63 * 128 + ch];
-#pragma unroll 1
-        for (int k0 = 0; k0 < 32; k0 += 4) {   // element e = tid + 256 k: row 2 k + tid / 128
-            float gv[4], dqd[4], dkd[4], dki[4], dkg[4], ov[4];
-            uint16_t dyv[4];
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int e = tid + (k0 + t) * kNT, i = e >> 7;
-                gv[t] = B[bG + e];
-                dqd[t] = B[bdQd + e];
-                dkd[t] = B[bdKd + e];
-                dki[t] = B[bdKi + e];
-                dkg[t] = B[bdKg + e];
-                if (p.dgate) {
-                    ov[t] = B[bO + e];
-                    dyv[t] = p.dy[((tok0 + min(i, len - 1)) * H + h) * kHeadDim + ch];
-                }
-            }
-#pragma unroll
-            for (int t = 0; t < 4; ++t) {
-                const int e = tid + (k0 + t) * kNT, i = e >> 7;
-                if (i >= len) continue;
-                const long o = ((tok0 + i) * H + h) * kHeadDim + ch;
-                const float g = gv[t], eg = expf(g);
-                p.dq[o] = dqd[t] * eg;
-                p.dk[o] = dkd[t] * eg + dki[t] * expf(-g) + dkg[t] * expf(gl - g);
-                if (p.dgate) p.dgate[o] = bf2f(dyv[t]) * c.scale * ov[t];
-            }
-        }
-    }
-    if (tid < len) p.dbeta[(tok0 + tid) * H + h] = dbeta_s[tid];
+    if (tid < len)
+        p.dbeta[(tok0 + tid) * H + h] = ((colb_s[0][tid] + colb_s[1][tid]) + (colb_s[2][tid] + colb_s[3][tid])) + kk_s[tid];
 }
 
 }  // namespace

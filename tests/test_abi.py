@@ -221,7 +221,7 @@ def backward(L, geom=None, dtype=1, ws=FAKE[16], ws_bytes=1 << 40, ptrs=None, cu
 def test_backward_workspace_bytes(L):
     t, hp = _cu([0, 100, 100, 228])
     al = lambda x: (x + 255) // 256 * 256
-    assert L.kda_chunk_backward_workspace_bytes(_geom(H=2), 3, hp) == al(4 * 4) + al(16 * 4) + 4 * 2 * 770560
+    assert L.kda_chunk_backward_workspace_bytes(_geom(H=2), 3, hp) == al(4 * 4) + al(16 * 4) + 4 * 2 * 573952
     assert L.kda_chunk_backward_workspace_bytes(_geom(H=2, d=64), 3, hp) == 0
 
 
