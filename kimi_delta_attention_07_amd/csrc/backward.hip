@@ -665,9 +665,9 @@ __device__ __forceinline__ float col_sum16(float v) {
 }
 
 // One block per (chunk, head).  The four gradients that sum to dk and dlog
-// alpha (dQd, dKg, dKd, dKi) are consumed where their product ends: dq and dk
-// go out from the accumulators, dG = dQd Qd + dKd Kd - dKi Ki - dKg Kg is summed
-// in registers and its reverse cumulative sum is taken from LDS.  dTB and the
+// alpha (dQd, dKg, dKd, dKi) are consumed where their product ends: dq goes out
+// from the accumulators, dk and dG = dQd Qd + dKd Kd - dKi Ki - dKg Kg are
+// summed in registers, and dG's reverse cumulative sum is taken from LDS.  dTB and the
 // strict lower part of Kd Ki^T are consumed the same way (dT, dbeta); dPm,
 // T^T dT and dA never leave LDS.  Only dW goes through the workspace.
 __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void bwd_grads_kernel(BwdParams p) {
@@ -689,7 +689,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void b
     if (tid < 64) beta_s[tid] = tid < len ? c.beta[(tok0 + tid) * H + h] : 0.f;
     // G is reloaded for each use (an L2 hit) rather than held across the
     // products, which keeps the kernel within two blocks' registers per CU
-    f32x4 G[8], acc[8], X[8], dG[8];
+    f32x4 G[8], acc[8], X[8], dG[8], dk[8];
     auto zero = [](f32x4 *a, int n) {
         for (int i = 0; i < n; ++i) a[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
@@ -702,7 +702,6 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void b
     auto st_out = [&](__amdgpu_buffer_rsrc_t rs, int r, int nb, float v) {
         __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(v), rs, out_off(r, nb), 0, 0);
     };
-    const __amdgpu_buffer_rsrc_t rs_dk = out_rs(p.dk);
     if (p.dgate) {   // O = Qd S0 + Pm U; dgate = dy scale O
         zero(acc, 8);
         bmm_acc<false, false, 128, 2>(acc, B + bQd, 128, B + bS0, 128, 128, sm);
@@ -773,21 +772,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void b
         }
     }
     bmm<false, true, 1, false, 64>(s_dPm, 64, B + bdO, 128, B + bU, 128, 128, 1.f, 64, sm);   // dPm = tril(dO U^T)
-    // The four terms of dk and dG.  dG stays in registers; dk is summed in
-    // the output itself (each lane rereads only what it wrote), since holding
-    // it as well would exceed the 256 registers of two blocks per CU.
-    auto add_dk = [&]() {   // dk += acc
-        f32x4 d[8];
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int nb = 0; nb < 8; ++nb)
-                d[nb][r] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rs_dk, out_off(r, nb), 0, 0));
-#pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-            for (int nb = 0; nb < 8; ++nb) st_out(rs_dk, r, nb, d[nb][r] + acc[nb][r]);
-    };
+    // The four terms of dk and dG, summed in registers.
     // dKd = TB^T dW + (beta dA) Ki: dk = dKd e^G, dG = dKd Kd
     zero(acc, 8);
     bmm_acc<true, false, 128, 2>(acc, B + bTB, 64, B + bdW, 128, 64, sm);
@@ -798,9 +783,10 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void b
     for (int nb = 0; nb < 8; ++nb) dG[nb] = acc[nb] * X[nb];
     materialize(dG);
 #pragma unroll
-    for (int r = 0; r < 4; ++r)
+    for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) st_out(rs_dk, r, nb, acc[nb][r] * __expf(G[nb][r]));
+        for (int r = 0; r < 4; ++r) dk[nb][r] = acc[nb][r] * __expf(G[nb][r]);
+    materialize(dk);
     // dKi = (beta dA)^T Kd + dPm^T Qd: dk += dKi e^-G, dG -= dKi Ki
     zero(acc, 8);
     bmm_acc<true, false, 128, 2>(acc, s_dA, kLdA, B + bKd, 128, 64, sm);
@@ -812,10 +798,10 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             dG[nb][r] -= acc[nb][r] * X[nb][r];
-            acc[nb][r] *= __expf(-G[nb][r]);
+            dk[nb][r] += acc[nb][r] * __expf(-G[nb][r]);
         }
     materialize(dG);
-    add_dk();
+    materialize(dk);
     // dQd = dO S0^T + dPm Ki: dq = dQd e^G, dG += dQd Qd
     zero(acc, 8);
     bmm_acc<false, true, 128, 2>(acc, B + bdO, 128, B + bS0, 128, 128, sm);
@@ -846,12 +832,18 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void b
             const float e = acc[nb][r] * X[nb][r];
             dG[nb][r] -= e;
             cs += e;
-            acc[nb][r] *= __expf(gl - G[nb][r]);
+            dk[nb][r] += acc[nb][r] * __expf(gl - G[nb][r]);
         }
         cs = col_sum16(cs);
         if (lg == 0) colq_s[w][16 * nb + lc] = cs;
     }
-    add_dk();
+    {
+        const __amdgpu_buffer_rsrc_t rs = out_rs(p.dk);
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+            for (int nb = 0; nb < 8; ++nb) st_out(rs, r, nb, dk[nb][r]);
+    }
     // dG to LDS (s_big is free: the last product's staging ended with a barrier)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
