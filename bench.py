@@ -296,9 +296,18 @@ def cpu_baseline(ki, seconds):
         if el >= seconds or reps >= 50:
             break
     cores = min(orc.num_threads(), H)
+    # the same workload on one thread, once (about 16 times one run above)
+    threads = orc.num_threads()
+    orc.set_num_threads(1)
+    t1 = time.perf_counter()
+    orc.prefill(inp)
+    el1 = time.perf_counter() - t1
+    orc.set_num_threads(threads)
     return {"value": reps * 4096 / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"the full T=4096 H=32 prefill workload, fp64 oracle, {reps} run(s) in {el:.1f} s "
-                      f"on {cores} OpenMP threads (heads in parallel)"}
+                      f"on {cores} OpenMP threads (heads in parallel)",
+            "single_thread": {"value": 4096 / el1, "unit": "tokens/s", "cores": 1,
+                              "sample": f"one run of the same workload on one thread, {el1:.1f} s"}}
 
 
 def bench_backward(torch, kda, ki, args, dev):

@@ -74,6 +74,7 @@ class Oracle:
         self.lib = ctypes.CDLL(path)
         L = self.lib
         L.kda_oracle_num_threads.restype = ctypes.c_int
+        L.kda_oracle_set_num_threads.argtypes = [ctypes.c_int]
         L.kda_oracle_conv.argtypes = [ctypes.c_int, _I, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                       _D, _D, _D, _D, ctypes.c_long, _D]
         L.kda_oracle_l2norm.argtypes = [ctypes.c_long, ctypes.c_int, ctypes.c_double, _D]
@@ -93,6 +94,10 @@ class Oracle:
 
     def num_threads(self):
         return int(self.lib.kda_oracle_num_threads())
+
+    def set_num_threads(self, n):
+        """Threads for later calls (timing only; the results do not depend on it)."""
+        self.lib.kda_oracle_set_num_threads(int(n))
 
     # ---- single steps --------------------------------------------------
     def conv(self, x, w, cu, act=ACT_SILU, cache_in=None):

@@ -58,6 +58,16 @@ int kda_oracle_num_threads(void) {
 #endif
 }
 
+/* Thread count of later parallel regions (heads run in parallel); n <= 0
+ * leaves it unchanged.  Timing control only: results do not depend on it. */
+void kda_oracle_set_num_threads(int n) {
+#ifdef _OPENMP
+    if (n > 0) omp_set_num_threads(n);
+#else
+    (void)n;
+#endif
+}
+
 static double sigmoid(double x) { return 1.0 / (1.0 + exp(-x)); }
 
 static double activation(int act, double x) {

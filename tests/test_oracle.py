@@ -364,6 +364,23 @@ def test_packed_equals_separate():
     assert np.array_equal(whole["conv_cache"][1], inp["conv_cache"][1].double().numpy())
 
 
+def test_thread_count_does_not_change_results():
+    """Heads run in parallel; the per-head arithmetic is the same on any
+    number of threads, so one thread and several give identical bits."""
+    import torch
+    inp = ki.prefill_inputs(34, [30, 9], H=4, d=8, K=3, dtype=torch.bfloat16)
+    threads = ORC.num_threads()
+    try:
+        ORC.set_num_threads(1)
+        one = ORC.prefill(inp)
+        ORC.set_num_threads(4)
+        many = ORC.prefill(inp)
+    finally:
+        ORC.set_num_threads(threads)
+    for key in ("y", "final_state", "conv_cache"):
+        assert np.array_equal(one[key], many[key]), key
+
+
 def test_decode_slot_remap():
     import torch
     dec = ki.decode_inputs(34, 3, H=2, d=8, K=4, steps=2, dtype=torch.bfloat16, n_slots=5,
