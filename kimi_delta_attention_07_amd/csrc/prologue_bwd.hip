@@ -266,6 +266,176 @@ __global__ __launch_bounds__(256) void prologue_bwd_dx128_kernel(PrologueBwdPara
     }
 }
 
+// ---- head dim 128: the three stages in one pass ---------------------------
+// A wave streams the 64 token rows of one block for one head (lane l:
+// channels 2l, 2l + 1), plus the K - 1 rows after them.  Each row's dpre (the
+// pre stage's arithmetic) goes into a ring of the last K rows: the row K - 1
+// earlier then has every dpre row its dx reads, and the row's own conv window
+// gives its tap-gradient terms.  dpre reaches HBM only for the first K - 1
+// rows of each sequence, which the incoming cache's gradient reads.  Each
+// row's loads are issued one row ahead.
+struct RowIn128 {
+    float2 dy[3], zg, dg, xr[3];   // dq, dk, dv reaching the outputs; gate logit, dgate; raw q, k, v
+    float zb, db;                  // beta logit, dbeta
+};
+template <int DT>
+__device__ __forceinline__ void load_row128(const PrologueBwdParams &p, long t, long C, long ch, int h,
+                                            RowIn128 &r) {
+    t = min(t, (long)p.T - 1);   // rows past the end: a repeated row, unused
+    const long o = t * C + ch;
+    r.dy[0] = *reinterpret_cast<const float2 *>(p.dq + o);
+    r.dy[1] = *reinterpret_cast<const float2 *>(p.dk + o);
+    r.dy[2] = *reinterpret_cast<const float2 *>(p.dv + o);
+    r.zg = r.dg = make_float2(0.f, 0.f);
+    if (p.gate_logit) {
+        r.zg = load2<DT>(p.gate_logit, o);
+        r.dg = *reinterpret_cast<const float2 *>(p.dgate + o);
+    }
+    r.zb = load1<DT>(p.beta_logit, t * p.H + h);
+    r.db = p.dbeta[t * p.H + h];
+    r.xr[0] = load2<DT>(p.q_raw, o);
+    r.xr[1] = load2<DT>(p.k_raw, o);
+    r.xr[2] = load2<DT>(p.v_raw, o);
+}
+
+template <int DT, int K>
+__global__ __launch_bounds__(256) void prologue_bwd_fused128_kernel(PrologueBwdParams p) {
+    constexpr int D = 128, Km1 = K - 1;
+    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+    const int h = 4 * blockIdx.y + w;
+    if (h >= p.H) return;   // wave-uniform; the kernel has no barrier
+    const long C = (long)p.H * D, ch = (long)h * D + 2 * l;
+    const long t0 = (long)blockIdx.x * kBwdTokBlock, t1 = min((long)p.T, t0 + kBwdTokBlock);
+    const float2 z2 = make_float2(0.f, 0.f);
+    float2 wt[3][K], acc[3][K], ring[3][K], xw[3][K];
+#pragma unroll
+    for (int X = 0; X < 3; ++X) {
+        load_taps<K>(p.conv_w, C, X, ch, wt[X]);
+#pragma unroll
+        for (int j = 0; j < K; ++j) acc[X][j] = ring[X][j] = xw[X][j] = z2;
+    }
+    // sequence of row t (n, its start and end) and of row tau = t - (K - 1)
+    // (nt, its end); the bounds are reloaded only when a sequence ends, since
+    // any load waited for in the loop would also wait for the prefetched row
+    int n = seq_of(p.cu, p.n_seqs, t0);
+    int nt = n;
+    long start = p.cu[n], end_n = p.cu[n + 1], end_nt = end_n;
+    float *outs[3] = {p.dq_raw, p.dk_raw, p.dv_raw};
+    RowIn128 cur, nxt;
+    load_row128<DT>(p, t0, C, ch, h, cur);
+    for (long t = t0; t < t1 + Km1; ++t) {
+        if (t + 1 < t1 + Km1) load_row128<DT>(p, t + 1, C, ch, h, nxt);
+        float2 g[3] = {z2, z2, z2};
+        if (t < p.T) {   // uniform
+            while (t >= end_n && n + 1 < p.n_seqs) {
+                ++n;
+                start = end_n;
+                end_n = p.cu[n + 1];
+            }
+            if (t == t0 || t - Km1 < start) {   // window rebuilt: block start, or history before the sequence
+#pragma unroll
+                for (int X = 0; X < 3; ++X)
+#pragma unroll
+                    for (int j = 0; j < K; ++j) xw[X][j] = raw2<DT>(p, X, n, start, t - Km1 + j, ch);
+            } else {   // rows t - K + 1 .. t - 1 are the previous row's window
+#pragma unroll
+                for (int X = 0; X < 3; ++X) {
+#pragma unroll
+                    for (int j = 0; j < Km1; ++j) xw[X][j] = xw[X][j + 1];
+                    xw[X][Km1] = cur.xr[X];
+                }
+            }
+            float pre[3][2], xa[3][2];
+#pragma unroll
+            for (int X = 0; X < 3; ++X) {
+                pre[X][0] = pre[X][1] = 0.f;
+#pragma unroll
+                for (int j = 0; j < K; ++j) {
+                    pre[X][0] += wt[X][j].x * xw[X][j].x;
+                    pre[X][1] += wt[X][j].y * xw[X][j].y;
+                }
+                xa[X][0] = activate(p.act, pre[X][0]);
+                xa[X][1] = activate(p.act, pre[X][1]);
+            }
+            float dxt[3][2];
+#pragma unroll
+            for (int X = 0; X < 2; ++X) {
+                const float v = wave_sum_pair(xa[X][0] * xa[X][0] + xa[X][1] * xa[X][1],
+                                              xa[X][0] * cur.dy[X].x + xa[X][1] * cur.dy[X].y);
+                const float inv = 1.0f / sqrtf(lane_value(v, 0) + p.eps);
+                const float k3 = lane_value(v, 16) * inv * inv * inv;
+                dxt[X][0] = cur.dy[X].x * inv - xa[X][0] * k3;
+                dxt[X][1] = cur.dy[X].y * inv - xa[X][1] * k3;
+            }
+            dxt[2][0] = cur.dy[2].x;
+            dxt[2][1] = cur.dy[2].y;
+#pragma unroll
+            for (int X = 0; X < 3; ++X)
+                g[X] = make_float2(dxt[X][0] * act_grad(p.act, pre[X][0]), dxt[X][1] * act_grad(p.act, pre[X][1]));
+            if (t < t1) {   // this block's own row
+                const long o = t * C + ch;
+                if (p.gate_logit) {
+                    const float s0 = sigmoidf(cur.zg.x), s1 = sigmoidf(cur.zg.y);
+                    *reinterpret_cast<float2 *>(p.dgate_logit + o) =
+                        make_float2(cur.dg.x * s0 * (1.f - s0), cur.dg.y * s1 * (1.f - s1));
+                }
+                if (l == 0) {
+                    const float sb = sigmoidf(cur.zb);
+                    p.dbeta_logit[t * p.H + h] = cur.db * sb * (1.f - sb);
+                }
+#pragma unroll
+                for (int X = 0; X < 3; ++X)
+#pragma unroll
+                    for (int j = 0; j < K; ++j) {
+                        acc[X][j].x += xw[X][j].x * g[X].x;
+                        acc[X][j].y += xw[X][j].y * g[X].y;
+                    }
+                if (t - start < Km1)   // the incoming cache's gradient reads these rows
+#pragma unroll
+                    for (int X = 0; X < 3; ++X)
+                        *reinterpret_cast<float2 *>(p.dpre + ((long)X * p.T + t) * C + ch) = g[X];
+            }
+        }
+        // ring: dpre of rows t - K + 1 .. t (rows past the end are 0)
+#pragma unroll
+        for (int X = 0; X < 3; ++X) {
+#pragma unroll
+            for (int j = 0; j < Km1; ++j) ring[X][j] = ring[X][j + 1];
+            ring[X][Km1] = g[X];
+        }
+        const long tau = t - Km1;   // every dpre row its dx reads is in the ring
+        if (tau >= t0) {
+            while (tau >= end_nt && nt + 1 < p.n_seqs) end_nt = p.cu[++nt + 1];
+            const long end = min(end_nt, (long)p.T);
+#pragma unroll
+            for (int X = 0; X < 3; ++X) {
+                float2 d = z2;
+#pragma unroll
+                for (int j = 0; j < K; ++j)
+                    if (t - j < end) {   // tap j of token t - j reads tau
+                        d.x += wt[X][j].x * ring[X][Km1 - j].x;
+                        d.y += wt[X][j].y * ring[X][Km1 - j].y;
+                    }
+                *reinterpret_cast<float2 *>(outs[X] + tau * C + ch) = d;
+            }
+        }
+        cur = nxt;
+    }
+    // tap partials of this block, [block][X][c][4 taps]
+#pragma unroll
+    for (int X = 0; X < 3; ++X) {
+        float a[4] = {0.f, 0.f, 0.f, 0.f}, b[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < K; ++j) {
+            a[j] = acc[X][j].x;
+            b[j] = acc[X][j].y;
+        }
+        float *part = p.dw_part + (((long)blockIdx.x * 3 + X) * C + ch) * 4;
+        *reinterpret_cast<float4 *>(part) = make_float4(a[0], a[1], a[2], a[3]);
+        *reinterpret_cast<float4 *>(part + 4) = make_float4(b[0], b[1], b[2], b[3]);
+    }
+}
+
 // grid (sequences, 3 streams x (K-1) history slots), threads over channel pairs
 __global__ __launch_bounds__(256) void prologue_bwd_dcache_kernel(PrologueBwdParams p) {
     const int n = blockIdx.x, Km1 = p.K - 1;
@@ -362,6 +532,12 @@ __global__ __launch_bounds__(256) void prologue_bwd_dw_sum_kernel(PrologueBwdPar
 
 template <int D, int K>
 void launch_stages(const PrologueBwdParams &p, int dtype, int nb, hipStream_t s) {
+    if constexpr (D == 128) {
+        const dim3 g((unsigned)nb, (unsigned)((p.H + 3) / 4));
+        if (dtype == 1) hipLaunchKernelGGL((prologue_bwd_fused128_kernel<1, K>), g, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((prologue_bwd_fused128_kernel<0, K>), g, dim3(256), 0, s, p);
+        return;
+    }
     constexpr int TPB = 256 / (D / 2);
     const dim3 grid((unsigned)((p.T + TPB - 1) / TPB), (unsigned)p.H);
     if (dtype == 1) hipLaunchKernelGGL((prologue_bwd_pre_kernel<D, 1, K>), grid, dim3(256), 0, s, p);
