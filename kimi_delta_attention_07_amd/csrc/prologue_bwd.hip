@@ -24,6 +24,8 @@
 //           does the same for the incoming cache's K-1 history rows;
 //   dw      partial tap sums over blocks of 64 tokens, then one fixed-order
 //           sum over the blocks (deterministic, no atomics).
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -273,29 +275,36 @@ __global__ __launch_bounds__(256) void prologue_bwd_dx128_kernel(PrologueBwdPara
 // earlier then has every dpre row its dx reads, and the row's own conv window
 // gives its tap-gradient terms.  dpre reaches HBM only for the first K - 1
 // rows of each sequence, which the incoming cache's gradient reads.  Each
-// row's loads are issued one row ahead.
-struct RowIn128 {
-    float2 dy[3], zg, dg, xr[3];   // dq, dk, dv reaching the outputs; gate logit, dgate; raw q, k, v
-    float zb, db;                  // beta logit, dbeta
-};
+// row's loads are issued a row ahead.
+// One token row's inputs as loaded (bf16 pairs stay packed until used: a
+// conversion right after the load would make the wave wait for it there).
 template <int DT>
-__device__ __forceinline__ void load_row128(const PrologueBwdParams &p, long t, long C, long ch, int h,
-                                            RowIn128 &r) {
-    t = min(t, (long)p.T - 1);   // rows past the end: a repeated row, unused
+struct RowIn128 {
+    using Pair = typename std::conditional<DT == 1, uint32_t, float2>::type;
+    float2 dy[3], dg;   // dq, dk, dv reaching the outputs; dgate
+    Pair zg, xr[3];     // gate logit; raw q, k, v
+};
+__device__ __forceinline__ float2 pair_f2(uint32_t u) { return make_float2(lo_bf(u), hi_bf(u)); }
+__device__ __forceinline__ float2 pair_f2(float2 v) { return v; }
+template <int DT>
+__device__ __forceinline__ typename RowIn128<DT>::Pair load_pair(const void *base, long idx) {
+    if constexpr (DT == 1) return *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(base) + idx);
+    else return *reinterpret_cast<const float2 *>(static_cast<const float *>(base) + idx);
+}
+// Rows past the end load the last row (unused).  Without a gate, the gate
+// loads read dq instead (in bounds, unused), so no branch splits the loads.
+template <int DT>
+__device__ __forceinline__ void load_row128(const PrologueBwdParams &p, long t, long C, long ch, RowIn128<DT> &r) {
+    t = min(t, (long)p.T - 1);
     const long o = t * C + ch;
     r.dy[0] = *reinterpret_cast<const float2 *>(p.dq + o);
     r.dy[1] = *reinterpret_cast<const float2 *>(p.dk + o);
     r.dy[2] = *reinterpret_cast<const float2 *>(p.dv + o);
-    r.zg = r.dg = make_float2(0.f, 0.f);
-    if (p.gate_logit) {
-        r.zg = load2<DT>(p.gate_logit, o);
-        r.dg = *reinterpret_cast<const float2 *>(p.dgate + o);
-    }
-    r.zb = load1<DT>(p.beta_logit, t * p.H + h);
-    r.db = p.dbeta[t * p.H + h];
-    r.xr[0] = load2<DT>(p.q_raw, o);
-    r.xr[1] = load2<DT>(p.k_raw, o);
-    r.xr[2] = load2<DT>(p.v_raw, o);
+    r.zg = load_pair<DT>(p.gate_logit ? p.gate_logit : static_cast<const void *>(p.dq), o);
+    r.dg = *reinterpret_cast<const float2 *>((p.gate_logit ? p.dgate : p.dq) + o);
+    r.xr[0] = load_pair<DT>(p.q_raw, o);
+    r.xr[1] = load_pair<DT>(p.k_raw, o);
+    r.xr[2] = load_pair<DT>(p.v_raw, o);
 }
 
 template <int DT, int K>
@@ -321,10 +330,13 @@ __global__ __launch_bounds__(256) void prologue_bwd_fused128_kernel(PrologueBwdP
     int nt = n;
     long start = p.cu[n], end_n = p.cu[n + 1], end_nt = end_n;
     float *outs[3] = {p.dq_raw, p.dk_raw, p.dv_raw};
-    RowIn128 cur, nxt;
-    load_row128<DT>(p, t0, C, ch, h, cur);
-    for (long t = t0; t < t1 + Km1; ++t) {
-        if (t + 1 < t1 + Km1) load_row128<DT>(p, t + 1, C, ch, h, nxt);
+    // beta logit and dbeta of own row t0 + i in lane i: a per-row load of
+    // them would be a scalar load, and waiting for it waits for every scalar
+    // load issued, the prefetched rows' included
+    static_assert(kBwdTokBlock == 64, "one lane per own row");
+    const long tb = min(t0 + l, (long)p.T - 1);
+    const float bz = load1<DT>(p.beta_logit, tb * p.H + h), bd = p.dbeta[tb * p.H + h];
+    auto row = [&](long t, const RowIn128<DT> &cur) {
         float2 g[3] = {z2, z2, z2};
         if (t < p.T) {   // uniform
             while (t >= end_n && n + 1 < p.n_seqs) {
@@ -342,7 +354,7 @@ __global__ __launch_bounds__(256) void prologue_bwd_fused128_kernel(PrologueBwdP
                 for (int X = 0; X < 3; ++X) {
 #pragma unroll
                     for (int j = 0; j < Km1; ++j) xw[X][j] = xw[X][j + 1];
-                    xw[X][Km1] = cur.xr[X];
+                    xw[X][Km1] = pair_f2(cur.xr[X]);
                 }
             }
             float pre[3][2], xa[3][2];
@@ -375,13 +387,16 @@ __global__ __launch_bounds__(256) void prologue_bwd_fused128_kernel(PrologueBwdP
             if (t < t1) {   // this block's own row
                 const long o = t * C + ch;
                 if (p.gate_logit) {
-                    const float s0 = sigmoidf(cur.zg.x), s1 = sigmoidf(cur.zg.y);
+                    const float2 zg = pair_f2(cur.zg);
+                    const float s0 = sigmoidf(zg.x), s1 = sigmoidf(zg.y);
                     *reinterpret_cast<float2 *>(p.dgate_logit + o) =
                         make_float2(cur.dg.x * s0 * (1.f - s0), cur.dg.y * s1 * (1.f - s1));
                 }
-                if (l == 0) {
-                    const float sb = sigmoidf(cur.zb);
-                    p.dbeta_logit[t * p.H + h] = cur.db * sb * (1.f - sb);
+                {
+                    const int r = (int)(t - t0);   // < 64
+                    const float zb = lane_value(bz, r), db = lane_value(bd, r);
+                    const float sb = sigmoidf(zb);
+                    if (l == 0) p.dbeta_logit[t * p.H + h] = db * sb * (1.f - sb);
                 }
 #pragma unroll
                 for (int X = 0; X < 3; ++X)
@@ -419,8 +434,20 @@ __global__ __launch_bounds__(256) void prologue_bwd_fused128_kernel(PrologueBwdP
                 *reinterpret_cast<float2 *>(outs[X] + tau * C + ch) = d;
             }
         }
-        cur = nxt;
+    };
+    // rows in pairs through two buffers, each refilled right after its row
+    // (no copy of a buffer in flight)
+    RowIn128<DT> A, B;
+    const long tE = t1 + Km1;
+    load_row128<DT>(p, t0, C, ch, A);
+    long t = t0;
+    for (; t + 1 < tE; t += 2) {
+        load_row128<DT>(p, t + 1, C, ch, B);
+        row(t, A);
+        load_row128<DT>(p, t + 2, C, ch, A);
+        row(t + 1, B);
     }
+    if (t < tE) row(t, A);
     // tap partials of this block, [block][X][c][4 taps]
 #pragma unroll
     for (int X = 0; X < 3; ++X) {
