@@ -15,15 +15,16 @@
 //   dz = dy s (1 - s) for both sigmoids.
 // The device copy of cu_seqlens is trusted to match the host copy the entry
 // point validated, but every index derived from it is clamped, so a mismatch
-// cannot reach outside the buffers.  Three memory-bound stages:
+// cannot reach outside the buffers.  Memory-bound stages:
 //   pre     (token, head) rows: recomputes the conv and activation, writes
 //           dpre of the three streams to the workspace, and the two sigmoid
 //           gradients;
-//   dx      gathers dx from the K taps' dpre rows of the same sequence (head
-//           dim 128: a register window of 16 rows per wave); a small kernel
-//           does the same for the incoming cache's K-1 history rows;
-//   dw      partial tap sums over blocks of 64 tokens, then one fixed-order
-//           sum over the blocks (deterministic, no atomics).
+//   dx      gathers dx from the K taps' dpre rows of the same sequence;
+//   dw      partial tap sums over blocks of 64 tokens;
+// at head dim 128 one streaming kernel does all three per (64 tokens, head),
+// dpre never leaving registers.  Then a small kernel forms the incoming
+// cache's gradient from the first K-1 dpre rows of each sequence, and one
+// fixed-order sum adds the tap partials (deterministic, no atomics).
 #include <type_traits>
 
 #include "kda_device.h"
@@ -101,8 +102,8 @@ __global__ __launch_bounds__(256) void prologue_bwd_pre_kernel(PrologueBwdParams
     const int n = seq_of(p.cu, p.n_seqs, tc);
     const long start = p.cu[n];
     float2 x[3][K], w[3][K];
-    // rows whose conv window lies inside the sequence (all but its first K-1;
-    // uniform across a wave at D = 128) load without a branch per tap
+    // rows whose conv window lies inside the sequence (all but its first K-1)
+    // load without a branch per tap
     if (tc - (K - 1) >= start) {
 #pragma unroll
         for (int X = 0; X < 3; ++X) {
@@ -141,23 +142,12 @@ __global__ __launch_bounds__(256) void prologue_bwd_pre_kernel(PrologueBwdParams
         xa[X][0] = activate(p.act, pre[X][0]);
         xa[X][1] = activate(p.act, pre[X][1]);
     }
-    // L2 backward of q and k: every lane takes part in the group sums (head
-    // dim 128: one token row per wave, two sums per DPP/permlane pass)
+    // L2 backward of q and k: every lane takes part in the group sums
     float sums[2][2];   // [q, k][sum x~^2, sum x~ dx^]
-    if constexpr (D == 128) {
 #pragma unroll
-        for (int X = 0; X < 2; ++X) {
-            const float v = wave_sum_pair(xa[X][0] * xa[X][0] + xa[X][1] * xa[X][1],
-                                          xa[X][0] * dy[X].x + xa[X][1] * dy[X].y);
-            sums[X][0] = lane_value(v, 0);
-            sums[X][1] = lane_value(v, 16);
-        }
-    } else {
-#pragma unroll
-        for (int X = 0; X < 2; ++X) {
-            sums[X][0] = group_sum(xa[X][0] * xa[X][0] + xa[X][1] * xa[X][1], LPT);
-            sums[X][1] = group_sum(xa[X][0] * dy[X].x + xa[X][1] * dy[X].y, LPT);
-        }
+    for (int X = 0; X < 2; ++X) {
+        sums[X][0] = group_sum(xa[X][0] * xa[X][0] + xa[X][1] * xa[X][1], LPT);
+        sums[X][1] = group_sum(xa[X][0] * dy[X].x + xa[X][1] * dy[X].y, LPT);
     }
     float dxt[3][2];
 #pragma unroll
@@ -222,49 +212,6 @@ __global__ __launch_bounds__(256) void prologue_bwd_dx_kernel(PrologueBwdParams 
             }
         }
         *reinterpret_cast<float2 *>(outs[X] + tau * C + ch) = acc;
-    }
-}
-
-// Head dim 128: a wave owns 16 consecutive token rows of one head (lane l:
-// channels 2l, 2l + 1) and loads the K - 1 + 16 dpre rows they read once per
-// stream, instead of once per tap; a block takes 4 adjacent heads.
-template <int K>
-__global__ __launch_bounds__(256) void prologue_bwd_dx128_kernel(PrologueBwdParams p) {
-    constexpr int D = 128, R = 16, NW = R + K - 1;
-    const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
-    const int h = 4 * blockIdx.y + w;
-    if (h >= p.H) return;   // wave-uniform; the kernel has no barrier
-    const long tau0 = (long)blockIdx.x * R;
-    const long C = (long)p.H * D, ch = (long)h * D + 2 * l;
-    float2 g[3][NW], wt[3][K];
-#pragma unroll
-    for (int X = 0; X < 3; ++X) {
-#pragma unroll
-        for (int r = 0; r < NW; ++r) {
-            const long t = min(tau0 + r, (long)p.T - 1);
-            g[X][r] = *reinterpret_cast<const float2 *>(p.dpre + ((long)X * p.T + t) * C + ch);
-        }
-        load_taps<K>(p.conv_w, C, X, ch, wt[X]);
-    }
-    int n = seq_of(p.cu, p.n_seqs, min(tau0, (long)p.T - 1));
-    float *outs[3] = {p.dq_raw, p.dk_raw, p.dv_raw};
-#pragma unroll
-    for (int r = 0; r < R; ++r) {
-        const long tau = tau0 + r;
-        while (tau >= p.cu[n + 1] && n + 1 < p.n_seqs) ++n;   // tau's sequence (uniform)
-        const long end = min((long)p.cu[n + 1], (long)p.T);
-#pragma unroll
-        for (int X = 0; X < 3; ++X) {
-            float2 acc = make_float2(0.f, 0.f);
-#pragma unroll
-            for (int j = 0; j < K; ++j) {
-                if (tau + (K - 1) - j < end) {
-                    acc.x += wt[X][j].x * g[X][r + (K - 1) - j].x;
-                    acc.y += wt[X][j].y * g[X][r + (K - 1) - j].y;
-                }
-            }
-            if (tau < p.T) *reinterpret_cast<float2 *>(outs[X] + tau * C + ch) = acc;
-        }
     }
 }
 
@@ -569,11 +516,7 @@ void launch_stages(const PrologueBwdParams &p, int dtype, int nb, hipStream_t s)
     const dim3 grid((unsigned)((p.T + TPB - 1) / TPB), (unsigned)p.H);
     if (dtype == 1) hipLaunchKernelGGL((prologue_bwd_pre_kernel<D, 1, K>), grid, dim3(256), 0, s, p);
     else hipLaunchKernelGGL((prologue_bwd_pre_kernel<D, 0, K>), grid, dim3(256), 0, s, p);
-    if constexpr (D == 128)
-        hipLaunchKernelGGL((prologue_bwd_dx128_kernel<K>), dim3((unsigned)((p.T + 15) / 16), (unsigned)((p.H + 3) / 4)),
-                           dim3(256), 0, s, p);
-    else
-        hipLaunchKernelGGL((prologue_bwd_dx_kernel<D, K>), grid, dim3(256), 0, s, p);
+    hipLaunchKernelGGL((prologue_bwd_dx_kernel<D, K>), grid, dim3(256), 0, s, p);
     const long C = (long)p.H * D;
     const dim3 g3((unsigned)nb, (unsigned)((C + 255) / 256), 3);
     if (dtype == 1) hipLaunchKernelGGL((prologue_bwd_dw_partial_kernel<1, K>), g3, dim3(256), 0, s, p);
