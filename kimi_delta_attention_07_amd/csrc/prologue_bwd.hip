@@ -410,14 +410,16 @@ __global__ __launch_bounds__(256) void prologue_bwd_fused128_kernel(PrologueBwdP
     }
 }
 
-// grid (sequences, 3 streams x (K-1) history slots), threads over channel pairs
+// grid (sequences, 3 streams x (K-1) history slots, channel blocks of 512),
+// thread: one channel pair
 __global__ __launch_bounds__(256) void prologue_bwd_dcache_kernel(PrologueBwdParams p) {
     const int n = blockIdx.x, Km1 = p.K - 1;
     const int X = blockIdx.y / Km1, s = blockIdx.y % Km1;
     const long C = (long)p.H * p.d;
     const long start = max(0L, (long)p.cu[n]), end = min((long)p.cu[n + 1], (long)p.T);
     const long tau = start - Km1 + s;   // the absolute position this slot stands for
-    for (long ch = 2 * (long)threadIdx.x; ch < C; ch += 2 * 256) {
+    const long ch = ((long)blockIdx.z * 256 + threadIdx.x) * 2;
+    if (ch < C) {
         float2 acc = make_float2(0.f, 0.f);
         for (int j = 0; j < p.K; ++j) {
             const long t = tau + Km1 - j;
@@ -488,11 +490,15 @@ __global__ __launch_bounds__(256) void prologue_bwd_dw_partial_kernel(PrologueBw
     *reinterpret_cast<float4 *>(part) = make_float4(out[0], out[1], out[2], out[3]);
 }
 
-__global__ __launch_bounds__(256) void prologue_bwd_dw_sum_kernel(PrologueBwdParams p, int n_blocks) {
+// One fixed-order sum over the blocks per (stream, channel): 64-thread blocks
+// spread it over the CUs, and the block loop is unrolled so its loads are in
+// flight together.
+__global__ __launch_bounds__(64) void prologue_bwd_dw_sum_kernel(PrologueBwdParams p, int n_blocks) {
     const long C = (long)p.H * p.d;
-    const long e = (long)blockIdx.x * 256 + threadIdx.x;   // (X, c)
+    const long e = (long)blockIdx.x * 64 + threadIdx.x;   // (X, c)
     if (e >= 3 * C) return;
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll 8
     for (int b = 0; b < n_blocks; ++b) {
         const float4 v = *reinterpret_cast<const float4 *>(p.dw_part + ((long)b * 3 * C + e) * 4);
         s.x += v.x;
@@ -556,9 +562,10 @@ hipError_t launch_prologue_backward(PrologueBwdParams p, int dtype, hipStream_t 
         }
     }
     if (p.dcache_in && p.K > 1)
-        hipLaunchKernelGGL(prologue_bwd_dcache_kernel, dim3((unsigned)p.n_seqs, (unsigned)(3 * (p.K - 1))), dim3(256), 0,
-                           s, p);
-    hipLaunchKernelGGL(prologue_bwd_dw_sum_kernel, dim3((unsigned)((3 * C + 255) / 256)), dim3(256), 0, s, p, p.T > 0 ? nb : 0);
+        hipLaunchKernelGGL(prologue_bwd_dcache_kernel,
+                           dim3((unsigned)p.n_seqs, (unsigned)(3 * (p.K - 1)), (unsigned)((C + 511) / 512)), dim3(256),
+                           0, s, p);
+    hipLaunchKernelGGL(prologue_bwd_dw_sum_kernel, dim3((unsigned)((3 * C + 63) / 64)), dim3(64), 0, s, p, p.T > 0 ? nb : 0);
     return hipGetLastError();
 }
 
