@@ -68,6 +68,21 @@ def test_prologue_backward_matches_oracle(seed, lengths, H, d, K, dtype, act, ga
     check(run_gpu(inp, grads, act), ref, f"seed {seed}")
 
 
+@pytest.mark.parametrize("seed,lengths,K,dtype,act,gate,cache", [
+    (21, [2, 65, 0, 130], 1, torch.float32, "silu", True, True),
+    (22, [1, 2, 64, 3, 200], 2, torch.bfloat16, "none", False, True),
+    (23, [129, 0, 66], 3, torch.float32, "silu", True, False),
+    (24, [63, 1, 64, 1], 4, torch.float32, "none", True, True),
+])
+def test_prologue_backward_head_dim_128_variants(seed, lengths, K, dtype, act, gate, cache):
+    """Head dim 128 runs the streaming kernel: every conv width, fp32 and
+    bf16 inputs, with and without activation, gate and cache, sequences
+    shorter than the window and ones crossing its 64-token blocks."""
+    inp, grads = make(seed, lengths, 2, 128, K, dtype, gate, cache)
+    ref = ORC.prologue_backward(inp, grads, act=1 if act == "silu" else 0)
+    check(run_gpu(inp, grads, act), ref, f"seed {seed}")
+
+
 def test_prologue_backward_empty_batch_and_odd_heads():
     """No tokens at all (the tap and cache gradients come out as zeros), and
     H = 5 at d = 128 (the four-heads-per-block kernel has idle waves)."""
