@@ -790,6 +790,12 @@ __global__ __launch_bounds__(128 * TPB) __attribute__((amdgpu_waves_per_eu(1, 1)
         load_chain(o0, rec_of(0), l, g, tile);
         load_chain(o1, rec_of(1), l, g, tile);
         auto step = [&](int i, ChainOperands &o) {
+            // The U~ tile is the first load of a chunk's set.  Used here, after
+            // the barrier: its bf16 unpacking, left free, is hoisted into the
+            // previous step, whose wait for it (waits are in order) would
+            // then also wait for the rest of this chunk's operands.
+#pragma unroll
+            for (int m = 0; m < 4; ++m) asm volatile("" : "+v"(o.U[m]));
             bf16x8 Sb[4];
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
