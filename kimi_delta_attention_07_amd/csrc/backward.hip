@@ -84,7 +84,7 @@ __device__ __forceinline__ void seq_chunks(const ChunkParams &c, int n, int &c_b
 // 128, K a multiple of 16 HALVES; operands 16-byte aligned with lda, ldb multiples of
 // 4.  The operands may be in global memory (written earlier by this block:
 // the barrier on entry orders them) or in LDS.
-template <bool TA, bool TB, int N, int HALVES>
+template <bool TA, bool TB, int N, int HALVES, bool DEEP = false>
 __device__ void bmm_acc(f32x4 (&acc)[N / 16], const float *A, int lda, const float *B, int ldb, int K, float *sm) {
     constexpr int LA = 68, LB = 132;   // LDS rows, padded (multiples of 4 for 16-byte accesses)
     constexpr int KS = 16 * HALVES;    // k slab
@@ -135,35 +135,38 @@ __device__ void bmm_acc(f32x4 (&acc)[N / 16], const float *A, int lda, const flo
         }
     };
     const float4 z4 = make_float4(0.f, 0.f, 0.f, 0.f);
-    float4 ra0, ra1 = z4, rb00, rb10 = z4, rb01 = z4, rb11 = z4;   // [half]: A piece, B pieces (second only for N = 128)
-    auto fetch = [&](int k0) {
-        ra0 = *reinterpret_cast<const float4 *>(a_ptr(k0));
-        rb00 = *reinterpret_cast<const float4 *>(b_ptr(k0, tid));
-        if constexpr (N == 128) rb01 = *reinterpret_cast<const float4 *>(b_ptr(k0, tid + kNT));
+    // [half]: A piece, B pieces (second only for N = 128); the s* set holds the
+    // odd slabs when DEEP (two slabs in flight)
+    float4 ra0, ra1 = z4, rb00, rb10 = z4, rb01 = z4, rb11 = z4;
+    float4 sa0 = z4, sa1 = z4, sb00 = z4, sb10 = z4, sb01 = z4, sb11 = z4;
+    auto fetch_set = [&](int k0, float4 &a0, float4 &a1, float4 &b00, float4 &b10, float4 &b01, float4 &b11) {
+        a0 = *reinterpret_cast<const float4 *>(a_ptr(k0));
+        b00 = *reinterpret_cast<const float4 *>(b_ptr(k0, tid));
+        if constexpr (N == 128) b01 = *reinterpret_cast<const float4 *>(b_ptr(k0, tid + kNT));
         if constexpr (HALVES == 2) {
-            ra1 = *reinterpret_cast<const float4 *>(a_ptr(k0 + 16));
-            rb10 = *reinterpret_cast<const float4 *>(b_ptr(k0 + 16, tid));
-            if constexpr (N == 128) rb11 = *reinterpret_cast<const float4 *>(b_ptr(k0 + 16, tid + kNT));
+            a1 = *reinterpret_cast<const float4 *>(a_ptr(k0 + 16));
+            b10 = *reinterpret_cast<const float4 *>(b_ptr(k0 + 16, tid));
+            if constexpr (N == 128) b11 = *reinterpret_cast<const float4 *>(b_ptr(k0 + 16, tid + kNT));
         }
     };
+    auto fetch = [&](int k0) { fetch_set(k0, ra0, ra1, rb00, rb10, rb01, rb11); };
     // wave w: output rows 16 w .. 16 w + 15, N / 16 column blocks, on fp32
     // MFMAs; lane l supplies op(A)[16 w + l % 16][k] and op(B)[k][16 nb + l % 16]
     // for k = k0 + 4 t + l / 16 and holds C[16 w + 4 (l / 16) + r][16 nb + l % 16]
     constexpr int NB = N / 16;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6), l = tid & 63, lg = l >> 4, lc = l & 15;
-    __syncthreads();   // operands written earlier by this block are complete; staging is free
-    fetch(0);
-    for (int k0 = 0; k0 < K; k0 += KS) {
-        put_a(ra0, 0);
-        put_b(rb00, tid, 0);
-        if constexpr (N == 128) put_b(rb01, tid + kNT, 0);
+    auto put_set = [&](const float4 &a0, const float4 &a1, const float4 &b00, const float4 &b10, const float4 &b01,
+                       const float4 &b11) {
+        put_a(a0, 0);
+        put_b(b00, tid, 0);
+        if constexpr (N == 128) put_b(b01, tid + kNT, 0);
         if constexpr (HALVES == 2) {
-            put_a(ra1, 16);
-            put_b(rb10, tid, 16);
-            if constexpr (N == 128) put_b(rb11, tid + kNT, 16);
+            put_a(a1, 16);
+            put_b(b10, tid, 16);
+            if constexpr (N == 128) put_b(b11, tid + kNT, 16);
         }
-        __syncthreads();
-        if (k0 + KS < K) fetch(k0 + KS);
+    };
+    auto slab = [&]() {
 #pragma unroll
         for (int t = 0; t < 4 * HALVES; ++t) {
             const int kk = 4 * t + lg;
@@ -171,7 +174,34 @@ __device__ void bmm_acc(f32x4 (&acc)[N / 16], const float *A, int lda, const flo
 #pragma unroll
             for (int nb = 0; nb < NB; ++nb) acc[nb] = mfma_f32(a, Bs[kk * LB + 16 * nb + lc], acc[nb]);
         }
-        __syncthreads();
+    };
+    __syncthreads();   // operands written earlier by this block are complete; staging is free
+    if constexpr (!DEEP) {
+        fetch(0);
+        for (int k0 = 0; k0 < K; k0 += KS) {
+            put_set(ra0, ra1, rb00, rb10, rb01, rb11);
+            __syncthreads();
+            if (k0 + KS < K) fetch(k0 + KS);
+            slab();
+            __syncthreads();
+        }
+    } else {   // two register sets used in turn, each refilled right after it reached LDS
+        fetch_set(0, ra0, ra1, rb00, rb10, rb01, rb11);
+        if (KS < K) fetch_set(KS, sa0, sa1, sb00, sb10, sb01, sb11);
+        for (int k0 = 0; k0 < K; k0 += 2 * KS) {
+            put_set(ra0, ra1, rb00, rb10, rb01, rb11);
+            __syncthreads();
+            if (k0 + 2 * KS < K) fetch_set(k0 + 2 * KS, ra0, ra1, rb00, rb10, rb01, rb11);
+            slab();
+            __syncthreads();
+            if (k0 + KS < K) {
+                put_set(sa0, sa1, sb00, sb10, sb01, sb11);
+                __syncthreads();
+                if (k0 + 3 * KS < K) fetch_set(k0 + 3 * KS, sa0, sa1, sb00, sb10, sb01, sb11);
+                slab();
+                __syncthreads();
+            }
+        }
     }
 }
 
@@ -199,13 +229,13 @@ __device__ void bmm_store(float *C, int ldc, const f32x4 (&acc)[N / 16], float a
 }
 
 
-template <bool TA, bool TB, int MASK, bool ACC, int N, int HALVES = 2>
+template <bool TA, bool TB, int MASK, bool ACC, int N, int HALVES = 2, bool DEEP = false>
 __device__ void bmm(float *C, int ldc, const float *A, int lda, const float *B, int ldb, int K, float alpha, int mrows,
                     float *sm) {
     f32x4 acc[N / 16];
 #pragma unroll
     for (int nb = 0; nb < N / 16; ++nb) acc[nb] = f32x4{0.f, 0.f, 0.f, 0.f};
-    bmm_acc<TA, TB, N, HALVES>(acc, A, lda, B, ldb, K, sm);
+    bmm_acc<TA, TB, N, HALVES, DEEP>(acc, A, lda, B, ldb, K, sm);
     bmm_store<MASK, ACC, N>(C, ldc, acc, alpha, mrows);
 }
 
@@ -313,7 +343,7 @@ __global__ __launch_bounds__(kNT) void bwd_prep_kernel(BwdParams p) {
         }
     }
     // A = tril(Kd Ki^T, -1), rows scaled by beta
-    bmm<false, true, 2, false, 64, 1>(big, 64, B + bKd, 128, B + bKi, 128, 128, 1.f, 64, sm);
+    bmm<false, true, 2, false, 64, 1, true>(big, 64, B + bKd, 128, B + bKi, 128, 128, 1.f, 64, sm);
     __syncthreads();
     for (int e = tid; e < 64 * 64; e += kNT) big[e] *= beta_s[e >> 6];
     __syncthreads();
@@ -362,9 +392,9 @@ __global__ __launch_bounds__(kNT) void bwd_prep_kernel(BwdParams p) {
         B[bT + e] = Tm[e];
         B[bTB + e] = Tm[e] * beta_s[e & 63];
     }
-    bmm<false, false, 0, false, 128, 1>(B + bW, 128, B + bTB, 64, B + bKd, 128, 64, -1.f, 64, sm);   // -W = -TB Kd
-    bmm<false, false, 0, false, 128, 1>(B + bUt, 128, B + bTB, 64, B + bV, 128, 64, 1.f, 64, sm);    // U~ = TB V
-    bmm<false, true, 1, false, 64, 1>(B + bPm, 64, B + bQd, 128, B + bKi, 128, 128, 1.f, 64, sm);    // Pm
+    bmm<false, false, 0, false, 128, 1, true>(B + bW, 128, B + bTB, 64, B + bKd, 128, 64, -1.f, 64, sm);   // -W = -TB Kd
+    bmm<false, false, 0, false, 128, 1, true>(B + bUt, 128, B + bTB, 64, B + bV, 128, 64, 1.f, 64, sm);    // U~ = TB V
+    bmm<false, true, 1, false, 64, 1, true>(B + bPm, 64, B + bQd, 128, B + bKi, 128, 128, 1.f, 64, sm);    // Pm
 }
 
 // Block -> (sequence, head, value tile) for the state passes: the eight tiles
