@@ -734,7 +734,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void b
     };
     if (p.dgate) {   // O = Qd S0 + Pm U; dgate = dy scale O
         zero(acc, 8);
-        bmm_acc<false, false, 128, 2>(acc, B + bQd, 128, B + bS0, 128, 128, sm);
+        bmm_acc<false, false, 128, 2, true>(acc, B + bQd, 128, B + bS0, 128, 128, sm);
         bmm_acc<false, false, 128, 2>(acc, B + bPm, 64, B + bU, 128, 64, sm);
         uint16_t dyv[4][8];
 #pragma unroll
@@ -748,13 +748,13 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) st_out(rs, r, nb, bf2f(dyv[r][nb]) * c.scale * acc[nb][r]);
     }
-    bmm<false, true, 0, false, 128>(B + bdW, 128, B + bdU, 128, B + bS0, 128, 128, -1.f, 64, sm);   // dW = -dU S0^T
+    bmm<false, true, 0, false, 128, 2, true>(B + bdW, 128, B + bdU, 128, B + bS0, 128, 128, -1.f, 64, sm);   // dW = -dU S0^T
     // dTB = dW Kd^T + dU V^T: dT = dTB diag(beta) into s_dA; dbeta gets sum_i dTB_ij T_ij
     {
         f32x4 a4[4], t4[4];
         zero(a4, 4);
-        bmm_acc<false, true, 64, 2>(a4, B + bdW, 128, B + bKd, 128, 128, sm);
-        bmm_acc<false, true, 64, 2>(a4, B + bdU, 128, B + bV, 128, 128, sm);
+        bmm_acc<false, true, 64, 2, true>(a4, B + bdW, 128, B + bKd, 128, 128, sm);
+        bmm_acc<false, true, 64, 2, true>(a4, B + bdU, 128, B + bV, 128, 128, sm);
         load_acc_layout<64>(t4, rs_B, bT, 64);
 #pragma unroll
         for (int nb = 0; nb < 4; ++nb) {
@@ -776,7 +776,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void b
     {
         f32x4 a4[4];
         zero(a4, 4);
-        bmm_acc<false, true, 64, 2>(a4, B + bKd, 128, B + bKi, 128, 128, sm);
+        bmm_acc<false, true, 64, 2, true>(a4, B + bKd, 128, B + bKi, 128, 128, sm);
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const int i = row0 + r;
@@ -801,7 +801,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void b
             s_dA[(e >> 6) * kLdA + (e & 63)] *= beta_s[e >> 6];
         }
     }
-    bmm<false, true, 1, false, 64>(s_dPm, 64, B + bdO, 128, B + bU, 128, 128, 1.f, 64, sm);   // dPm = tril(dO U^T)
+    bmm<false, true, 1, false, 64, 2, true>(s_dPm, 64, B + bdO, 128, B + bU, 128, 128, 1.f, 64, sm);   // dPm = tril(dO U^T)
     // The four terms of dk and dG, summed in registers.
     // dKd = TB^T dW + (beta dA) Ki: dk = dKd e^G, dG = dKd Kd
     zero(acc, 8);
