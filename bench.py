@@ -20,10 +20,14 @@ reported under "backward", and the packed varlen and long-context prefill
 workloads under "prefill_workloads" (informative; the headline stays the
 4096-token sequence).
 
-Every kernel is timed with HIP events on the stream it is launched on; the
-roofline object is for the kernel that takes the longest, with the algorithmic
-bytes of that kernel's own inputs and outputs.  The oracle (CPU, fp64) is
-timed on the same prefill workload as "cpu_baseline".  Prints ONE JSON line.
+Every kernel is timed with HIP events on the stream it is launched on.  The
+roofline object counts the path's algorithmic bytes only (49,216 B per token:
+q, k, v, log alpha, gate and beta in, y out, plus the fp32 state and conv
+cache in and out), never the chunk records the two stages pass between them:
+"frac" is those bytes over the longest kernel's own time, "path.frac" over
+the whole step; "traffic" is what the counters measured for both kernels.
+The oracle (CPU, fp64) is timed on the same prefill workload as
+"cpu_baseline".  Prints ONE JSON line.
 """
 from __future__ import annotations
 
@@ -42,13 +46,9 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, TFLOP/s
 
 H, D, K, CHUNK = 32, 128, 4, 64
-# Algorithmic bytes per token (all 32 heads, bf16 activations) of each stage's
-# compulsory inputs and outputs.
-PROLOGUE_B_PER_TOK = 3 * 8192 + 64 + 8192 + 3 * 8192 + 128 + 8192           # 65,728
-PREPARE_B_PER_TOK = 3 * 8192 + 8192 + 128 + 74240 * H // CHUNK                # 70,016
-SCAN_B_PER_TOK = 74240 * H // CHUNK + 8192 + 8192                              # 53,504
-PATH_B_PER_TOK = 5 * 8192 + 64 + 8192                                          # 49,216 (q,k,v,log-a,gate,beta in; y out)
-FUSED_PREPARE_B_PER_TOK = 3 * 8192 + 8192 + 64 + 74240 * H // CHUNK          # 69,952 (raw q,k,v, log-a, beta logit in; record out)
+# Algorithmic bytes per token of the prefill path (all 32 heads, bf16): q, k,
+# v, log alpha and gate in (8,192 B each), beta in (64 B), y out (8,192 B).
+PATH_B_PER_TOK = 5 * 8192 + 64 + 8192                                          # 49,216
 STATE_B = H * D * D * 4                                                        # one sequence's fp32 state
 CONV_CACHE_B = 3 * (K - 1) * H * D * 4
 FLOP_PER_TOK = 4_496_032                                                       # useful chunked-form flops (H=32)
@@ -63,33 +63,82 @@ BWD_FLOP_PER_CHUNK_HEAD = 2 * 18_350_080
 FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector, TFLOP/s
 
 
-# bench timing slot -> kernel whose counters profiles/traffic.json holds
+# bench timing slot -> the kernel it launches at head dim 128, conv 4, SiLU
+# (the batched varlen scan runs the two-tiles-per-block instance), and the
+# sources that kernel is built from: a counter record is used only while the
+# hash of those sources matches the one stored with it
 TRAFFIC_KERNEL = {"prologue": "prologue128_kernel<4, 1>", "chunk_prepare": "prepare_kernel<false, 4, 0>",
                   "chunk_scan": "scan_kernel<true, 1>", "prefill_prepare": "prepare_kernel<true, 4, 1>",
                   "prefill_scan": "scan_kernel<true, 1>", "decode": "decode_kernel<128, 1, 0>"}
-KERNEL_SOURCES = {"prologue128_kernel<4, 1>": ["prologue.hip"], "prepare_kernel<false, 4, 0>": ["chunk.hip"],
-                  "prepare_kernel<true, 4, 1>": ["chunk.hip"], "scan_kernel<true, 1>": ["chunk.hip"],
-                  "decode_kernel<128, 1, 0>": ["decode.hip"]}
+KERNEL_SOURCES = {"prologue": ["prologue.hip"], "chunk_prepare": ["chunk.hip"], "chunk_scan": ["chunk.hip"],
+                  "prefill_prepare": ["chunk.hip"], "prefill_scan": ["chunk.hip"], "decode": ["decode.hip"]}
 
 
-def measured_traffic(slot):
+def _src_sha(slot):
+    import hashlib
+
+    h = hashlib.sha256()
+    for fn in KERNEL_SOURCES[slot] + ["kda_device.h", "kda_internal.h"]:
+        with open(os.path.join(ROOT, "kimi_delta_attention_07_amd", "csrc", fn), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _counter_record(fname, slot, workload="T4096"):
+    """The record of the kernel behind a bench timing slot in a counter file
+    under profiles/ (written from rocprofv3 runs of this bench), or None when
+    the file is missing or the kernel's sources changed since."""
+    path = os.path.join(ROOT, "profiles", fname)
+    if slot not in KERNEL_SOURCES or not os.path.exists(path):
+        return None
+    rec = json.load(open(path)).get("records", {}).get(f"{slot} @ {workload}")
+    if not rec or rec.get("src_sha") != _src_sha(slot):
+        return None
+    return rec
+
+
+def measured_traffic(slot, workload="T4096"):
     """HBM bytes per launch measured by rocprofv3 (FETCH_SIZE, WRITE_SIZE, both
     calibrated against a 1 GiB copy) and kept in profiles/traffic.json, or None
     when that file is missing or the kernel's sources changed since."""
-    import hashlib
+    rec = _counter_record("traffic.json", slot, workload)
+    return rec["bytes_per_launch"] if rec else None
 
-    path = os.path.join(ROOT, "profiles", "traffic.json")
-    name = TRAFFIC_KERNEL.get(slot)
-    if not name or not os.path.exists(path):
-        return None
-    rec = json.load(open(path)).get("kernels", {}).get(name)
-    if not rec:
-        return None
-    h = hashlib.sha256()
-    for fn in KERNEL_SOURCES[name] + ["kda_device.h", "kda_internal.h"]:
-        with open(os.path.join(ROOT, "kimi_delta_attention_07_amd", "csrc", fn), "rb") as f:
-            h.update(f.read())
-    return rec["bytes_per_launch"] if h.hexdigest()[:16] == rec["src_sha"] else None
+
+def measured_mfma(slot, workload="T4096"):
+    """Matrix-core counters per launch (rocprofv3 --pmc), from
+    profiles/mfma.json: bf16 MFMA flops executed and MFMA-busy cycles."""
+    return _counter_record("mfma.json", slot, workload)
+
+
+def path_roofline(path_bytes, per_kernel_ms, ms_step, slots, workload="T4096", tokens=4096):
+    """The roofline object of one prefill workload: the path's algorithmic
+    bytes over the longest kernel's time (frac) and over the whole step
+    (path.frac), the measured traffic of the step's kernels beside them, and
+    the matrix-core fractions (useful flops from the flop model; executed
+    flops and busy cycles from the counters when they are current)."""
+    dom = max(per_kernel_ms, key=per_kernel_ms.get)
+    t_dom = per_kernel_ms[dom] * 1e-3
+    ach = path_bytes / t_dom / 1e9
+    tr = {k: measured_traffic(k, workload) for k in slots}
+    traffic = sum(tr.values()) if all(v is not None for v in tr.values()) else None
+    useful = FLOP_PER_TOK * tokens
+    mf = {k: measured_mfma(k, workload) for k in slots}
+    out = {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": ach / HBM_PEAK_GBS,
+           "traffic": traffic, "kernel": TRAFFIC_KERNEL.get(dom, dom), "bytes_per_launch": path_bytes,
+           "traffic_over_algorithmic": traffic / path_bytes if traffic else None,
+           "traffic_per_kernel": tr,
+           "path": {"achieved": path_bytes / (ms_step * 1e-3) / 1e9,
+                    "frac": path_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                    "floor_us": path_bytes / (HBM_PEAK_GBS * 1e9) * 1e6},
+           "mfma": {"useful_flop_per_step": useful,
+                    "useful_frac": useful / (ms_step * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)}}
+    if all(v is not None for v in mf.values()):
+        ex = sum(v["bf16_flop"] for v in mf.values())
+        out["mfma"]["executed_bf16_flop_per_step"] = ex
+        out["mfma"]["executed_frac"] = ex / (ms_step * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)
+        out["mfma"]["busy_frac_per_kernel"] = {k: v["busy_frac"] for k, v in mf.items()}
+    return out
 
 
 def parse():
@@ -190,7 +239,19 @@ def bench_prefill(torch, kda, ki, args, dev):
         for j, k in enumerate(slots):
             per[k] += e[j].elapsed_time(e[j + 1])
     per = {k: v / args.steps for k, v in per.items()}
-    return dict(ms_per_step=total_ms / args.steps, wall_s=wall, per_kernel_ms=per)
+    # per-step times: the same K steps once more, one event at each step
+    # boundary only; their median is reported beside the K-step mean
+    bev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    bev[0].record()
+    for i in range(args.steps):
+        step(kda, sets[i % 2], ws)
+        bev[i + 1].record()
+    torch.cuda.synchronize()
+    steps_ms = sorted(bev[i].elapsed_time(bev[i + 1]) for i in range(args.steps))
+    n = len(steps_ms)
+    median = steps_ms[n // 2] if n % 2 else 0.5 * (steps_ms[n // 2 - 1] + steps_ms[n // 2])
+    return dict(ms_per_step=total_ms / args.steps, wall_s=wall, per_kernel_ms=per, step_ms_median=median,
+                step_ms_min=steps_ms[0], step_ms_max=steps_ms[-1])
 
 
 def bench_prefill_workloads(torch, kda, ki, args, dev):
@@ -225,13 +286,18 @@ def bench_prefill_workloads(torch, kda, ki, args, dev):
         b.record()
         torch.cuda.synchronize()
         ms = a.elapsed_time(b) / reps
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(reps)]
+        for e in evs:
+            run_fused_step(kda, g, ws, e)
+        torch.cuda.synchronize()
+        per = {"prefill_prepare": sum(e[0].elapsed_time(e[1]) for e in evs) / reps,
+               "prefill_scan": sum(e[1].elapsed_time(e[2]) for e in evs) / reps}
         floor_b = T * PATH_B_PER_TOK + N * (2 * STATE_B + 2 * CONV_CACHE_B)
         n_chunks = sum((int(x) + CHUNK - 1) // CHUNK for x in inp["lengths"])
         out[name] = {"workload": desc + f" ({T} tokens), H=32 dk=dv=128, conv 4, chunk 64, bf16 inputs",
                      "tokens": T, "sequences": N, "chunks": n_chunks, "ms_per_call": ms,
-                     "value": T / (ms * 1e-3), "unit": "tokens/s",
-                     "path_hbm_frac": floor_b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                     "mfma_frac": FLOP_PER_TOK * T / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12)}
+                     "value": T / (ms * 1e-3), "unit": "tokens/s", "per_kernel_ms": per,
+                     "roofline": path_roofline(floor_b, per, ms, list(per), name, T)}
         del g, ws
         torch.cuda.empty_cache()
     return out
@@ -264,7 +330,7 @@ def bench_decode(torch, kda, ki, args, dev):
     return {"workload": "batched decode: 256 resident fp32 states x 1 token, H=32 d=128 conv 4, 64 steps",
             "value": 256 / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("decode"),
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": measured_traffic("decode", "B256"),
                          "bytes_per_launch": 256 * DECODE_B_PER_ROW}}
 
 
@@ -288,6 +354,7 @@ def cpu_baseline(ki, seconds):
 
     orc = oracle.get()
     inp = ki.config_prefill(1)
+    threads = orc.num_threads()
     reps, t0 = 0, time.perf_counter()
     while True:
         orc.prefill(inp)
@@ -295,17 +362,25 @@ def cpu_baseline(ki, seconds):
         el = time.perf_counter() - t0
         if el >= seconds or reps >= 50:
             break
-    cores = min(orc.num_threads(), H)
+    cores = min(orc.num_threads(), H)   # one (sequence, head) pair per thread at most
     # the same workload on one thread, once (about 16 times one run above)
-    threads = orc.num_threads()
     orc.set_num_threads(1)
     t1 = time.perf_counter()
     orc.prefill(inp)
     el1 = time.perf_counter() - t1
     orc.set_num_threads(threads)
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
     return {"value": reps * 4096 / el, "unit": "tokens/s", "cores": cores, "kind": "oracle",
             "sample": f"the full T=4096 H=32 prefill workload, fp64 oracle, {reps} run(s) in {el:.1f} s "
                       f"on {cores} OpenMP threads (heads in parallel)",
+            "cpu_model": model, "affinity_cores": len(os.sched_getaffinity(0)), "omp_threads": threads,
             "single_thread": {"value": 4096 / el1, "unit": "tokens/s", "cores": 1,
                               "sample": f"one run of the same workload on one thread, {el1:.1f} s"}}
 
@@ -395,14 +470,7 @@ def main():
     ms = pre["ms_per_step"]
     tok_s = 4096 / (ms * 1e-3)
     per = pre["per_kernel_ms"]
-    bytes_per_launch = {"prologue": 4096 * PROLOGUE_B_PER_TOK + 2 * CONV_CACHE_B + 3 * H * D * K * 4,
-                        "chunk_prepare": 4096 * PREPARE_B_PER_TOK,
-                        "chunk_scan": 4096 * SCAN_B_PER_TOK + 2 * STATE_B,
-                        "prefill_prepare": 4096 * FUSED_PREPARE_B_PER_TOK + 2 * CONV_CACHE_B + 3 * H * D * K * 4,
-                        "prefill_scan": 4096 * SCAN_B_PER_TOK + 2 * STATE_B}
-    dom = max(per, key=per.get)
-    ach = bytes_per_launch[dom] / (per[dom] * 1e-3) / 1e9
-    path_bytes = 4096 * PATH_B_PER_TOK + 2 * STATE_B + 2 * CONV_CACHE_B
+    path_bytes = 4096 * PATH_B_PER_TOK + 2 * STATE_B + 2 * CONV_CACHE_B   # 206,077,952
     res = {
         "metric": METRIC, "value": tok_s, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
@@ -411,13 +479,10 @@ def main():
                                "bf16 inputs, fp32 initial/final state", "global_batch": 1, "seq_len": 4096,
                    "parallelism": "single GPU", "path": "kda_prefill (fused)" if args.path == "fused"
                    else "kda_prologue + kda_chunk_forward"},
-        "roofline": {"bound": "hbm", "achieved": ach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": ach / HBM_PEAK_GBS, "traffic": measured_traffic(dom), "kernel": dom,
-                     "bytes_per_launch": bytes_per_launch[dom]},
-        "prefill": {"per_kernel_ms": per,
-                    "mfma_frac": FLOP_PER_TOK * 4096 / (ms * 1e-3) / (BF16_PEAK_TFLOPS * 1e12),
-                    "path_hbm_frac": path_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                    "path_roofline_floor_us": path_bytes / (HBM_PEAK_GBS * 1e9) * 1e6},
+        "step_ms_median": pre["step_ms_median"],
+        "roofline": path_roofline(path_bytes, per, ms, list(per)),
+        "prefill": {"per_kernel_ms": per, "step_ms_median": pre["step_ms_median"],
+                    "step_ms_min": pre["step_ms_min"], "step_ms_max": pre["step_ms_max"]},
     }
     if not args.no_workloads:
         res["prefill_workloads"] = bench_prefill_workloads(torch, kda, ki, args, dev)

@@ -35,8 +35,10 @@
  *     error nothing is launched and nothing is written; the return value
  *     says why and kda_last_error_detail() gives a sentence (per thread).
  *     Unsupported inputs are rejected, never approximated.
- *   - Device-side values are not inspected: NaN/Inf propagate; out-of-range
- *     slot indices or log_alpha > 0 are undefined behaviour.
+ *   - Device-side values are not inspected: NaN/Inf propagate and
+ *     log_alpha > 0 is outside the method's range (results unspecified).
+ *     kda_decode_step skips a row whose slot index is out of range (see
+ *     there).
  *   - Layouts are row-major (last index fastest).  Tokens of all sequences
  *     are packed ("THD": [total_tokens, H, d]); sequence n owns tokens
  *     cu_seqlens[n] .. cu_seqlens[n+1]-1 (int32, cu_seqlens[0] = 0,
@@ -121,7 +123,12 @@ kda_status kda_prologue(const kda_geom *geom, int32_t n_seqs, int32_t total_toke
                         void *stream);
 
 /*
- * Chunked prefill (d = 128, bf16, chunk = 64 tokens).  Inputs are the
+ * kda_chunk_forward: chunked prefill, the path the k3 README names for KDA
+ * prefill ("What this repository is": the CUDA compute path is FLA's
+ * chunk_kda) and whose state it carries is the forum post's "recurrent KDA
+ * state" (implementation list), with the fp32 read-modify-write state of
+ * the kimi_k3 API docs (Structs: KdaState).
+ * (d = 128, bf16, chunk = 64 tokens.)  Inputs are the
  * prologue's outputs plus the per-channel log decay.  Each sequence is cut
  * into 64-token chunks from its own start (the last one may be shorter);
  * within a chunk the recurrence is evaluated in its WY/UT form (cumulative
@@ -138,16 +145,21 @@ kda_status kda_prologue(const kda_geom *geom, int32_t n_seqs, int32_t total_toke
  *   initial_state NULL (zeros) or [n_seqs][H][128][128] fp32;
  *   final_state NULL (skip) or same shape, may alias initial_state;
  *   out [T][H][128] bf16 = scale * o (.) gate;
+ *   chunk: the chunk length, must be 64 (anything else: KDA_ERR_UNSUPPORTED);
  *   workspace: device memory of at least kda_chunk_workspace_bytes(...) bytes,
  *     16-byte aligned; its contents are scratch (only kda_chunk_scan reads
  *     what kda_chunk_prepare wrote there).
+ * kda_chunk_workspace_bytes(geom, n_seqs, total_tokens) returns a size that
+ * suffices for any split of total_tokens into n_seqs sequences (it counts
+ * floor((total_tokens + 63 n_seqs) / 64) chunks, the most such a batch can
+ * have), or 0 for an invalid geometry or n_seqs <= 0 or total_tokens < 0.
+ * Each (chunk, head) takes 74,240 bytes.
  */
-size_t kda_chunk_workspace_bytes(const kda_geom *geom, int32_t n_seqs,
-                                 const int32_t *cu_seqlens_host);
+size_t kda_chunk_workspace_bytes(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens);
 
 kda_status kda_chunk_forward(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
                              const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host,
-                             kda_dtype in_dtype, const void *q, const void *k, const void *v,
+                             kda_dtype in_dtype, int32_t chunk, const void *q, const void *k, const void *v,
                              const void *log_alpha, const float *beta, const void *gate,
                              const float *initial_state, float *final_state, void *out,
                              void *workspace, size_t workspace_bytes, void *stream);
@@ -179,7 +191,7 @@ kda_status kda_chunk_scan(const kda_geom *geom, int32_t n_seqs, int32_t total_to
  * applies sigmoid(gate_logit) to the output.  kda_prefill runs both.  The
  * result equals kda_prologue followed by kda_chunk_forward, except that q^,
  * k^, v^ are never rounded to bf16 in between.
- *   geom: d = 128, conv_k in [1, 4]; in_dtype must be KDA_BF16;
+ *   geom: d = 128, conv_k in [1, 4]; in_dtype must be KDA_BF16; chunk = 64;
  *   q_raw, k_raw, v_raw [T][H][128] bf16 (pre-conv); conv_w [3][H*128][conv_k]
  *   fp32; conv_cache_in NULL (zeros) or [n_seqs][3][conv_k-1][H*128] fp32;
  *   conv_cache_out NULL (skip) or same shape, may alias conv_cache_in;
@@ -190,7 +202,7 @@ kda_status kda_chunk_scan(const kda_geom *geom, int32_t n_seqs, int32_t total_to
  */
 kda_status kda_prefill(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
                        const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host, kda_dtype in_dtype,
-                       const void *q_raw, const void *k_raw, const void *v_raw, const float *conv_w,
+                       int32_t chunk, const void *q_raw, const void *k_raw, const void *v_raw, const float *conv_w,
                        const float *conv_cache_in, float *conv_cache_out, const void *log_alpha,
                        const void *beta_logit, const void *gate_logit, const float *initial_state,
                        float *final_state, void *out, void *workspace, size_t workspace_bytes, void *stream);
@@ -212,7 +224,9 @@ kda_status kda_prefill_scan(const kda_geom *geom, int32_t n_seqs, int32_t total_
  * shift and conv, activation, L2(q, k), sigmoid gates, then one step of the
  * recurrence on the row's resident state, read and written once.
  *   slot_idx_dev NULL (row b uses slot b, needs batch <= n_slots) or
- *     [batch] int32 distinct slot numbers in [0, n_slots);
+ *     [batch] int32 distinct slot numbers in [0, n_slots); a row whose slot
+ *     lies outside [0, n_slots) is skipped: no state, cache or output element
+ *     of it is read or written (its output row keeps its old contents);
  *   in_dtype: dtype of q_raw, k_raw, v_raw [batch][H][d], log_alpha
  *     [batch][H][d], beta_logit [batch][H], gate_logit NULL or [batch][H][d];
  *   conv_w [3][H*d][conv_k] fp32; conv_cache [n_slots][3][conv_k-1][H*d] fp32
@@ -280,12 +294,13 @@ kda_status kda_prologue_backward(const kda_geom *geom, int32_t n_seqs, int32_t t
  *     [n_seqs][H][128][128];
  *   workspace: device buffer of at least kda_chunk_backward_workspace_bytes()
  *     bytes, 16-byte aligned, contents not needed before or after the call
- *     (573,952 B per (chunk, head) plus the chunk table).
+ *     (573,952 B per (chunk, head) plus the chunk table; sized, like
+ *     kda_chunk_workspace_bytes, from the totals n_seqs and total_tokens).
  * Runs the forward's chunk quantities again (nothing from a forward call is
  * reused) and is stream-ordered like every other entry point.  Errors as for
  * kda_chunk_forward; nothing is launched when validation fails.
  */
-size_t kda_chunk_backward_workspace_bytes(const kda_geom *geom, int32_t n_seqs, const int32_t *cu_seqlens_host);
+size_t kda_chunk_backward_workspace_bytes(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens);
 
 kda_status kda_chunk_backward(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
                               const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host,

@@ -53,11 +53,11 @@ def load(path=LIB_PATH):
     G = ctypes.POINTER(Geom)
     L.kda_prologue.argtypes = [G, _I, _I, _P, _P, _I] + [_P] * 13 + [_P]
     L.kda_prologue.restype = _I
-    L.kda_chunk_workspace_bytes.argtypes = [G, _I, _P]
+    L.kda_chunk_workspace_bytes.argtypes = [G, _I, _I]
     L.kda_chunk_workspace_bytes.restype = ctypes.c_size_t
-    L.kda_chunk_forward.argtypes = [G, _I, _I, _P, _P, _I] + [_P] * 10 + [ctypes.c_size_t, _P]
+    L.kda_chunk_forward.argtypes = [G, _I, _I, _P, _P, _I, _I] + [_P] * 10 + [ctypes.c_size_t, _P]
     L.kda_chunk_forward.restype = _I
-    L.kda_chunk_backward_workspace_bytes.argtypes = [G, _I, _P]
+    L.kda_chunk_backward_workspace_bytes.argtypes = [G, _I, _I]
     L.kda_chunk_backward_workspace_bytes.restype = ctypes.c_size_t
     L.kda_chunk_backward.argtypes = [G, _I, _I, _P, _P, _I] + [_P] * 17 + [ctypes.c_size_t, _P]
     L.kda_chunk_backward.restype = _I
@@ -69,7 +69,7 @@ def load(path=LIB_PATH):
     L.kda_chunk_prepare.restype = _I
     L.kda_chunk_scan.argtypes = [G, _I, _I, _P, _P, _I] + [_P] * 5 + [ctypes.c_size_t, _P]
     L.kda_chunk_scan.restype = _I
-    L.kda_prefill.argtypes = [G, _I, _I, _P, _P, _I] + [_P] * 13 + [ctypes.c_size_t, _P]
+    L.kda_prefill.argtypes = [G, _I, _I, _P, _P, _I, _I] + [_P] * 13 + [ctypes.c_size_t, _P]
     L.kda_prefill.restype = _I
     L.kda_prefill_prepare.argtypes = [G, _I, _I, _P, _P, _I] + [_P] * 9 + [ctypes.c_size_t, _P]
     L.kda_prefill_prepare.restype = _I
@@ -172,10 +172,11 @@ def prologue_backward(q_raw, k_raw, v_raw, conv_w, cu_seqlens, beta_logit, gate_
 
 
 def chunk_workspace_bytes(H, d, cu_seqlens_host):
-    h = cu_seqlens_host.to("cpu", torch.int32).contiguous()
+    """Workspace bytes for a batch shaped like ``cu_seqlens_host`` (the ABI
+    sizes it from the sequence count and the token total only)."""
+    h = cu_seqlens_host.to("cpu", torch.int32)
     g = geom(H, d, 4)
-    return int(load().kda_chunk_workspace_bytes(ctypes.byref(g), h.numel() - 1,
-                                                ctypes.cast(h.data_ptr(), ctypes.c_void_p)))
+    return int(load().kda_chunk_workspace_bytes(ctypes.byref(g), h.numel() - 1, int(h[-1])))
 
 
 def chunk_workspace(H, d, cu_seqlens_host, device):
@@ -195,17 +196,16 @@ def chunk_forward(q, k, v, log_alpha, beta, gate, cu_seqlens, initial_state=None
     if final_state is None and want_final_state:
         final_state = torch.empty((n, H, d, d), dtype=torch.float32, device=q.device)
     g = geom(H, d, 4, scale=scale)
-    _check(load().kda_chunk_forward(ctypes.byref(g), n, T, _ptr(cu_seqlens), hptr, _dtype(q), _ptr(q), _ptr(k),
+    _check(load().kda_chunk_forward(ctypes.byref(g), n, T, _ptr(cu_seqlens), hptr, _dtype(q), CHUNK, _ptr(q), _ptr(k),
                                     _ptr(v), _ptr(log_alpha), _ptr(beta), _ptr(gate), _ptr(initial_state),
                                     _ptr(final_state), _ptr(out), _ptr(workspace), workspace.numel(), _stream(q)))
     return out, final_state
 
 
 def chunk_backward_workspace_bytes(H, d, cu_seqlens_host):
-    h = cu_seqlens_host.to("cpu", torch.int32).contiguous()
+    h = cu_seqlens_host.to("cpu", torch.int32)
     g = geom(H, d, 4)
-    return int(load().kda_chunk_backward_workspace_bytes(ctypes.byref(g), h.numel() - 1,
-                                                         ctypes.cast(h.data_ptr(), ctypes.c_void_p)))
+    return int(load().kda_chunk_backward_workspace_bytes(ctypes.byref(g), h.numel() - 1, int(h[-1])))
 
 
 def chunk_backward(q, k, v, log_alpha, beta, gate, cu_seqlens, dy, initial_state=None, d_final_state=None, *,
@@ -268,7 +268,7 @@ def prefill(q_raw, k_raw, v_raw, conv_w, log_alpha, beta_logit, gate_logit, cu_s
     if final_state is None and want_final_state:
         final_state = torch.empty((n, H, d, d), dtype=torch.float32, device=q_raw.device)
     g = geom(H, d, K, act, eps, scale)
-    _check(load().kda_prefill(ctypes.byref(g), n, T, _ptr(cu_seqlens), hptr, _dtype(q_raw), _ptr(q_raw),
+    _check(load().kda_prefill(ctypes.byref(g), n, T, _ptr(cu_seqlens), hptr, _dtype(q_raw), CHUNK, _ptr(q_raw),
                               _ptr(k_raw), _ptr(v_raw), _ptr(conv_w), _ptr(conv_cache_in), _ptr(conv_cache_out),
                               _ptr(log_alpha), _ptr(beta_logit), _ptr(gate_logit), _ptr(initial_state),
                               _ptr(final_state), _ptr(out), _ptr(workspace), workspace.numel(), _stream(q_raw)))

@@ -40,6 +40,10 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
 
     const int b = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
     const int slot = p.slot_idx ? p.slot_idx[b] : b;
+    // A row whose slot lies outside [0, n_slots) is skipped whole (the slot
+    // is block-uniform, so the early exit is before every barrier): nothing
+    // of it is read or written, its output row included.
+    if ((unsigned)slot >= (unsigned)p.n_slots) return;
     const int C = p.H * D;
     const long row = ((long)b * p.H + h) * D;   // [b][h][0] of the per-row inputs
     const int Km1 = p.K - 1;

@@ -75,6 +75,20 @@ kda_status check_seqlens(int32_t n_seqs, int32_t total_tokens, const int32_t *cu
     return KDA_OK;
 }
 
+// Most chunks n sequences of T tokens in all can have: sequence i has
+// ceil(L_i / 64) = floor((L_i + 63) / 64), and a sum of floors is at most the
+// floor of the sum.  Workspace sizes are computed from this bound, so the
+// caller needs only the two totals.
+long chunk_bound(int32_t n_seqs, int32_t total_tokens) {
+    return ((long)total_tokens + (long)(kda::kChunk - 1) * n_seqs) / kda::kChunk;
+}
+
+kda_status check_chunk_len(int32_t chunk) {
+    if (chunk != kda::kChunk)
+        return fail(KDA_ERR_UNSUPPORTED, "chunk = %d: the chunk path uses 64-token chunks only", chunk);
+    return KDA_OK;
+}
+
 kda_status check_dtype(kda_dtype t) {
     if (t != KDA_F32 && t != KDA_BF16) return fail(KDA_ERR_DTYPE, "dtype %d is not a kda_dtype", (int)t);
     return KDA_OK;
@@ -172,12 +186,10 @@ kda::ChunkParams chunk_params(const kda_geom *geom, int32_t n_seqs, int32_t tota
 
 extern "C" {
 
-size_t kda_chunk_backward_workspace_bytes(const kda_geom *geom, int32_t n_seqs, const int32_t *cu_seqlens_host) {
+size_t kda_chunk_backward_workspace_bytes(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens) {
     if (check_geom(geom, true) != KDA_OK) return 0;
-    if (n_seqs <= 0 || !cu_seqlens_host) return 0;
-    long n_chunks = 0;
-    if (check_seqlens(n_seqs, cu_seqlens_host[n_seqs], cu_seqlens_host, &n_chunks) != KDA_OK) return 0;
-    return kda::bwd_workspace_bytes(geom->H, n_seqs, n_chunks);
+    if (n_seqs <= 0 || total_tokens < 0) return 0;
+    return kda::bwd_workspace_bytes(geom->H, n_seqs, chunk_bound(n_seqs, total_tokens));
 }
 
 kda_status kda_chunk_backward(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
@@ -357,12 +369,10 @@ kda_status kda_prologue_backward(const kda_geom *geom, int32_t n_seqs, int32_t t
     return launched(kda::launch_prologue_backward(p, (int)in_dtype, (hipStream_t)stream), "prologue backward");
 }
 
-size_t kda_chunk_workspace_bytes(const kda_geom *geom, int32_t n_seqs, const int32_t *cu_seqlens_host) {
+size_t kda_chunk_workspace_bytes(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens) {
     if (check_geom(geom, true) != KDA_OK) return 0;
-    if (n_seqs <= 0 || !cu_seqlens_host) return 0;
-    long n_chunks = 0;
-    if (check_seqlens(n_seqs, cu_seqlens_host[n_seqs], cu_seqlens_host, &n_chunks) != KDA_OK) return 0;
-    return kda::chunk_workspace_bytes(geom->H, n_seqs, n_chunks);
+    if (n_seqs <= 0 || total_tokens < 0) return 0;
+    return kda::chunk_workspace_bytes(geom->H, n_seqs, chunk_bound(n_seqs, total_tokens));
 }
 
 kda_status kda_chunk_prepare(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
@@ -405,10 +415,11 @@ kda_status kda_chunk_scan(const kda_geom *geom, int32_t n_seqs, int32_t total_to
 
 kda_status kda_chunk_forward(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
                              const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host, kda_dtype in_dtype,
-                             const void *q, const void *k, const void *v, const void *log_alpha,
+                             int32_t chunk, const void *q, const void *k, const void *v, const void *log_alpha,
                              const float *beta, const void *gate, const float *initial_state, float *final_state,
                              void *out, void *workspace, size_t workspace_bytes, void *stream) {
     // validate everything the two stages need before launching either
+    KDA_TRY(check_chunk_len(chunk));
     long n_chunks = 0;
     KDA_TRY(check_chunk_common(geom, n_seqs, total_tokens, cu_seqlens_dev, cu_seqlens_host, in_dtype, workspace,
                                workspace_bytes, &n_chunks));
@@ -502,12 +513,13 @@ kda_status kda_prefill_scan(const kda_geom *geom, int32_t n_seqs, int32_t total_
 }
 
 kda_status kda_prefill(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens, const int32_t *cu_seqlens_dev,
-                       const int32_t *cu_seqlens_host, kda_dtype in_dtype, const void *q_raw, const void *k_raw,
-                       const void *v_raw, const float *conv_w, const float *conv_cache_in, float *conv_cache_out,
-                       const void *log_alpha, const void *beta_logit, const void *gate_logit,
-                       const float *initial_state, float *final_state, void *out, void *workspace,
-                       size_t workspace_bytes, void *stream) {
+                       const int32_t *cu_seqlens_host, kda_dtype in_dtype, int32_t chunk, const void *q_raw,
+                       const void *k_raw, const void *v_raw, const float *conv_w, const float *conv_cache_in,
+                       float *conv_cache_out, const void *log_alpha, const void *beta_logit,
+                       const void *gate_logit, const float *initial_state, float *final_state, void *out,
+                       void *workspace, size_t workspace_bytes, void *stream) {
     // validate what both stages need before launching either
+    KDA_TRY(check_chunk_len(chunk));
     long n_chunks = 0;
     KDA_TRY(check_chunk_common(geom, n_seqs, total_tokens, cu_seqlens_dev, cu_seqlens_host, in_dtype, workspace,
                                workspace_bytes, &n_chunks));

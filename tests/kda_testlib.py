@@ -59,7 +59,21 @@ def chunk_tol_violations(got, want):
 def assert_chunk_close(got, want, what):
     nbad, maxabs, maxrel = chunk_tol_violations(got, want)
     assert nbad == 0, f"{what}: {nbad} elements outside 2e-2 + 1e-2|ref| (max abs {maxabs:.3e})"
+    report(what, got, want)
     return maxabs
+
+
+def report(what, got, want, bar="chunk"):
+    """Print one line of error figures for the log of a GPU run: max abs error,
+    max abs of the reference, and the largest fraction of the bar any element
+    uses (bar "chunk": 2e-2 + 1e-2|ref|; "fp32": 1e-5)."""
+    got = np64(got) if torch.is_tensor(got) else got
+    if got.size == 0:
+        return
+    err = np.abs(got - want)
+    lim = 2e-2 + 1e-2 * np.abs(want) if bar == "chunk" else np.full_like(want, 1e-5)
+    print(f"PARITY {what}: max_abs {err.max():.3e} max_ref {np.abs(want).max():.3e} "
+          f"bar_frac {(err / lim).max():.3f}", flush=True)
 
 
 def assert_fp32_close(got, want, what, tol=1e-5):

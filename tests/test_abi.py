@@ -151,20 +151,38 @@ def test_prologue_rejects_pointers(L):
 
 
 def test_chunk_workspace_bytes(L):
-    t, hp = _cu([0, 100, 100, 228])
-    n_chunks = 2 + 0 + 2
+    # 3 sequences, 228 tokens: at most (228 + 3 * 63) // 64 = 6 chunks (e.g.
+    # lengths 100, 0, 128 have 4; 1, 1, 226 have 6)
+    n_chunks = 6
     al = lambda x: (x + 255) // 256 * 256
     want = al(4 * 4) + al(16 * n_chunks) + n_chunks * 32 * 74240
-    assert L.kda_chunk_workspace_bytes(_geom(H=32), 3, hp) == want
-    assert L.kda_chunk_workspace_bytes(_geom(H=32, d=64), 3, hp) == 0
-    assert L.kda_chunk_workspace_bytes(None, 3, hp) == 0
+    assert L.kda_chunk_workspace_bytes(_geom(H=32), 3, 228) == want
+    assert L.kda_chunk_workspace_bytes(_geom(H=32), 1, 4096) == al(8) + al(16 * 64) + 64 * 32 * 74240
+    assert L.kda_chunk_workspace_bytes(_geom(H=32, d=64), 3, 228) == 0
+    assert L.kda_chunk_workspace_bytes(None, 3, 228) == 0
+    assert L.kda_chunk_workspace_bytes(_geom(H=32), 0, 228) == 0
+    assert L.kda_chunk_workspace_bytes(_geom(H=32), 3, -1) == 0
 
 
-def chunk_forward(L, geom=None, dtype=1, ws=FAKE[16], ws_bytes=1 << 40, ptrs=None, cu_vals=(0, 100, 228)):
+def test_chunk_bound_covers_every_split():
+    """The sizing bound is at least the chunk count of every split of the
+    total into n sequences (checked exhaustively for small totals)."""
+    import itertools
+    for n, T_max in ((1, 300), (2, 300), (3, 140)):
+        for T in range(T_max):
+            bound = (T + 63 * n) // 64
+            worst = 0
+            for cuts in itertools.combinations_with_replacement(range(T + 1), n - 1):
+                edges = (0,) + cuts + (T,)
+                worst = max(worst, sum((b - a + 63) // 64 for a, b in zip(edges, edges[1:])))
+            assert worst <= bound, (n, T)
+
+
+def chunk_forward(L, geom=None, dtype=1, ws=FAKE[16], ws_bytes=1 << 40, ptrs=None, cu_vals=(0, 100, 228), chunk=64):
     t, hp = _cu(list(cu_vals))
     p = list(FAKE[:9]) if ptrs is None else ptrs
     return L.kda_chunk_forward(geom if geom is not None else _geom(), len(cu_vals) - 1, cu_vals[-1], FAKE[15], hp,
-                               dtype, *p, ws, ws_bytes, None)
+                               dtype, chunk, *p, ws, ws_bytes, None)
 
 
 def test_chunk_rejects(L):
@@ -175,6 +193,8 @@ def test_chunk_rejects(L):
     assert chunk_forward(L, ws_bytes=1000) == WORKSPACE
     assert chunk_forward(L, ws=ctypes.c_void_p(0x10010 + 8)) == ALIGN
     assert chunk_forward(L, cu_vals=(0, 100, 50)) == SEQLENS
+    assert chunk_forward(L, chunk=32) == UNSUP
+    assert chunk_forward(L, chunk=0) == UNSUP
     p = list(FAKE[:9])
     p[3] = None   # log_alpha
     assert chunk_forward(L, ptrs=p) == NULL
@@ -186,11 +206,11 @@ def test_chunk_rejects(L):
     assert chunk_forward(L, ptrs=p) == ALIGN
 
 
-def prefill(L, geom=None, dtype=1, ws=FAKE[16], ws_bytes=1 << 40, ptrs=None, cu_vals=(0, 100, 228)):
+def prefill(L, geom=None, dtype=1, ws=FAKE[16], ws_bytes=1 << 40, ptrs=None, cu_vals=(0, 100, 228), chunk=64):
     t, hp = _cu(list(cu_vals))
     p = list(FAKE[:12]) if ptrs is None else ptrs
     return L.kda_prefill(geom if geom is not None else _geom(), len(cu_vals) - 1, cu_vals[-1], FAKE[15], hp,
-                         dtype, *p, ws, ws_bytes, None)
+                         dtype, chunk, *p, ws, ws_bytes, None)
 
 
 def test_prefill_rejects(L):
@@ -199,6 +219,7 @@ def test_prefill_rejects(L):
     assert prefill(L, dtype=0) == UNSUP
     assert prefill(L, ws_bytes=10) == WORKSPACE
     assert prefill(L, cu_vals=(2, 100, 228)) == SEQLENS
+    assert prefill(L, chunk=128) == UNSUP
     for i, name in ((0, "q_raw"), (3, "conv_w"), (6, "log_alpha"), (7, "beta_logit"), (11, "out")):
         p = list(FAKE[:12])
         p[i] = None
@@ -219,10 +240,9 @@ def backward(L, geom=None, dtype=1, ws=FAKE[16], ws_bytes=1 << 40, ptrs=None, cu
 
 
 def test_backward_workspace_bytes(L):
-    t, hp = _cu([0, 100, 100, 228])
     al = lambda x: (x + 255) // 256 * 256
-    assert L.kda_chunk_backward_workspace_bytes(_geom(H=2), 3, hp) == al(4 * 4) + al(16 * 4) + 4 * 2 * 573952
-    assert L.kda_chunk_backward_workspace_bytes(_geom(H=2, d=64), 3, hp) == 0
+    assert L.kda_chunk_backward_workspace_bytes(_geom(H=2), 3, 228) == al(4 * 4) + al(16 * 6) + 6 * 2 * 573952
+    assert L.kda_chunk_backward_workspace_bytes(_geom(H=2, d=64), 3, 228) == 0
 
 
 def test_backward_rejects(L):

@@ -19,7 +19,7 @@ import kda_inputs as ki
 import kimi_delta_attention_07_amd as kda
 import oracle
 from kda_testlib import (assert_bf16_rounding, assert_chunk_close, assert_fp32_close, gpu_prefill,
-                         gpu_prefill_fused, np64, slice_heads, slice_seqs, to_dev)
+                         gpu_prefill_fused, np64, report, slice_heads, slice_seqs, to_dev)
 
 pytestmark = pytest.mark.gpu
 ORC = oracle.get()
@@ -83,6 +83,31 @@ def test_decode_slot_map_and_dims(d):
     assert_fp32_close(gst, st, "state")
     untouched = sorted(set(range(9)) - set(dec["slot_idx"].tolist()))
     assert torch.equal(gst.cpu()[untouched], before[untouched])
+
+
+def test_decode_out_of_range_slot_is_skipped():
+    """Rows whose slot index lies outside [0, n_slots) (one past the end, one
+    negative) are skipped: their output rows keep what was there, no slot's
+    state or conv cache changes through them, and the other rows match the
+    oracle."""
+    dec = ki.decode_inputs(48, 4, H=2, d=64, K=4, steps=1, n_slots=6, state_std=0.1)
+    step = dec["steps"][0]
+    slot_idx = torch.tensor([2, 6, 5, -1], dtype=torch.int32)
+    good = [0, 2]
+    st = dec["state"].double().numpy().copy()
+    ca = dec["conv_cache"].double().numpy().copy()
+    sub = {k: v[good].contiguous() for k, v in step.items()}
+    want = ORC.decode_step(st, ca, dec["conv_w"], sub, slot_idx=slot_idx[good])
+    gst, gca = dec["state"].cuda(), dec["conv_cache"].cuda()
+    s = _step_dev(step)
+    out = torch.full((4, 2, 64), 7.0, device="cuda")
+    kda.decode_step(s["q_raw"], s["k_raw"], s["v_raw"], dec["conv_w"].cuda(), gca, gst, s["log_alpha"],
+                    s["beta_logit"], s["gate_logit"], slot_idx.cuda(), out=out)
+    torch.cuda.synchronize()
+    assert_fp32_close(out[good], want, "rows with valid slots")
+    assert torch.all(out[[1, 3]].cpu() == 7.0), "a skipped row's output was written"
+    assert_fp32_close(gst, st, "state")
+    assert_fp32_close(gca, ca, "conv cache", 0.0)
 
 
 def test_decode_bf16_output_and_no_gate():
@@ -363,36 +388,73 @@ def test_prefill_T4096_full():
     print(f"T=4096 full: max |err| y {e[0]:.2e} final state {e[1]:.2e}")
 
 
-def test_prefill_varlen_full_sampled():
-    """32 packed sequences (lengths U[256, 8192]); oracle on sampled sequences x heads."""
+@pytest.fixture(scope="module")
+def varlen_case():
+    """32 packed sequences (lengths U[256, 8192]); the oracle on the shortest,
+    the longest, the first and one more sequence, each on three heads."""
     inp = ki.config_prefill(3)
-    res = gpu_prefill(inp)
     lens = inp["lengths"]
     seqs = sorted({0, int(np.argmax(lens)), int(np.argmin(lens)), 17})
     heads = [0, 13, 31]
-    sub = slice_heads(slice_seqs(inp, seqs), heads)
-    ref = ORC.prefill(sub)
+    ref = ORC.prefill(slice_heads(slice_seqs(inp, seqs), heads))
+    return inp, seqs, heads, ref
+
+
+@pytest.mark.parametrize("path", ["fused", "unfused"])
+def test_prefill_varlen_full_sampled(varlen_case, path):
+    """The packed varlen workload in full, in the launch configuration the
+    benchmark times (fused: kda_prefill) and through the three-call path;
+    sampled sequences x heads against the oracle, conv cache of every
+    sequence exactly."""
+    inp, seqs, heads, ref = varlen_case
+    res = gpu_prefill_fused(inp) if path == "fused" else gpu_prefill(inp)
     cu = inp["cu_seqlens"].tolist()
     y = torch.cat([res["y"][cu[n]:cu[n + 1]] for n in seqs])[:, heads]
     S = res["final_state"][seqs][:, heads]
-    e1 = assert_chunk_close(y, ref["y"], "varlen y")
-    e2 = assert_chunk_close(S, ref["final_state"], "varlen final state")
-    print(f"varlen T={inp['T']}: sampled max |err| y {e1:.2e} S {e2:.2e}")
+    e1 = assert_chunk_close(y, ref["y"], f"varlen {path} y")
+    e2 = assert_chunk_close(S, ref["final_state"], f"varlen {path} final state")
+    # the outgoing conv cache of every sequence: the last 3 raw rows, exactly
+    K1 = inp["conv_w"].shape[2] - 1
+    cc = np64(res["conv_cache"])
+    for n in range(inp["N"]):
+        for X, key in enumerate(("q_raw", "k_raw", "v_raw")):
+            want = inp[key][cu[n + 1] - K1:cu[n + 1]].double().reshape(K1, -1).numpy()
+            assert np.array_equal(cc[n, X], want), f"conv cache of sequence {n}, stream {X}"
+    print(f"varlen {path} T={inp['T']}: sampled max |err| y {e1:.2e} S {e2:.2e}")
+    del res
+    torch.cuda.empty_cache()
 
 
-def test_prefill_T65536_full_sampled_and_decode_tail():
-    """T=65536 with slow decay (1024 chunks); oracle on two heads; then 128
-    decode tokens from the GPU's final state and conv cache (fp32 bar)."""
+@pytest.fixture(scope="module")
+def long_case():
+    """T=65536 with slow decay (1024 chunks); the oracle on heads 0 and 31."""
     inp = ki.config_prefill(4)
-    res = gpu_prefill(inp)
     heads = [0, 31]
     ref = ORC.prefill(slice_heads(inp, heads))
-    e1 = assert_chunk_close(res["y"][:, heads], ref["y"], "T=65536 y")
-    e2 = assert_chunk_close(res["final_state"][:, heads], ref["final_state"], "T=65536 final state")
-    print(f"T=65536: sampled max |err| y {e1:.2e} S {e2:.2e}")
+    return inp, heads, ref
+
+
+@pytest.mark.parametrize("path", ["fused", "unfused"])
+def test_prefill_T65536_full_sampled_and_decode_tail(long_case, path):
+    """T=65536 in full (fused: the benchmark's kda_prefill launch), two heads
+    against the oracle, the conv cache exactly; then 128 decode tokens that
+    continue from this path's own final state and conv cache, every output
+    and the state after them against the oracle at the fp32 bar."""
+    inp, heads, ref = long_case
+    res = gpu_prefill_fused(inp) if path == "fused" else gpu_prefill(inp)
+    e1 = assert_chunk_close(res["y"][:, heads], ref["y"], f"T=65536 {path} y")
+    e2 = assert_chunk_close(res["final_state"][:, heads], ref["final_state"], f"T=65536 {path} final state")
+    K1 = inp["conv_w"].shape[2] - 1
+    for X, key in enumerate(("q_raw", "k_raw", "v_raw")):
+        want = inp[key][-K1:].double().reshape(K1, -1).numpy()
+        assert np.array_equal(np64(res["conv_cache"])[0, X], want), f"conv cache stream {X}"
+    print(f"T=65536 {path}: sampled max |err| y {e1:.2e} S {e2:.2e}")
     dec = dict(state=res["final_state"].cpu(), conv_cache=res["conv_cache"].cpu(), conv_w=inp["conv_w"],
                slot_idx=None, steps=inp["tail"])
+    del res
+    torch.cuda.empty_cache()
     errs, (gst, st), _ = run_decode(dec)
     worst = max(assert_fp32_close(got, want, f"tail y step {t}") for t, (got, want) in enumerate(errs))
     assert_fp32_close(gst, st, "tail state")
-    print(f"decode tail 128 steps: worst |y err| {worst:.2e}")
+    report(f"T=65536 {path} decode tail y (worst step)", errs[-1][0], errs[-1][1], bar="fp32")
+    print(f"decode tail after {path} prefill, 128 steps: worst |y err| {worst:.2e}")
