@@ -220,6 +220,34 @@ kda_status kda_prefill_scan(const kda_geom *geom, int32_t n_seqs, int32_t total_
                             void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * kda_prefill_noalloc: kda_prefill for callers that cannot allocate device
+ * memory -- code under HIP graph capture, serving loops and harnesses that
+ * forbid hipMalloc.  It takes no workspace and calls no allocating routine:
+ * the chunk workspace is a fixed array of KDA_NOALLOC_SCRATCH_BYTES bytes
+ * inside the library, one per GPU, held until the process ends.  Arguments
+ * and results are kda_prefill's (the same kernels: identical bits).
+ *   Limit: a batch whose chunk workspace (kda_chunk_workspace_bytes's count
+ *   for its exact chunks: 74,240 B per (chunk, head) plus a small table) is
+ *   larger than the scratch is rejected with KDA_ERR_WORKSPACE before
+ *   anything is launched -- at most 903 (chunk, head) pairs, e.g. one
+ *   1,792-token sequence at 32 heads or 14,400 tokens at 4 heads.
+ *   Nothing in the scratch needs to start at zero: every byte a call reads
+ *   was written earlier in the same call.  All calls on one GPU share its
+ *   scratch, which keeps the last call's contents: calls that may overlap on
+ *   one GPU (other streams, other threads) race, and the caller must order
+ *   them.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES (64u * 1024u * 1024u)
+
+kda_status kda_prefill_noalloc(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
+                               const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host,
+                               kda_dtype in_dtype, int32_t chunk, const void *q_raw, const void *k_raw,
+                               const void *v_raw, const float *conv_w, const float *conv_cache_in,
+                               float *conv_cache_out, const void *log_alpha, const void *beta_logit,
+                               const void *gate_logit, const float *initial_state, float *final_state,
+                               void *out, void *stream);
+
+/*
  * kda_decode_step: one token for each of `batch` rows, fused: conv-cache
  * shift and conv, activation, L2(q, k), sigmoid gates, then one step of the
  * recurrence on the row's resident state, read and written once.

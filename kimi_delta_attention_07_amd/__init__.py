@@ -6,6 +6,7 @@ include/kda.h); this package is its thin Python binding:
     prologue(...)       short conv + activation + L2(q, k) + sigmoid gates
     chunk_forward(...)  chunked prefill over packed varlen sequences
     prefill(...)        the same from raw inputs, prologue fused into the chunk path
+    prefill_noalloc(...) prefill() on the library's fixed per-GPU scratch (no workspace)
     chunk_backward(...) gradients of chunk_forward
     prologue_backward(...) gradients of prologue, back to the raw inputs and conv taps
     decode_step(...)    one token for a batch of resident fp32 states
@@ -26,6 +27,7 @@ from ._lib import (  # noqa: F401
     decode_step,
     load,
     prefill,
+    prefill_noalloc,
     prefill_prepare,
     prefill_scan,
     prologue,

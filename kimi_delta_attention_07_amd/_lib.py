@@ -22,7 +22,7 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE"
 EXPORTS = ("kda_prologue", "kda_chunk_workspace_bytes", "kda_chunk_forward", "kda_chunk_prepare",
            "kda_chunk_scan", "kda_prefill", "kda_prefill_prepare", "kda_prefill_scan", "kda_decode_step",
            "kda_chunk_backward_workspace_bytes", "kda_chunk_backward", "kda_prologue_backward_workspace_bytes",
-           "kda_prologue_backward", "kda_status_str", "kda_last_error_detail")
+           "kda_prologue_backward", "kda_prefill_noalloc", "kda_status_str", "kda_last_error_detail")
 
 
 class KdaError(RuntimeError):
@@ -75,6 +75,8 @@ def load(path=LIB_PATH):
     L.kda_prefill_prepare.restype = _I
     L.kda_prefill_scan.argtypes = [G, _I, _I, _P, _P, _I] + [_P] * 5 + [ctypes.c_size_t, _P]
     L.kda_prefill_scan.restype = _I
+    L.kda_prefill_noalloc.argtypes = [G, _I, _I, _P, _P, _I, _I] + [_P] * 12 + [_P]
+    L.kda_prefill_noalloc.restype = _I
     L.kda_decode_step.argtypes = [G, _I, _P, _I, _I] + [_P] * 9 + [_I, _P, _P]
     L.kda_decode_step.restype = _I
     L.kda_status_str.argtypes = [_I]
@@ -272,6 +274,28 @@ def prefill(q_raw, k_raw, v_raw, conv_w, log_alpha, beta_logit, gate_logit, cu_s
                               _ptr(k_raw), _ptr(v_raw), _ptr(conv_w), _ptr(conv_cache_in), _ptr(conv_cache_out),
                               _ptr(log_alpha), _ptr(beta_logit), _ptr(gate_logit), _ptr(initial_state),
                               _ptr(final_state), _ptr(out), _ptr(workspace), workspace.numel(), _stream(q_raw)))
+    return out, final_state
+
+
+def prefill_noalloc(q_raw, k_raw, v_raw, conv_w, log_alpha, beta_logit, gate_logit, cu_seqlens, initial_state=None,
+                    conv_cache_in=None, conv_cache_out=None, *, final_state=None, out=None, act="silu", eps=1e-6,
+                    scale=1.0, cu_seqlens_host=None, want_final_state=True):
+    """prefill() through kda_prefill_noalloc: no workspace argument, the
+    library's fixed per-GPU scratch instead (output tensors are still
+    allocated here unless passed in).  Returns (out, final_state)."""
+    T, H, d = q_raw.shape
+    K = conv_w.shape[2]
+    n = cu_seqlens.numel() - 1
+    hcu, hptr = _host_cu(cu_seqlens, cu_seqlens_host)
+    if out is None:
+        out = torch.empty_like(v_raw)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((n, H, d, d), dtype=torch.float32, device=q_raw.device)
+    g = geom(H, d, K, act, eps, scale)
+    _check(load().kda_prefill_noalloc(ctypes.byref(g), n, T, _ptr(cu_seqlens), hptr, _dtype(q_raw), CHUNK,
+                                      _ptr(q_raw), _ptr(k_raw), _ptr(v_raw), _ptr(conv_w), _ptr(conv_cache_in),
+                                      _ptr(conv_cache_out), _ptr(log_alpha), _ptr(beta_logit), _ptr(gate_logit),
+                                      _ptr(initial_state), _ptr(final_state), _ptr(out), _stream(q_raw)))
     return out, final_state
 
 

@@ -10,6 +10,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 #include "kda_internal.h"
@@ -180,6 +181,35 @@ kda::ChunkParams chunk_params(const kda_geom *geom, int32_t n_seqs, int32_t tota
         }
     }
     return p;
+}
+
+// Scratch of kda_prefill_noalloc: the chunk workspace of callers that cannot
+// allocate.  Each GPU the library runs on holds its own copy for the life of
+// the process.  In host code `scratch` names a host-side stand-in, never the
+// device memory: its device address is taken once per device with
+// hipGetSymbolAddress and only that address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[KDA_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[64];
+
+// Device address of `scratch` on the current device (looked up on the first
+// call on that device, with it current).
+kda_status scratch_address(void **out) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "hipGetDevice: %s", hipGetErrorString(e));
+    if (dev < 0 || dev >= 64) return fail(KDA_ERR_UNSUPPORTED, "device ordinal %d out of range", dev);
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr)
+            return fail(KDA_ERR_HIP, "hipGetSymbolAddress(scratch) on device %d: %s", dev, hipGetErrorString(e));
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return KDA_OK;
 }
 
 }  // namespace
@@ -577,6 +607,45 @@ kda_status kda_decode_step(const kda_geom *geom, int32_t batch, const int32_t *s
     p.state = state;
     p.out = out;
     return launched(kda::launch_decode(p, (int)in_dtype, (int)out_dtype, (hipStream_t)stream), "decode");
+}
+
+kda_status kda_prefill_noalloc(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
+                               const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host, kda_dtype in_dtype,
+                               int32_t chunk, const void *q_raw, const void *k_raw, const void *v_raw,
+                               const float *conv_w, const float *conv_cache_in, float *conv_cache_out,
+                               const void *log_alpha, const void *beta_logit, const void *gate_logit,
+                               const float *initial_state, float *final_state, void *out, void *stream) {
+    // Host checks first (nothing here touches a device), then the size limit.
+    KDA_TRY(check_chunk_len(chunk));
+    KDA_TRY(check_geom(geom, true));
+    long n_chunks = 0;
+    KDA_TRY(check_seqlens(n_seqs, total_tokens, cu_seqlens_host, &n_chunks));
+    const size_t need = kda::chunk_workspace_bytes(geom->H, n_seqs, n_chunks);
+    if (need > (size_t)KDA_NOALLOC_SCRATCH_BYTES)
+        return fail(KDA_ERR_WORKSPACE,
+                    "kda_prefill_noalloc: this batch needs %zu bytes of chunk workspace (%ld chunks x %d heads x "
+                    "74,240 B + table), more than its fixed scratch of %zu bytes; use kda_prefill with a "
+                    "caller-allocated workspace",
+                    need, n_chunks, geom->H, (size_t)KDA_NOALLOC_SCRATCH_BYTES);
+    // The checks kda_prefill makes of its other arguments, here too, so that
+    // every invalid call is answered before a device is touched (the scratch
+    // address lookup needs one).
+    KDA_TRY(check_dtype(in_dtype));
+    if (in_dtype != KDA_BF16) return fail(KDA_ERR_UNSUPPORTED, "the chunk path takes bf16 inputs only");
+    KDA_TRY(check_required({{cu_seqlens_dev, "cu_seqlens_dev"}, {q_raw, "q_raw"}, {k_raw, "k_raw"},
+                            {v_raw, "v_raw"}, {conv_w, "conv_w"}, {log_alpha, "log_alpha"},
+                            {beta_logit, "beta_logit"}}));
+    if (total_tokens > 0) KDA_TRY(check_required({{out, "out"}}));
+    KDA_TRY(check_aligned({{q_raw, "q_raw"}, {k_raw, "k_raw"}, {v_raw, "v_raw"}, {conv_w, "conv_w"},
+                           {conv_cache_in, "conv_cache_in"}, {conv_cache_out, "conv_cache_out"},
+                           {log_alpha, "log_alpha"}, {beta_logit, "beta_logit"}, {gate_logit, "gate_logit"},
+                           {initial_state, "initial_state"}, {final_state, "final_state"}, {out, "out"}}));
+    KDA_TRY(check_device());
+    void *ws = nullptr;
+    KDA_TRY(scratch_address(&ws));
+    return kda_prefill(geom, n_seqs, total_tokens, cu_seqlens_dev, cu_seqlens_host, in_dtype, chunk, q_raw, k_raw,
+                       v_raw, conv_w, conv_cache_in, conv_cache_out, log_alpha, beta_logit, gate_logit,
+                       initial_state, final_state, out, ws, (size_t)KDA_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 }  // extern "C"

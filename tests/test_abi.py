@@ -38,6 +38,17 @@ def test_library_exports_every_declared_symbol(L):
         assert hasattr(L, name), name
 
 
+def test_binding_argument_counts_match_the_header(L):
+    """Each ctypes prototype declares exactly the parameters the header's
+    declaration has (ctypes would otherwise pass a shifted argument list)."""
+    src = open(HEADER).read()
+    decls = re.findall(r"^(?:kda_status|size_t|const char \*)\s*(kda_\w+)\s*\(([^;]*?)\)\s*;", src, re.M | re.S)
+    assert {n for n, _ in decls} == set(kda.EXPORTS)
+    for name, params in decls:
+        n = 0 if params.strip() == "void" else len(params.split(","))
+        assert len(getattr(L, name).argtypes) == n, name
+
+
 def test_missing_library_raises(tmp_path):
     saved = _lib._lib
     _lib._lib = None
