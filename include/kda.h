@@ -137,10 +137,13 @@ kda_status kda_prologue(const kda_geom *geom, int32_t n_seqs, int32_t total_toke
  * The result equals the token-by-token recurrence up to rounding.
  *
  *   q, k [T][H][128] bf16 (L2-normalised), v [T][H][128] bf16,
- *   log_alpha [T][H][128] bf16, <= 0; the chunk form multiplies by
- *     exp(+-cumulative log decay) within a chunk, so the sum of |log_alpha|
- *     over any 64 consecutive tokens of a channel must stay below 80
- *     (e.g. log_alpha >= -1.25 per token); beyond that results overflow;
+ *   log_alpha [T][H][128] bf16, <= 0.  Inside a chunk the decays enter
+ *     the matrix-core products as per-token factors: referenced to the chunk
+ *     start when every channel's decay over the chunk is at most 64 in log2
+ *     units, else to the ends of 16-token sub-chunks, where no factor
+ *     exceeds e^{(sum of |log_alpha| over one 16-token sub-chunk)}.  Bound:
+ *     that sum stays below 87 per channel (a per-token average above -5.4);
+ *     beyond it results overflow to inf/NaN;
  *   beta [T][H] fp32 (post-sigmoid), gate NULL or [T][H][128] bf16 (post-sigmoid);
  *   initial_state NULL (zeros) or [n_seqs][H][128][128] fp32;
  *   final_state NULL (skip) or same shape, may alias initial_state;
@@ -325,7 +328,9 @@ kda_status kda_prologue_backward(const kda_geom *geom, int32_t n_seqs, int32_t t
  *     (573,952 B per (chunk, head) plus the chunk table; sized, like
  *     kda_chunk_workspace_bytes, from the totals n_seqs and total_tokens).
  * Runs the forward's chunk quantities again (nothing from a forward call is
- * reused) and is stream-ordered like every other entry point.  Errors as for
+ * reused) and is stream-ordered like every other entry point.  Its decays
+ * are referenced to each chunk's start (fp32): the sum of |log_alpha| over
+ * each 64-token chunk must stay below 80 per channel.  Errors as for
  * kda_chunk_forward; nothing is launched when validation fails.
  */
 size_t kda_chunk_backward_workspace_bytes(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens);

@@ -10,8 +10,12 @@
 //     P = tril(sum_c q_ic k_jc e^{G_ic - G_jc})
 //     O = (Q e^G) S + P U,   S_next = Diag(e^{G_L}) S + (K e^{G_L - G})^T U
 // which equals the token loop exactly in exact arithmetic.  The decay factor
-// e^{G_i - G_j} is split as e^{G_i} e^{-G_j} with G counted from the chunk
-// start, so every product is an MFMA contraction over channels.
+// e^{G_i - G_j} is split into per-token factors so every product is an MFMA
+// contraction over channels: e^{G_i} e^{-G_j} with G counted from the chunk
+// start when the chunk's whole decay is small, otherwise through reference
+// points at the ends of 16-token sub-chunks, so that no factor exceeds the
+// decay of 16 tokens (see phase 1).  W, Q e^G, K e^{G_L - G} and e^{G_L} only
+// ever take e^{<= 0}.
 //
 // Two stages:
 //  prepare  grid chunks x heads (heads fastest), 256 threads.  Everything that does not
@@ -116,6 +120,36 @@ constexpr int kOffBeta = kOffTm + 64 * kRowT * 2;         // fp32 [64]
 constexpr int kLdsPrepare = kOffBeta + 64 * 4;            // 81,152 B: two workgroups per CU
 static_assert(3 * 64 * kRowA * 2 <= kRegionR, "phase-1 tiles must fit region R");
 static_assert(4 * 128 * 4 <= 64 * kRowT * 2, "cumsum totals alias the T tile");
+// Per-channel decay factors of the sub-chunk form (phases 1-2 only, in the T
+// tile after the totals): E_off[4] = e^{R_{w-1}}, Hd[4] = e^{R_{I-1} - R_I},
+// F[3] = e^{R_{I-1} - R_J} for (I, J) = (2, 0), (3, 1), (3, 0); fp32 [128] each.
+constexpr int kOffEoff = kOffTm + 4 * 128 * 4;
+constexpr int kOffHd = kOffEoff + 4 * 128 * 4;
+constexpr int kOffF = kOffHd + 4 * 128 * 4;
+static_assert(kOffF + 3 * 128 * 4 <= kOffTm + 64 * kRowT * 2, "decay factors alias the T tile");
+// A chunk whose total decay stays within this (log2 units, every channel) is
+// formed with every decay referenced to the chunk start: operands e^{+-G}
+// within 2^+-64.  Beyond it, the 16-token sub-chunk form.
+constexpr float kChunkStartRefMax = 64.0f;
+
+// compile-time flag for the two instances of the decay-dependent phases
+template <bool B>
+struct SubForm {
+    static constexpr bool value = B;
+};
+
+// 8 bf16 (one MFMA fragment: channels c0 .. c0 + 7) times 8 per-channel
+// factors, re-rounded to bf16.
+__device__ __forceinline__ bf16x8 scale_frag(const bf16x8 &x, const float *f) {
+    const u32x4 w = __builtin_bit_cast(u32x4, x);
+    const f32x4 f0 = *reinterpret_cast<const f32x4 *>(f), f1 = *reinterpret_cast<const f32x4 *>(f + 4);
+    u32x4 o;
+    o[0] = pack_bf2(lo_bf(w[0]) * f0[0], hi_bf(w[0]) * f0[1]);
+    o[1] = pack_bf2(lo_bf(w[1]) * f0[2], hi_bf(w[1]) * f0[3]);
+    o[2] = pack_bf2(lo_bf(w[2]) * f1[0], hi_bf(w[2]) * f1[1]);
+    o[3] = pack_bf2(lo_bf(w[3]) * f1[2], hi_bf(w[3]) * f1[3]);
+    return as_bf16x8(o);
+}
 
 // A (fp32 [64][64]) keeps the 16-byte column groups of row i XORed with
 // (i & 15): sixteen rows read at the same columns land in sixteen different
@@ -293,6 +327,45 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
     }
     const float2 egl = make_float2(__builtin_amdgcn_exp2f(GL.x), __builtin_amdgcn_exp2f(GL.y));   // e^{G_L}
     if (w == 0) *reinterpret_cast<float2 *>(rec + kOffGL + 8 * l) = egl;
+    // Reference points of the decays.  With R_J the cumulative log decay at
+    // the end of sub-chunk J (16 tokens; R_{-1} = 0), e^{G_i - G_j} for token
+    // i of sub-chunk I and j of J <= I is
+    //   e^{G_i - R_{I-1}} * e^{R_{I-1} - R_J} * e^{R_J - G_j},
+    // three factors <= 1 for J < I; for J = I the middle one is
+    // e^{R_{I-1} - R_I} >= 1, bounded by the decay of 16 tokens.  The row
+    // operands (K, Q of A and P) then carry e^{G_i - R_{I-1}}, the column
+    // operand K e^{R_J - G_j}, and phase 2 multiplies the column fragments by
+    // the middle factor.  When the whole chunk's decay is small (every
+    // channel's |G_L| <= kChunkStartRefMax) the chunk-start reference R = 0
+    // for all tokens is exact in range too and needs no factors: the block
+    // takes that form (the choice is the same in every wave: each reduces the
+    // same 128 totals).
+    float gmax = fmaxf(-GL.x, -GL.y);
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) gmax = fmaxf(gmax, __shfl_xor(gmax, o, 64));
+    // NaN decays take the sub-chunk form; readfirstlane makes the flag
+    // scalar, so every test of it below is a scalar branch
+    const bool sub = __builtin_amdgcn_readfirstlane((int)!(gmax <= kChunkStartRefMax)) != 0;
+    const float2 tw = make_float2(tot[w * 128 + 2 * l], tot[w * 128 + 2 * l + 1]);   // R_w - R_{w-1}
+    // e^G = el * eoff and e^{G_L - G} = ec * etail for the record's operands
+    float2 eoff = make_float2(1.f, 1.f), etail = egl;
+    if (sub) {   // block-uniform
+        eoff = make_float2(__builtin_amdgcn_exp2f(off.x), __builtin_amdgcn_exp2f(off.y));
+        etail = make_float2(__builtin_amdgcn_exp2f(GL.x - off.x - tw.x), __builtin_amdgcn_exp2f(GL.y - off.y - tw.y));
+        float *fv = reinterpret_cast<float *>(lds);
+        *reinterpret_cast<float2 *>(fv + kOffEoff / 4 + w * 128 + 2 * l) = eoff;
+        *reinterpret_cast<float2 *>(fv + kOffHd / 4 + w * 128 + 2 * l) =
+            make_float2(__builtin_amdgcn_exp2f(-tw.x), __builtin_amdgcn_exp2f(-tw.y));
+        if (w == 1) *reinterpret_cast<float2 *>(fv + kOffF / 4 + 0 * 128 + 2 * l) =
+            make_float2(__builtin_amdgcn_exp2f(tw.x), __builtin_amdgcn_exp2f(tw.y));
+        if (w == 2) {
+            const float2 t1 = make_float2(tot[128 + 2 * l], tot[128 + 2 * l + 1]);
+            *reinterpret_cast<float2 *>(fv + kOffF / 4 + 1 * 128 + 2 * l) =
+                make_float2(__builtin_amdgcn_exp2f(tw.x), __builtin_amdgcn_exp2f(tw.y));
+            *reinterpret_cast<float2 *>(fv + kOffF / 4 + 2 * 128 + 2 * l) =
+                make_float2(__builtin_amdgcn_exp2f(tw.x + t1.x), __builtin_amdgcn_exp2f(tw.y + t1.y));
+        }
+    }
     if constexpr (FUSED) {
         if (!(w == 0 && ci.first)) {   // otherwise halo holds the incoming cache rows
 #pragma unroll
@@ -322,132 +395,194 @@ __global__ __launch_bounds__(256, 2) void prepare_kernel(ChunkParams p) {
 #pragma unroll
                 for (int j = 0; j < 4; ++j) wc[X][e][j] *= kLog2e;
     }
+    // The token loop in two instances, one per decay form (block-uniform).
+    auto token_loop = [&](auto form) {
+        constexpr bool SUB = decltype(form)::value;
 #pragma unroll
-    for (int ii = 0; ii < 16; ++ii) {
-        const int tk = 16 * w + ii;
-        const float gx = G[ii].x + off.x, gy = G[ii].y + off.y;
-        float2 q2 = make_float2(0.f, 0.f), k2 = q2, v2 = q2;
-        if constexpr (FUSED) {
-            // conv over rows ii .. ii+3 of the window (row ii+3 is token tk)
-            float x[3][2];
+        for (int ii = 0; ii < 16; ++ii) {
+            const int tk = 16 * w + ii;
+            float2 q2 = make_float2(0.f, 0.f), k2 = q2, v2 = q2;
+            if constexpr (FUSED) {
+                // conv over rows ii .. ii+3 of the window (row ii+3 is token tk)
+                float x[3][2];
 #pragma unroll
-            for (int X = 0; X < 3; ++X) {
-                const uint32_t *u = X == 0 ? uq : (X == 1 ? uk : uv);
-                float a0 = 0.f, a1 = 0.f;
+                for (int X = 0; X < 3; ++X) {
+                    const uint32_t *u = X == 0 ? uq : (X == 1 ? uk : uv);
+                    float a0 = 0.f, a1 = 0.f;
 #pragma unroll
-                for (int j = 4 - KC; j < 4; ++j) {
-                    const int r = ii + j;
-                    const float2 v = r < 3 ? halo[X][r] : make_float2(lo_bf(u[r]), hi_bf(u[r]));
-                    a0 += wc[X][0][j] * v.x;
-                    a1 += wc[X][1][j] * v.y;
+                    for (int j = 4 - KC; j < 4; ++j) {
+                        const int r = ii + j;
+                        const float2 v = r < 3 ? halo[X][r] : make_float2(lo_bf(u[r]), hi_bf(u[r]));
+                        a0 += wc[X][0][j] * v.x;
+                        a1 += wc[X][1][j] * v.y;
+                    }
+                    // with SiLU the taps carry log2 e (see below): x = log2e * silu(conv)
+                    x[X][0] = ACT == 1 ? a0 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a0)) : a0;
+                    x[X][1] = ACT == 1 ? a1 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a1)) : a1;
                 }
-                // with SiLU the taps carry log2 e (see below): x = log2e * silu(conv)
-                x[X][0] = ACT == 1 ? a0 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a0)) : a0;
-                x[X][1] = ACT == 1 ? a1 * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-a1)) : a1;
+                const float r = __builtin_amdgcn_rsqf(
+                    wave_sum_pair(x[0][0] * x[0][0] + x[0][1] * x[0][1], x[1][0] * x[1][0] + x[1][1] * x[1][1]) + eps_n);
+                // tokens past the end: q, k scaled to 0 (their conv window still
+                // holds real rows); v needs nothing, every product of v carries
+                // beta = 0
+                const bool live = tk < len;
+                const float rq = live ? lane_value(r, 0) : 0.0f, rk = live ? lane_value(r, 16) : 0.0f;
+                q2 = make_float2(x[0][0] * rq, x[0][1] * rq);
+                k2 = make_float2(x[1][0] * rk, x[1][1] * rk);
+                v2 = make_float2(x[2][0], x[2][1]);
+            } else {   // rows past the end are 0
+                q2 = make_float2(lo_bf(uq[ii]), hi_bf(uq[ii]));
+                k2 = make_float2(lo_bf(uk[ii]), hi_bf(uk[ii]));
+                v2 = make_float2(lo_bf(uv[ii]), hi_bf(uv[ii]));
             }
-            const float r = __builtin_amdgcn_rsqf(
-                wave_sum_pair(x[0][0] * x[0][0] + x[0][1] * x[0][1], x[1][0] * x[1][0] + x[1][1] * x[1][1]) + eps_n);
-            // tokens past the end: q, k scaled to 0 (their conv window still
-            // holds real rows); v needs nothing, every product of v carries
-            // beta = 0
-            const bool live = tk < len;
-            const float rq = live ? lane_value(r, 0) : 0.0f, rk = live ? lane_value(r, 16) : 0.0f;
-            q2 = make_float2(x[0][0] * rq, x[0][1] * rq);
-            k2 = make_float2(x[1][0] * rk, x[1][1] * rk);
-            v2 = make_float2(x[2][0], x[2][1]);
-        } else {   // rows past the end are 0
-            q2 = make_float2(lo_bf(uq[ii]), hi_bf(uq[ii]));
-            k2 = make_float2(lo_bf(uk[ii]), hi_bf(uk[ii]));
-            v2 = make_float2(lo_bf(uv[ii]), hi_bf(uv[ii]));
+            // row factor (chunk-start form e^{G}, sub-chunk form e^{G - R_{w-1}})
+            // and column factor (e^{-G}, e^{R_w - G})
+            float ex, ey, ix, iy;
+            if constexpr (SUB) {
+                ex = __builtin_amdgcn_exp2f(G[ii].x);
+                ey = __builtin_amdgcn_exp2f(G[ii].y);
+                ix = __builtin_amdgcn_exp2f(tw.x - G[ii].x);
+                iy = __builtin_amdgcn_exp2f(tw.y - G[ii].y);
+            } else {
+                const float gx = G[ii].x + off.x, gy = G[ii].y + off.y;
+                ex = __builtin_amdgcn_exp2f(gx);
+                ey = __builtin_amdgcn_exp2f(gy);
+                ix = __builtin_amdgcn_exp2f(-gx);
+                iy = __builtin_amdgcn_exp2f(-gy);
+            }
+            const float bt = beta_s[tk];
+            const int e = tk * kRowA + 2 * l;
+            const float kx = k2.x * ex, ky = k2.y * ey, kix = k2.x * ix, kiy = k2.y * iy;
+            reinterpret_cast<uint32_t *>(lds + kOffKd)[e / 2] = pack_bf2(kx, ky);
+            reinterpret_cast<uint32_t *>(lds + kOffKi)[e / 2] = pack_bf2(kix, kiy);
+            reinterpret_cast<uint32_t *>(lds + kOffQs)[e / 2] = pack_bf2(q2.x * ex, q2.y * ey);
+            const float bv = bt * v_unscale;
+            const float cur[3][2] = {{SUB ? bt * eoff.x * kx : bt * kx, SUB ? bt * eoff.y * ky : bt * ky},
+                                     {bv * v2.x, bv * v2.y},
+                                     {kix * (SUB ? etail.x : egl.x), kiy * (SUB ? etail.y : egl.y)}};
+#pragma unroll
+            for (int a = 0; a < 3; ++a)
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    if (ii % 2 == 0) prev[a][c] = cur[a][c];
+                    else pk[a][c][ii / 2] = pack_bf2(prev[a][c], cur[a][c]);
+                }
         }
-        const float ex = __builtin_amdgcn_exp2f(gx), ey = __builtin_amdgcn_exp2f(gy);     // e^{G}
-        const float ix = __builtin_amdgcn_exp2f(-gx), iy = __builtin_amdgcn_exp2f(-gy);   // e^{-G}
-        const float bt = beta_s[tk];
-        const int e = tk * kRowA + 2 * l;
-        const float kx = k2.x * ex, ky = k2.y * ey, kix = k2.x * ix, kiy = k2.y * iy;
-        reinterpret_cast<uint32_t *>(lds + kOffKd)[e / 2] = pack_bf2(kx, ky);
-        reinterpret_cast<uint32_t *>(lds + kOffKi)[e / 2] = pack_bf2(kix, kiy);
-        reinterpret_cast<uint32_t *>(lds + kOffQs)[e / 2] = pack_bf2(q2.x * ex, q2.y * ey);
-        const float bv = bt * v_unscale;
-        const float cur[3][2] = {{bt * kx, bt * ky}, {bv * v2.x, bv * v2.y}, {kix * egl.x, kiy * egl.y}};
-#pragma unroll
-        for (int a = 0; a < 3; ++a)
-#pragma unroll
-            for (int c = 0; c < 2; ++c) {
-                if (ii % 2 == 0) prev[a][c] = cur[a][c];
-                else pk[a][c][ii / 2] = pack_bf2(prev[a][c], cur[a][c]);
-            }
-    }
+    };
+    if (sub) token_loop(SubForm<true>{});
+    else token_loop(SubForm<false>{});
     __syncthreads();
 
     // ---- phase 2: A (row block I = w) and P^T (column block I = 3 - w) -----
-    {
-        // the row block's K e^G fragments serve every column block J
-        const int I = w;
-        bf16x8 a[4];
+    // Sub-chunk form: the column fragments of block J, as used against row
+    // block I, take the factor e^{R_{I-1} - R_J} (none for J = I - 1).
+    auto phase2 = [&](auto form) {
+        constexpr bool SUB = decltype(form)::value;
+        const float *fvec = reinterpret_cast<const float *>(lds);
+        auto col_factor = [&](int I, int J) -> const float * {   // per-channel factor vector, or null
+            if constexpr (!SUB) {
+                return nullptr;
+            } else {
+                if (J == I - 1) return nullptr;
+                if (J == I) return fvec + kOffHd / 4 + I * 128;
+                return fvec + kOffF / 4 + (I == 2 ? 0 : (J == 1 ? 1 : 2)) * 128;
+            }
+        };
+        {
+            // the row block's K e^G fragments serve every column block J
+            const int I = w;
+            bf16x8 a[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) a[s] = lds_frag(lds, kOffKd + ((16 * I + c16) * kRowA + 32 * s + 8 * g) * 2);
-        float bi[4];
+            for (int s = 0; s < 4; ++s) a[s] = lds_frag(lds, kOffKd + ((16 * I + c16) * kRowA + 32 * s + 8 * g) * 2);
+            float bi[4];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) bi[r] = beta_s[16 * I + 4 * g + r];
+            for (int r = 0; r < 4; ++r) bi[r] = beta_s[16 * I + 4 * g + r];
 #pragma unroll
-        for (int J = 0; J < 4; ++J) {
-            if (J <= I) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int J = 0; J < 4; ++J) {
+                if (J <= I) {
+                    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                    const float *fc = col_factor(I, J);
+                    if (fc) {   // uniform: sub-chunk form, a scaled column block
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    acc = mfma16(a[s], lds_frag(lds, kOffKi + ((16 * J + c16) * kRowA + 32 * s + 8 * g) * 2), acc);
-                // every entry is written, the diagonal and above as 0 (no
-                // divergent stores; the inverse reads the blocks unmasked)
-                const int j = 16 * J + c16;
+                        for (int s = 0; s < 4; ++s)
+                            acc = mfma16(a[s], scale_frag(lds_frag(lds, kOffKi + ((16 * J + c16) * kRowA + 32 * s + 8 * g) * 2),
+                                                          fc + 32 * s + 8 * g), acc);
+                    } else {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    const int i = 16 * I + 4 * g + r;
-                    A[aix(i, j)] = J < I || j < i ? bi[r] * acc[r] : 0.0f;
+                        for (int s = 0; s < 4; ++s)
+                            acc = mfma16(a[s], lds_frag(lds, kOffKi + ((16 * J + c16) * kRowA + 32 * s + 8 * g) * 2), acc);
+                    }
+                    // every entry is written, the diagonal and above as 0 (no
+                    // divergent stores; the inverse reads the blocks unmasked)
+                    const int j = 16 * J + c16;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const int i = 16 * I + 4 * g + r;
+                        A[aix(i, j)] = J < I || j < i ? bi[r] * acc[r] : 0.0f;
+                    }
                 }
             }
         }
-    }
-    {
-        // the column block's Q e^G fragments serve every row block J
-        const int I = 3 - w;
-        bf16x8 b[4];
+        {
+            // the column block's Q e^G fragments serve every row block J
+            const int I = 3 - w;
+            bf16x8 b[4];
 #pragma unroll
-        for (int s = 0; s < 4; ++s) b[s] = lds_frag(lds, kOffQs + ((16 * I + c16) * kRowA + 32 * s + 8 * g) * 2);
-        f32x4 blk[4];
+            for (int s = 0; s < 4; ++s) b[s] = lds_frag(lds, kOffQs + ((16 * I + c16) * kRowA + 32 * s + 8 * g) * 2);
+            f32x4 blk[4];
 #pragma unroll
-        for (int J = 0; J < 4; ++J) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            if (J <= I) {
+            for (int J = 0; J < 4; ++J) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+                if (J <= I) {
+                    const float *fc = col_factor(I, J);
+                    if (fc) {   // uniform: sub-chunk form, a scaled column block
 #pragma unroll
-                for (int s = 0; s < 4; ++s)
-                    acc = mfma16(lds_frag(lds, kOffKi + ((16 * J + c16) * kRowA + 32 * s + 8 * g) * 2), b[s], acc);
-                const int i = 16 * I + c16;
+                        for (int s = 0; s < 4; ++s)
+                            acc = mfma16(scale_frag(lds_frag(lds, kOffKi + ((16 * J + c16) * kRowA + 32 * s + 8 * g) * 2),
+                                                    fc + 32 * s + 8 * g), b[s], acc);
+                    } else {
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (16 * J + 4 * g + r > i) acc[r] = 0.f;
+                        for (int s = 0; s < 4; ++s)
+                            acc = mfma16(lds_frag(lds, kOffKi + ((16 * J + c16) * kRowA + 32 * s + 8 * g) * 2), b[s], acc);
+                    }
+                    const int i = 16 * I + c16;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r)
+                        if (16 * J + 4 * g + r > i) acc[r] = 0.f;
+                }
+                blk[J] = acc;
             }
-            blk[J] = acc;
-        }
 #pragma unroll
-        for (int sp = 0; sp < 2; ++sp) {
-            const bf16x8 f = pack8(blk[2 * sp], blk[2 * sp + 1]);
-            *reinterpret_cast<bf16x8 *>(rec + kOffP + ((I * 2 + sp) * 64 + l) * 16) = f;
+            for (int sp = 0; sp < 2; ++sp) {
+                const bf16x8 f = pack8(blk[2 * sp], blk[2 * sp + 1]);
+                *reinterpret_cast<bf16x8 *>(rec + kOffP + ((I * 2 + sp) * 64 + l) * 16) = f;
+            }
         }
-    }
-    // Qg fragments: token tile m = w, channel k-steps s = 0..3
+        // Qg fragments: token tile m = w, channel k-steps s = 0..3 (sub-chunk
+        // form: the tile holds Q e^{G - R_{w-1}}; e^{R_{w-1}} per channel restores Q e^G)
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-        const int base = kOffQs + ((16 * w + c16) * kRowA + 32 * s + 4 * g) * 2;
-        u32x4 f;
-        const u32x2 lo = *reinterpret_cast<const u32x2 *>(lds + base);
-        const u32x2 hi = *reinterpret_cast<const u32x2 *>(lds + base + 32);
-        f[0] = lo[0];
-        f[1] = lo[1];
-        f[2] = hi[0];
-        f[3] = hi[1];
-        *reinterpret_cast<u32x4 *>(rec + kOffQg + ((w * 4 + s) * 64 + l) * 16) = f;
-    }
+        for (int s = 0; s < 4; ++s) {
+            const int base = kOffQs + ((16 * w + c16) * kRowA + 32 * s + 4 * g) * 2;
+            u32x4 f;
+            const u32x2 lo = *reinterpret_cast<const u32x2 *>(lds + base);
+            const u32x2 hi = *reinterpret_cast<const u32x2 *>(lds + base + 32);
+            f[0] = lo[0];
+            f[1] = lo[1];
+            f[2] = hi[0];
+            f[3] = hi[1];
+            if (SUB && w > 0) {
+                const float *fe = fvec + kOffEoff / 4 + w * 128 + 32 * s + 4 * g;
+                const f32x4 f0 = *reinterpret_cast<const f32x4 *>(fe), f1 = *reinterpret_cast<const f32x4 *>(fe + 16);
+                f[0] = pack_bf2(lo_bf(f[0]) * f0[0], hi_bf(f[0]) * f0[1]);
+                f[1] = pack_bf2(lo_bf(f[1]) * f0[2], hi_bf(f[1]) * f0[3]);
+                f[2] = pack_bf2(lo_bf(f[2]) * f1[0], hi_bf(f[2]) * f1[1]);
+                f[3] = pack_bf2(lo_bf(f[3]) * f1[2], hi_bf(f[3]) * f1[3]);
+            }
+            *reinterpret_cast<u32x4 *>(rec + kOffQg + ((w * 4 + s) * 64 + l) * 16) = f;
+        }
+    };
+    if (sub) phase2(SubForm<true>{});
+    else phase2(SubForm<false>{});
     __syncthreads();
 
     // ---- phase 3: transposed, beta-scaled copies into region R -------------

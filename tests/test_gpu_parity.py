@@ -378,6 +378,61 @@ def test_prefill_fused_T4096_full():
 
 
 # ----------------------------------------------------------------------------
+# strong decays: chunks whose decay is too large for the chunk-start reference
+# take the 16-token sub-chunk form
+# ----------------------------------------------------------------------------
+def _both_paths(inp, what):
+    ref = ORC.prefill(inp)
+    for name, res in (("fused", gpu_prefill_fused(inp)), ("unfused", gpu_prefill(inp))):
+        assert_chunk_close(res["y"], ref["y"], f"{what} {name} y")
+        assert_chunk_close(res["final_state"], ref["final_state"], f"{what} {name} final state")
+        assert_fp32_close(res["conv_cache"], ref["conv_cache"], f"{what} {name} conv cache", 0.0)
+
+
+def test_prefill_strong_decay_range():
+    """log alpha = -exp(U(-1, 1.5)) (per token -0.37 .. -4.5, about -105 per
+    chunk): every full chunk takes the sub-chunk form; ragged tails, an empty
+    and a one-chunk sequence."""
+    inp = ki.prefill_inputs(130, [300, 64, 17, 0, 200], H=4, d=128, K=4, la_range=(-1.0, 1.5), cache_std=1.0)
+    _both_paths(inp, "strong decay")
+
+
+@pytest.mark.parametrize("la", [-2.0, -4.0, -5.0])
+def test_prefill_constant_decay(la):
+    """Constant log alpha: -2 and -4 (the values that overflowed the
+    chunk-start form) and -5 (80 per 16-token sub-chunk, near that form's
+    bound)."""
+    inp = ki.prefill_inputs(131, [300, 45], H=2, d=128, K=4, cache_std=1.0)
+    inp["log_alpha"] = torch.full_like(inp["log_alpha"], la)
+    _both_paths(inp, f"log alpha = {la}")
+
+
+def test_prefill_decay_forms_mixed():
+    """One sequence whose chunks alternate between mild decay (chunk-start
+    form) and strong decay (sub-chunk form), plus chunks where only one
+    16-token sub-chunk decays strongly: the state passes between chunks of
+    both forms."""
+    mild = ki.prefill_inputs(132, [640], H=4, d=128, K=4, cache_std=1.0)
+    strong = ki.prefill_inputs(132, [640], H=4, d=128, K=4, la_range=(-1.0, 1.5), cache_std=1.0)
+    t = torch.arange(640)
+    use_strong = ((t // 64) % 2 == 1) | ((t // 64 == 4) & ((t % 64) // 16 == 2))
+    inp = dict(mild)
+    inp["log_alpha"] = torch.where(use_strong[:, None, None], strong["log_alpha"], mild["log_alpha"])
+    _both_paths(inp, "mixed decay forms")
+
+
+def test_prefill_strong_decay_T4096():
+    """The T=4096 launch shape (one sequence, 64 chunks) at 8 heads with
+    strong decay, every element against the oracle (fused path, as the
+    benchmark runs it)."""
+    inp = ki.prefill_inputs(133, [4096], H=8, d=128, K=4, la_range=(-1.0, 1.5))
+    res = gpu_prefill_fused(inp)
+    ref = ORC.prefill(inp)
+    assert_chunk_close(res["y"], ref["y"], "strong decay T=4096 y")
+    assert_chunk_close(res["final_state"], ref["final_state"], "strong decay T=4096 final state")
+
+
+# ----------------------------------------------------------------------------
 # full-size workloads (the benchmark's launch configuration)
 # ----------------------------------------------------------------------------
 def test_prefill_T4096_full():

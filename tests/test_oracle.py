@@ -132,6 +132,20 @@ def pin_brute_force(orc):
     return ok
 
 
+def pin_brute_force_strong_decay(orc):
+    """The same dense matrices at strong decays: log alpha = -exp(U(-1, 1.5))
+    (per token down to -4.5) and constant -5, where a chunk's cumulative decay
+    runs far past what e^{+G} can hold; the token loop never forms e^{+G}."""
+    rng = np.random.default_rng(14)
+    ok = True
+    for lengths, H, dk, dv in [([70], 2, 4, 4), ([30, 0, 41], 1, 5, 3)]:
+        p = rand_prepared(rng, lengths, H, dk, dv, la_lo=-1.0, la_hi=1.5)
+        ok &= all(close(a, b) for a, b in zip(run_oracle(orc, p), brute_force(p)))
+        p["la"] = np.full_like(p["la"], -5.0)
+        ok &= all(close(a, b) for a, b in zip(run_oracle(orc, p), brute_force(p)))
+    return ok
+
+
 def pin_chunked(orc):
     rng = np.random.default_rng(11)
     p = rand_prepared(rng, [37, 150, 64, 1], 2, 5, 4)
@@ -202,7 +216,7 @@ def pin_decode_equals_prefill(orc):
             and close(cache, ref["conv_cache"], 0, 0))
 
 
-PINS = [pin_brute_force, pin_chunked, pin_conv, pin_gates, pin_decode_equals_prefill]
+PINS = [pin_brute_force, pin_brute_force_strong_decay, pin_chunked, pin_conv, pin_gates, pin_decode_equals_prefill]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
