@@ -24,6 +24,8 @@
  *   kda_decode_step     one token for a batch of resident states: conv update
  *                       then recurrent step (kimi_k3 API docs, Functions:
  *                       kda_decode_token)
+ *   kda_in_projection, kda_out_projection, kda_mixer_prefill
+ *                       the mixer's linear maps around the operator
  *
  * Conventions shared by every entry point
  *   - Tensor pointers are DEVICE pointers owned by the caller.  The library
@@ -249,6 +251,55 @@ kda_status kda_prefill_noalloc(const kda_geom *geom, int32_t n_seqs, int32_t tot
                                float *conv_cache_out, const void *log_alpha, const void *beta_logit,
                                const void *gate_logit, const float *initial_state, float *final_state,
                                void *out, void *stream);
+
+/*
+ * The KDA mixer around the operator: the projections, which the k3 README
+ * ("Use this repository as a template") places in the KDA module beside the
+ * output gate, around the recurrence primitive.  The output gating itself is the
+ * sigmoid gate inside kda_prefill / kda_decode_step.
+ *
+ * kda_in_projection: one GEMM of hidden states onto every raw input of
+ * kda_prefill.
+ *   geom: H, d (any d >= 1; the chunk path that consumes the outputs needs 128);
+ *   x [T][hidden] bf16; w_in [5 H d + H][hidden] bf16, one row per output
+ *     feature, rows in the order q, k, v, gate logit, decay pre-activation
+ *     (H d each, head-major) and beta logit (H);
+ *   a_log NULL (0) or [H] fp32; dt_bias NULL (0) or [H d] fp32;
+ *   outputs bf16, overwritten: q_raw, k_raw, v_raw, gate_logit, log_alpha
+ *     [T][H][d], beta_logit [T][H];
+ *   log_alpha = -exp(a_log[h]) * softplus(z + dt_bias[h d + c]) for the decay
+ *     pre-activation z: a reading (the pages do not say how the decay comes
+ *     from the projection); with a_log and dt_bias NULL it is -softplus(z),
+ *     which maps any real onto log alpha <= 0.
+ *   hidden must be a positive multiple of 8 (KDA_ERR_UNSUPPORTED otherwise);
+ *   each operand must stay below 4 GiB (KDA_ERR_SHAPE).  bf16 matrix-core
+ *   products with fp32 accumulation; results rounded to bf16.
+ *
+ * kda_out_projection: out [T][hidden] = y [T][H d] w_out^T, with w_out
+ *   [hidden][H d] bf16 (one row per hidden feature); H d a multiple of 8.
+ *
+ * kda_mixer_prefill: kda_in_projection, kda_prefill (chunk 64, d = 128,
+ *   conv cache and state as there) and kda_out_projection in one call, the
+ *   intermediates in `workspace` (at least kda_mixer_workspace_bytes(geom,
+ *   n_seqs, total_tokens) bytes: the projection outputs, the KDA output and
+ *   the chunk workspace).  out [T][hidden] bf16.  Every argument is checked
+ *   before the first launch.
+ */
+kda_status kda_in_projection(const kda_geom *geom, int32_t T, int32_t hidden, const void *x, const void *w_in,
+                             const float *a_log, const float *dt_bias, void *q_raw, void *k_raw, void *v_raw,
+                             void *gate_logit, void *log_alpha, void *beta_logit, void *stream);
+
+kda_status kda_out_projection(const kda_geom *geom, int32_t T, int32_t hidden, const void *y, const void *w_out,
+                              void *out, void *stream);
+
+size_t kda_mixer_workspace_bytes(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens);
+
+kda_status kda_mixer_prefill(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
+                             const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host, int32_t hidden,
+                             const void *x, const void *w_in, const float *a_log, const float *dt_bias,
+                             const float *conv_w, const float *conv_cache_in, float *conv_cache_out,
+                             const float *initial_state, float *final_state, const void *w_out, void *out,
+                             void *workspace, size_t workspace_bytes, void *stream);
 
 /*
  * kda_decode_step: one token for each of `batch` rows, fused: conv-cache

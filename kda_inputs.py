@@ -36,6 +36,7 @@ __all__ = [
     "decode_inputs",
     "config_prefill",
     "config_decode",
+    "mixer_inputs",
     "tokens_as_steps",
     "CONFIG_NAMES",
 ]
@@ -117,6 +118,38 @@ def _step(g, batch, H, d, dtype, la_range):
         log_alpha=_log_alpha(g, (batch, H, d), *la_range).to(dtype),
         gate_logit=_normal(g, (batch, H, d)).to(dtype),
     )
+
+
+def mixer_inputs(seed, lengths, hidden, H, d, K, state_std=0.01):
+    """Hidden states and weights for the KDA mixer (input projection, the
+    operator, output projection) on one packed batch.
+
+    Draw order: conv weights N(0, 0.5); x [T, hidden] N(0, 1); w_in
+    [5 H d + H, hidden] N(0, 1/sqrt(hidden)) (so the projected q, k, v and
+    logits come out near unit scale); w_out [hidden, H d] N(0, 1/sqrt(H d));
+    a_log [H] U(-4, -1); dt_bias [H d] N(0, 1); initial state N(0, state_std).
+    bf16 tensors are drawn in fp32 and rounded; a_log, dt_bias, conv weights
+    and state stay fp32; the conv cache is zero.  The pages give no hidden
+    size or decay parameters: these are synthetic.
+    """
+    g = torch.Generator().manual_seed(seed)
+    lengths = [int(x) for x in lengths]
+    N, T = len(lengths), sum(lengths)
+    cu = torch.zeros(N + 1, dtype=torch.int32)
+    if N:
+        cu[1:] = torch.cumsum(torch.tensor(lengths, dtype=torch.int64), 0).to(torch.int32)
+    C = H * d
+    conv_w = _normal(g, (3, C, K), 0.5)
+    x = _normal(g, (T, hidden)).to(torch.bfloat16)
+    w_in = _normal(g, (5 * C + H, hidden), hidden ** -0.5).to(torch.bfloat16)
+    w_out = _normal(g, (hidden, C), C ** -0.5).to(torch.bfloat16)
+    a_log = _uniform(g, (H,), -4.0, -1.0)
+    dt_bias = _normal(g, (C,))
+    s0 = _normal(g, (N, H, d, d), state_std)
+    cache = torch.zeros(N, 3, max(K - 1, 0), C, dtype=torch.float32)
+    return dict(seed=seed, H=H, d=d, K=K, N=N, T=T, hidden=hidden, lengths=lengths, cu_seqlens=cu,
+                conv_w=conv_w, x=x, w_in=w_in, w_out=w_out, a_log=a_log, dt_bias=dt_bias,
+                initial_state=s0, conv_cache=cache)
 
 
 def tokens_as_steps(inp):

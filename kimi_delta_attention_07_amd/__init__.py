@@ -10,6 +10,8 @@ include/kda.h); this package is its thin Python binding:
     chunk_backward(...) gradients of chunk_forward
     prologue_backward(...) gradients of prologue, back to the raw inputs and conv taps
     decode_step(...)    one token for a batch of resident fp32 states
+    in_projection(...), out_projection(...), mixer_prefill(...)
+                        the mixer's linear maps around the operator, and the whole mixer
 
 Build the library with ``python -m kimi_delta_attention_07_amd.build``.
 """
@@ -28,6 +30,10 @@ from ._lib import (  # noqa: F401
     load,
     prefill,
     prefill_noalloc,
+    in_projection,
+    out_projection,
+    mixer_prefill,
+    mixer_workspace_bytes,
     prefill_prepare,
     prefill_scan,
     prologue,

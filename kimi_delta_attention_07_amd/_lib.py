@@ -22,7 +22,8 @@ STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE"
 EXPORTS = ("kda_prologue", "kda_chunk_workspace_bytes", "kda_chunk_forward", "kda_chunk_prepare",
            "kda_chunk_scan", "kda_prefill", "kda_prefill_prepare", "kda_prefill_scan", "kda_decode_step",
            "kda_chunk_backward_workspace_bytes", "kda_chunk_backward", "kda_prologue_backward_workspace_bytes",
-           "kda_prologue_backward", "kda_prefill_noalloc", "kda_status_str", "kda_last_error_detail")
+           "kda_prologue_backward", "kda_prefill_noalloc", "kda_in_projection", "kda_out_projection",
+           "kda_mixer_workspace_bytes", "kda_mixer_prefill", "kda_status_str", "kda_last_error_detail")
 
 
 class KdaError(RuntimeError):
@@ -77,6 +78,14 @@ def load(path=LIB_PATH):
     L.kda_prefill_scan.restype = _I
     L.kda_prefill_noalloc.argtypes = [G, _I, _I, _P, _P, _I, _I] + [_P] * 12 + [_P]
     L.kda_prefill_noalloc.restype = _I
+    L.kda_in_projection.argtypes = [G, _I, _I] + [_P] * 10 + [_P]
+    L.kda_in_projection.restype = _I
+    L.kda_out_projection.argtypes = [G, _I, _I, _P, _P, _P, _P]
+    L.kda_out_projection.restype = _I
+    L.kda_mixer_workspace_bytes.argtypes = [G, _I, _I]
+    L.kda_mixer_workspace_bytes.restype = ctypes.c_size_t
+    L.kda_mixer_prefill.argtypes = [G, _I, _I, _P, _P, _I] + [_P] * 12 + [ctypes.c_size_t, _P]
+    L.kda_mixer_prefill.restype = _I
     L.kda_decode_step.argtypes = [G, _I, _P, _I, _I] + [_P] * 9 + [_I, _P, _P]
     L.kda_decode_step.restype = _I
     L.kda_status_str.argtypes = [_I]
@@ -296,6 +305,63 @@ def prefill_noalloc(q_raw, k_raw, v_raw, conv_w, log_alpha, beta_logit, gate_log
                                       _ptr(q_raw), _ptr(k_raw), _ptr(v_raw), _ptr(conv_w), _ptr(conv_cache_in),
                                       _ptr(conv_cache_out), _ptr(log_alpha), _ptr(beta_logit), _ptr(gate_logit),
                                       _ptr(initial_state), _ptr(final_state), _ptr(out), _stream(q_raw)))
+    return out, final_state
+
+
+def in_projection(x, w_in, H, d, a_log=None, dt_bias=None, *, outs=None):
+    """The mixer's input projection of x [T, hidden] (bf16) with w_in
+    [5 H d + H, hidden]: returns dict(q_raw, k_raw, v_raw, gate_logit,
+    log_alpha [T, H, d], beta_logit [T, H]), bf16."""
+    T, hidden = x.shape
+    if outs is None:
+        mk = lambda *shape: torch.empty(shape, dtype=torch.bfloat16, device=x.device)
+        outs = dict(q_raw=mk(T, H, d), k_raw=mk(T, H, d), v_raw=mk(T, H, d), gate_logit=mk(T, H, d),
+                    log_alpha=mk(T, H, d), beta_logit=mk(T, H))
+    g = geom(H, d, 1)
+    _check(load().kda_in_projection(ctypes.byref(g), T, hidden, _ptr(x), _ptr(w_in), _ptr(a_log), _ptr(dt_bias),
+                                    _ptr(outs["q_raw"]), _ptr(outs["k_raw"]), _ptr(outs["v_raw"]),
+                                    _ptr(outs["gate_logit"]), _ptr(outs["log_alpha"]), _ptr(outs["beta_logit"]),
+                                    _stream(x)))
+    return outs
+
+
+def out_projection(y, w_out, *, out=None):
+    """out [T, hidden] = y [T, H, d] (or [T, H d]) @ w_out^T, w_out [hidden, H d]; bf16."""
+    T = y.shape[0]
+    hidden, C = w_out.shape
+    if out is None:
+        out = torch.empty((T, hidden), dtype=torch.bfloat16, device=y.device)
+    g = geom(1, C, 1)
+    _check(load().kda_out_projection(ctypes.byref(g), T, hidden, _ptr(y), _ptr(w_out), _ptr(out), _stream(y)))
+    return out
+
+
+def mixer_workspace_bytes(H, d, n_seqs, total_tokens):
+    g = geom(H, d, 4)
+    return int(load().kda_mixer_workspace_bytes(ctypes.byref(g), n_seqs, total_tokens))
+
+
+def mixer_prefill(x, w_in, w_out, conv_w, cu_seqlens, a_log=None, dt_bias=None, initial_state=None,
+                  conv_cache_in=None, conv_cache_out=None, *, H, d=128, final_state=None, out=None, act="silu",
+                  eps=1e-6, scale=1.0, workspace=None, cu_seqlens_host=None, want_final_state=True):
+    """The KDA mixer on hidden states x [T, hidden]: input projection, the
+    fused chunked prefill, output projection.  Returns (out [T, hidden] bf16,
+    final_state)."""
+    T, hidden = x.shape
+    K = conv_w.shape[2]
+    n = cu_seqlens.numel() - 1
+    hcu, hptr = _host_cu(cu_seqlens, cu_seqlens_host)
+    if workspace is None:
+        workspace = torch.empty(max(mixer_workspace_bytes(H, d, n, T), 16), dtype=torch.uint8, device=x.device)
+    if out is None:
+        out = torch.empty((T, hidden), dtype=torch.bfloat16, device=x.device)
+    if final_state is None and want_final_state:
+        final_state = torch.empty((n, H, d, d), dtype=torch.float32, device=x.device)
+    g = geom(H, d, K, act, eps, scale)
+    _check(load().kda_mixer_prefill(ctypes.byref(g), n, T, _ptr(cu_seqlens), hptr, hidden, _ptr(x), _ptr(w_in),
+                                    _ptr(a_log), _ptr(dt_bias), _ptr(conv_w), _ptr(conv_cache_in),
+                                    _ptr(conv_cache_out), _ptr(initial_state), _ptr(final_state), _ptr(w_out),
+                                    _ptr(out), _ptr(workspace), workspace.numel(), _stream(x)))
     return out, final_state
 
 

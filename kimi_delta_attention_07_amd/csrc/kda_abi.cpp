@@ -609,6 +609,154 @@ kda_status kda_decode_step(const kda_geom *geom, int32_t batch, const int32_t *s
     return launched(kda::launch_decode(p, (int)in_dtype, (int)out_dtype, (hipStream_t)stream), "decode");
 }
 
+// ---------------------------------------------------------------------------
+// The mixer's linear maps and the whole mixer prefill
+// ---------------------------------------------------------------------------
+namespace {
+
+kda_status check_proj_geom(const kda_geom *geom) {
+    if (!geom) return fail(KDA_ERR_NULL, "geom is NULL");
+    if (geom->H <= 0 || geom->d <= 0) return fail(KDA_ERR_SHAPE, "H = %d and d = %d must be > 0", geom->H, geom->d);
+    if ((long)geom->H * geom->d > (1L << 24)) return fail(KDA_ERR_SHAPE, "H * d too large");
+    return KDA_OK;
+}
+
+// rows x K bf16 operand of the GEMM: K a multiple of 8 (16-byte rows), and
+// the whole matrix addressable by one buffer resource (< 4 GiB)
+kda_status check_gemm_dims(long rows, long K, const char *what) {
+    if (K <= 0 || K % 8 != 0)
+        return fail(KDA_ERR_UNSUPPORTED, "%s: inner dimension %ld must be a positive multiple of 8", what, K);
+    if (rows * K * 2 >= (1L << 32)) return fail(KDA_ERR_SHAPE, "%s: %ld x %ld bf16 exceeds 4 GiB", what, rows, K);
+    return KDA_OK;
+}
+
+kda::ProjParams in_proj_params(const kda_geom *geom, int32_t T, int32_t hidden, const void *x, const void *w_in,
+                               const float *a_log, const float *dt_bias, void *const outs[6]) {
+    kda::ProjParams p{};
+    p.M = T;
+    p.N = 5 * geom->H * geom->d + geom->H;
+    p.K = hidden;
+    p.a = static_cast<const uint16_t *>(x);
+    p.b = static_cast<const uint16_t *>(w_in);
+    p.epi = 1;
+    p.H = geom->H;
+    p.d = geom->d;
+    for (int i = 0; i < 6; ++i) p.seg[i] = static_cast<uint16_t *>(outs[i]);
+    p.a_log = a_log;
+    p.bias = dt_bias;
+    return p;
+}
+
+size_t al256(size_t x) { return (x + 255) & ~size_t(255); }
+
+}  // namespace
+
+kda_status kda_in_projection(const kda_geom *geom, int32_t T, int32_t hidden, const void *x, const void *w_in,
+                             const float *a_log, const float *dt_bias, void *q_raw, void *k_raw, void *v_raw,
+                             void *gate_logit, void *log_alpha, void *beta_logit, void *stream) {
+    KDA_TRY(check_proj_geom(geom));
+    if (T < 0) return fail(KDA_ERR_SHAPE, "T = %d must be >= 0", T);
+    const long N = 5L * geom->H * geom->d + geom->H;
+    KDA_TRY(check_gemm_dims(T, hidden, "x"));
+    KDA_TRY(check_gemm_dims(N, hidden, "w_in"));
+    KDA_TRY(check_required({{w_in, "w_in"}}));
+    if (T > 0)
+        KDA_TRY(check_required({{x, "x"}, {q_raw, "q_raw"}, {k_raw, "k_raw"}, {v_raw, "v_raw"},
+                                {gate_logit, "gate_logit"}, {log_alpha, "log_alpha"}, {beta_logit, "beta_logit"}}));
+    KDA_TRY(check_aligned({{x, "x"}, {w_in, "w_in"}, {a_log, "a_log"}, {dt_bias, "dt_bias"}, {q_raw, "q_raw"},
+                           {k_raw, "k_raw"}, {v_raw, "v_raw"}, {gate_logit, "gate_logit"},
+                           {log_alpha, "log_alpha"}, {beta_logit, "beta_logit"}}));
+    KDA_TRY(check_device());
+    void *outs[6] = {q_raw, k_raw, v_raw, gate_logit, log_alpha, beta_logit};
+    return launched(kda::launch_gemm(in_proj_params(geom, T, hidden, x, w_in, a_log, dt_bias, outs),
+                                     (hipStream_t)stream), "in projection");
+}
+
+kda_status kda_out_projection(const kda_geom *geom, int32_t T, int32_t hidden, const void *y, const void *w_out,
+                              void *out, void *stream) {
+    KDA_TRY(check_proj_geom(geom));
+    if (T < 0) return fail(KDA_ERR_SHAPE, "T = %d must be >= 0", T);
+    if (hidden <= 0) return fail(KDA_ERR_SHAPE, "hidden = %d must be > 0", hidden);
+    const long K = (long)geom->H * geom->d;
+    KDA_TRY(check_gemm_dims(T, K, "y"));
+    KDA_TRY(check_gemm_dims(hidden, K, "w_out"));
+    KDA_TRY(check_required({{w_out, "w_out"}}));
+    if (T > 0) KDA_TRY(check_required({{y, "y"}, {out, "out"}}));
+    KDA_TRY(check_aligned({{y, "y"}, {w_out, "w_out"}, {out, "out"}}));
+    KDA_TRY(check_device());
+    kda::ProjParams p{};
+    p.M = T;
+    p.N = hidden;
+    p.K = (int)K;
+    p.a = static_cast<const uint16_t *>(y);
+    p.b = static_cast<const uint16_t *>(w_out);
+    p.out = static_cast<uint16_t *>(out);
+    return launched(kda::launch_gemm(p, (hipStream_t)stream), "out projection");
+}
+
+size_t kda_mixer_workspace_bytes(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens) {
+    if (check_geom(geom, true) != KDA_OK || n_seqs <= 0 || total_tokens < 0) return 0;
+    const size_t T = (size_t)total_tokens, C = (size_t)geom->H * geom->d;
+    return 5 * al256(T * C * 2) + al256(T * geom->H * 2) + al256(T * C * 2) +
+           kda::chunk_workspace_bytes(geom->H, n_seqs, chunk_bound(n_seqs, total_tokens));
+}
+
+kda_status kda_mixer_prefill(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
+                             const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host, int32_t hidden,
+                             const void *x, const void *w_in, const float *a_log, const float *dt_bias,
+                             const float *conv_w, const float *conv_cache_in, float *conv_cache_out,
+                             const float *initial_state, float *final_state, const void *w_out, void *out,
+                             void *workspace, size_t workspace_bytes, void *stream) {
+    // every check of the three stages before the first launch
+    KDA_TRY(check_geom(geom, true));
+    long n_chunks = 0;
+    KDA_TRY(check_seqlens(n_seqs, total_tokens, cu_seqlens_host, &n_chunks));
+    const long C = (long)geom->H * geom->d, N = 5 * C + geom->H;
+    KDA_TRY(check_gemm_dims(total_tokens, hidden, "x"));
+    KDA_TRY(check_gemm_dims(N, hidden, "w_in"));
+    KDA_TRY(check_gemm_dims(hidden, C, "w_out"));
+    KDA_TRY(check_gemm_dims(total_tokens, C, "the KDA output"));
+    KDA_TRY(check_required({{cu_seqlens_dev, "cu_seqlens_dev"}, {w_in, "w_in"}, {w_out, "w_out"},
+                            {conv_w, "conv_w"}, {workspace, "workspace"}}));
+    if (total_tokens > 0) KDA_TRY(check_required({{x, "x"}, {out, "out"}}));
+    KDA_TRY(check_aligned({{x, "x"}, {w_in, "w_in"}, {w_out, "w_out"}, {a_log, "a_log"}, {dt_bias, "dt_bias"},
+                           {conv_w, "conv_w"}, {conv_cache_in, "conv_cache_in"},
+                           {conv_cache_out, "conv_cache_out"}, {initial_state, "initial_state"},
+                           {final_state, "final_state"}, {out, "out"}, {workspace, "workspace"}}));
+    const size_t need = kda_mixer_workspace_bytes(geom, n_seqs, total_tokens);
+    if (workspace_bytes < need)
+        return fail(KDA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    KDA_TRY(check_device());
+    const size_t T = (size_t)total_tokens;
+    unsigned char *w = static_cast<unsigned char *>(workspace);
+    void *seg[6];
+    for (int i = 0; i < 5; ++i) {
+        seg[i] = w;
+        w += al256(T * C * 2);
+    }
+    seg[5] = w;
+    w += al256(T * geom->H * 2);
+    void *y = w;
+    w += al256(T * C * 2);
+    void *chunk_ws = w;
+    const size_t chunk_bytes = workspace_bytes - (size_t)(w - static_cast<unsigned char *>(workspace));
+    if (total_tokens > 0)
+        KDA_TRY(launched(kda::launch_gemm(in_proj_params(geom, total_tokens, hidden, x, w_in, a_log, dt_bias, seg),
+                                          (hipStream_t)stream), "in projection"));
+    KDA_TRY(kda_prefill(geom, n_seqs, total_tokens, cu_seqlens_dev, cu_seqlens_host, KDA_BF16, kda::kChunk, seg[0],
+                        seg[1], seg[2], conv_w, conv_cache_in, conv_cache_out, seg[4], seg[5], seg[3], initial_state,
+                        final_state, y, chunk_ws, chunk_bytes, stream));
+    if (total_tokens == 0) return ok();
+    kda::ProjParams p{};
+    p.M = total_tokens;
+    p.N = hidden;
+    p.K = (int)C;
+    p.a = static_cast<const uint16_t *>(y);
+    p.b = static_cast<const uint16_t *>(w_out);
+    p.out = static_cast<uint16_t *>(out);
+    return launched(kda::launch_gemm(p, (hipStream_t)stream), "out projection");
+}
+
 kda_status kda_prefill_noalloc(const kda_geom *geom, int32_t n_seqs, int32_t total_tokens,
                                const int32_t *cu_seqlens_dev, const int32_t *cu_seqlens_host, kda_dtype in_dtype,
                                int32_t chunk, const void *q_raw, const void *k_raw, const void *v_raw,

@@ -121,6 +121,22 @@ struct PrologueBwdParams {
     void *workspace;                            // prologue_bwd_workspace_bytes()
     float *dpre, *dw_part;                      // carved from the workspace by the launcher
 };
+// Linear maps of the mixer: C = A B^T, A [M][K], B [N][K] bf16 (K contiguous,
+// K % 8 == 0), fp32 accumulation, bf16 out.  epi 0: out [M][N]; epi 1: the KDA
+// input projection, columns split into q, k, v, gate, decay (H d each) and
+// beta (H) segments written to seg[0..5] ([M][width] each), the decay segment
+// through log alpha = -exp(a_log[h]) softplus(z + bias[h d + c]).
+struct ProjParams {
+    int M, N, K;
+    const uint16_t *a, *b;
+    int epi;
+    uint16_t *out;
+    int H, d;
+    uint16_t *seg[6];
+    const float *a_log, *bias;   // [H], [H d]; either may be null
+};
+hipError_t launch_gemm(const ProjParams &p, hipStream_t s);
+
 size_t prologue_bwd_workspace_bytes(int H, int d, long T);
 hipError_t launch_prologue_backward(PrologueBwdParams p, int dtype, hipStream_t s);
 

@@ -91,6 +91,8 @@ class Oracle:
         L.kda_oracle_decode_step.argtypes = [ctypes.c_int, _I, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                              ctypes.c_int, ctypes.c_double, ctypes.c_double,
                                              _D, _D, _D, _D, _D, _D, _D, _D, _D, _D]
+        L.kda_oracle_linear.argtypes = [ctypes.c_long, ctypes.c_int, ctypes.c_int, _D, _D, _D]
+        L.kda_oracle_log_decay.argtypes = [ctypes.c_long, ctypes.c_int, ctypes.c_int, _D, _D, _D, _D]
 
     def num_threads(self):
         return int(self.lib.kda_oracle_num_threads())
@@ -158,6 +160,37 @@ class Oracle:
             _p(dy), _p(ds_final), _p(out["dq"]), _p(out["dk"]), _p(out["dv"]), _p(out["dla"]), _p(out["dbeta"]),
             _p(out["dgate"]), _p(out["ds0"]))
         return out
+
+    def linear(self, x, w):
+        """x [..., in] @ w[out, in]^T -> [..., out] (fp64 triple loop)."""
+        x, w = _f64(x), _f64(w)
+        lead = x.shape[:-1]
+        rows = int(np.prod(lead)) if lead else 1
+        out, inn = w.shape
+        y = np.zeros((rows, out))
+        self.lib.kda_oracle_linear(rows, inn, out, _p(np.ascontiguousarray(x.reshape(rows, inn))), _p(w), _p(y))
+        return y.reshape(*lead, out)
+
+    def log_decay(self, z, a_log=None, bias=None):
+        """log alpha = -exp(a_log[h]) softplus(z + bias[h, c]); z [rows, H, d]."""
+        z, a_log, bias = _f64(z), _f64(a_log), _f64(bias)
+        rows, H, d = z.shape
+        la = np.zeros_like(z)
+        self.lib.kda_oracle_log_decay(rows, H, d, _p(z), _p(a_log), _p(bias), _p(la))
+        return la
+
+    def in_projection(self, x, w_in, H, d, a_log=None, bias=None):
+        """The mixer's input projection of hidden states x [T, hidden] with
+        w_in [5 H d + H, hidden], rows in the order q, k, v, gate, decay (each
+        H d, head-major) and beta (H).  Returns q_raw, k_raw, v_raw,
+        gate_logit [T, H, d], log_alpha [T, H, d] and beta_logit [T, H]."""
+        y = self.linear(x, w_in)
+        T = y.shape[0]
+        C = H * d
+        seg = lambda i: y[:, i * C:(i + 1) * C].reshape(T, H, d)
+        return dict(q_raw=seg(0), k_raw=seg(1), v_raw=seg(2), gate_logit=seg(3),
+                    log_alpha=self.log_decay(np.ascontiguousarray(seg(4)), a_log, bias),
+                    beta_logit=y[:, 5 * C:5 * C + H])
 
     # ---- composed paths ----------------------------------------------------
     def prologue(self, inp, act=ACT_SILU, eps=L2_EPS, cache_in=None):

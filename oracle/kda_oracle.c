@@ -34,6 +34,15 @@
  *    docs' struct KdaState keeps both as fp32 read-modify-write buffers; fp64
  *    here).
  *
+ *  - the KDA mixer's linear maps around the operator (the k3 README, "Use
+ *    this repository as a template", puts the projections and the output gate
+ *    in the KDA module): one projection of the hidden states to the raw q, k, v, the
+ *    gate logits, the decay pre-activations and the beta logits, the decay
+ *    log alpha = -exp(a_log[h]) * softplus(z + bias[channel]) (a reading: the
+ *    pages do not say how log alpha comes from the projection; with a_log and
+ *    bias absent it is -softplus(z), which maps any real onto log alpha <= 0),
+ *    and the output projection back to the hidden size.
+ *
  * Readings taken where the pages are silent: conv tap K-1 multiplies the
  * current token, no conv bias, zero history at a sequence start unless a
  * cache is given, and the conv never crosses sequences; the output scale is
@@ -431,4 +440,38 @@ void kda_oracle_recurrence_backward(int n_seqs, const int32_t *cu, int H, int dk
             free(St);
         }
     }
+}
+
+/* ---------------------------------------------------------------------------
+ * The mixer's linear maps (k3 README, "Use this repository as a template":
+ * the KDA module owns the projections and the output gating).
+ * ------------------------------------------------------------------------- */
+
+/* y[r][o] = sum_i x[r][i] w[o][i]: x [rows][in], w [out][in] (one row of
+ * weights per output feature), y [rows][out]; a plain triple loop. */
+void kda_oracle_linear(long rows, int in, int out, const double *x, const double *w, double *y) {
+#pragma omp parallel for schedule(static)
+    for (long r = 0; r < rows; ++r)
+        for (int o = 0; o < out; ++o) {
+            double acc = 0.0;
+            for (int i = 0; i < in; ++i) acc += x[r * in + i] * w[(long)o * in + i];
+            y[r * out + o] = acc;
+        }
+}
+
+static double softplus(double x) { return x > 0 ? x + log1p(exp(-x)) : log1p(exp(x)); }
+
+/* log alpha from its projection, per (row, head, channel):
+ * la = -exp(a_log[h]) * softplus(z + bias[h * d + c]); a_log, bias may be
+ * NULL (read as 0). z, la [rows][H][d]. */
+void kda_oracle_log_decay(long rows, int H, int d, const double *z, const double *a_log, const double *bias,
+                          double *la) {
+    for (long r = 0; r < rows; ++r)
+        for (int h = 0; h < H; ++h) {
+            const double A = a_log ? exp(a_log[h]) : 1.0;
+            for (int c = 0; c < d; ++c) {
+                const long e = (r * H + h) * d + c;
+                la[e] = -A * softplus(z[e] + (bias ? bias[h * d + c] : 0.0));
+            }
+        }
 }

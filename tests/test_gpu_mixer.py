@@ -1,0 +1,121 @@
+"""GPU parity of the KDA mixer's linear maps and of the whole mixer prefill
+(input projection, the fused chunked prefill, output projection), through
+the C ABI, against the CPU oracle on the same seeded inputs.
+
+Bars:
+  projections: |gpu - oracle| <= 2^-8 |oracle| + K 2^-24 S + 1e-6 per
+    element, S = sum_k |x_k w_k| (one bf16 rounding of the result plus the
+    fp32 accumulation bound over K terms in any order); the decay segment
+    carries the bound of its pre-activation through -exp(a_log) softplus
+    (slope <= exp(a_log)) plus one bf16 rounding;
+  the operator inside the mixer: the chunked path's 2e-2 + 1e-2 |oracle|,
+    on the projection's own (bf16) outputs;
+  the mixer itself: bit-identical to its three stages called one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+import kda_inputs as ki
+import kimi_delta_attention_07_amd as kda
+import oracle
+from kda_testlib import assert_chunk_close, np64, report
+
+pytestmark = pytest.mark.gpu
+ORC = oracle.get()
+U = 2.0 ** -24
+
+
+def assert_gemm_close(got, want, S, K, what, slope=None):
+    got = np64(got)
+    err = np.abs(got - want)
+    acc = K * U * S * (1.0 if slope is None else slope)
+    bar = 2.0 ** -8 * np.abs(want) + acc + 1e-6
+    bad = err > bar
+    assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond the bar (max abs {err.max():.3e})"
+    print(f"PARITY {what}: max_abs {err.max():.3e} max_ref {np.abs(want).max():.3e} "
+          f"bar_frac {(err / bar).max():.3f}", flush=True)
+
+
+def check_in_projection(inp, res):
+    """GPU input projection against the oracle's on the same bf16 x and w_in."""
+    H, d, hidden = inp["H"], inp["d"], inp["hidden"]
+    x, w = np64(inp["x"]), np64(inp["w_in"])
+    ref = ORC.in_projection(x, w, H, d, np64(inp["a_log"]), np64(inp["dt_bias"]))
+    S = np.abs(x) @ np.abs(w).T
+    C = H * d
+    T = x.shape[0]
+    segS = lambda i: S[:, i * C:(i + 1) * C].reshape(T, H, d)
+    for i, key in enumerate(("q_raw", "k_raw", "v_raw", "gate_logit")):
+        assert_gemm_close(res[key], ref[key], segS(i), hidden, f"in projection {key}")
+    slope = np.exp(np64(inp["a_log"]))[None, :, None]
+    assert_gemm_close(res["log_alpha"], ref["log_alpha"], segS(4), hidden, "in projection log_alpha", slope)
+    assert_gemm_close(res["beta_logit"], ref["beta_logit"], S[:, 5 * C:5 * C + H], hidden, "in projection beta_logit")
+    assert (np64(res["log_alpha"]) <= 0).all()
+
+
+@pytest.mark.parametrize("T,hidden,H,d", [(7, 16, 2, 4), (300, 16, 2, 4), (300, 1032, 4, 128), (513, 512, 3, 32)])
+def test_in_projection(T, hidden, H, d):
+    """The tiny K3Config widths (hidden 16, 2 heads of 4; the k3 README's
+    Tutorial 3), a production-like head dim with a ragged output width
+    (5*4*128 + 4 = 2564 columns) and hidden 1032 (K tail), and an odd mix;
+    row counts span several 256-row tiles and a ragged one."""
+    inp = ki.mixer_inputs(140 + T + hidden, [T], hidden, H, d, 4)
+    res = kda.in_projection(inp["x"].cuda(), inp["w_in"].cuda(), H, d, inp["a_log"].cuda(), inp["dt_bias"].cuda())
+    torch.cuda.synchronize()
+    check_in_projection(inp, res)
+
+
+def test_in_projection_no_decay_parameters():
+    """a_log and dt_bias absent: log alpha = -softplus(z)."""
+    inp = ki.mixer_inputs(150, [64], 64, 2, 8, 4)
+    res = kda.in_projection(inp["x"].cuda(), inp["w_in"].cuda(), 2, 8)
+    torch.cuda.synchronize()
+    x, w = np64(inp["x"]), np64(inp["w_in"])
+    ref = ORC.in_projection(x, w, 2, 8)
+    S = (np.abs(x) @ np.abs(w).T)[:, 64:80].reshape(64, 2, 8)
+    assert_gemm_close(res["log_alpha"], ref["log_alpha"], S, 64, "log_alpha without a_log, dt_bias")
+
+
+@pytest.mark.parametrize("T,C,hidden", [(300, 512, 1032), (5, 8, 16), (1024, 4096, 256)])
+def test_out_projection(T, C, hidden):
+    g = torch.Generator().manual_seed(160 + T)
+    y = torch.randn(T, C, generator=g).to(torch.bfloat16)
+    w = (torch.randn(hidden, C, generator=g) * C ** -0.5).to(torch.bfloat16)
+    out = kda.out_projection(y.cuda(), w.cuda())
+    torch.cuda.synchronize()
+    ref = ORC.linear(np64(y), np64(w))
+    assert_gemm_close(out, ref, np.abs(np64(y)) @ np.abs(np64(w)).T, C, f"out projection {T}x{C}->{hidden}")
+
+
+def test_mixer_prefill():
+    """The whole mixer on a packed batch (ragged, an empty sequence): equal to
+    its three stages called one by one, and each stage against the oracle."""
+    inp = ki.mixer_inputs(170, [300, 77, 0, 130], 512, 4, 128, 4)
+    H, d, hidden = 4, 128, 512
+    dev = {k: (v.cuda() if torch.is_tensor(v) else v) for k, v in inp.items()}
+    cu_h = inp["cu_seqlens"]
+    cache_out = torch.empty_like(dev["conv_cache"])
+    out, S = kda.mixer_prefill(dev["x"], dev["w_in"], dev["w_out"], dev["conv_w"], dev["cu_seqlens"], dev["a_log"],
+                               dev["dt_bias"], dev["initial_state"], dev["conv_cache"], cache_out, H=H, d=d,
+                               cu_seqlens_host=cu_h)
+    # the same three stages, one call each
+    pro = kda.in_projection(dev["x"], dev["w_in"], H, d, dev["a_log"], dev["dt_bias"])
+    cache2 = torch.empty_like(dev["conv_cache"])
+    y, S2 = kda.prefill(pro["q_raw"], pro["k_raw"], pro["v_raw"], dev["conv_w"], pro["log_alpha"], pro["beta_logit"],
+                        pro["gate_logit"], dev["cu_seqlens"], dev["initial_state"], dev["conv_cache"], cache2,
+                        cu_seqlens_host=cu_h)
+    out2 = kda.out_projection(y.reshape(inp["T"], H * d), dev["w_out"])
+    torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(S, S2) and torch.equal(cache_out, cache2)
+    check_in_projection(inp, {k: v.cpu() for k, v in pro.items()})
+    # the operator on the projection's own outputs
+    op_inp = dict(H=H, d=d, K=4, N=inp["N"], T=inp["T"], lengths=inp["lengths"], cu_seqlens=cu_h,
+                  conv_w=inp["conv_w"], initial_state=inp["initial_state"], conv_cache=inp["conv_cache"],
+                  **{k: pro[k].cpu() for k in ("q_raw", "k_raw", "v_raw", "log_alpha", "beta_logit", "gate_logit")})
+    ref = ORC.prefill(op_inp)
+    assert_chunk_close(y, ref["y"], "mixer operator y")
+    assert_chunk_close(S, ref["final_state"], "mixer operator final state")
+    yn = np64(y).reshape(inp["T"], H * d)
+    wn = np64(dev["w_out"])
+    assert_gemm_close(out, ORC.linear(yn, wn), np.abs(yn) @ np.abs(wn).T, H * d, "mixer out projection")
