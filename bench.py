@@ -16,9 +16,10 @@ The metric's second half, decode, is measured in the same run on the batched
 decode workload (256 resident fp32 states x 1 token, 64 consecutive
 kda_decode_step calls with distinct inputs) and reported under "decode".
 The chunked backward (kda_chunk_backward) on the prefill workload's shapes is
-reported under "backward", and the packed varlen and long-context prefill
-workloads under "prefill_workloads" (informative; the headline stays the
-4096-token sequence).
+reported under "backward", the packed varlen and long-context prefill
+workloads under "prefill_workloads", and the KDA mixer (input projection,
+prefill, output projection at a synthetic hidden size) under "mixer"
+(informative; the headline stays the 4096-token sequence).
 
 Every kernel is timed with HIP events on the stream it is launched on.  The
 roofline object counts the path's algorithmic bytes only (49,216 B per token:
@@ -152,6 +153,8 @@ def parse():
     ap.add_argument("--no-backward", action="store_true", help="skip the chunked backward measurement")
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the varlen and long-context prefill measurements")
+    ap.add_argument("--no-mixer", action="store_true", help="skip the KDA mixer (projections) measurement")
+    ap.add_argument("--mixer-hidden", type=int, default=7168, help="hidden size of the mixer measurement")
     ap.add_argument("--backward-steps", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--path", choices=("fused", "unfused"), default="fused")
@@ -452,6 +455,62 @@ def bench_backward(torch, kda, ki, args, dev):
                                   "hbm_frac": pro_bytes / (ms_pro * 1e-3) / 1e9 / HBM_PEAK_GBS}}
 
 
+def bench_mixer(torch, kda, ki, args, dev):
+    """The KDA mixer on one 4096-token sequence: input projection (hidden ->
+    q, k, v, gate, decay, beta), the fused prefill, output projection.  The
+    pages give no hidden size; --mixer-hidden sets a synthetic one.  The two
+    projections are MFMA-bound GEMMs: each is timed alone and priced on its
+    dense bf16 flops, 2 T hidden N."""
+    T, hidden = 4096, args.mixer_hidden
+    inp = ki.mixer_inputs(11, [T], hidden, H, D, K)
+    g = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in inp.items()}
+    cu_h = inp["cu_seqlens"]
+    n_in, n_out = 5 * H * D + H, hidden
+    outs = kda.in_projection(g["x"], g["w_in"], H, D, g["a_log"], g["dt_bias"])
+    y = torch.empty(T, H * D, dtype=torch.bfloat16, device=dev).normal_()
+    o = kda.out_projection(y, g["w_out"])
+    ws = torch.empty(kda.mixer_workspace_bytes(H, D, 1, T), dtype=torch.uint8, device=dev)
+    fs = torch.empty(1, H, D, D, dtype=torch.float32, device=dev)
+    cco = torch.empty_like(g["conv_cache"])
+
+    def mixer():
+        kda.mixer_prefill(g["x"], g["w_in"], g["w_out"], g["conv_w"], g["cu_seqlens"], g["a_log"], g["dt_bias"],
+                          g["initial_state"], g["conv_cache"], cco, H=H, d=D, final_state=fs, out=o,
+                          workspace=ws, cu_seqlens_host=cu_h)
+
+    def timed(fn, reps):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    reps = max(args.steps // 2, 5)
+    ms_in = timed(lambda: kda.in_projection(g["x"], g["w_in"], H, D, g["a_log"], g["dt_bias"], outs=outs), reps)
+    ms_out = timed(lambda: kda.out_projection(y, g["w_out"], out=o), reps)
+    ms_mix = timed(mixer, reps)
+    f_in, f_out = 2.0 * T * hidden * n_in, 2.0 * T * H * D * n_out
+    tf_in, tf_out = f_in / (ms_in * 1e-3) / 1e12, f_out / (ms_out * 1e-3) / 1e12
+    tf_mix = (f_in + f_out) / (ms_mix * 1e-3) / 1e12
+    return {"workload": f"KDA mixer, 1 sequence x {T} tokens, hidden {hidden} (synthetic), H=32 dk=dv=128, conv 4: "
+                        "input projection, fused prefill, output projection; bf16 weights and activations",
+            "value": T / (ms_mix * 1e-3), "unit": "tokens/s", "ms_per_step": ms_mix, "steps": reps,
+            "in_projection": {"ms_per_call": ms_in, "shape": f"[{T} x {hidden}] x [{n_in} x {hidden}]^T",
+                              "tflops": tf_in, "mfma_frac": tf_in / BF16_PEAK_TFLOPS},
+            "out_projection": {"ms_per_call": ms_out, "shape": f"[{T} x {H * D}] x [{n_out} x {H * D}]^T",
+                               "tflops": tf_out, "mfma_frac": tf_out / BF16_PEAK_TFLOPS},
+            "roofline": {"bound": "mfma", "achieved": tf_in, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": tf_in / BF16_PEAK_TFLOPS, "traffic": None, "kernel": "gemm_kernel<1> (input projection)",
+                         "flop_per_launch": f_in},
+            "projection_flops_frac_of_step": (f_in + f_out) / (ms_mix * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
+            "step_tflops": tf_mix}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -490,6 +549,8 @@ def main():
         res["decode"] = bench_decode(torch, kda, ki, args, dev)
     if not args.no_backward:
         res["backward"] = bench_backward(torch, kda, ki, args, dev)
+    if not args.no_mixer:
+        res["mixer"] = bench_mixer(torch, kda, ki, args, dev)
     res["copy_gbs"] = copy_bandwidth(torch, dev)
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(ki, args.cpu_seconds)

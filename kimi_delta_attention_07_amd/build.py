@@ -4,7 +4,10 @@
 
 Each source is compiled to an object under _build/ (in parallel), then
 linked into kimi_delta_attention_07_amd/libkda.so.  Every device compile
-disables packed-fp32 instructions (-packed-fp32-ops).
+disables packed-fp32 instructions (-packed-fp32-ops).  Sources listed in
+EXTRA_FLAGS get their own additional options: the projection GEMM keeps its
+MFMA accumulators in architectural VGPRs (-amdgpu-mfma-vgpr-form), where the
+compiler updates them in place instead of copying them between AGPRs.
 """
 from __future__ import annotations
 
@@ -26,10 +29,12 @@ FLAGS = [
     "-Wall", "-Wno-unused-function", "-I" + os.path.join(ROOT, "include"),
 ]
 
+EXTRA_FLAGS = {"proj.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form=1"]}
+
 
 def _compile(src):
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, *FLAGS, *EXTRA_FLAGS.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
