@@ -93,6 +93,9 @@ class Oracle:
                                              _D, _D, _D, _D, _D, _D, _D, _D, _D, _D]
         L.kda_oracle_linear.argtypes = [ctypes.c_long, ctypes.c_int, ctypes.c_int, _D, _D, _D]
         L.kda_oracle_log_decay.argtypes = [ctypes.c_long, ctypes.c_int, ctypes.c_int, _D, _D, _D, _D]
+        L.kda_oracle_mla_decode_step.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                                 ctypes.c_int, ctypes.c_int, ctypes.c_double, _I, _D, _D, _D, _D,
+                                                 _D, _D, _D]
 
     def num_threads(self):
         return int(self.lib.kda_oracle_num_threads())
@@ -191,6 +194,26 @@ class Oracle:
         return dict(q_raw=seg(0), k_raw=seg(1), v_raw=seg(2), gate_logit=seg(3),
                     log_alpha=self.log_decay(np.ascontiguousarray(seg(4)), a_log, bias),
                     beta_logit=y[:, 5 * C:5 * C + H])
+
+    def mla_decode_step(self, q, k_new, v_new, k_cache, v_cache, cache_len, gate_logit=None, scale=None):
+        """One MLA decode token (NoPE).  q [B, H, d_qk], k_new [B, H_kv, d_qk],
+        v_new [B, H_kv, d_v], gate_logit [B, H, d_v] or None; k_cache
+        [B, H_kv, max_len, d_qk] and v_cache [B, H_kv, max_len, d_v] must be
+        float64 numpy arrays and are updated in place (the new token is written
+        at cache_len[b]).  scale None = 1 / sqrt(d_qk).  Returns out
+        [B, H, d_v]."""
+        for c in (k_cache, v_cache):
+            assert c.dtype == np.float64 and c.flags.c_contiguous
+        q, kn, vn, gl = _f64(q), _f64(k_new), _f64(v_new), _f64(gate_logit)
+        B, H, dqk = q.shape
+        Hkv, L, dv = v_cache.shape[1], v_cache.shape[2], v_cache.shape[3]
+        assert H % Hkv == 0 and k_cache.shape == (B, Hkv, L, dqk) and v_cache.shape[0] == B
+        if scale is None:
+            scale = 1.0 / np.sqrt(dqk)
+        out = np.zeros((B, H, dv))
+        self.lib.kda_oracle_mla_decode_step(B, H, Hkv, dqk, dv, L, float(scale), _p(_i32(cache_len), _I), _p(q),
+                                            _p(kn), _p(vn), _p(gl), _p(k_cache), _p(v_cache), _p(out))
+        return out
 
     # ---- composed paths ----------------------------------------------------
     def prologue(self, inp, act=ACT_SILU, eps=L2_EPS, cache_in=None):

@@ -42,6 +42,10 @@
  *    pages do not say how log alpha comes from the projection; with a_log and
  *    bias absent it is -softplus(z), which maps any real onto log alpha <= 0),
  *    and the output projection back to the hidden size.
+ *  - the MLA decode token (kimi_k3 API docs, Functions: mla_decode_token and
+ *    gated_mla_attend): append the new token's k and v to the per-sequence
+ *    cache, softmax attention of each head's q over every cached token, then
+ *    the optional sigmoid output gate (NoPE: no rotary step).
  *
  * Readings taken where the pages are silent: conv tap K-1 multiplies the
  * current token, no conv bias, zero history at a sequence start unless a
@@ -474,4 +478,71 @@ void kda_oracle_log_decay(long rows, int H, int d, const double *z, const double
                 la[e] = -A * softplus(z[e] + (bias ? bias[h * d + c] : 0.0));
             }
         }
+}
+
+/* ---------------------------------------------------------------------------
+ * The MLA decode token (kimi_k3 API docs, Functions: mla_decode_token, whose
+ * steps are optional RoPE, K/V append, SDPA and an optional output gate, and
+ * gated_mla_attend, the gated NoPE form that skips RoPE).  The projections
+ * stay outside, in the MLA mixer, so the step sees each head's q and the new
+ * token's per-head k and v.  Readings where the docs stop: the cache holds
+ * one k (d_qk = nope + rope channels) and one v (d_v channels) per token and
+ * kv head; the new token goes to position cache_len[b] and then attends to
+ * positions 0 .. cache_len[b] inclusive; q head h reads kv head
+ * h / (H / H_kv); the attention is softmax(scale q k^T) v; the gate is
+ * sigmoid(gate_logit) per (head, value channel), multiplied into the output.
+ * NoPE: no rotary step.  A sequence whose cache_len is outside
+ * [0, max_len) is left alone: its caches are not written and its output is 0.
+ * ------------------------------------------------------------------------- */
+
+/* q [batch][H][d_qk], k_new [batch][H_kv][d_qk], v_new [batch][H_kv][d_v],
+ * gate_logit [batch][H][d_v] or NULL, k_cache [batch][H_kv][max_len][d_qk],
+ * v_cache [batch][H_kv][max_len][d_v] (both updated), out [batch][H][d_v]. */
+void kda_oracle_mla_decode_step(int batch, int H, int H_kv, int d_qk, int d_v, int max_len, double scale,
+                                const int32_t *cache_len, const double *q, const double *k_new,
+                                const double *v_new, const double *gate_logit, double *k_cache,
+                                double *v_cache, double *out) {
+    const int G = H / H_kv;
+    for (int b = 0; b < batch; ++b) {
+        const int pos = cache_len[b];
+        if (pos < 0 || pos >= max_len) {
+            for (int i = 0; i < H * d_v; ++i) out[(long)b * H * d_v + i] = 0.0;
+            continue;
+        }
+        /* append */
+        for (int hk = 0; hk < H_kv; ++hk) {
+            double *kc = k_cache + (((long)b * H_kv + hk) * max_len + pos) * d_qk;
+            double *vc = v_cache + (((long)b * H_kv + hk) * max_len + pos) * d_v;
+            for (int c = 0; c < d_qk; ++c) kc[c] = k_new[((long)b * H_kv + hk) * d_qk + c];
+            for (int c = 0; c < d_v; ++c) vc[c] = v_new[((long)b * H_kv + hk) * d_v + c];
+        }
+        /* SDPA per q head over the pos + 1 cached tokens */
+        double *s = malloc(sizeof(double) * (pos + 1));
+        for (int h = 0; h < H; ++h) {
+            const int hk = h / G;
+            const double *qh = q + ((long)b * H + h) * d_qk;
+            const double *K = k_cache + ((long)b * H_kv + hk) * max_len * d_qk;
+            const double *V = v_cache + ((long)b * H_kv + hk) * max_len * d_v;
+            double m = -INFINITY;
+            for (int j = 0; j <= pos; ++j) {
+                double dot = 0.0;
+                for (int c = 0; c < d_qk; ++c) dot += qh[c] * K[(long)j * d_qk + c];
+                s[j] = scale * dot;
+                if (s[j] > m) m = s[j];
+            }
+            double den = 0.0;
+            for (int j = 0; j <= pos; ++j) {
+                s[j] = exp(s[j] - m);
+                den += s[j];
+            }
+            double *o = out + ((long)b * H + h) * d_v;
+            for (int c = 0; c < d_v; ++c) {
+                double acc = 0.0;
+                for (int j = 0; j <= pos; ++j) acc += s[j] * V[(long)j * d_v + c];
+                o[c] = acc / den;
+                if (gate_logit) o[c] *= sigmoid(gate_logit[((long)b * H + h) * d_v + c]);
+            }
+        }
+        free(s);
+    }
 }
