@@ -18,8 +18,9 @@ kda_decode_step calls with distinct inputs) and reported under "decode".
 The chunked backward (kda_chunk_backward) on the prefill workload's shapes is
 reported under "backward", the packed varlen and long-context prefill
 workloads under "prefill_workloads", and the KDA mixer (input projection,
-prefill, output projection at a synthetic hidden size) under "mixer"
-(informative; the headline stays the 4096-token sequence).
+prefill, output projection at a synthetic hidden size) under "mixer", and
+the MLA decode token under "mla_decode" (informative; the headline stays the
+4096-token sequence).
 
 Every kernel is timed with HIP events on the stream it is launched on.  The
 roofline object counts the path's algorithmic bytes only (49,216 B per token:
@@ -154,6 +155,7 @@ def parse():
     ap.add_argument("--no-workloads", action="store_true",
                     help="skip the varlen and long-context prefill measurements")
     ap.add_argument("--no-mixer", action="store_true", help="skip the KDA mixer (projections) measurement")
+    ap.add_argument("--no-mla", action="store_true", help="skip the MLA decode measurement")
     ap.add_argument("--mixer-hidden", type=int, default=7168, help="hidden size of the mixer measurement")
     ap.add_argument("--backward-steps", type=int, default=10)
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -511,6 +513,50 @@ def bench_mixer(torch, kda, ki, args, dev):
             "step_tflops": tf_mix}
 
 
+def bench_mla(torch, kda, ki, args, dev):
+    """The MLA decode token on 16 sequences x 64 heads, 192 q/k channels
+    (128 nope + 64 rope), 128 value channels, a 4096-slot bf16 K/V cache
+    filled to U[1024, 4095] tokens (the pages give the tiny config's widths
+    only; these are synthetic).  Repeated calls rewrite the same slot, so
+    every call does the same work.  Priced on HBM bytes: the cached k and v
+    of every sequence's tokens, q, the new k and v (read, then written into
+    the cache), the gate logits in and the output out."""
+    B, Hq, Hkv, dqk, dv, L = 16, 64, 64, 192, 128, 4096
+    inp = ki.mla_inputs(45, B, Hq, Hkv, dqk, dv, L, len_range=(1024, 4095))
+    g = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in inp.items()}
+    ws = torch.empty(kda.mla_decode_workspace_bytes(Hq, Hkv, dqk, dv, B, L), dtype=torch.uint8, device=dev)
+    out = torch.empty(B, Hq, dv, dtype=torch.bfloat16, device=dev)
+
+    def one():
+        kda.mla_decode_step(g["q"], g["k_new"], g["v_new"], g["k_cache"], g["v_cache"], g["cache_len"],
+                            g["gate_logit"], out=out, workspace=ws)
+
+    for _ in range(3):
+        one()
+    torch.cuda.synchronize()
+    reps = max(args.steps, 20)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
+    evs[0].record()
+    for i in range(reps):
+        one()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(reps))
+    ms = per[reps // 2]
+    tokens = int(inp["cache_len"].sum())
+    nbytes = (tokens * Hkv * (dqk + dv) * 2 + B * Hq * dqk * 2 + 2 * B * Hkv * (dqk + dv) * 2
+              + 2 * B * Hq * dv * 2)
+    gbs = nbytes / (ms * 1e-3) / 1e9
+    return {"workload": f"MLA decode token, {B} sequences x {Hq} heads ({Hkv} kv heads), q/k {dqk} (128 nope + 64 "
+                        f"rope, NoPE), v {dv}, bf16 K/V cache of {L} slots holding U[1024, 4095] tokens "
+                        f"({tokens} in all), gated",
+            "value": B / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "steps": reps,
+            "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "kernel": "mla_attend_kernel<3, 2, true> + mla_combine_kernel (one call)",
+                         "bytes_per_launch": nbytes}}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -551,6 +597,8 @@ def main():
         res["backward"] = bench_backward(torch, kda, ki, args, dev)
     if not args.no_mixer:
         res["mixer"] = bench_mixer(torch, kda, ki, args, dev)
+    if not args.no_mla:
+        res["mla_decode"] = bench_mla(torch, kda, ki, args, dev)
     res["copy_gbs"] = copy_bandwidth(torch, dev)
     if not args.no_cpu:
         res["cpu_baseline"] = cpu_baseline(ki, args.cpu_seconds)

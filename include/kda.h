@@ -394,6 +394,61 @@ kda_status kda_chunk_backward(const kda_geom *geom, int32_t n_seqs, int32_t tota
                               float *dq, float *dk, float *dv, float *dlog_alpha, float *dbeta, float *dgate,
                               float *d_initial_state, void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * The MLA decode token: the other mixer of the hybrid decoder, one token per
+ * sequence (kimi_k3 API docs, Functions: mla_decode_token, whose steps are
+ * optional RoPE, K/V append, SDPA and an optional output gate, the
+ * projections staying in the MLA mixer; gated_mla_attend, the gated NoPE
+ * form without the rotary step, which this is).  Per sequence b and query
+ * head h, with kv head h / (H / H_kv) and pos = cache_len[b]:
+ *   k_cache[b][kv][pos] = k_new[b][kv], v_cache[b][kv][pos] = v_new[b][kv];
+ *   o = softmax over j = 0 .. pos of (scale q[b][h] . k_cache[b][kv][j]),
+ *       applied to v_cache[b][kv][j];
+ *   out[b][h] = o * sigmoid(gate_logit[b][h])   (no gate: o).
+ * The cache holds one k and one v per token and kv head (the docs' MlaKv
+ * holds a layer's K/V; the layout is this library's); the new token's
+ * position is the count of tokens already cached; the gate is elementwise
+ * per (head, value channel).  These are readings of the docs.
+ *
+ *   geom: H query heads and H_kv kv heads (H a multiple of H_kv), d_qk q/k
+ *     channels per head (nope + rope), d_v value channels, both in [1, 256];
+ *     scale the softmax scale (1 / sqrt(d_qk) is the usual one);
+ *   batch in [0, 65535] sequences, max_len the cache capacity in tokens;
+ *   cache_len_dev [batch] int32, device: tokens already cached per sequence.
+ *     The call neither reads past it nor advances it (the caller adds 1 after
+ *     the call).  A sequence whose cache_len is outside [0, max_len) is left
+ *     alone: nothing is written to its caches and its output is 0;
+ *   q [batch][H][d_qk], k_new [batch][H_kv][d_qk], v_new [batch][H_kv][d_v],
+ *     gate_logit [batch][H][d_v] or NULL: bf16, device;
+ *   k_cache [batch][H_kv][max_len][d_qk], v_cache [batch][H_kv][max_len][d_v]:
+ *     bf16, device, caller-owned; the call writes slot pos of each and reads
+ *     slots 0 .. pos - 1 (nothing else);
+ *   out [batch][H][d_v] bf16, device, overwritten;
+ *   workspace: device, 16-byte aligned, at least
+ *     kda_mla_decode_workspace_bytes() bytes, contents not needed before or
+ *     after the call (split partials: 8 + 4 d_v bytes per (sequence, head,
+ *     256 cache slots)).
+ * fp32 scores, softmax and accumulation.  Every pointer must be 16-byte
+ * aligned (KDA_ERR_ALIGN).  Stream-ordered; calls that share a workspace or
+ * a cache must not overlap.  Errors: KDA_ERR_NULL, KDA_ERR_SHAPE,
+ * KDA_ERR_UNSUPPORTED (head dims above 256), KDA_ERR_ALIGN,
+ * KDA_ERR_WORKSPACE, KDA_ERR_HIP; nothing is launched when validation fails.
+ */
+typedef struct {
+    int32_t H;      /* query heads */
+    int32_t H_kv;   /* key/value heads; H % H_kv == 0 */
+    int32_t d_qk;   /* q and k channels per head (nope + rope) */
+    int32_t d_v;    /* value channels per head */
+    float scale;    /* softmax scale */
+} kda_mla_geom;
+
+size_t kda_mla_decode_workspace_bytes(const kda_mla_geom *geom, int32_t batch, int32_t max_len);
+
+kda_status kda_mla_decode_step(const kda_mla_geom *geom, int32_t batch, int32_t max_len,
+                               const int32_t *cache_len_dev, const void *q, const void *k_new, const void *v_new,
+                               const void *gate_logit, void *k_cache, void *v_cache, void *out, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
 /* Short name of a status code (static string). */
 const char *kda_status_str(kda_status s);
 /* Sentence describing the last error returned on the calling thread ("" if none). */

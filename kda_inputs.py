@@ -152,6 +152,31 @@ def mixer_inputs(seed, lengths, hidden, H, d, K, state_std=0.01):
                 initial_state=s0, conv_cache=cache)
 
 
+def mla_inputs(seed, batch, H, H_kv, d_qk, d_v, max_len, lens=None, len_range=None, gate=True):
+    """One MLA decode token for a batch: q [B, H, d_qk], k_new [B, H_kv, d_qk],
+    v_new [B, H_kv, d_v], gate_logit [B, H, d_v], caches [B, H_kv, max_len,
+    d_qk / d_v] (every slot filled, written or not), cache_len [B] int32.
+
+    Draw order: lengths (given, or U[len_range] inclusive), q, k_new, v_new,
+    k_cache, v_cache, gate; all N(0, 1) drawn in fp32 and rounded to bf16.
+    The pages give no MLA widths beyond the tiny config's; these are
+    synthetic."""
+    g = torch.Generator().manual_seed(seed)
+    if lens is None:
+        lo, hi = len_range
+        lens = torch.randint(lo, hi + 1, (batch,), generator=g).tolist()
+    cache_len = torch.tensor([int(x) for x in lens], dtype=torch.int32)
+    bf = lambda shape: _normal(g, shape).to(torch.bfloat16)
+    q = bf((batch, H, d_qk))
+    k_new = bf((batch, H_kv, d_qk))
+    v_new = bf((batch, H_kv, d_v))
+    k_cache = bf((batch, H_kv, max_len, d_qk))
+    v_cache = bf((batch, H_kv, max_len, d_v))
+    gate_logit = bf((batch, H, d_v)) if gate else None
+    return dict(seed=seed, batch=batch, H=H, H_kv=H_kv, d_qk=d_qk, d_v=d_v, max_len=max_len, cache_len=cache_len,
+                q=q, k_new=k_new, v_new=v_new, k_cache=k_cache, v_cache=v_cache, gate_logit=gate_logit)
+
+
 def tokens_as_steps(inp):
     """Split a single-sequence prefill input into per-token decode steps
     (pure re-layout: token t becomes step t with batch 1)."""

@@ -12,6 +12,7 @@ include/kda.h); this package is its thin Python binding:
     decode_step(...)    one token for a batch of resident fp32 states
     in_projection(...), out_projection(...), mixer_prefill(...)
                         the mixer's linear maps around the operator, and the whole mixer
+    mla_decode_step(...) the MLA mixer's decode token: K/V append, attention, output gate
 
 Build the library with ``python -m kimi_delta_attention_07_amd.build``.
 """
@@ -34,6 +35,8 @@ from ._lib import (  # noqa: F401
     out_projection,
     mixer_prefill,
     mixer_workspace_bytes,
+    mla_decode_step,
+    mla_decode_workspace_bytes,
     prefill_prepare,
     prefill_scan,
     prologue,

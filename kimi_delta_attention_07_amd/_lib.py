@@ -23,7 +23,8 @@ EXPORTS = ("kda_prologue", "kda_chunk_workspace_bytes", "kda_chunk_forward", "kd
            "kda_chunk_scan", "kda_prefill", "kda_prefill_prepare", "kda_prefill_scan", "kda_decode_step",
            "kda_chunk_backward_workspace_bytes", "kda_chunk_backward", "kda_prologue_backward_workspace_bytes",
            "kda_prologue_backward", "kda_prefill_noalloc", "kda_in_projection", "kda_out_projection",
-           "kda_mixer_workspace_bytes", "kda_mixer_prefill", "kda_status_str", "kda_last_error_detail")
+           "kda_mixer_workspace_bytes", "kda_mixer_prefill", "kda_mla_decode_workspace_bytes",
+           "kda_mla_decode_step", "kda_status_str", "kda_last_error_detail")
 
 
 class KdaError(RuntimeError):
@@ -36,6 +37,11 @@ class KdaError(RuntimeError):
 class Geom(ctypes.Structure):
     _fields_ = [("H", ctypes.c_int32), ("d", ctypes.c_int32), ("conv_k", ctypes.c_int32),
                 ("act", ctypes.c_int32), ("l2_eps", ctypes.c_float), ("scale", ctypes.c_float)]
+
+
+class MlaGeom(ctypes.Structure):
+    _fields_ = [("H", ctypes.c_int32), ("H_kv", ctypes.c_int32), ("d_qk", ctypes.c_int32),
+                ("d_v", ctypes.c_int32), ("scale", ctypes.c_float)]
 
 
 _P = ctypes.c_void_p
@@ -89,6 +95,11 @@ def load(path=LIB_PATH):
     L.kda_decode_step.argtypes = [G, _I, _P, _I, _I] + [_P] * 9 + [_I, _P, _P]
     L.kda_decode_step.restype = _I
     L.kda_status_str.argtypes = [_I]
+    MG = ctypes.POINTER(MlaGeom)
+    L.kda_mla_decode_workspace_bytes.argtypes = [MG, _I, _I]
+    L.kda_mla_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.kda_mla_decode_step.argtypes = [MG, _I, _I] + [_P] * 9 + [ctypes.c_size_t, _P]
+    L.kda_mla_decode_step.restype = _I
     L.kda_status_str.restype = ctypes.c_char_p
     L.kda_last_error_detail.argtypes = []
     L.kda_last_error_detail.restype = ctypes.c_char_p
@@ -401,4 +412,34 @@ def decode_step(q_raw, k_raw, v_raw, conv_w, conv_cache, state, log_alpha, beta_
                                   _ptr(k_raw), _ptr(v_raw), _ptr(conv_w), _ptr(conv_cache), _ptr(state),
                                   _ptr(log_alpha), _ptr(beta_logit), _ptr(gate_logit), _dtype(out), _ptr(out),
                                   _stream(q_raw)))
+    return out
+
+
+def mla_geom(H, H_kv, d_qk, d_v, scale=None):
+    return MlaGeom(H, H_kv, d_qk, d_v, float(d_qk ** -0.5 if scale is None else scale))
+
+
+def mla_decode_workspace_bytes(H, H_kv, d_qk, d_v, batch, max_len):
+    g = mla_geom(H, H_kv, d_qk, d_v)
+    return int(load().kda_mla_decode_workspace_bytes(ctypes.byref(g), batch, max_len))
+
+
+def mla_decode_step(q, k_new, v_new, k_cache, v_cache, cache_len, gate_logit=None, *, scale=None, out=None,
+                    workspace=None):
+    """One MLA decode token (NoPE) for a batch: q [B, H, d_qk], k_new
+    [B, H_kv, d_qk], v_new [B, H_kv, d_v], gate_logit [B, H, d_v] or None,
+    caches [B, H_kv, max_len, d_qk / d_v], all bf16 on the device;
+    cache_len [B] int32 on the device (tokens already cached; not advanced).
+    Writes the new token into the caches and returns out [B, H, d_v] bf16."""
+    B, H, dqk = q.shape
+    Hkv, L, dv = v_cache.shape[1], v_cache.shape[2], v_cache.shape[3]
+    g = mla_geom(H, Hkv, dqk, dv, scale)
+    if workspace is None:
+        workspace = torch.empty(max(mla_decode_workspace_bytes(H, Hkv, dqk, dv, B, L), 16), dtype=torch.uint8,
+                                device=q.device)
+    if out is None:
+        out = torch.empty((B, H, dv), dtype=torch.bfloat16, device=q.device)
+    _check(load().kda_mla_decode_step(ctypes.byref(g), B, L, _ptr(cache_len), _ptr(q), _ptr(k_new), _ptr(v_new),
+                                      _ptr(gate_logit), _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(workspace),
+                                      workspace.numel(), _stream(q)))
     return out

@@ -21,7 +21,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libkda.so")
-SOURCES = ["kda_abi.cpp", "decode.hip", "prologue.hip", "chunk.hip", "backward.hip", "prologue_bwd.hip", "proj.hip"]
+SOURCES = ["kda_abi.cpp", "decode.hip", "prologue.hip", "chunk.hip", "backward.hip", "prologue_bwd.hip", "proj.hip", "mla.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-fPIC", "-std=c++17",

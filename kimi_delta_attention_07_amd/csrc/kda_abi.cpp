@@ -6,7 +6,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -794,6 +796,80 @@ kda_status kda_prefill_noalloc(const kda_geom *geom, int32_t n_seqs, int32_t tot
     return kda_prefill(geom, n_seqs, total_tokens, cu_seqlens_dev, cu_seqlens_host, in_dtype, chunk, q_raw, k_raw,
                        v_raw, conv_w, conv_cache_in, conv_cache_out, log_alpha, beta_logit, gate_logit,
                        initial_state, final_state, out, ws, (size_t)KDA_NOALLOC_SCRATCH_BYTES, stream);
+}
+
+// ---------------------------------------------------------------------------
+// MLA decode token
+// ---------------------------------------------------------------------------
+namespace {
+
+kda_status check_mla_geom(const kda_mla_geom *g) {
+    if (!g) return fail(KDA_ERR_NULL, "geom is NULL");
+    if (g->H <= 0 || g->H_kv <= 0 || g->H % g->H_kv != 0)
+        return fail(KDA_ERR_SHAPE, "H = %d and H_kv = %d: both must be > 0 and H a multiple of H_kv", g->H, g->H_kv);
+    if (g->d_qk <= 0 || g->d_v <= 0) return fail(KDA_ERR_SHAPE, "d_qk = %d and d_v = %d must be > 0", g->d_qk, g->d_v);
+    if (g->d_qk > 256 || g->d_v > 256)
+        return fail(KDA_ERR_UNSUPPORTED, "d_qk = %d and d_v = %d must be <= 256", g->d_qk, g->d_v);
+    if (!std::isfinite(g->scale)) return fail(KDA_ERR_SHAPE, "scale must be finite");
+    return KDA_OK;
+}
+
+long mla_n_split(int32_t max_len) { return (max_len - 1) / kda::mla_split_tokens() + 1; }
+
+}  // namespace
+
+size_t kda_mla_decode_workspace_bytes(const kda_mla_geom *geom, int32_t batch, int32_t max_len) {
+    if (check_mla_geom(geom) != KDA_OK || batch < 0 || max_len <= 0) return 0;
+    const size_t n = (size_t)batch * geom->H * mla_n_split(max_len);
+    return al256(n * 2 * sizeof(float)) + al256(n * geom->d_v * sizeof(float));
+}
+
+kda_status kda_mla_decode_step(const kda_mla_geom *geom, int32_t batch, int32_t max_len,
+                               const int32_t *cache_len_dev, const void *q, const void *k_new, const void *v_new,
+                               const void *gate_logit, void *k_cache, void *v_cache, void *out, void *workspace,
+                               size_t workspace_bytes, void *stream) {
+    KDA_TRY(check_mla_geom(geom));
+    if (batch < 0 || batch > 65535) return fail(KDA_ERR_SHAPE, "batch = %d must be in [0, 65535]", batch);
+    if (geom->H > 65535) return fail(KDA_ERR_SHAPE, "H = %d must be <= 65535", geom->H);
+    if (max_len <= 0) return fail(KDA_ERR_SHAPE, "max_len = %d must be > 0", max_len);
+    // one buffer resource spans a (sequence, kv head) cache block, and one the
+    // whole q; each must stay below 4 GiB
+    if ((long)max_len * std::max(geom->d_qk, geom->d_v) * 2 >= (1L << 32) ||
+        (long)batch * geom->H * std::max(geom->d_qk, geom->d_v) * 2 >= (1L << 32))
+        return fail(KDA_ERR_SHAPE, "max_len = %d or batch = %d too large for 32-bit offsets", max_len, batch);
+    if (batch == 0) return ok();
+    KDA_TRY(check_required({{cache_len_dev, "cache_len_dev"}, {q, "q"}, {k_new, "k_new"}, {v_new, "v_new"},
+                            {k_cache, "k_cache"}, {v_cache, "v_cache"}, {out, "out"}, {workspace, "workspace"}}));
+    KDA_TRY(check_aligned({{cache_len_dev, "cache_len_dev"}, {q, "q"}, {k_new, "k_new"}, {v_new, "v_new"},
+                           {gate_logit, "gate_logit"}, {k_cache, "k_cache"}, {v_cache, "v_cache"}, {out, "out"},
+                           {workspace, "workspace"}}));
+    const size_t need = kda_mla_decode_workspace_bytes(geom, batch, max_len);
+    if (workspace_bytes < need)
+        return fail(KDA_ERR_WORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, need);
+    KDA_TRY(check_device());
+    kda::MlaParams p{};
+    p.batch = batch;
+    p.H = geom->H;
+    p.H_kv = geom->H_kv;
+    p.dqk = geom->d_qk;
+    p.dv = geom->d_v;
+    p.max_len = max_len;
+    p.n_split = (int)mla_n_split(max_len);
+    p.scale = geom->scale;
+    p.cache_len = cache_len_dev;
+    p.q = q;
+    p.k_new = k_new;
+    p.v_new = v_new;
+    p.gate = gate_logit;
+    p.k_cache = k_cache;
+    p.v_cache = v_cache;
+    p.out = out;
+    const size_t n = (size_t)batch * geom->H * p.n_split;
+    p.ws_ml = static_cast<float *>(workspace);
+    p.ws_acc = reinterpret_cast<float *>(static_cast<unsigned char *>(workspace) + al256(n * 2 * sizeof(float)));
+    // whole 16-byte chunks when every row is a multiple of 8 channels
+    const bool vec = geom->d_qk % 8 == 0 && geom->d_v % 8 == 0;
+    return launched(kda::launch_mla_decode(p, vec, (hipStream_t)stream), "mla decode");
 }
 
 }  // extern "C"

@@ -137,6 +137,19 @@ struct ProjParams {
 };
 hipError_t launch_gemm(const ProjParams &p, hipStream_t s);
 
+// MLA decode token (mla.hip): bf16 q, k_new, v_new, gate, caches and output
+struct MlaParams {
+    int batch, H, H_kv, dqk, dv, max_len, n_split;
+    float scale;
+    const int32_t *cache_len;                 // [batch], device
+    const void *q, *k_new, *v_new, *gate;     // gate may be null
+    void *k_cache, *v_cache, *out;
+    float *ws_ml;                             // [batch][H][n_split][2]: max, sum
+    float *ws_acc;                            // [batch][H][n_split][dv]
+};
+int mla_split_tokens();
+hipError_t launch_mla_decode(const MlaParams &p, bool vec, hipStream_t s);
+
 size_t prologue_bwd_workspace_bytes(int H, int d, long T);
 hipError_t launch_prologue_backward(PrologueBwdParams p, int dtype, hipStream_t s);
 

@@ -310,3 +310,48 @@ def test_prologue_backward_rejects(L):
     p = list(FAKE[:20])
     p[16] = ctypes.c_void_p(0x10008)   # dconv_cache_in misaligned
     assert prologue_backward(L, ptrs=p) == ALIGN
+
+
+def _mla_geom(H=4, H_kv=2, d_qk=192, d_v=128, scale=0.07):
+    return ctypes.byref(_lib.MlaGeom(H, H_kv, d_qk, d_v, scale))
+
+
+def test_mla_workspace_bytes(L):
+    al = lambda x: (x + 255) // 256 * 256
+    # partials per (sequence, head, 256-slot split): max and sum, then d_v sums
+    n = 3 * 4 * ((1000 - 1) // 256 + 1)
+    assert L.kda_mla_decode_workspace_bytes(_mla_geom(), 3, 1000) == al(n * 8) + al(n * 128 * 4)
+    assert L.kda_mla_decode_workspace_bytes(_mla_geom(), 3, 256) == al(12 * 8) + al(12 * 128 * 4)
+    assert L.kda_mla_decode_workspace_bytes(_mla_geom(), 3, 257) == al(24 * 8) + al(24 * 128 * 4)
+    assert L.kda_mla_decode_workspace_bytes(None, 3, 1000) == 0
+    assert L.kda_mla_decode_workspace_bytes(_mla_geom(H=3), 3, 1000) == 0
+    assert L.kda_mla_decode_workspace_bytes(_mla_geom(), 3, 0) == 0
+
+
+@pytest.mark.parametrize("case,code", [
+    ("geom_null", NULL), ("H_not_multiple", SHAPE), ("H_kv0", SHAPE), ("dqk0", SHAPE), ("dv257", UNSUP),
+    ("scale_nan", SHAPE), ("batch_neg", SHAPE), ("batch_huge", SHAPE), ("max_len0", SHAPE),
+    ("q_null", NULL), ("cache_null", NULL), ("lens_null", NULL), ("misaligned", ALIGN), ("ws_small", WORKSPACE),
+])
+def test_mla_decode_rejects(L, case, code):
+    geom = {"geom_null": None, "H_not_multiple": _mla_geom(H=3), "H_kv0": _mla_geom(H_kv=0),
+            "dqk0": _mla_geom(d_qk=0), "dv257": _mla_geom(d_v=257),
+            "scale_nan": _mla_geom(scale=float("nan"))}.get(case, _mla_geom())
+    batch = {"batch_neg": -1, "batch_huge": 70000}.get(case, 2)
+    max_len = 0 if case == "max_len0" else 300
+    p = list(FAKE[:9])   # cache_len, q, k_new, v_new, gate, k_cache, v_cache, out, workspace
+    if case == "q_null":
+        p[1] = None
+    if case == "cache_null":
+        p[5] = None
+    if case == "lens_null":
+        p[0] = None
+    if case == "misaligned":
+        p[2] = ctypes.c_void_p(0x10008)
+    ws = 16 if case == "ws_small" else 1 << 30
+    assert L.kda_mla_decode_step(geom, batch, max_len, *p, ws, None) == code
+    assert L.kda_last_error_detail().decode() != ""
+
+
+def test_mla_decode_empty_batch_is_a_no_op(L):
+    assert L.kda_mla_decode_step(_mla_geom(), 0, 300, *([None] * 9), 0, None) == OK
