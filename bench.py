@@ -71,9 +71,13 @@ FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector, TFLOP/s
 # hash of those sources matches the one stored with it
 TRAFFIC_KERNEL = {"prologue": "prologue128_kernel<4, 1>", "chunk_prepare": "prepare_kernel<false, 4, 0>",
                   "chunk_scan": "scan_kernel<true, 1>", "prefill_prepare": "prepare_kernel<true, 4, 1>",
-                  "prefill_scan": "scan_kernel<true, 1>", "decode": "decode_kernel<128, 1, 0>"}
+                  "prefill_scan": "scan_kernel<true, 1>", "decode": "decode_kernel<128, 1, 0>",
+                  "in_projection": "gemm_kernel<1>", "out_projection": "gemm_kernel<0>",
+                  "mla_attend": "mla_attend_kernel<3, 2, true>", "mla_combine": "mla_combine_kernel"}
 KERNEL_SOURCES = {"prologue": ["prologue.hip"], "chunk_prepare": ["chunk.hip"], "chunk_scan": ["chunk.hip"],
-                  "prefill_prepare": ["chunk.hip"], "prefill_scan": ["chunk.hip"], "decode": ["decode.hip"]}
+                  "prefill_prepare": ["chunk.hip"], "prefill_scan": ["chunk.hip"], "decode": ["decode.hip"],
+                  "in_projection": ["proj.hip"], "out_projection": ["proj.hip"], "mla_attend": ["mla.hip"],
+                  "mla_combine": ["mla.hip"]}
 
 
 def _src_sha(slot):
@@ -507,8 +511,9 @@ def bench_mixer(torch, kda, ki, args, dev):
             "out_projection": {"ms_per_call": ms_out, "shape": f"[{T} x {H * D}] x [{n_out} x {H * D}]^T",
                                "tflops": tf_out, "mfma_frac": tf_out / BF16_PEAK_TFLOPS},
             "roofline": {"bound": "mfma", "achieved": tf_in, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": tf_in / BF16_PEAK_TFLOPS, "traffic": None, "kernel": "gemm_kernel<1> (input projection)",
-                         "flop_per_launch": f_in},
+                         "frac": tf_in / BF16_PEAK_TFLOPS, "traffic": measured_traffic("in_projection", "mixer"),
+                         "kernel": "gemm_kernel<1> (input projection)", "flop_per_launch": f_in,
+                         "mfma_counters": measured_mfma("in_projection", "mixer")},
             "projection_flops_frac_of_step": (f_in + f_out) / (ms_mix * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             "step_tflops": tf_mix}
 
@@ -547,14 +552,17 @@ def bench_mla(torch, kda, ki, args, dev):
     nbytes = (tokens * Hkv * (dqk + dv) * 2 + B * Hq * dqk * 2 + 2 * B * Hkv * (dqk + dv) * 2
               + 2 * B * Hq * dv * 2)
     gbs = nbytes / (ms * 1e-3) / 1e9
+    tr = [measured_traffic("mla_attend", "mla"), measured_traffic("mla_combine", "mla")]
+    mla_traffic = sum(tr) if all(t is not None for t in tr) else None
     return {"workload": f"MLA decode token, {B} sequences x {Hq} heads ({Hkv} kv heads), q/k {dqk} (128 nope + 64 "
                         f"rope, NoPE), v {dv}, bf16 K/V cache of {L} slots holding U[1024, 4095] tokens "
                         f"({tokens} in all), gated",
             "value": B / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "steps": reps,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": gbs / HBM_PEAK_GBS, "traffic": None,
+                         "frac": gbs / HBM_PEAK_GBS, "traffic": mla_traffic,
                          "kernel": "mla_attend_kernel<3, 2, true> + mla_combine_kernel (one call)",
-                         "bytes_per_launch": nbytes}}
+                         "bytes_per_launch": nbytes,
+                         "traffic_over_algorithmic": mla_traffic / nbytes if mla_traffic else None}}
 
 
 def main():

@@ -3,9 +3,9 @@
 the C ABI, against the CPU oracle on the same seeded inputs.
 
 Bars:
-  projections: |gpu - oracle| <= 2^-8 |oracle| + K 2^-24 S + 1e-6 per
-    element, S = sum_k |x_k w_k| (one bf16 rounding of the result plus the
-    fp32 accumulation bound over K terms in any order); the decay segment
+  projections: |gpu - oracle| <= 2^-8 |oracle| + (1 + 2^-8) K 2^-24 S + 1e-6
+    per element, S = sum_k |x_k w_k| (the fp32 accumulation bound over K
+    terms in any order, then one bf16 rounding of that fp32 value); the decay segment
     carries the bound of its pre-activation through -exp(a_log) softplus
     (slope <= exp(a_log)) plus one bf16 rounding;
   the operator inside the mixer: the chunked path's 2e-2 + 1e-2 |oracle|,
@@ -30,7 +30,9 @@ def assert_gemm_close(got, want, S, K, what, slope=None):
     got = np64(got)
     err = np.abs(got - want)
     acc = K * U * S * (1.0 if slope is None else slope)
-    bar = 2.0 ** -8 * np.abs(want) + acc + 1e-6
+    # the bf16 rounding acts on the fp32 result, which may already sit acc
+    # away from the exact value: 2^-8 (|want| + acc)
+    bar = 2.0 ** -8 * np.abs(want) + (1.0 + 2.0 ** -8) * acc + 1e-6
     bad = err > bar
     assert not bad.any(), f"{what}: {int(bad.sum())} elements beyond the bar (max abs {err.max():.3e})"
     print(f"PARITY {what}: max_abs {err.max():.3e} max_ref {np.abs(want).max():.3e} "
