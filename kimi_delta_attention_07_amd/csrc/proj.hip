@@ -9,23 +9,22 @@
 // either (16 rows x 8 consecutive k per lane) is one 16-byte read.  fp32
 // accumulation on v_mfma_f32_16x16x32_bf16, bf16 results.
 //
-// Block tile 256 (M) x 128 (N), K tile 64, eight waves (two per SIMD) in a
-// 4 x 2 grid, each owning 64 x 64 (4 x 4 MFMA tiles, 16 fp32x4 accumulators
-// kept in architectural VGPRs, which the compiler updates in place), one
-// block per CU.  While one wave of a SIMD waits for LDS, the other issues
-// MFMAs.  Tiles travel from memory straight into LDS (buffer loads with the
-// LDS destination: no staging registers) into a three-stage ring: tile kt + 2
-// is requested while tile kt is multiplied, so each load has two iterations
-// to arrive.  Per iteration a wave first waits for its own loads of tile kt
-// (its loads of tile kt + 1 may still be in flight), then the block barrier
-// makes every wave's part of tile kt visible and tells every wave that stage
-// (kt + 2) % 3, read during iteration kt - 1, is free again.  The three stages
-// are separate LDS arrays and the loop is unrolled by three, so the compiler
-// sees which stage each LDS read touches and never waits for a load into
-// another stage.  LDS rows are 128 bytes with the 16-byte chunk kc of row r
-// stored at chunk kc ^ ((r >> 1) & 7): the 16 rows of a fragment read then
-// cover all 64 banks once.  Out-of-range rows, weight rows, K tails and the
-// tiles past K's end load as zero through buffer resources.
+// Block tile 256 x 256, K tile 64, eight waves (two per SIMD) in a 2 x 4
+// grid, each owning 128 x 64 (8 x 4 MFMA tiles, 32 fp32x4 accumulators kept
+// in architectural VGPRs, which the compiler updates in place), one block per
+// CU.  While one wave of a SIMD waits for LDS, the other issues MFMAs.  Tiles
+// travel from memory straight into LDS (buffer loads with the LDS
+// destination: no staging registers) through two stages: tile kt + 1 is
+// requested while tile kt is multiplied.  Per iteration a wave first waits
+// for its own loads of tile kt and its LDS reads of tile kt - 1, then the
+// block barrier makes every wave's part of tile kt visible and frees the
+// stage that tile kt + 1 goes into.  The two stages are separate LDS arrays
+// and the loop is unrolled by two, so the compiler sees which stage each LDS
+// read touches and never waits for a load into the other one.  LDS rows are
+// 128 bytes with the 16-byte chunk kc of row r stored at chunk
+// kc ^ ((r >> 1) & 7): the 16 rows of a fragment read then cover all 64
+// banks once.  Out-of-range rows, weight rows, K tails and the tile past K's
+// end load as zero through buffer resources.
 //
 // Epilogues: plain (one [M][N] bf16 output) or the KDA input projection,
 // whose N columns are six segments: q, k, v, gate, decay (H d each,
@@ -40,9 +39,9 @@ namespace kda {
 
 namespace {
 
-constexpr int kBM = 256, kBN = 128, kBK = 64;
+constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kABytes = kBM * kBK * 2, kBBytes = kBN * kBK * 2;
-constexpr int kStage = kABytes + kBBytes;                // 49,152 B per K tile
+constexpr int kStage = kABytes + kBBytes;                // 65,536 B per K tile
 constexpr int kGroupM = 4;                               // M tiles per ordering group
 
 // byte offset of the 16-byte chunk kc (8 bf16) of row r in a 128-byte-row tile
@@ -61,14 +60,16 @@ __device__ __forceinline__ float softplus_f(float x) {
 
 typedef __attribute__((address_space(3))) unsigned char lds_byte;
 
-// s_waitcnt operand: vmcnt = n (n < 16), expcnt and lgkmcnt left unconstrained
+// s_waitcnt operands: vmcnt = n (n < 16), expcnt left unconstrained, and
+// lgkmcnt either unconstrained or 0
 constexpr int waitcnt_vm(int n) { return (n & 0xf) | (0x7 << 4) | (0xf << 8); }
+constexpr int waitcnt_vm_lgkm0(int n) { return (n & 0xf) | (0x7 << 4); }
 
 template <int EPI>
 __global__ __launch_bounds__(512, 1) void gemm_kernel(ProjParams p) {
-    __shared__ __attribute__((aligned(16))) unsigned char st0[kStage], st1[kStage], st2[kStage];
+    __shared__ __attribute__((aligned(16))) unsigned char st0[kStage], st1[kStage];
     const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w >> 1, wn = w & 1;   // 4 x 2 waves
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w >> 2, wn = w & 3;   // 2 x 4 waves
     const int tiles_m = (p.M + kBM - 1) / kBM, tiles_n = (p.N + kBN - 1) / kBN;
     const int total = tiles_m * tiles_n;
     // blocks go round the 8 XCDs in turn: XCD x = b % 8 takes a contiguous run
@@ -79,7 +80,9 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(ProjParams p) {
     const int u = x * xq + min(x, xr) + b / 8;
     const int per_group = kGroupM * tiles_n, first_m = (u / per_group) * kGroupM;
     const int gm = min(tiles_m - first_m, kGroupM), ug = u % per_group;
-    const int bm = first_m + ug % gm, bn = ug / gm;
+    // N tiles in reverse: a narrow last column (the input projection's beta
+    // outputs) is dispatched in the first round, not alone in an extra one
+    const int bm = first_m + ug % gm, bn = tiles_n - 1 - ug / gm;
     const int row0 = bm * kBM, col0 = bn * kBN;
     const int nk = (p.K + kBK - 1) / kBK;
     const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(p.a, (uint32_t)((long)p.M * p.K * 2));
@@ -87,8 +90,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(ProjParams p) {
 
     // tile kt into one stage: each load instruction fills 1 KB (8 rows) of the
     // stage, lane l the 16 bytes at 16 l; the lane fetches the chunk that the
-    // swizzle puts there.  A takes 4 instructions per wave, B 2: 6 per tile.
-    constexpr int kLoadsPerTile = 6;
+    // swizzle puts there.  A takes 4 instructions per wave, B 4: 8 per tile.
+    constexpr int kLoadsPerTile = 8;
     auto issue_tile = [&](int kt, unsigned char *st) {
         const int k0 = kt * kBK;
 #pragma unroll
@@ -100,8 +103,8 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(ProjParams p) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, (lds_byte *)(st + blk * 1024), 16, off, 0, 0, 0);
         }
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const int blk = w * 2 + i, r = blk * 8 + (l >> 3), kc = (l & 7) ^ ((r >> 1) & 7);
+        for (int i = 0; i < 4; ++i) {
+            const int blk = w * 4 + i, r = blk * 8 + (l >> 3), kc = (l & 7) ^ ((r >> 1) & 7);
             const int k = k0 + 8 * kc;
             const uint32_t off = (k < p.K && col0 + r < p.N) ? (uint32_t)(((long)(col0 + r) * p.K + k) * 2)
                                                              : 0xffffffffu;
@@ -109,48 +112,48 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(ProjParams p) {
         }
     };
 
-    f32x4 acc[4][4];
+    f32x4 acc[8][4];
 #pragma unroll
-    for (int m = 0; m < 4; ++m)
+    for (int m = 0; m < 8; ++m)
 #pragma unroll
         for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // one iteration: tile kt sits in stage `cur`; `nxt` (= stage (kt + 2) % 3)
-    // receives tile kt + 2
+    // one iteration: tile kt sits in stage `cur`; `nxt` (the other stage)
+    // receives tile kt + 1
     auto step = [&](int kt, const unsigned char *cur, unsigned char *nxt) {
         // the barrier without __syncthreads' fences, which would wait for every
         // load in flight; the empty asm statements keep the compiler from moving
-        // LDS accesses across it
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(kLoadsPerTile));   // this wave's part of tile kt
+        // LDS accesses across it.  Before it, each wave waits for its own part of
+        // tile kt and for its LDS reads of the previous tile (lgkmcnt 0), whose
+        // stage the loads issued after the barrier overwrite
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm_lgkm0(0));
         asm volatile("" ::: "memory");
         __builtin_amdgcn_s_barrier();                            // everyone's part; stage nxt free
         asm volatile("" ::: "memory");
-        issue_tile(kt + 2, nxt);
+        issue_tile(kt + 1, nxt);
         asm volatile("" ::: "memory");   // requests out before this tile's reads
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            bf16x8 fa[4], fb[4];
+            bf16x8 fa[8], fb[4];
 #pragma unroll
-            for (int m = 0; m < 4; ++m) fa[m] = lds_frag16(cur, swz(64 * wm + 16 * m + c16, 4 * kk + g));
+            for (int m = 0; m < 8; ++m) fa[m] = lds_frag16(cur, swz(128 * wm + 16 * m + c16, 4 * kk + g));
 #pragma unroll
             for (int n = 0; n < 4; ++n) fb[n] = lds_frag16(cur, kABytes + swz(64 * wn + 16 * n + c16, 4 * kk + g));
 #pragma unroll
-            for (int m = 0; m < 4; ++m)
+            for (int m = 0; m < 8; ++m)
 #pragma unroll
                 for (int n = 0; n < 4; ++n) acc[m][n] = mfma16(fa[m], fb[n], acc[m][n]);
         }
     };
 
     issue_tile(0, st0);
-    issue_tile(1, st1);
-    for (int kt = 0; kt < nk; kt += 3) {   // up to two trailing all-zero tiles
-        step(kt, st0, st2);
+    for (int kt = 0; kt < nk; kt += 2) {   // an odd nk adds one all-zero tile
+        step(kt, st0, st1);
         step(kt + 1, st1, st0);
-        step(kt + 2, st2, st1);
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // the trailing (all-zero) tile loads
 
-    // epilogue: element (m, n, r) is row row0 + 64 wm + 16 m + 4 g + r,
+    // epilogue: element (m, n, r) is row row0 + 128 wm + 16 m + 4 g + r,
     // column col0 + 64 wn + 16 n + c16
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
@@ -175,10 +178,10 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(ProjParams p) {
             }
         }
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
+        for (int m = 0; m < 8; ++m)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                const int row = row0 + 64 * wm + 16 * m + 4 * g + r;
+                const int row = row0 + 128 * wm + 16 * m + 4 * g + r;
                 float v = acc[m][n][r];
                 if (decay) v = -A * softplus_f(v + bias);
                 if (row < p.M) dst[(long)row * width + within] = f2bf(v);
