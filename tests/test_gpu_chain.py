@@ -1,11 +1,13 @@
-"""GPU parity of the composed layer gradient: kda_prologue, kda_chunk_backward
-on its outputs, then kda_prologue_backward on the gradients that reach them,
-against the oracle's recurrence and prologue gradients composed the same way
-(the composition is pinned by finite differences in test_oracle_chain.py).
-The oracle's recurrence gradient takes the GPU prologue's bf16 outputs, the
-point the chunk backward differentiates at; its prologue gradient works from
-the raw inputs, as the GPU's does.  Bar per tensor and element, as for each
-stage: |gpu - oracle| <= 1e-4 max|oracle| + 1e-3 |oracle|."""
+"""GPU parity of the composed layer gradient: kda_chunk_backward, then
+kda_prologue_backward on the gradients it produces, against the oracle's
+recurrence and prologue gradients composed the same way (the composition is
+pinned by finite differences in test_oracle_chain.py).  Both chains start
+from the oracle's forward prologue outputs rounded to bf16, the point the
+chunk backward differentiates at (the forward prologue kernel's own parity
+is tested on its own); both prologue gradients work from the raw inputs.
+The oracle is given seeded inputs and its own results only.  Bar per tensor
+and element, as for each stage: |gpu - oracle| <= 1e-4 max|oracle| +
+1e-3 |oracle|."""
 import numpy as np
 import pytest
 import torch
@@ -33,8 +35,12 @@ def test_layer_gradient_chain(seed, lengths, H):
     cu = inp["cu_seqlens"]
     dev = lambda t: t.cuda() if t is not None else None
     raw = [dev(inp[k]) for k in ("q_raw", "k_raw", "v_raw")]
-    pro = kda.prologue(*raw, dev(inp["conv_w"]), dev(cu), dev(inp["beta_logit"]), dev(inp["gate_logit"]),
-                       dev(inp["conv_cache"]), cu_seqlens_host=cu)
+    # the forward prologue's outputs from the oracle, rounded to the chunk
+    # path's bf16 (beta fp32): both backward chains start from these values
+    po = ORC.prologue(inp)
+    bf = lambda a: torch.tensor(a).to(torch.bfloat16)
+    host = dict(q=bf(po["q"]), k=bf(po["k"]), v=bf(po["v"]), gate=bf(po["gate"]), beta=torch.tensor(po["beta"]).float())
+    pro = {k: dev(v) for k, v in host.items()}
     g = torch.Generator().manual_seed(seed + 1)
     dy = torch.randn(inp["T"], H, 128, generator=g).to(torch.bfloat16)
     dsf = torch.randn(inp["N"], H, 128, 128, generator=g) * 0.1
@@ -44,7 +50,6 @@ def test_layer_gradient_chain(seed, lengths, H):
                                dev(inp["conv_cache"]), gb["dq"], gb["dk"], gb["dv"], gb["dbeta"], gb["dgate"],
                                act="silu", cu_seqlens_host=cu)
     torch.cuda.synchronize()
-    host = {k: pro[k].cpu() for k in ("q", "k", "v", "beta", "gate")}
     ro = ORC.recurrence_backward(host["q"], host["k"], host["v"], inp["log_alpha"], host["beta"], host["gate"], cu,
                                  dy, dsf, 1.0, inp["initial_state"])
     rr = ORC.prologue_backward(inp, {k: torch.from_numpy(ro[k]) for k in ("dq", "dk", "dv", "dbeta", "dgate")})

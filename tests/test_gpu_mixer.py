@@ -9,7 +9,8 @@ Bars:
     carries the bound of its pre-activation through -exp(a_log) softplus
     (slope <= exp(a_log)) plus one bf16 rounding;
   the operator inside the mixer: the chunked path's 2e-2 + 1e-2 |oracle|,
-    on the projection's own (bf16) outputs;
+    on the oracle's projections rounded to bf16 (both sides take them; the
+    oracle is only ever given seeded inputs and its own results);
   the mixer itself: bit-identical to its three stages called one by one.
 """
 import numpy as np
@@ -111,13 +112,25 @@ def test_mixer_prefill():
     torch.cuda.synchronize()
     assert torch.equal(out, out2) and torch.equal(S, S2) and torch.equal(cache_out, cache2)
     check_in_projection(inp, {k: v.cpu() for k, v in pro.items()})
-    # the operator on the projection's own outputs
+    # the operator and the output projection, each on the oracle's own
+    # results rounded to bf16 (the operator's input and output precision):
+    # the oracle's projections for the prefill, its prefill output for the
+    # output projection; the GPU stages take the same values
+    refp = ORC.in_projection(np64(inp["x"]), np64(inp["w_in"]), H, d, np64(inp["a_log"]), np64(inp["dt_bias"]))
+    bf = lambda a: torch.tensor(a).to(torch.bfloat16)
+    keys = ("q_raw", "k_raw", "v_raw", "log_alpha", "beta_logit", "gate_logit")
     op_inp = dict(H=H, d=d, K=4, N=inp["N"], T=inp["T"], lengths=inp["lengths"], cu_seqlens=cu_h,
                   conv_w=inp["conv_w"], initial_state=inp["initial_state"], conv_cache=inp["conv_cache"],
-                  **{k: pro[k].cpu() for k in ("q_raw", "k_raw", "v_raw", "log_alpha", "beta_logit", "gate_logit")})
+                  **{k: bf(refp[k]) for k in keys})
     ref = ORC.prefill(op_inp)
-    assert_chunk_close(y, ref["y"], "mixer operator y")
-    assert_chunk_close(S, ref["final_state"], "mixer operator final state")
-    yn = np64(y).reshape(inp["T"], H * d)
-    wn = np64(dev["w_out"])
-    assert_gemm_close(out, ORC.linear(yn, wn), np.abs(yn) @ np.abs(wn).T, H * d, "mixer out projection")
+    g = {k: op_inp[k].cuda() for k in keys}
+    y3, S3 = kda.prefill(g["q_raw"], g["k_raw"], g["v_raw"], dev["conv_w"], g["log_alpha"], g["beta_logit"],
+                         g["gate_logit"], dev["cu_seqlens"], dev["initial_state"], dev["conv_cache"],
+                         cu_seqlens_host=cu_h)
+    yb = bf(ref["y"]).reshape(inp["T"], H * d)
+    out3 = kda.out_projection(yb.cuda(), dev["w_out"])
+    torch.cuda.synchronize()
+    assert_chunk_close(y3, ref["y"], "mixer operator y")
+    assert_chunk_close(S3, ref["final_state"], "mixer operator final state")
+    yn, wn = np64(yb), np64(dev["w_out"])
+    assert_gemm_close(out3, ORC.linear(yn, wn), np.abs(yn) @ np.abs(wn).T, H * d, "mixer out projection")

@@ -183,14 +183,30 @@ def _check_prefill(inp, res, what, scale=1.0):
     return e1, e2
 
 
-def _check_chunk_isolated(inp, res, what, scale=1.0):
-    """Oracle recurrence on the GPU prologue's (bf16) outputs: isolates the chunk kernels."""
-    pro = res["pro"]
+def _oracle_prologue_bf16(inp):
+    """The oracle's prologue outputs, q^, k^, v^ and the gate rounded to bf16
+    (the chunk path's input precision), beta in fp32: inputs that the chunk
+    kernels and the oracle recurrence can both take."""
+    pro = ORC.prologue(inp)
+    bf = lambda a: torch.tensor(a).to(torch.bfloat16)
+    return dict(q=bf(pro["q"]), k=bf(pro["k"]), v=bf(pro["v"]), gate=bf(pro["gate"]),
+                beta=torch.tensor(pro["beta"]).float())
+
+
+def _check_chunk_isolated(inp, what, scale=1.0):
+    """The chunk kernels alone: kda_chunk_forward and the oracle recurrence on
+    the same bf16 inputs (the oracle's own prologue outputs, rounded)."""
+    pro = _oracle_prologue_bf16(inp)
+    dev = lambda t: t.cuda() if t is not None else None
+    yg, Sg = kda.chunk_forward(dev(pro["q"]), dev(pro["k"]), dev(pro["v"]), dev(inp["log_alpha"]), dev(pro["beta"]),
+                               dev(pro["gate"]), dev(inp["cu_seqlens"]), dev(inp["initial_state"]), scale=scale,
+                               cu_seqlens_host=inp["cu_seqlens"])
+    torch.cuda.synchronize()
     y, S = ORC.recurrence(pro["q"], pro["k"], pro["v"], inp["log_alpha"], pro["beta"], pro["gate"],
                           inp["cu_seqlens"], scale, inp["initial_state"])
-    assert_chunk_close(res["y"], y, f"{what} y (isolated)")
-    assert_chunk_close(res["final_state"], S, f"{what} final state (isolated)")
-    return float(np.abs(np64(res["y"]) - y).max()), float(np.abs(np64(res["final_state"]) - S).max())
+    assert_chunk_close(yg, y, f"{what} y (isolated)")
+    assert_chunk_close(Sg, S, f"{what} final state (isolated)")
+    return float(np.abs(np64(yg) - y).max()), float(np.abs(np64(Sg) - S).max())
 
 
 def test_chunk_single_sequence_reduced():
@@ -198,7 +214,7 @@ def test_chunk_single_sequence_reduced():
     inp = ki.config_prefill(1, scale_T=300)
     res = gpu_prefill(inp)
     e = _check_prefill(inp, res, "T=300")
-    iso = _check_chunk_isolated(inp, res, "T=300")
+    iso = _check_chunk_isolated(inp, "T=300")
     print(f"T=300: end-to-end max |err| y {e[0]:.2e} S {e[1]:.2e}; chunk-only y {iso[0]:.2e} S {iso[1]:.2e}")
 
 
@@ -206,7 +222,7 @@ def test_chunk_varlen_edges():
     inp = ki.prefill_inputs(70, [0, 1, 63, 64, 65, 130, 0, 200], H=4, d=128, K=4, cache_std=1.0)
     res = gpu_prefill(inp)
     _check_prefill(inp, res, "varlen edges")
-    _check_chunk_isolated(inp, res, "varlen edges")
+    _check_chunk_isolated(inp, "varlen edges")
     S = np64(res["final_state"])
     for n in (0, 6):   # empty sequences pass their state through exactly
         assert np.array_equal(S[n], inp["initial_state"][n].double().numpy())
@@ -233,14 +249,16 @@ def test_chunk_zero_state_alias_scale():
 
 
 def test_chunk_no_gate_deterministic():
+    """No gate, run twice: bit-identical, and within the bar of the oracle
+    recurrence on the same bf16 inputs (the oracle's prologue outputs)."""
     inp = ki.prefill_inputs(72, [190], H=2, d=128, K=4)
     g = to_dev(inp)
-    pro = kda.prologue(g["q_raw"], g["k_raw"], g["v_raw"], g["conv_w"], g["cu_seqlens"], g["beta_logit"], None,
-                       cu_seqlens_host=inp["cu_seqlens"])
+    pro = {k: v.cuda() for k, v in _oracle_prologue_bf16(inp).items()}
     outs = [kda.chunk_forward(pro["q"], pro["k"], pro["v"], g["log_alpha"], pro["beta"], None, g["cu_seqlens"],
                               g["initial_state"], cu_seqlens_host=inp["cu_seqlens"]) for _ in range(2)]
     torch.cuda.synchronize()
     assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    pro = {k: v.cpu() for k, v in pro.items()}
     y, S = ORC.recurrence(pro["q"], pro["k"], pro["v"], inp["log_alpha"], pro["beta"], None, inp["cu_seqlens"],
                           1.0, inp["initial_state"])
     assert_chunk_close(outs[0][0], y, "ungated y")
@@ -493,8 +511,9 @@ def long_case():
 def test_prefill_T65536_full_sampled_and_decode_tail(long_case, path):
     """T=65536 in full (fused: the benchmark's kda_prefill launch), two heads
     against the oracle, the conv cache exactly; then 128 decode tokens that
-    continue from this path's own final state and conv cache, every output
-    and the state after them against the oracle at the fp32 bar."""
+    continue the long context from the oracle's final state on those heads,
+    every output and the state after them against the oracle at the fp32
+    bar."""
     inp, heads, ref = long_case
     res = gpu_prefill_fused(inp) if path == "fused" else gpu_prefill(inp)
     e1 = assert_chunk_close(res["y"][:, heads], ref["y"], f"T=65536 {path} y")
@@ -504,12 +523,30 @@ def test_prefill_T65536_full_sampled_and_decode_tail(long_case, path):
         want = inp[key][-K1:].double().reshape(K1, -1).numpy()
         assert np.array_equal(np64(res["conv_cache"])[0, X], want), f"conv cache stream {X}"
     print(f"T=65536 {path}: sampled max |err| y {e1:.2e} S {e2:.2e}")
-    dec = dict(state=res["final_state"].cpu(), conv_cache=res["conv_cache"].cpu(), conv_w=inp["conv_w"],
-               slot_idx=None, steps=inp["tail"])
+    # 128 decode tokens continuing the long context.  Both sides start from
+    # the same state: on the sampled heads the oracle's final state rounded
+    # to fp32, the conv cache the sequence's last raw rows (equal, bit for
+    # bit, to what this path wrote: checked above); the GPU's other heads
+    # keep this path's own final state and are not compared.
+    H, d = inp["H"], inp["d"]
+    state = res["final_state"].cpu()
+    state[:, heads] = torch.from_numpy(ref["final_state"]).float()
+    cache = torch.stack([inp[key][-K1:].float().reshape(K1, H * d) for key in ("q_raw", "k_raw", "v_raw")])[None]
     del res
     torch.cuda.empty_cache()
-    errs, (gst, st), _ = run_decode(dec)
-    worst = max(assert_fp32_close(got, want, f"tail y step {t}") for t, (got, want) in enumerate(errs))
-    assert_fp32_close(gst, st, "tail state")
-    report(f"T=65536 {path} decode tail y (worst step)", errs[-1][0], errs[-1][1], bar="fp32")
+    gst, gca, cw = state.cuda(), cache.cuda(), inp["conv_w"].cuda()
+    ch = torch.cat([torch.arange(h * d, (h + 1) * d) for h in heads])
+    st = state[:, heads].double().numpy().copy()
+    ca = cache[..., ch].double().numpy().copy()
+    cw_o = inp["conv_w"][:, ch]
+    worst = 0.0
+    for t, step in enumerate(inp["tail"]):
+        sdev = _step_dev(step)
+        got = kda.decode_step(sdev["q_raw"], sdev["k_raw"], sdev["v_raw"], cw, gca, gst, sdev["log_alpha"],
+                              sdev["beta_logit"], sdev["gate_logit"])
+        want = ORC.decode_step(st, ca, cw_o, {k: v[:, heads] for k, v in step.items()})
+        worst = max(worst, assert_fp32_close(got[:, heads], want, f"tail y step {t}"))
+    torch.cuda.synchronize()
+    assert_fp32_close(gst[:, heads], st, "tail state")
+    report(f"T=65536 {path} decode tail y (last step)", got[:, heads], want, bar="fp32")
     print(f"decode tail after {path} prefill, 128 steps: worst |y err| {worst:.2e}")
