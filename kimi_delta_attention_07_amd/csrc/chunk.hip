@@ -809,6 +809,23 @@ __device__ __forceinline__ void load_chain(ChainOperands &o, const unsigned char
         o.gl[mm] = *reinterpret_cast<const f32x4 *>(rec + kOffGL + (16 * mm + 4 * g) * 4);
 }
 
+// The two halves of load_chain, for the one-set schedule: U~ and W (used
+// first in a step), then Kg and e^{G_L}.
+__device__ __forceinline__ void load_chain_uw(ChainOperands &o, const unsigned char *rec, int l, int tile) {
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+        o.U[m] = *reinterpret_cast<const u32x2 *>(rec + kOffU + ((tile * 4 + m) * 64 + l) * 8);
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o.W[i] = *frag_ptr(rec, kOffW, i, l);
+}
+__device__ __forceinline__ void load_chain_kg(ChainOperands &o, const unsigned char *rec, int l, int g) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) o.Kg[i] = *frag_ptr(rec, kOffKg, i, l);
+#pragma unroll
+    for (int mm = 0; mm < 8; ++mm)
+        o.gl[mm] = *reinterpret_cast<const f32x4 *>(rec + kOffGL + (16 * mm + 4 * g) * 4);
+}
+
 // Operands of the output for one chunk and one tile.
 struct OutOperands {
     u32x4 Q[16];    // Q e^G fragments, index m * 4 + s
@@ -858,14 +875,21 @@ __device__ __forceinline__ void load_out_gate(OutOperands &o, const ChunkParams 
 // loads.  One barrier per chunk keeps the two waves in step.  Blocks are
 // numbered so that the eight tiles of one (sequence, head) land on the same XCD.
 //
-// TPB = 2 puts two adjacent tiles of one (sequence, head) in one block (waves
-// 0, 1: their chains; waves 2, 3: their outputs).  The two waves of each role
-// issue the same fragment loads at the same time, so the second is served by
-// the CU's L1 and the block pulls the chunk's shared fragments from L2 once
-// for 32 columns.  It is launched when the batch gives every CU at least two
-// tiles' work anyway; a single sequence keeps one tile per block (256 blocks).
-template <bool GATED, int TPB>
-__global__ __launch_bounds__(128 * TPB) __attribute__((amdgpu_waves_per_eu(1, 1))) void scan_kernel(ChunkParams p) {
+// TPB > 1 puts TPB adjacent tiles of one (sequence, head) in one block (waves
+// 0 .. TPB-1: their chains; the next TPB: their outputs).  The waves of each
+// role issue the same fragment loads at the same time, so all but the first
+// are served by the CU's L1 and the block pulls the chunk's shared fragments
+// from L2 once for 16 TPB columns.
+//
+// DEEP (one tile per block, the single-sequence launch): each wave keeps two
+// chunks of operands in flight, one wave per SIMD.  Otherwise (TPB = 4 or 2,
+// launched when the batch gives every CU several tiles' work) the chain wave
+// keeps one: it requests the chunk's Kg and e^{G_L} once its U product is
+// issued, and the next chunk's U~ and W into the registers that product has
+// just read.  That fits in 256 registers, so two blocks share each CU and one
+// block's waits are filled by the other's work.
+template <bool GATED, int TPB, bool DEEP = true>
+__global__ __launch_bounds__(128 * TPB) __attribute__((amdgpu_waves_per_eu(DEEP ? 1 : 2, DEEP ? 1 : 2))) void scan_kernel(ChunkParams p) {
     constexpr int kOS = 20;                           // fp32 row stride of the output tile
     constexpr int kUnits = kTilesV / TPB;             // blocks per (sequence, head)
     __shared__ __attribute__((aligned(16))) u32x4 xfer_all[TPB][2][6][64];   // [tile][slot][Sb0..3, Ub0..1][lane]
@@ -922,8 +946,12 @@ __global__ __launch_bounds__(128 * TPB) __attribute__((amdgpu_waves_per_eu(1, 1)
             for (int mm = 0; mm < 8; ++mm) S[mm] = f32x4{0.f, 0.f, 0.f, 0.f};
         }
         ChainOperands o0, o1;
-        load_chain(o0, rec_of(0), l, g, tile);
-        load_chain(o1, rec_of(1), l, g, tile);
+        if constexpr (DEEP) {
+            load_chain(o0, rec_of(0), l, g, tile);
+            load_chain(o1, rec_of(1), l, g, tile);
+        } else {
+            load_chain_uw(o0, rec_of(0), l, tile);
+        }
         auto step = [&](int i, ChainOperands &o) {
             // The U~ tile is the first load of a chunk's set.  Used here, after
             // the barrier: its bf16 unpacking, left free, is hoisted into the
@@ -949,6 +977,12 @@ __global__ __launch_bounds__(128 * TPB) __attribute__((amdgpu_waves_per_eu(1, 1)
             for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int m = 0; m < 4; ++m) U[m] = mfma16(as_bf16x8(o.W[m * 4 + s]), Sb[s], U[m]);
+            if constexpr (!DEEP) {
+                // this chunk's Kg and e^{G_L}, then the next chunk's U~ and W
+                // (into the registers the products above have just read)
+                load_chain_kg(o, rec_of(i), l, g);
+                load_chain_uw(o, rec_of(i + 1), l, tile);
+            }
             bf16x8 Ub[2];
             Ub[0] = pack8(U[0], U[1]);
             Ub[1] = pack8(U[2], U[3]);
@@ -960,7 +994,7 @@ __global__ __launch_bounds__(128 * TPB) __attribute__((amdgpu_waves_per_eu(1, 1)
             for (int sp = 0; sp < 2; ++sp)
 #pragma unroll
                 for (int mm = 0; mm < 8; ++mm) S[mm] = mfma16(as_bf16x8(o.Kg[mm * 2 + sp]), Ub[sp], S[mm]);
-            load_chain(o, rec_of(i + 2), l, g, tile);
+            if constexpr (DEEP) load_chain(o, rec_of(i + 2), l, g, tile);
         };
         // barriers: one after each chunk, one more while the output wave
         // finishes the last chunk (nch + 1, as in the output wave)
@@ -968,7 +1002,7 @@ __global__ __launch_bounds__(128 * TPB) __attribute__((amdgpu_waves_per_eu(1, 1)
         for (; i + 1 < nch; i += 2) {
             step(i, o0);
             __syncthreads();
-            step(i + 1, o1);
+            step(i + 1, DEEP ? o1 : o0);
             __syncthreads();
         }
         if (i < nch) {
@@ -1134,12 +1168,17 @@ hipError_t launch_prefill_prepare(const ChunkParams &p, hipStream_t s) {
 hipError_t launch_chunk_scan(const ChunkParams &p, hipStream_t s) {
     const long heads = (long)p.n_seqs * p.H;
     if (heads == 0) return hipGetLastError();
-    // two tiles per block once the one-tile grid would put two blocks on
-    // every CU (256 CUs) and the two-tile grid still divides by 8 (XCDs)
-    if (heads * kTilesV >= 512 && heads % 2 == 0) {
+    // several tiles per block once the one-tile grid would put two blocks on
+    // every CU (256 CUs) and the grid still divides by 8 (XCDs): four when the
+    // head count allows, else two
+    if (heads * kTilesV >= 512 && heads % 4 == 0) {
+        const dim3 grid((unsigned)(heads * kTilesV / 4));
+        if (p.gate) hipLaunchKernelGGL((scan_kernel<true, 4, false>), grid, dim3(512), 0, s, p);
+        else hipLaunchKernelGGL((scan_kernel<false, 4, false>), grid, dim3(512), 0, s, p);
+    } else if (heads * kTilesV >= 512 && heads % 2 == 0) {
         const dim3 grid((unsigned)(heads * kTilesV / 2));
-        if (p.gate) hipLaunchKernelGGL((scan_kernel<true, 2>), grid, dim3(256), 0, s, p);
-        else hipLaunchKernelGGL((scan_kernel<false, 2>), grid, dim3(256), 0, s, p);
+        if (p.gate) hipLaunchKernelGGL((scan_kernel<true, 2, false>), grid, dim3(256), 0, s, p);
+        else hipLaunchKernelGGL((scan_kernel<false, 2, false>), grid, dim3(256), 0, s, p);
     } else {
         const dim3 grid((unsigned)(heads * kTilesV));
         if (p.gate) hipLaunchKernelGGL((scan_kernel<true, 1>), grid, dim3(128), 0, s, p);

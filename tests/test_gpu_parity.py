@@ -331,19 +331,21 @@ def test_prefill_many_sequences():
         assert np.array_equal(S[3], inp["initial_state"][3].double().numpy())
 
 
-def test_prefill_two_tiles_per_block():
-    """40 sequences x 2 heads (80 heads: the scan puts two value tiles in each
-    block, with the chunk table in the kernel arguments), empty and one-token
-    sequences included; fused and unfused path, every element checked."""
+@pytest.mark.parametrize("n_seqs", [40, 33])
+def test_prefill_two_tiles_per_block(n_seqs):
+    """n sequences x 2 heads: 80 heads put four value tiles in each scan block,
+    66 heads two (both with one chain operand set in flight and the chunk
+    table in the kernel arguments); empty and one-token sequences included;
+    fused and unfused path, every element checked."""
     g = torch.Generator().manual_seed(97)
-    lens = torch.randint(0, 151, (40,), generator=g).tolist()
-    lens[0], lens[9], lens[39] = 0, 1, 64
+    lens = torch.randint(0, 151, (n_seqs,), generator=g).tolist()
+    lens[0], lens[9], lens[n_seqs - 1] = 0, 1, 64
     inp = ki.prefill_inputs(97, lens, H=2, d=128, K=4, cache_std=1.0)
     ref = ORC.prefill(inp)
     for name, res in (("fused", gpu_prefill_fused(inp)), ("unfused", gpu_prefill(inp))):
-        assert_chunk_close(res["y"], ref["y"], f"40 seqs {name} y")
-        assert_chunk_close(res["final_state"], ref["final_state"], f"40 seqs {name} final state")
-        assert_fp32_close(res["conv_cache"], ref["conv_cache"], f"40 seqs {name} conv cache", 0.0)
+        assert_chunk_close(res["y"], ref["y"], f"{n_seqs} seqs {name} y")
+        assert_chunk_close(res["final_state"], ref["final_state"], f"{n_seqs} seqs {name} final state")
+        assert_fp32_close(res["conv_cache"], ref["conv_cache"], f"{n_seqs} seqs {name} conv cache", 0.0)
         assert np.array_equal(np64(res["final_state"])[0], inp["initial_state"][0].double().numpy())
 
 
