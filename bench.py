@@ -22,7 +22,11 @@ prefill, output projection at a synthetic hidden size) under "mixer", and
 the MLA decode token under "mla_decode" (informative; the headline stays the
 4096-token sequence).
 
-Every kernel is timed with HIP events on the stream it is launched on.  The
+The headline's W warm-up steps (600 by default, about 0.1 s) and a time-based
+warm-up of 0.1 s before every other leg let the GPU's clocks settle before
+anything is timed (a few calls are not enough: the first timed batch then
+runs several percent slow).  Every kernel is timed with HIP events on the
+stream it is launched on.  The
 roofline object counts the path's algorithmic bytes only (49,216 B per token:
 q, k, v, log alpha, gate and beta in, y out, plus the fp32 state and conv
 cache in and out), never the chunk records the two stages pass between them:
@@ -147,11 +151,26 @@ def path_roofline(path_bytes, per_kernel_ms, ms_step, slots, workload="T4096", t
     return out
 
 
+def spin_up(torch, fn, ms=100.0):
+    """Untimed warm-up: call fn until ms of wall time have passed (the GPU's
+    clocks settle well after a few calls; every leg starts after CPU-side
+    input generation has left the GPU idle)."""
+    t0 = time.perf_counter()
+    n = 0
+    while (time.perf_counter() - t0) * 1e3 < ms or n < 2:
+        fn()
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def parse():
     ap = argparse.ArgumentParser(description=__doc__.split("\n\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=600,
+                    help="untimed prefill steps before the timed ones (600: about 0.1 s, enough for the clocks)")
     ap.add_argument("--decode-reps", type=int, default=3, help="timed passes of 64 decode steps")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU oracle baseline")
     ap.add_argument("--no-decode", action="store_true", help="skip the decode measurement")
@@ -284,9 +303,7 @@ def bench_prefill_workloads(torch, kda, ki, args, dev):
         g["final_state"] = torch.empty_like(g["initial_state"])
         g["cu_host"] = inp["cu_seqlens"]
         ws = kda.chunk_workspace(H, D, g["cu_host"], dev)
-        for _ in range(2):
-            run_fused_step(kda, g, ws)
-        torch.cuda.synchronize()
+        spin_up(torch, lambda: run_fused_step(kda, g, ws))
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         reps = 5
         a.record()
@@ -322,9 +339,8 @@ def bench_decode(torch, kda, ki, args, dev):
         kda.decode_step(s["q_raw"], s["k_raw"], s["v_raw"], cw, cache, state, s["log_alpha"], s["beta_logit"],
                         s["gate_logit"], out=out)
 
-    for s in steps[:8]:
-        one(s)
-    torch.cuda.synchronize()
+    it = iter(range(1 << 30))
+    spin_up(torch, lambda: one(steps[next(it) % len(steps)]))
     times = []
     for _ in range(args.decode_reps):
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -412,9 +428,8 @@ def bench_backward(torch, kda, ki, args, dev):
         return kda.chunk_backward(pro["q"], pro["k"], pro["v"], g["log_alpha"], pro["beta"], pro["gate"],
                                   g["cu_seqlens"], dy, g["initial_state"], dsf, workspace=ws, cu_seqlens_host=cu_h)
 
-    for _ in range(3):
-        grads = one()
-    torch.cuda.synchronize()
+    grads = one()
+    spin_up(torch, one)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
     for _ in range(args.backward_steps):
@@ -431,9 +446,7 @@ def bench_backward(torch, kda, ki, args, dev):
                                      g["beta_logit"], g["gate_logit"], g["conv_cache"], grads["dq"], grads["dk"],
                                      grads["dv"], grads["dbeta"], grads["dgate"], cu_seqlens_host=cu_h, workspace=pws)
 
-    for _ in range(3):
-        one_pro()
-    torch.cuda.synchronize()
+    spin_up(torch, one_pro)
     a.record()
     for _ in range(args.backward_steps):
         one_pro()
@@ -485,9 +498,7 @@ def bench_mixer(torch, kda, ki, args, dev):
                           workspace=ws, cu_seqlens_host=cu_h)
 
     def timed(fn, reps):
-        for _ in range(3):
-            fn()
-        torch.cuda.synchronize()
+        spin_up(torch, fn)
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
         for _ in range(reps):
@@ -536,9 +547,7 @@ def bench_mla(torch, kda, ki, args, dev):
         kda.mla_decode_step(g["q"], g["k_new"], g["v_new"], g["k_cache"], g["v_cache"], g["cache_len"],
                             g["gate_logit"], out=out, workspace=ws)
 
-    for _ in range(3):
-        one()
-    torch.cuda.synchronize()
+    spin_up(torch, one)
     reps = max(args.steps, 20)
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     evs[0].record()

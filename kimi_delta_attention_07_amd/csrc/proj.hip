@@ -112,6 +112,24 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(ProjParams p) {
         }
     };
 
+    // the KDA input projection's per-column epilogue parameters, loaded now
+    // so that their latency passes under the main loop: decay columns take
+    // a_log[h] and their bias, every other column (and absent ones) 0
+    float epi_A[4], epi_b[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+        epi_A[n] = 0.0f;
+        epi_b[n] = 0.0f;
+        if constexpr (EPI == 1) {
+            const int C = p.H * p.d, col = col0 + 64 * wn + 16 * n + c16;
+            if (col >= 4 * C && col < 5 * C) {
+                const int within = col - 4 * C;
+                if (p.a_log) epi_A[n] = p.a_log[within / p.d];
+                if (p.bias) epi_b[n] = p.bias[within];
+            }
+        }
+    }
+
     f32x4 acc[8][4];
 #pragma unroll
     for (int m = 0; m < 8; ++m)
@@ -155,37 +173,48 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(ProjParams p) {
 
     // epilogue: element (m, n, r) is row row0 + 128 wm + 16 m + 4 g + r,
     // column col0 + 64 wn + 16 n + c16
+    // one column group of 16 (fixed n): out[row][within] for the 32 rows this
+    // lane holds, through the decay activation or not
+    auto store_cols = [&](int n, uint16_t *dst, int width, int within, bool decay, float A, float bias) {
+        if (decay) {
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = row0 + 128 * wm + 16 * m + 4 * g + r;
+                    const float v = -A * softplus_f(acc[m][n][r] + bias);
+                    if (row < p.M) dst[(long)row * width + within] = f2bf(v);
+                }
+        } else {
+#pragma unroll
+            for (int m = 0; m < 8; ++m)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = row0 + 128 * wm + 16 * m + 4 * g + r;
+                    if (row < p.M) dst[(long)row * width + within] = f2bf(acc[m][n][r]);
+                }
+        }
+    };
 #pragma unroll
     for (int n = 0; n < 4; ++n) {
         const int col = col0 + 64 * wn + 16 * n + c16;
-        if (col >= p.N) continue;
-        // destination: the whole [M][N] output, or one segment of the KDA
-        // input projection (q, k, v, gate, decay: H d columns; beta: H)
-        uint16_t *dst = p.out;
-        int width = p.N, within = col;
-        bool decay = false;
-        float A = 1.0f, bias = 0.0f;
-        if constexpr (EPI == 1) {
+        if constexpr (EPI == 0) {
+            if (col < p.N) store_cols(n, p.out, p.N, col, false, 1.0f, 0.0f);
+        } else {
+            // one segment of the KDA input projection: q, k, v, gate, decay
+            // (H d columns each) or beta (H).  With H d a multiple of 16, the
+            // wave's 16 columns of this group lie in one segment: the segment
+            // is then wave-uniform, and so is the decay branch
             const int C = p.H * p.d;
-            const int seg = col < 5 * C ? col / C : 5;
-            within = col - seg * C;
-            width = seg < 5 ? C : p.H;
-            dst = p.seg[seg];
-            decay = seg == 4;
-            if (decay) {
-                if (p.a_log) A = __expf(p.a_log[within / p.d]);
-                if (p.bias) bias = p.bias[within];
-            }
+            int seg = col < 5 * C ? col / C : 5;
+            if (C % 16 == 0) seg = __builtin_amdgcn_readfirstlane(seg);
+            // the pointer is picked with constant indices (a runtime index
+            // into the argument array would go through scratch memory)
+            uint16_t *dst = seg == 0 ? p.seg[0] : seg == 1 ? p.seg[1] : seg == 2 ? p.seg[2]
+                          : seg == 3 ? p.seg[3] : seg == 4 ? p.seg[4] : p.seg[5];
+            const int within = col - seg * C, width = seg < 5 ? C : p.H;
+            if (col < p.N) store_cols(n, dst, width, within, seg == 4, __expf(epi_A[n]), epi_b[n]);
         }
-#pragma unroll
-        for (int m = 0; m < 8; ++m)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int row = row0 + 128 * wm + 16 * m + 4 * g + r;
-                float v = acc[m][n][r];
-                if (decay) v = -A * softplus_f(v + bias);
-                if (row < p.M) dst[(long)row * width + within] = f2bf(v);
-            }
     }
 }
 
