@@ -77,7 +77,7 @@ TRAFFIC_KERNEL = {"prologue": "prologue128_kernel<4, 1>", "chunk_prepare": "prep
                   "chunk_scan": "scan_kernel<true, 1>", "prefill_prepare": "prepare_kernel<true, 4, 1>",
                   "prefill_scan": "scan_kernel<true, 1>", "decode": "decode_kernel<128, 1, 0>",
                   "in_projection": "gemm_kernel<1>", "out_projection": "gemm_kernel<0>",
-                  "mla_attend": "mla_attend_kernel<3, 2, true>", "mla_combine": "mla_combine_kernel"}
+                  "mla_attend": "mla_attend_kernel<3, 2, true, true>", "mla_combine": "mla_combine_kernel"}
 KERNEL_SOURCES = {"prologue": ["prologue.hip"], "chunk_prepare": ["chunk.hip"], "chunk_scan": ["chunk.hip"],
                   "prefill_prepare": ["chunk.hip"], "prefill_scan": ["chunk.hip"], "decode": ["decode.hip"],
                   "in_projection": ["proj.hip"], "out_projection": ["proj.hip"], "mla_attend": ["mla.hip"],
@@ -569,7 +569,7 @@ def bench_mla(torch, kda, ki, args, dev):
             "value": B / (ms * 1e-3), "unit": "tokens/s", "ms_per_step": ms, "steps": reps,
             "roofline": {"bound": "hbm", "achieved": gbs, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": gbs / HBM_PEAK_GBS, "traffic": mla_traffic,
-                         "kernel": "mla_attend_kernel<3, 2, true> + mla_combine_kernel (one call)",
+                         "kernel": "mla_attend_kernel<3, 2, true, true> + mla_combine_kernel (one call)",
                          "bytes_per_launch": nbytes,
                          "traffic_over_algorithmic": mla_traffic / nbytes if mla_traffic else None}}
 

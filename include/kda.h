@@ -413,7 +413,8 @@ kda_status kda_chunk_backward(const kda_geom *geom, int32_t n_seqs, int32_t tota
  *   geom: H query heads and H_kv kv heads (H a multiple of H_kv), d_qk q/k
  *     channels per head (nope + rope), d_v value channels, both in [1, 256];
  *     scale the softmax scale (1 / sqrt(d_qk) is the usual one);
- *   batch in [0, 65535] sequences, max_len the cache capacity in tokens;
+ *   batch in [0, 65535] sequences, max_len the cache capacity in tokens,
+ *     at most 65535 * 256 = 16,776,960;
  *   cache_len_dev [batch] int32, device: tokens already cached per sequence.
  *     The call neither reads past it nor advances it (the caller adds 1 after
  *     the call).  A sequence whose cache_len is outside [0, max_len) is left

@@ -832,6 +832,8 @@ kda_status kda_mla_decode_step(const kda_mla_geom *geom, int32_t batch, int32_t 
     if (batch < 0 || batch > 65535) return fail(KDA_ERR_SHAPE, "batch = %d must be in [0, 65535]", batch);
     if (geom->H > 65535) return fail(KDA_ERR_SHAPE, "H = %d must be <= 65535", geom->H);
     if (max_len <= 0) return fail(KDA_ERR_SHAPE, "max_len = %d must be > 0", max_len);
+    if (mla_n_split(max_len) > 65535)   // the splits are the grid's third dimension
+        return fail(KDA_ERR_SHAPE, "max_len = %d must be <= %d", max_len, 65535 * kda::mla_split_tokens());
     // one buffer resource spans a (sequence, kv head) cache block, and one the
     // whole q; each must stay below 4 GiB
     if ((long)max_len * std::max(geom->d_qk, geom->d_v) * 2 >= (1L << 32) ||

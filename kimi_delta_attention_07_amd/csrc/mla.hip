@@ -8,7 +8,11 @@
 //
 // Decode attention is a stream over the cache with a few flops per byte, so
 // the design is for HBM bandwidth, without MFMA:
-//   attend: one block of four waves per (256-token split, q head, sequence).
+//   attend: one block of four waves per (256-token split, q head, sequence),
+//     the split index slowest in the grid: every sequence's first splits are
+//     dispatched first and the last, partial or empty ones at the end, so the
+//     launch does not end on a round of full splits.  The q heads of one kv
+//     group run on one XCD and share its L2.
 //     Eight lanes share one cached token: a k or v row is cut into chunks of
 //     eight channels (16 bytes of bf16), chunk c held by lane c % 8 of the
 //     token's lane group, so every load instruction reads whole 128-byte runs.
@@ -19,8 +23,11 @@
 //     groups, then the waves, merge at the end, and the block writes one
 //     (max, sum, weighted sum) partial.  The block whose split holds pos
 //     also takes the new token from k_new / v_new (so no block reads a slot
-//     that another block is writing) and writes it into the cache.
-//   combine: per (q head, sequence), merges the split partials, applies the
+//     that another block is writing) and writes it into the cache.  When
+//     every kv head serves one q head (H = H_kv), each cached row is read by
+//     one block only, and its loads are marked non-temporal.
+//   combine: per (q head, sequence), merges the split partials in one pass
+//     (eight splits' loads at a time, rescaled to a running max), applies the
 //     gate and writes bf16.
 // Loads go through buffer resources: rows past the cache end read as zero.
 #include <cmath>
@@ -37,13 +44,14 @@ constexpr int kThreads = 256;    // four waves, 64 tokens each, 8 per iteration
 
 // 8 bf16 of one chunk of a row (row_elem0 = the row's first element), or
 // zeros where the chunk lies past d; VEC: the chunk is whole and 16-byte
-// aligned, one load; otherwise element by element
-template <bool VEC>
+// aligned, one load; otherwise element by element.  NT: a row read once
+// (the cache policy's non-temporal bit).
+template <bool VEC, bool NT = false>
 __device__ __forceinline__ u32x4 load_chunk(__amdgpu_buffer_rsrc_t r, long row_elem0, int d, int chunk,
                                             bool valid) {
     if constexpr (VEC) {
         const uint32_t off = (valid && chunk * 8 < d) ? (uint32_t)((row_elem0 + chunk * 8) * 2) : 0xffffffffu;
-        return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0);
+        return __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, NT ? 2 : 0);
     } else {
         uint32_t h[8];
 #pragma unroll
@@ -77,12 +85,17 @@ __device__ __forceinline__ void merge(float &m, float &l, float (&a)[N], float m
     m = M;
 }
 
-// KC, VC: 8-channel chunks per lane for k and v (d_qk <= 64 KC, d_v <= 64 VC)
-template <int KC, int VC, bool VEC>
+// KC, VC: 8-channel chunks per lane for k and v (d_qk <= 64 KC, d_v <= 64 VC);
+// NT: cache rows are loaded non-temporally (each is read by this block only)
+template <int KC, int VC, bool VEC, bool NT>
 __global__ __launch_bounds__(kThreads) void mla_attend_kernel(MlaParams p) {
     __shared__ float red_ml[4][2];
     __shared__ float red_acc[4][8 * 8 * VC];
-    const int s = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int b = blockIdx.y, s = blockIdx.z;
+    // Blocks go to the eight XCDs in turn, so with H a multiple of 8, grid x
+    // and x + 8 share an XCD: XCD k takes heads k H / 8 .. (k + 1) H / 8 - 1,
+    // and the q heads of one kv group meet in one L2.
+    const int h = (p.H & 7) ? (int)blockIdx.x : (int)(blockIdx.x & 7) * (p.H >> 3) + (int)(blockIdx.x >> 3);
     const int pos = p.cache_len[b];
     if (pos < 0 || pos >= p.max_len || s > pos / kSplit) return;   // block-uniform
     const int hk = h / (p.H / p.H_kv);
@@ -147,9 +160,9 @@ __global__ __launch_bounds__(kThreads) void mla_attend_kernel(MlaParams p) {
             const int j = j0 + 8 * it + tg;
             const bool valid = j < pos;
 #pragma unroll
-            for (int c = 0; c < KC; ++c) kr[c] = load_chunk<VEC>(rk, (long)j * dqk, dqk, 8 * c + li, valid);
+            for (int c = 0; c < KC; ++c) kr[c] = load_chunk<VEC, NT>(rk, (long)j * dqk, dqk, 8 * c + li, valid);
 #pragma unroll
-            for (int c = 0; c < VC; ++c) vr[c] = load_chunk<VEC>(rv, (long)j * dv, dv, 8 * c + li, valid);
+            for (int c = 0; c < VC; ++c) vr[c] = load_chunk<VEC, NT>(rv, (long)j * dv, dv, 8 * c + li, valid);
         };
         fetch(0, kb[0], vb[0]);
 #pragma unroll
@@ -233,30 +246,54 @@ __global__ __launch_bounds__(kThreads) void mla_attend_kernel(MlaParams p) {
 __global__ __launch_bounds__(256) void mla_combine_kernel(MlaParams p) {
     const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
     if (t >= p.dv) return;
-    uint16_t *out = static_cast<uint16_t *>(p.out) + ((long)b * p.H + h) * p.dv;
+    const long ob = ((long)b * p.H + h) * p.dv + t;
+    uint16_t *out = static_cast<uint16_t *>(p.out) + ob;
+    const float gz = p.gate ? bf2f(static_cast<const uint16_t *>(p.gate)[ob]) : 0.0f;
     const int pos = p.cache_len[b];
     if (pos < 0 || pos >= p.max_len) {
-        out[t] = 0;
+        *out = 0;
         return;
     }
-    const int ns = pos / kSplit + 1;
+    const int ns = pos / kSplit + 1;   // every split below ns holds at least one token
     const long base = ((long)b * p.H + h) * p.n_split;
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, p.ws_ml[2 * (base + s)]);
-    float L = 0.0f, a = 0.0f;
-    for (int s = 0; s < ns; ++s) {
-        const float e = __expf(p.ws_ml[2 * (base + s)] - M);
-        L += p.ws_ml[2 * (base + s) + 1] * e;
-        a += p.ws_acc[(base + s) * p.dv + t] * e;
+    // split partials past ns read as (-inf, 0, 0) through the resources' ends
+    const __amdgpu_buffer_rsrc_t rml = buffer_rsrc(p.ws_ml + 2 * base, (uint32_t)(2 * ns * 4));
+    const __amdgpu_buffer_rsrc_t racc = buffer_rsrc(p.ws_acc + base * p.dv, (uint32_t)((long)ns * p.dv * 4));
+    float M = -INFINITY, L = 0.0f, a = 0.0f;
+    for (int s0 = 0; s0 < ns; s0 += 8) {
+        float ms[8], ls[8], as[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const int s = s0 + k;
+            ms[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rml, (uint32_t)(8 * s), 0, 0));
+            ls[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(rml, (uint32_t)(8 * s + 4), 0, 0));
+            as[k] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(racc, (uint32_t)(((long)s * p.dv + t) * 4), 0, 0));
+            if (s >= ns) ms[k] = -INFINITY;
+        }
+        float Mn = M;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) Mn = fmaxf(Mn, ms[k]);
+        const float sc = M == -INFINITY ? 0.0f : __expf(M - Mn);   // Mn is finite: split s0 holds a token
+        L *= sc;
+        a *= sc;
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+            const float e = ms[k] == -INFINITY ? 0.0f : __expf(ms[k] - Mn);
+            L += ls[k] * e;
+            a += as[k] * e;
+        }
+        M = Mn;
     }
     float o = a / L;
-    if (p.gate) o *= sigmoidf(bf2f(static_cast<const uint16_t *>(p.gate)[((long)b * p.H + h) * p.dv + t]));
-    out[t] = f2bf(o);
+    if (p.gate) o *= sigmoidf(gz);
+    *out = f2bf(o);
 }
 
 template <int KC, int VC, bool VEC>
 void launch_attend(const MlaParams &p, hipStream_t st) {
-    hipLaunchKernelGGL((mla_attend_kernel<KC, VC, VEC>), dim3(p.n_split, p.H, p.batch), dim3(kThreads), 0, st, p);
+    const dim3 grid(p.H, p.batch, p.n_split);
+    if (p.H == p.H_kv) hipLaunchKernelGGL((mla_attend_kernel<KC, VC, VEC, true>), grid, dim3(kThreads), 0, st, p);
+    else hipLaunchKernelGGL((mla_attend_kernel<KC, VC, VEC, false>), grid, dim3(kThreads), 0, st, p);
 }
 
 }  // namespace

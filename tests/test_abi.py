@@ -331,14 +331,16 @@ def test_mla_workspace_bytes(L):
 @pytest.mark.parametrize("case,code", [
     ("geom_null", NULL), ("H_not_multiple", SHAPE), ("H_kv0", SHAPE), ("dqk0", SHAPE), ("dv257", UNSUP),
     ("scale_nan", SHAPE), ("batch_neg", SHAPE), ("batch_huge", SHAPE), ("max_len0", SHAPE),
-    ("q_null", NULL), ("cache_null", NULL), ("lens_null", NULL), ("misaligned", ALIGN), ("ws_small", WORKSPACE),
+    ("max_len_grid", SHAPE), ("q_null", NULL), ("cache_null", NULL), ("lens_null", NULL), ("misaligned", ALIGN), ("ws_small", WORKSPACE),
 ])
 def test_mla_decode_rejects(L, case, code):
     geom = {"geom_null": None, "H_not_multiple": _mla_geom(H=3), "H_kv0": _mla_geom(H_kv=0),
             "dqk0": _mla_geom(d_qk=0), "dv257": _mla_geom(d_v=257),
-            "scale_nan": _mla_geom(scale=float("nan"))}.get(case, _mla_geom())
+            "scale_nan": _mla_geom(scale=float("nan")),
+            # 8 channels keep the cache within 32-bit offsets: only the split count is too large
+            "max_len_grid": _mla_geom(d_qk=8, d_v=8)}.get(case, _mla_geom())
     batch = {"batch_neg": -1, "batch_huge": 70000}.get(case, 2)
-    max_len = 0 if case == "max_len0" else 300
+    max_len = {"max_len0": 0, "max_len_grid": 65535 * 256 + 1}.get(case, 300)
     p = list(FAKE[:9])   # cache_len, q, k_new, v_new, gate, k_cache, v_cache, out, workspace
     if case == "q_null":
         p[1] = None
@@ -351,6 +353,8 @@ def test_mla_decode_rejects(L, case, code):
     ws = 16 if case == "ws_small" else 1 << 30
     assert L.kda_mla_decode_step(geom, batch, max_len, *p, ws, None) == code
     assert L.kda_last_error_detail().decode() != ""
+    if case == "max_len_grid":
+        assert "must be <= 16776960" in L.kda_last_error_detail().decode()
 
 
 def test_mla_decode_empty_batch_is_a_no_op(L):
