@@ -38,7 +38,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     __shared__ float red[8][NT];                // column partials (z[4], w[4]) per thread
     __shared__ float wred[4][3];
 
-    const int b = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+    // heads fastest: consecutive blocks stream consecutive 64 KB states of one row
+    const int h = (int)(blockIdx.x % (unsigned)p.H), b = (int)(blockIdx.x / (unsigned)p.H), t = threadIdx.x;
     const int slot = p.slot_idx ? p.slot_idx[b] : b;
     // A row whose slot lies outside [0, n_slots) is skipped whole (the slot
     // is block-uniform, so the early exit is before every barrier): nothing
@@ -157,7 +158,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
 
 template <int D>
 hipError_t launch_d(const DecodeParams &p, int dti, int dto, hipStream_t s) {
-    dim3 grid(p.batch, p.H), block(256);
+    dim3 grid((unsigned)p.batch * (unsigned)p.H), block(256);
     if (dti == 1 && dto == 1) hipLaunchKernelGGL((decode_kernel<D, 1, 1>), grid, block, 0, s, p);
     else if (dti == 1) hipLaunchKernelGGL((decode_kernel<D, 1, 0>), grid, block, 0, s, p);
     else if (dto == 1) hipLaunchKernelGGL((decode_kernel<D, 0, 1>), grid, block, 0, s, p);

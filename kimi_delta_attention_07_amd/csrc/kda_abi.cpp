@@ -577,7 +577,8 @@ kda_status kda_decode_step(const kda_geom *geom, int32_t batch, const int32_t *s
     if (n_slots <= 0) return fail(KDA_ERR_SHAPE, "n_slots = %d must be > 0", n_slots);
     if (!slot_idx_dev && batch > n_slots)
         return fail(KDA_ERR_SHAPE, "batch = %d > n_slots = %d with identity slots", batch, n_slots);
-    if (batch > 65535 * 256 || geom->H > 65535) return fail(KDA_ERR_SHAPE, "batch or H too large for the grid");
+    if (batch > 65535 * 256 || geom->H > 65535 || (long)batch * geom->H > 0x7fffffffL)
+        return fail(KDA_ERR_SHAPE, "batch or H too large for the grid");
     KDA_TRY(check_dtype(in_dtype));
     KDA_TRY(check_dtype(out_dtype));
     KDA_TRY(check_required({{q_raw, "q_raw"}, {k_raw, "k_raw"}, {v_raw, "v_raw"}, {conv_w, "conv_w"},
