@@ -872,8 +872,8 @@ __device__ __forceinline__ void load_out_gate(OutOperands &o, const ChunkParams 
 // right after using it.  Every path issues the same loads (the refill index
 // is clamped to the last chunk, masked rows go through buffer resources), so
 // a wave waits only for the buffer it is about to use, never for all of its
-// loads.  One barrier per chunk keeps the two waves in step.  Blocks are
-// numbered so that the eight tiles of one (sequence, head) land on the same XCD.
+// loads.  One barrier per chunk keeps the two waves in step.  The eight tiles
+// of one (sequence, head) land on the same XCD.
 //
 // TPB > 1 puts TPB adjacent tiles of one (sequence, head) in one block (waves
 // 0 .. TPB-1: their chains; the next TPB: their outputs).  The waves of each
@@ -896,15 +896,31 @@ __global__ __launch_bounds__(128 * TPB) __attribute__((amdgpu_waves_per_eu(DEEP 
     __shared__ __attribute__((aligned(16))) float O_all[TPB][64 * kOS];
     const int H = p.H;
     const int total = p.n_seqs * H * kUnits;    // a multiple of 8 (the launcher checks it)
-    const int per_xcd = total / 8;
     const int b = blockIdx.x;
-    const int u = (b % 8) * per_xcd + b / 8;    // consecutive u share an XCD
-    const int h = (u / kUnits) % H;
-    const int n = u / (kUnits * H);
+    // Blocks go to the eight XCDs in turn (b % 8).  A (sequence, head) item's
+    // kUnits blocks stay on one XCD, so they share its L2.  When the item
+    // count divides by 8, items are dealt to the XCDs in turn and dispatched
+    // in rank order: every XCD gets an even share, and with a host-side plan
+    // the longest sequences are dispatched first, so a batch of mixed lengths
+    // does not end on one long sequence started late.  Otherwise each XCD
+    // takes a contiguous eighth of the blocks.
+    int n, h, unit;
+    if ((p.n_seqs * H) % 8 == 0) {
+        const int slot = b / 8, item = (slot / kUnits) * 8 + b % 8;
+        const int rank = item / H;
+        h = item % H;
+        n = p.plan_in_args ? (int)p.plan_order[rank] : rank;
+        unit = slot % kUnits;
+    } else {
+        const int u = (b % 8) * (total / 8) + b / 8;
+        h = (u / kUnits) % H;
+        n = u / (kUnits * H);
+        unit = u % kUnits;
+    }
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const bool chain = wave < TPB;              // wave-uniform role
     const int sub = chain ? wave : wave - TPB;  // which of the block's tiles
-    const int tile = (u % kUnits) * TPB + sub;
+    const int tile = unit * TPB + sub;
     auto &xfer = xfer_all[sub];
     float *O_lds = O_all[sub];
     const int l = threadIdx.x & 63, g = l >> 4, c16 = l & 15;

@@ -181,6 +181,11 @@ kda::ChunkParams chunk_params(const kda_geom *geom, int32_t n_seqs, int32_t tota
             p.plan_off[n] = off;
             if (n < n_seqs) off += (cu_host[n + 1] - cu_host[n] + kda::kChunk - 1) / kda::kChunk;
         }
+        // the scan takes sequences longest first (ties in index order)
+        for (int n = 0; n < n_seqs; ++n) p.plan_order[n] = (uint8_t)n;
+        std::stable_sort(p.plan_order, p.plan_order + n_seqs, [&](uint8_t a, uint8_t b) {
+            return p.plan_off[a + 1] - p.plan_off[a] > p.plan_off[b + 1] - p.plan_off[b];
+        });
     }
     return p;
 }

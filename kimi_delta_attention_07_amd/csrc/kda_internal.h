@@ -54,6 +54,7 @@ struct PrologueParams {
 // Batches of up to kPlanSeqs sequences carry their chunk table in the kernel
 // arguments (built on the host from cu_seqlens_host), so no table kernel runs.
 constexpr int kPlanSeqs = 128;
+static_assert(kPlanSeqs <= 256, "plan_order holds sequence numbers in 8 bits");
 
 struct ChunkParams {
     int T, H, n_seqs, n_chunks;
@@ -75,10 +76,12 @@ struct ChunkParams {
     const float *s0;
     float *s_final;
     uint16_t *out;
-    // small batches: first chunk of each sequence and cu_seqlens, [n_seqs+1]
+    // small batches: first chunk of each sequence and cu_seqlens, [n_seqs+1],
+    // and the scan's dispatch order, sequences by decreasing chunk count
     int plan_in_args;
     int32_t plan_off[kPlanSeqs + 1];
     int32_t plan_cu[kPlanSeqs + 1];
+    uint8_t plan_order[kPlanSeqs];
 };
 
 struct DecodeParams {
