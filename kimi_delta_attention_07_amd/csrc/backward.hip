@@ -397,15 +397,26 @@ __global__ __launch_bounds__(kNT) void bwd_prep_kernel(BwdParams p) {
     bmm<false, true, 1, false, 64, 1, true>(B + bPm, 64, B + bQd, 128, B + bKi, 128, 128, 1.f, 64, sm);    // Pm
 }
 
-// Block -> (sequence, head, value tile) for the state passes: the eight tiles
-// of one (sequence, head) get consecutive numbers within one XCD's share of
-// the grid (blocks are dealt to the XCDs round robin), so they share its L2.
+// Block -> (sequence, head, value tile) for the state passes, as in the
+// forward scan: blocks go to the XCDs in turn (b % 8) and the eight tiles of
+// one (sequence, head) item stay on one XCD, so they share its L2.  When the
+// item count divides by 8 the items are dealt to the XCDs in turn, longest
+// sequences first with a host-side plan (each block's time grows with its
+// sequence's length); otherwise each XCD takes a contiguous eighth.
 __device__ __forceinline__ void tile_of(const ChunkParams &c, int &n, int &h, int &tile) {
-    const int total = c.n_seqs * c.H * kTilesV, per_xcd = total / 8;
-    const int b = blockIdx.x, u = (b % 8) * per_xcd + b / 8;
-    tile = u % kTilesV;
-    h = (u / kTilesV) % c.H;
-    n = u / (kTilesV * c.H);
+    const int b = blockIdx.x;
+    if ((c.n_seqs * c.H) % 8 == 0) {
+        const int slot = b / 8, item = (slot / kTilesV) * 8 + b % 8;
+        tile = slot % kTilesV;
+        h = item % c.H;
+        n = c.plan_in_args ? (int)c.plan_order[item / c.H] : item / c.H;
+    } else {
+        const int total = c.n_seqs * c.H * kTilesV, per_xcd = total / 8;
+        const int u = (b % 8) * per_xcd + b / 8;
+        tile = u % kTilesV;
+        h = (u / kTilesV) % c.H;
+        n = u / (kTilesV * c.H);
+    }
 }
 
 // The state passes run on fp32 MFMAs (16x16x4): lane l supplies A[l % 16][l / 16]
