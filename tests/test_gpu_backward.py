@@ -90,6 +90,16 @@ def test_backward_many_sequences():
     assert_grads_close(run_gpu(c), run_oracle(c), "150 sequences")
 
 
+def test_backward_many_sequences_dealt_to_xcds():
+    """136 short sequences x 1 head: 136 items, a multiple of 8, so the state
+    passes deal them to the XCDs in turn, with the device-built table."""
+    g = torch.Generator().manual_seed(97)
+    lens = torch.randint(0, 91, (136,), generator=g).tolist()
+    lens[7] = 0
+    c = make_case(13, lens, 1)
+    assert_grads_close(run_gpu(c), run_oracle(c), "136 sequences")
+
+
 def test_backward_slow_decay_long():
     """Decays near 1 (log alpha = -exp(U(-8, -2))) over 16 chunks."""
     c = make_case(5, [1024], 2, la_range=(-8.0, -2.0))

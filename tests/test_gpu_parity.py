@@ -331,6 +331,22 @@ def test_prefill_many_sequences():
         assert np.array_equal(S[3], inp["initial_state"][3].double().numpy())
 
 
+def test_prefill_many_sequences_dealt_to_xcds():
+    """136 short sequences x 2 heads: 272 (sequence, head) items, a multiple
+    of 8, so the scan deals them to the XCDs in turn; with more than 128
+    sequences the table is built on the device and the dispatch order is the
+    sequences' own.  Fused and unfused path, every element checked."""
+    g = torch.Generator().manual_seed(98)
+    lens = torch.randint(0, 91, (136,), generator=g).tolist()
+    lens[0], lens[50] = 0, 1
+    inp = ki.prefill_inputs(98, lens, H=2, d=128, K=4, cache_std=1.0)
+    ref = ORC.prefill(inp)
+    for name, res in (("fused", gpu_prefill_fused(inp)), ("unfused", gpu_prefill(inp))):
+        assert_chunk_close(res["y"], ref["y"], f"136 seqs {name} y")
+        assert_chunk_close(res["final_state"], ref["final_state"], f"136 seqs {name} final state")
+        assert_fp32_close(res["conv_cache"], ref["conv_cache"], f"136 seqs {name} conv cache", 0.0)
+
+
 @pytest.mark.parametrize("n_seqs", [40, 33])
 def test_prefill_two_tiles_per_block(n_seqs):
     """n sequences x 2 heads: 80 heads put four value tiles in each scan block,
