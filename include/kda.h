@@ -314,6 +314,8 @@ kda_status kda_mixer_prefill(const kda_geom *geom, int32_t n_seqs, int32_t total
  *   conv_w [3][H*d][conv_k] fp32; conv_cache [n_slots][3][conv_k-1][H*d] fp32
  *     and state [n_slots][H][d][d] fp32 are updated in place;
  *   out [batch][H][d] in out_dtype (fp32 keeps the step's fp32 accuracy).
+ * One 256-thread workgroup per (row, head), heads fastest in a 1-D grid:
+ * batch <= 65535 * 256 and batch * H <= 2^31 - 1 (else KDA_ERR_SHAPE).
  */
 kda_status kda_decode_step(const kda_geom *geom, int32_t batch, const int32_t *slot_idx_dev,
                            int32_t n_slots, kda_dtype in_dtype, const void *q_raw,

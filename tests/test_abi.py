@@ -91,7 +91,7 @@ def decode(L, geom=None, batch=2, slot=None, n_slots=2, dti=1, ptrs=None, dto=0)
 @pytest.mark.parametrize("case,code", [
     ("geom_null", NULL), ("d5", UNSUP), ("d256", UNSUP), ("conv_k5", UNSUP), ("conv_k0", UNSUP),
     ("act7", UNSUP), ("batch0", SHAPE), ("H0", SHAPE), ("slots_short", SHAPE), ("dtype7", DTYPE),
-    ("out_dtype7", DTYPE), ("q_null", NULL), ("state_null", NULL), ("misaligned", ALIGN),
+    ("out_dtype7", DTYPE), ("q_null", NULL), ("state_null", NULL), ("misaligned", ALIGN), ("grid_product", SHAPE),
 ])
 def test_decode_rejects(L, case, code):
     kw = {}
@@ -115,6 +115,8 @@ def test_decode_rejects(L, case, code):
         kw["geom"] = _geom(H=0)
     elif case == "slots_short":
         kw["batch"], kw["n_slots"] = 3, 2
+    elif case == "grid_product":   # one block per (row, head): 60000 x 40000 > 2^31 - 1
+        kw["geom"], kw["batch"], kw["n_slots"] = _geom(H=40000), 60000, 60000
     elif case == "dtype7":
         kw["dti"] = 7
     elif case == "out_dtype7":
@@ -131,6 +133,8 @@ def test_decode_rejects(L, case, code):
         kw["ptrs"] = p
     assert decode(L, **kw) == code
     assert L.kda_last_error_detail().decode() != ""
+    if case == "grid_product":
+        assert "too large for the grid" in L.kda_last_error_detail().decode()
 
 
 def prologue(L, cu_vals=(0, 5, 9), total=9, geom=None, dtype=1, ptrs=None):
