@@ -3,9 +3,13 @@
 Inputs are the prologue outputs rounded to bf16 (the forward's input
 precision), the same bf16 values going to both sides, so the comparison
 isolates the backward's own arithmetic, which is fp32 throughout.  Bar, per
-gradient tensor and element: |gpu - oracle| <= 1e-4 max|oracle| + 1e-3 |oracle|
-(fp32 products of length <= 128 chained over up to a few hundred chunks;
-measured errors are below 1e-6 of the tensor's maximum).
+gradient tensor and element: |gpu - oracle| <= 1e-5 max|oracle| + 1e-4 |oracle|.
+Each fp32 product has length <= 128, so its rounding stays within
+128 * 2^-24 ~ 7.6e-6 of the sum of its terms' magnitudes.  The chunk-to-chunk
+transitions the gradients pass through cannot amplify it: the decays are at
+most 1, beta lies in (0, 1) and k has unit norm, so I - beta k k^T has norm
+at most 1.  Measured errors stay within 5e-6 of the tensor's maximum up to
+1024 chunks.
 """
 import numpy as np
 import pytest
@@ -60,7 +64,7 @@ def assert_grads_close(got, ref, what, heads=None):
         if w.size == 0:
             continue
         err = np.abs(g - w)
-        bar = 1e-4 * np.abs(w).max() + 1e-3 * np.abs(w)
+        bar = 1e-5 * np.abs(w).max() + 1e-4 * np.abs(w)
         bad = err > bar
         assert not bad.any(), f"{what} {a}: {int(bad.sum())} elements off (max err {err.max():.3e}, max |ref| " \
                               f"{np.abs(w).max():.3e})"
