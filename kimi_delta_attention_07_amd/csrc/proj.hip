@@ -28,7 +28,11 @@
 //
 // Epilogues: plain (one [M][N] bf16 output) or the KDA input projection,
 // whose N columns are six segments: q, k, v, gate, decay (H d each,
-// head-major) and beta (H).  The decay segment leaves as
+// head-major) and beta (H).  The beta columns go to a narrow kernel of their
+// own: in the tile grid they would add a column of tiles that costs as much
+// as a full one (at T = 4096, hidden 7168, H = 32: 1296 tiles, a sixth round
+// on 256 CUs for 16 of them; without them 1280, five rounds).  The decay
+// segment leaves as
 //   log alpha = -exp(a_log[h]) * softplus(z + bias[h d + c]),
 // a mapping the pages leave open (this library's reading; a_log and bias may
 // be absent, giving -softplus(z)).
@@ -218,14 +222,71 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(ProjParams p) {
     }
 }
 
+// out[M][n_cols] (row stride ldo) = A B^T for a narrow B (rows b[0 .. n_cols),
+// each K long).  A block takes 16 rows x 32 columns; its eight waves split
+// the K steps of 32 (wave w: steps w, w + 8, ...), each with four steps' loads
+// in flight, and add their partial sums in LDS in wave order.  Rows, columns
+// and K chunks past the ends load as zero through the buffer resources.
+__global__ __launch_bounds__(512) void gemm_narrow_kernel(ProjParams p, const uint16_t *b, int n_cols,
+                                                          uint16_t *out, int ldo) {
+    __shared__ __attribute__((aligned(16))) f32x4 red[8][2][64];
+    const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int row0 = blockIdx.x * 16, n0 = blockIdx.y * 32;
+    const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(p.a, (uint32_t)((long)p.M * p.K * 2));
+    const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(b, (uint32_t)((long)n_cols * p.K * 2));
+    // byte offset of a fragment chunk, or past every resource when the row or
+    // the chunk lies outside (K is a multiple of 8: a chunk is all in or out)
+    auto off = [&](long row, long rows, int k) -> uint32_t {
+        return (row < rows && k < p.K) ? (uint32_t)((row * p.K + k) * 2) : 0xffffffffu;
+    };
+    auto load = [&](int ks, u32x4 &fa, u32x4 (&fb)[2]) {
+        const int k = ks * 32 + 8 * g;
+        fa = __builtin_amdgcn_raw_buffer_load_b128(ra, off(row0 + c16, p.M, k), 0, 0);
+#pragma unroll
+        for (int nn = 0; nn < 2; ++nn)
+            fb[nn] = __builtin_amdgcn_raw_buffer_load_b128(rb, off(n0 + 16 * nn + c16, n_cols, k), 0, 0);
+    };
+    const int nks = (p.K + 31) / 32, steps = (nks + 31) / 32 * 4;   // per wave, a multiple of 4
+    f32x4 acc[2] = {f32x4{0.f, 0.f, 0.f, 0.f}, f32x4{0.f, 0.f, 0.f, 0.f}};
+    u32x4 fa[4], fb[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) load(w + 8 * i, fa[i], fb[i]);
+    for (int j = 0; j < steps; j += 4) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+#pragma unroll
+            for (int nn = 0; nn < 2; ++nn) acc[nn] = mfma16(as_bf16x8(fa[i]), as_bf16x8(fb[i][nn]), acc[nn]);
+            load(w + 8 * (j + i + 4), fa[i], fb[i]);
+        }
+    }
+    // acc[nn][r]: row row0 + 4 g + r, column n0 + 16 nn + c16
+#pragma unroll
+    for (int nn = 0; nn < 2; ++nn) red[w][nn][l] = acc[nn];
+    __syncthreads();
+    const int nn = tid >> 8, ll = (tid >> 2) & 63, r = tid & 3;
+    float sum = 0.0f;
+#pragma unroll
+    for (int ww = 0; ww < 8; ++ww) sum += red[ww][nn][ll][r];
+    const int row = row0 + 4 * (ll >> 4) + r, col = n0 + 16 * nn + (ll & 15);
+    if (row < p.M && col < n_cols) out[(long)row * ldo + col] = f2bf(sum);
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const ProjParams &p, hipStream_t s) {
     if (p.M == 0 || p.N == 0) return hipGetLastError();
-    const long tiles = (long)((p.M + kBM - 1) / kBM) * ((p.N + kBN - 1) / kBN);
-    const dim3 grid((unsigned)tiles);
-    if (p.epi == 1) hipLaunchKernelGGL((gemm_kernel<1>), grid, dim3(512), 0, s, p);
-    else hipLaunchKernelGGL((gemm_kernel<0>), grid, dim3(512), 0, s, p);
+    ProjParams q = p;
+    if (p.epi == 1) q.N = 5 * p.H * p.d;   // the beta columns: gemm_narrow_kernel below
+    const long tiles = (long)((q.M + kBM - 1) / kBM) * ((q.N + kBN - 1) / kBN);
+    if (tiles > 0) {
+        if (q.epi == 1) hipLaunchKernelGGL((gemm_kernel<1>), dim3((unsigned)tiles), dim3(512), 0, s, q);
+        else hipLaunchKernelGGL((gemm_kernel<0>), dim3((unsigned)tiles), dim3(512), 0, s, q);
+    }
+    if (p.epi == 1) {
+        const dim3 grid((unsigned)((p.M + 15) / 16), (unsigned)((p.H + 31) / 32));
+        hipLaunchKernelGGL(gemm_narrow_kernel, grid, dim3(512), 0, s, p, p.b + (long)q.N * p.K, p.H, p.seg[5], p.H);
+    }
     return hipGetLastError();
 }
 
