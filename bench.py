@@ -76,11 +76,13 @@ FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector, TFLOP/s
 TRAFFIC_KERNEL = {"prologue": "prologue128_kernel<4, 1>", "chunk_prepare": "prepare_kernel<false, 4, 0>",
                   "chunk_scan": "scan_kernel<true, 1>", "prefill_prepare": "prepare_kernel<true, 4, 1>",
                   "prefill_scan": "scan_kernel<true, 1>", "decode": "decode_kernel<128, 1, 0>",
-                  "in_projection": "gemm_kernel<1>", "out_projection": "gemm_kernel<0>",
+                  "in_projection": "gemm_kernel<1>", "in_projection_beta": "gemm_narrow_kernel",
+                  "out_projection": "gemm_kernel<0>",
                   "mla_attend": "mla_attend_kernel<3, 2, true, true>", "mla_combine": "mla_combine_kernel"}
 KERNEL_SOURCES = {"prologue": ["prologue.hip"], "chunk_prepare": ["chunk.hip"], "chunk_scan": ["chunk.hip"],
                   "prefill_prepare": ["chunk.hip"], "prefill_scan": ["chunk.hip"], "decode": ["decode.hip"],
-                  "in_projection": ["proj.hip"], "out_projection": ["proj.hip"], "mla_attend": ["mla.hip"],
+                  "in_projection": ["proj.hip"], "in_projection_beta": ["proj.hip"], "out_projection": ["proj.hip"],
+                  "mla_attend": ["mla.hip"],
                   "mla_combine": ["mla.hip"]}
 
 
@@ -514,6 +516,8 @@ def bench_mixer(torch, kda, ki, args, dev):
     f_in, f_out = 2.0 * T * hidden * n_in, 2.0 * T * H * D * n_out
     tf_in, tf_out = f_in / (ms_in * 1e-3) / 1e12, f_out / (ms_out * 1e-3) / 1e12
     tf_mix = (f_in + f_out) / (ms_mix * 1e-3) / 1e12
+    tr_in = [measured_traffic("in_projection", "mixer"), measured_traffic("in_projection_beta", "mixer")]
+    in_traffic = sum(tr_in) if all(t is not None for t in tr_in) else None
     return {"workload": f"KDA mixer, 1 sequence x {T} tokens, hidden {hidden} (synthetic), H=32 dk=dv=128, conv 4: "
                         "input projection, fused prefill, output projection; bf16 weights and activations",
             "value": T / (ms_mix * 1e-3), "unit": "tokens/s", "ms_per_step": ms_mix, "steps": reps,
@@ -522,9 +526,11 @@ def bench_mixer(torch, kda, ki, args, dev):
             "out_projection": {"ms_per_call": ms_out, "shape": f"[{T} x {H * D}] x [{n_out} x {H * D}]^T",
                                "tflops": tf_out, "mfma_frac": tf_out / BF16_PEAK_TFLOPS},
             "roofline": {"bound": "mfma", "achieved": tf_in, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": tf_in / BF16_PEAK_TFLOPS, "traffic": measured_traffic("in_projection", "mixer"),
-                         "kernel": "gemm_kernel<1> (input projection)", "flop_per_launch": f_in,
-                         "mfma_counters": measured_mfma("in_projection", "mixer")},
+                         "frac": tf_in / BF16_PEAK_TFLOPS, "traffic": in_traffic,
+                         "kernel": "gemm_kernel<1> + gemm_narrow_kernel (input projection: the 5 H d columns, "
+                                   "then the H beta columns)", "flop_per_launch": f_in,
+                         "mfma_counters": {"gemm_kernel<1>": measured_mfma("in_projection", "mixer"),
+                                           "gemm_narrow_kernel": measured_mfma("in_projection_beta", "mixer")}},
             "projection_flops_frac_of_step": (f_in + f_out) / (ms_mix * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             "step_tflops": tf_mix}
 
