@@ -57,12 +57,15 @@ def check_in_projection(inp, res):
     assert (np64(res["log_alpha"]) <= 0).all()
 
 
-@pytest.mark.parametrize("T,hidden,H,d", [(7, 16, 2, 4), (300, 16, 2, 4), (300, 1032, 4, 128), (513, 512, 3, 32)])
+@pytest.mark.parametrize("T,hidden,H,d", [(7, 16, 2, 4), (300, 16, 2, 4), (300, 1032, 4, 128), (513, 512, 3, 32),
+                                         (130, 1064, 40, 4)])
 def test_in_projection(T, hidden, H, d):
     """The tiny K3Config widths (hidden 16, 2 heads of 4; the k3 README's
     Tutorial 3), a production-like head dim with a ragged output width
     (5*4*128 + 4 = 2564 columns) and hidden 1032 (K tail), and an odd mix;
-    row counts span several 256-row tiles and a ragged one."""
+    row counts span several 256-row tiles and a ragged one.  40 heads give
+    the beta columns' narrow kernel two column blocks, the second partial,
+    with a K that is not a multiple of its 32-wide steps."""
     inp = ki.mixer_inputs(140 + T + hidden, [T], hidden, H, d, 4)
     res = kda.in_projection(inp["x"].cuda(), inp["w_in"].cuda(), H, d, inp["a_log"].cuda(), inp["dt_bias"].cuda())
     torch.cuda.synchronize()
