@@ -43,10 +43,24 @@ namespace kda {
 
 namespace {
 
-constexpr int kBM = 256, kBN = 256, kBK = 64;
-constexpr int kABytes = kBM * kBK * 2, kBBytes = kBN * kBK * 2;
-constexpr int kStage = kABytes + kBBytes;                // 65,536 B per K tile
+constexpr int kBM = 256, kBK = 64;
+constexpr int kABytes = kBM * kBK * 2;
 constexpr int kGroupM = 4;                               // M tiles per ordering group
+
+// Tile widths: 256 (eight waves in a 2 x 4 grid of 128 x 64 wave tiles) or
+// 224 (4 x 2 waves of 64 x 112), the latter for outputs whose tile count
+// would leave the last round on the CUs mostly idle: N = 7168 at M = 4096 is
+// 448 tiles of 256 (two rounds on 256 CUs, the second three-quarters full)
+// or 512 of 224 (two full rounds of 7/8-size tiles).
+template <int BN>
+struct TileShape {
+    static constexpr int WN = BN == 256 ? 4 : 2;   // waves along N
+    static constexpr int WM = 8 / WN;              // waves along M
+    static constexpr int MT = kBM / WM / 16;       // 16 x 16 MFMA tiles per wave, along M
+    static constexpr int NT = BN / WN / 16;        // ... along N
+    static constexpr int kStage = kABytes + BN * kBK * 2;
+    static_assert(WM * MT * 16 == kBM && WN * NT * 16 == BN, "wave tiles cover the block tile");
+};
 
 // byte offset of the 16-byte chunk kc (8 bf16) of row r in a 128-byte-row tile
 __device__ __forceinline__ int swz(int r, int kc) { return r * 128 + ((kc ^ ((r >> 1) & 7)) << 4); }
@@ -69,12 +83,14 @@ typedef __attribute__((address_space(3))) unsigned char lds_byte;
 constexpr int waitcnt_vm(int n) { return (n & 0xf) | (0x7 << 4) | (0xf << 8); }
 constexpr int waitcnt_vm_lgkm0(int n) { return (n & 0xf) | (0x7 << 4); }
 
-template <int EPI>
+template <int EPI, int BN>
 __global__ __launch_bounds__(512, 1) void gemm_kernel(ProjParams p) {
-    __shared__ __attribute__((aligned(16))) unsigned char st0[kStage], st1[kStage];
+    using TS = TileShape<BN>;
+    constexpr int MT = TS::MT, NT = TS::NT, WTM = MT * 16, WTN = NT * 16;   // wave tile WTM x WTN
+    __shared__ __attribute__((aligned(16))) unsigned char st0[TS::kStage], st1[TS::kStage];
     const int tid = threadIdx.x, l = tid & 63, g = l >> 4, c16 = l & 15;
-    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w >> 2, wn = w & 3;   // 2 x 4 waves
-    const int tiles_m = (p.M + kBM - 1) / kBM, tiles_n = (p.N + kBN - 1) / kBN;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6), wm = w / TS::WN, wn = w % TS::WN;
+    const int tiles_m = (p.M + kBM - 1) / kBM, tiles_n = (p.N + BN - 1) / BN;
     const int total = tiles_m * tiles_n;
     // blocks go round the 8 XCDs in turn: XCD x = b % 8 takes a contiguous run
     // of tile indices u, and within it tiles are ordered in groups of kGroupM M
@@ -87,15 +103,15 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(ProjParams p) {
     // N tiles in reverse: a narrow last column (the input projection's beta
     // outputs) is dispatched in the first round, not alone in an extra one
     const int bm = first_m + ug % gm, bn = tiles_n - 1 - ug / gm;
-    const int row0 = bm * kBM, col0 = bn * kBN;
+    const int row0 = bm * kBM, col0 = bn * BN;
     const int nk = (p.K + kBK - 1) / kBK;
     const __amdgpu_buffer_rsrc_t ra = buffer_rsrc(p.a, (uint32_t)((long)p.M * p.K * 2));
     const __amdgpu_buffer_rsrc_t rb = buffer_rsrc(p.b, (uint32_t)((long)p.N * p.K * 2));
 
     // tile kt into one stage: each load instruction fills 1 KB (8 rows) of the
     // stage, lane l the 16 bytes at 16 l; the lane fetches the chunk that the
-    // swizzle puts there.  A takes 4 instructions per wave, B 4: 8 per tile.
-    constexpr int kLoadsPerTile = 8;
+    // swizzle puts there.  A takes 4 instructions per wave, B BN / 64 (blocks
+    // of 8 rows w * 4 .. w * 4 + 3 that exist: at BN = 224 wave 7 has none).
     auto issue_tile = [&](int kt, unsigned char *st) {
         const int k0 = kt * kBK;
 #pragma unroll
@@ -109,23 +125,26 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(ProjParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int blk = w * 4 + i, r = blk * 8 + (l >> 3), kc = (l & 7) ^ ((r >> 1) & 7);
-            const int k = k0 + 8 * kc;
-            const uint32_t off = (k < p.K && col0 + r < p.N) ? (uint32_t)(((long)(col0 + r) * p.K + k) * 2)
-                                                             : 0xffffffffu;
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_byte *)(st + kABytes + blk * 1024), 16, off, 0, 0, 0);
+            if (BN == 256 || blk < BN / 8) {   // wave-uniform
+                const int k = k0 + 8 * kc;
+                const uint32_t off = (k < p.K && col0 + r < p.N) ? (uint32_t)(((long)(col0 + r) * p.K + k) * 2)
+                                                                 : 0xffffffffu;
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_byte *)(st + kABytes + blk * 1024), 16, off, 0, 0,
+                                                         0);
+            }
         }
     };
 
     // the KDA input projection's per-column epilogue parameters, loaded now
     // so that their latency passes under the main loop: decay columns take
     // a_log[h] and their bias, every other column (and absent ones) 0
-    float epi_A[4], epi_b[4];
+    float epi_A[NT], epi_b[NT];
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
+    for (int n = 0; n < NT; ++n) {
         epi_A[n] = 0.0f;
         epi_b[n] = 0.0f;
         if constexpr (EPI == 1) {
-            const int C = p.H * p.d, col = col0 + 64 * wn + 16 * n + c16;
+            const int C = p.H * p.d, col = col0 + WTN * wn + 16 * n + c16;
             if (col >= 4 * C && col < 5 * C) {
                 const int within = col - 4 * C;
                 if (p.a_log) epi_A[n] = p.a_log[within / p.d];
@@ -134,11 +153,11 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(ProjParams p) {
         }
     }
 
-    f32x4 acc[8][4];
+    f32x4 acc[MT][NT];
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
+    for (int m = 0; m < MT; ++m)
 #pragma unroll
-        for (int n = 0; n < 4; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int n = 0; n < NT; ++n) acc[m][n] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     // one iteration: tile kt sits in stage `cur`; `nxt` (the other stage)
     // receives tile kt + 1
@@ -156,15 +175,15 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(ProjParams p) {
         asm volatile("" ::: "memory");   // requests out before this tile's reads
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
-            bf16x8 fa[8], fb[4];
+            bf16x8 fa[MT], fb[NT];
 #pragma unroll
-            for (int m = 0; m < 8; ++m) fa[m] = lds_frag16(cur, swz(128 * wm + 16 * m + c16, 4 * kk + g));
+            for (int m = 0; m < MT; ++m) fa[m] = lds_frag16(cur, swz(WTM * wm + 16 * m + c16, 4 * kk + g));
 #pragma unroll
-            for (int n = 0; n < 4; ++n) fb[n] = lds_frag16(cur, kABytes + swz(64 * wn + 16 * n + c16, 4 * kk + g));
+            for (int n = 0; n < NT; ++n) fb[n] = lds_frag16(cur, kABytes + swz(WTN * wn + 16 * n + c16, 4 * kk + g));
 #pragma unroll
-            for (int m = 0; m < 8; ++m)
+            for (int m = 0; m < MT; ++m)
 #pragma unroll
-                for (int n = 0; n < 4; ++n) acc[m][n] = mfma16(fa[m], fb[n], acc[m][n]);
+                for (int n = 0; n < NT; ++n) acc[m][n] = mfma16(fa[m], fb[n], acc[m][n]);
         }
     };
 
@@ -175,33 +194,33 @@ __global__ __launch_bounds__(512, 1) void gemm_kernel(ProjParams p) {
     }
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));   // the trailing (all-zero) tile loads
 
-    // epilogue: element (m, n, r) is row row0 + 128 wm + 16 m + 4 g + r,
-    // column col0 + 64 wn + 16 n + c16
+    // epilogue: element (m, n, r) is row row0 + WTM wm + 16 m + 4 g + r,
+    // column col0 + WTN wn + 16 n + c16
     // one column group of 16 (fixed n): out[row][within] for the 32 rows this
     // lane holds, through the decay activation or not
     auto store_cols = [&](int n, uint16_t *dst, int width, int within, bool decay, float A, float bias) {
         if (decay) {
 #pragma unroll
-            for (int m = 0; m < 8; ++m)
+            for (int m = 0; m < MT; ++m)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int row = row0 + 128 * wm + 16 * m + 4 * g + r;
+                    const int row = row0 + WTM * wm + 16 * m + 4 * g + r;
                     const float v = -A * softplus_f(acc[m][n][r] + bias);
                     if (row < p.M) dst[(long)row * width + within] = f2bf(v);
                 }
         } else {
 #pragma unroll
-            for (int m = 0; m < 8; ++m)
+            for (int m = 0; m < MT; ++m)
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
-                    const int row = row0 + 128 * wm + 16 * m + 4 * g + r;
+                    const int row = row0 + WTM * wm + 16 * m + 4 * g + r;
                     if (row < p.M) dst[(long)row * width + within] = f2bf(acc[m][n][r]);
                 }
         }
     };
 #pragma unroll
-    for (int n = 0; n < 4; ++n) {
-        const int col = col0 + 64 * wn + 16 * n + c16;
+    for (int n = 0; n < NT; ++n) {
+        const int col = col0 + WTN * wn + 16 * n + c16;
         if constexpr (EPI == 0) {
             if (col < p.N) store_cols(n, p.out, p.N, col, false, 1.0f, 0.0f);
         } else {
@@ -278,10 +297,24 @@ hipError_t launch_gemm(const ProjParams &p, hipStream_t s) {
     if (p.M == 0 || p.N == 0) return hipGetLastError();
     ProjParams q = p;
     if (p.epi == 1) q.N = 5 * p.H * p.d;   // the beta columns: gemm_narrow_kernel below
-    const long tiles = (long)((q.M + kBM - 1) / kBM) * ((q.N + kBN - 1) / kBN);
-    if (tiles > 0) {
-        if (q.epi == 1) hipLaunchKernelGGL((gemm_kernel<1>), dim3((unsigned)tiles), dim3(512), 0, s, q);
-        else hipLaunchKernelGGL((gemm_kernel<0>), dim3((unsigned)tiles), dim3(512), 0, s, q);
+    const long tiles_m = (q.M + kBM - 1) / kBM;
+    auto tiles = [&](int bn) { return tiles_m * ((q.N + bn - 1) / bn); };
+    if (tiles(256) > 0) {
+        if (q.epi == 1) {
+            hipLaunchKernelGGL((gemm_kernel<1, 256>), dim3((unsigned)tiles(256)), dim3(512), 0, s, q);
+        } else {
+            // the tile width whose rounds over the CUs, each as long as its
+            // tile is wide, add up to less (ties: 256)
+            int dev = 0, cus = 0;
+            if (hipGetDevice(&dev) != hipSuccess ||
+                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+                cus = 256;
+            auto cost = [&](int bn) { return (tiles(bn) + cus - 1) / cus * bn; };
+            if (cost(224) < cost(256))
+                hipLaunchKernelGGL((gemm_kernel<0, 224>), dim3((unsigned)tiles(224)), dim3(512), 0, s, q);
+            else
+                hipLaunchKernelGGL((gemm_kernel<0, 256>), dim3((unsigned)tiles(256)), dim3(512), 0, s, q);
+        }
     }
     if (p.epi == 1) {
         const dim3 grid((unsigned)((p.M + 15) / 16), (unsigned)((p.H + 31) / 32));
