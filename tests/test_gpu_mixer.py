@@ -83,8 +83,11 @@ def test_in_projection_no_decay_parameters():
     assert_gemm_close(res["log_alpha"], ref["log_alpha"], S, 64, "log_alpha without a_log, dt_bias")
 
 
-@pytest.mark.parametrize("T,C,hidden", [(300, 512, 1032), (5, 8, 16), (1024, 4096, 256)])
+@pytest.mark.parametrize("T,C,hidden", [(300, 512, 1032), (5, 8, 16), (1024, 4096, 256), (4096, 512, 4096)])
 def test_out_projection(T, C, hidden):
+    """Ragged shapes take the 224-wide tile; 4096 x 4096 outputs fill 256
+    CUs once with 256-wide tiles (16 x 16) and would need a second round
+    with 224-wide ones (16 x 19), so they take the 256-wide tile."""
     g = torch.Generator().manual_seed(160 + T)
     y = torch.randn(T, C, generator=g).to(torch.bfloat16)
     w = (torch.randn(hidden, C, generator=g) * C ** -0.5).to(torch.bfloat16)
