@@ -76,8 +76,8 @@ FP32_PEAK_TFLOPS = 157.3       # MI355X fp32 vector, TFLOP/s
 TRAFFIC_KERNEL = {"prologue": "prologue128_kernel<4, 1>", "chunk_prepare": "prepare_kernel<false, 4, 0>",
                   "chunk_scan": "scan_kernel<true, 1>", "prefill_prepare": "prepare_kernel<true, 4, 1>",
                   "prefill_scan": "scan_kernel<true, 1>", "decode": "decode_kernel<128, 1, 0>",
-                  "in_projection": "gemm_kernel<1>", "in_projection_beta": "gemm_narrow_kernel",
-                  "out_projection": "gemm_kernel<0>",
+                  "in_projection": "gemm_kernel<1, 256>", "in_projection_beta": "gemm_narrow_kernel",
+                  "out_projection": "gemm_kernel<0, 224 or 256>",
                   "mla_attend": "mla_attend_kernel<3, 2, true, true>", "mla_combine": "mla_combine_kernel"}
 KERNEL_SOURCES = {"prologue": ["prologue.hip"], "chunk_prepare": ["chunk.hip"], "chunk_scan": ["chunk.hip"],
                   "prefill_prepare": ["chunk.hip"], "prefill_scan": ["chunk.hip"], "decode": ["decode.hip"],
@@ -527,9 +527,9 @@ def bench_mixer(torch, kda, ki, args, dev):
                                "tflops": tf_out, "mfma_frac": tf_out / BF16_PEAK_TFLOPS},
             "roofline": {"bound": "mfma", "achieved": tf_in, "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": tf_in / BF16_PEAK_TFLOPS, "traffic": in_traffic,
-                         "kernel": "gemm_kernel<1> + gemm_narrow_kernel (input projection: the 5 H d columns, "
+                         "kernel": "gemm_kernel<1, 256> + gemm_narrow_kernel (input projection: the 5 H d columns, "
                                    "then the H beta columns)", "flop_per_launch": f_in,
-                         "mfma_counters": {"gemm_kernel<1>": measured_mfma("in_projection", "mixer"),
+                         "mfma_counters": {"gemm_kernel<1, 256>": measured_mfma("in_projection", "mixer"),
                                            "gemm_narrow_kernel": measured_mfma("in_projection_beta", "mixer")}},
             "projection_flops_frac_of_step": (f_in + f_out) / (ms_mix * 1e-3) / 1e12 / BF16_PEAK_TFLOPS,
             "step_tflops": tf_mix}
