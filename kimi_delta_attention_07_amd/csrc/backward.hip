@@ -699,6 +699,10 @@ __device__ __forceinline__ void materialize(f32x4 (&a)[8]) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) asm volatile("" : "+v"(a[i]));
 }
+// Keeps the compiler from hoisting the next operand's loads above this point,
+// so one 32-register operand (Kd, Ki, Qd or Kg, then G) is live at a time
+// beside the accumulators and the dk, dG sums.
+__device__ __forceinline__ void one_operand_at_a_time() { asm volatile("" ::: "memory"); }
 // Sum over the 16 rows a wave holds of one column block (lanes l, l ^ 16, l ^ 32, l ^ 48).
 __device__ __forceinline__ float col_sum16(float v) {
     v += __shfl_xor(v, 16, 64);
@@ -730,7 +734,7 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void b
     if (tid < 64) beta_s[tid] = tid < len ? c.beta[(tok0 + tid) * H + h] : 0.f;
     // G is reloaded for each use (an L2 hit) rather than held across the
     // products, which keeps the kernel within two blocks' registers per CU
-    f32x4 G[8], acc[8], X[8], dG[8], dk[8];
+    f32x4 acc[8], X[8], dG[8], dk[8];
     auto zero = [](f32x4 *a, int n) {
         for (int i = 0; i < n; ++i) a[i] = f32x4{0.f, 0.f, 0.f, 0.f};
     };
@@ -819,64 +823,73 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void b
     bmm_acc<true, false, 128, 2>(acc, B + bTB, 64, B + bdW, 128, 64, sm);
     bmm_acc<false, false, 128, 2>(acc, s_dA, kLdA, B + bKi, 128, 64, sm);
     load_acc_layout<128>(X, rs_B, bKd, 128);
-    load_acc_layout<128>(G, rs_B, bG, 128);
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) dG[nb] = acc[nb] * X[nb];
     materialize(dG);
+    one_operand_at_a_time();
+    load_acc_layout<128>(X, rs_B, bG, 128);   // X now holds G
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) dk[nb][r] = acc[nb][r] * __expf(G[nb][r]);
+        for (int r = 0; r < 4; ++r) dk[nb][r] = acc[nb][r] * __expf(X[nb][r]);
     materialize(dk);
     // dKi = (beta dA)^T Kd + dPm^T Qd: dk += dKi e^-G, dG -= dKi Ki
     zero(acc, 8);
     bmm_acc<true, false, 128, 2>(acc, s_dA, kLdA, B + bKd, 128, 64, sm);
     bmm_acc<true, false, 128, 2>(acc, s_dPm, 64, B + bQd, 128, 64, sm);
     load_acc_layout<128>(X, rs_B, bKi, 128);
-    load_acc_layout<128>(G, rs_B, bG, 128);
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            dG[nb][r] -= acc[nb][r] * X[nb][r];
-            dk[nb][r] += acc[nb][r] * __expf(-G[nb][r]);
-        }
+        for (int r = 0; r < 4; ++r) dG[nb][r] -= acc[nb][r] * X[nb][r];
     materialize(dG);
+    one_operand_at_a_time();
+    load_acc_layout<128>(X, rs_B, bG, 128);   // X now holds G
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dk[nb][r] += acc[nb][r] * __expf(-X[nb][r]);
     materialize(dk);
     // dQd = dO S0^T + dPm Ki: dq = dQd e^G, dG += dQd Qd
     zero(acc, 8);
     bmm_acc<false, true, 128, 2>(acc, B + bdO, 128, B + bS0, 128, 128, sm);
     bmm_acc<false, false, 128, 2>(acc, s_dPm, 64, B + bKi, 128, 64, sm);
     load_acc_layout<128>(X, rs_B, bQd, 128);
-    load_acc_layout<128>(G, rs_B, bG, 128);
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) dG[nb] += acc[nb] * X[nb];
     materialize(dG);
+    one_operand_at_a_time();
+    load_acc_layout<128>(X, rs_B, bG, 128);   // X now holds G
     {
         const __amdgpu_buffer_rsrc_t rs = out_rs(p.dq);
 #pragma unroll
         for (int r = 0; r < 4; ++r)
 #pragma unroll
-            for (int nb = 0; nb < 8; ++nb) st_out(rs, r, nb, acc[nb][r] * __expf(G[nb][r]));
+            for (int nb = 0; nb < 8; ++nb) st_out(rs, r, nb, acc[nb][r] * __expf(X[nb][r]));
     }
     // dKg = U dS_L^T: dk += dKg e^{G_L - G}, dG -= dKg Kg, and its column sums for dG_L
     zero(acc, 8);
     bmm_acc<false, true, 128, 2>(acc, B + bU, 128, B + bdSL, 128, 128, sm);
     load_acc_layout<128>(X, rs_B, bKg, 128);
-    load_acc_layout<128>(G, rs_B, bG, 128);
 #pragma unroll
     for (int nb = 0; nb < 8; ++nb) {
-        const float gl = lds1(rs_B, bG + 63 * 128 + 16 * nb + lc);
         float cs = 0.f;
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             const float e = acc[nb][r] * X[nb][r];
             dG[nb][r] -= e;
             cs += e;
-            dk[nb][r] += acc[nb][r] * __expf(gl - G[nb][r]);
         }
         cs = col_sum16(cs);
         if (lg == 0) colq_s[w][16 * nb + lc] = cs;
+    }
+    one_operand_at_a_time();
+    load_acc_layout<128>(X, rs_B, bG, 128);   // X now holds G
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+        const float gl = lds1(rs_B, bG + 63 * 128 + 16 * nb + lc);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dk[nb][r] += acc[nb][r] * __expf(gl - X[nb][r]);
     }
     {
         const __amdgpu_buffer_rsrc_t rs = out_rs(p.dk);
@@ -885,22 +898,28 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void b
 #pragma unroll
             for (int nb = 0; nb < 8; ++nb) st_out(rs, r, nb, dk[nb][r]);
     }
+    // From here on the lane's indices are recomputed from a fresh copy of the
+    // thread index: kept from the start of the kernel, they would stay live
+    // across every product (and spill).
+    int t2 = tid;
+    asm volatile("" : "+v"(t2));
+    const int row0b = 16 * (t2 >> 6) + 4 * ((t2 & 63) >> 4), lcb = t2 & 15;
     // dG to LDS (s_big is free: the last product's staging ended with a barrier)
 #pragma unroll
     for (int r = 0; r < 4; ++r)
 #pragma unroll
-        for (int nb = 0; nb < 8; ++nb) s_big[(row0 + r) * 128 + 16 * nb + lc] = dG[nb][r];
+        for (int nb = 0; nb < 8; ++nb) s_big[(row0b + r) * 128 + 16 * nb + lcb] = dG[nb][r];
     float dgl = 0.f;
-    if (tid < 128) {   // dG_L = colsum(dKg Kg) + gL rowsum(S0 dS_L)
-        const int ch = tid;
+    if (t2 < 128) {   // dG_L = colsum(dKg Kg) + gL rowsum(S0 dS_L)
+        const int ch = t2;
         float t = 0.f;
 #pragma unroll 16
         for (int j = 0; j < 128; ++j) t += B[bS0 + ch * 128 + j] * B[bdSL + ch * 128 + j];
         dgl = ((colq_s[0][ch] + colq_s[1][ch]) + (colq_s[2][ch] + colq_s[3][ch])) + B[bGL + ch] * t;
     }
     __syncthreads();
-    if (tid < 128) {   // dlog alpha: reverse cumulative sum of dG, plus dG_L
-        const int ch = tid;
+    if (t2 < 128) {   // dlog alpha: reverse cumulative sum of dG, plus dG_L
+        const int ch = t2;
         float run = dgl;
 #pragma unroll 8
         for (int i = 63; i >= 0; --i) {
@@ -908,8 +927,8 @@ __global__ __launch_bounds__(kNT) __attribute__((amdgpu_waves_per_eu(2))) void b
             if (i < len) p.dla[((tok0 + i) * H + h) * kHeadDim + ch] = run;
         }
     }
-    if (tid < len)
-        p.dbeta[(tok0 + tid) * H + h] = ((colb_s[0][tid] + colb_s[1][tid]) + (colb_s[2][tid] + colb_s[3][tid])) + kk_s[tid];
+    if (t2 < len)
+        p.dbeta[(tok0 + t2) * H + h] = ((colb_s[0][t2] + colb_s[1][t2]) + (colb_s[2][t2] + colb_s[3][t2])) + kk_s[t2];
 }
 
 }  // namespace
