@@ -1,6 +1,6 @@
 """The library's entry points inside HIP graphs (captured with torch's graph
-API on its capture stream): the fused prefill, a 4-step KDA decode loop and
-an MLA decode token.  Each graph is replayed three times with eager work and
+API on its capture stream): the fused prefill, a 4-step KDA decode loop, an
+MLA decode token and the whole KDA mixer.  Each graph is replayed three times with eager work and
 synchronizations between the replays, and every replay must reproduce the
 eager result bit for bit (same kernels, same inputs: deterministic).  The
 library records no memset, allocation, copy or synchronization, so every
@@ -131,3 +131,41 @@ def test_mla_decode_graph_replays_match_eager():
         graph.replay()
         torch.cuda.synchronize()
         assert torch.equal(out, ref) and torch.equal(kc, kc_e) and torch.equal(vc, vc_e), f"replay {r}"
+
+
+def test_mixer_prefill_graph_replays_match_eager():
+    """The whole KDA mixer (input projection with its narrow beta-column
+    kernel, the fused prefill, the output projection, whose tile width the
+    launcher picks from the device's CU count) captured as one graph."""
+    dev = torch.device("cuda")
+    inp = ki.mixer_inputs(64, [300, 0, 77], 512, 4, 128, 4)
+    g = {k: (v.to(dev) if torch.is_tensor(v) else v) for k, v in inp.items()}
+    cu_h = inp["cu_seqlens"]
+    ws = torch.empty(kda.mixer_workspace_bytes(4, 128, len(cu_h) - 1, inp["T"]), dtype=torch.uint8, device=dev)
+
+    def call(out, S, cc):
+        return kda.mixer_prefill(g["x"], g["w_in"], g["w_out"], g["conv_w"], g["cu_seqlens"], g["a_log"],
+                                 g["dt_bias"], g["initial_state"], g["conv_cache"], cc, H=4, d=128,
+                                 cu_seqlens_host=cu_h, workspace=ws, out=out, final_state=S)
+
+    o0 = torch.empty(inp["T"], 512, dtype=torch.bfloat16, device=dev)
+    S0 = torch.empty(inp["N"], 4, 128, 128, dtype=torch.float32, device=dev)
+    c0 = torch.empty_like(g["conv_cache"])
+    call(o0, S0, c0)
+    torch.cuda.synchronize()
+    o1, S1, c1 = torch.full_like(o0, 7.0), torch.full_like(S0, 7.0), torch.full_like(c0, 7.0)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        call(o1, S1, c1)
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        call(o1, S1, c1)
+    for r in range(3):
+        o1.fill_(7.0), S1.fill_(7.0), c1.fill_(7.0)
+        _eager_noise(dev)
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(o1, o0) and torch.equal(S1, S0) and torch.equal(c1, c0), f"replay {r}"
