@@ -294,7 +294,7 @@ def bench_prefill_workloads(torch, kda, ki, args, dev):
     out = {}
     cases = [("varlen", dict(seed=3, lengths=None, draw_lengths=(256, 8192, 32)),
               "packed varlen prefill, 32 sequences of U[256, 8192] tokens"),
-             ("long_context", dict(seed=4, lengths=[65536], la_range=(-8.0, -2.0)),
+             ("long_context", dict(seed=4, lengths=[65536], la_range=(-8.0, -2.0), tail_steps=128),
               "long-context prefill, 1 sequence x 65,536 tokens, log alpha = -exp(U(-8, -2))")]
     for name, kw, desc in cases:
         inp = ki.prefill_inputs(kw.pop("seed"), kw.pop("lengths"), H=H, d=D, K=K, **kw)
@@ -326,9 +326,56 @@ def bench_prefill_workloads(torch, kda, ki, args, dev):
                      "tokens": T, "sequences": N, "chunks": n_chunks, "ms_per_call": ms,
                      "value": T / (ms * 1e-3), "unit": "tokens/s", "per_kernel_ms": per,
                      "roofline": path_roofline(floor_b, per, ms, list(per), name, T)}
+        if inp["tail"]:
+            out[name]["decode_tail"] = decode_tail(torch, kda, g, inp["tail"], dev)
         del g, ws
         torch.cuda.empty_cache()
     return out
+
+
+def decode_tail(torch, kda, g, tail, dev):
+    """The long-context workload's decode tail: kda_decode_step for one
+    sequence, token after token, continuing from the prefill's final state
+    and conv cache (the state is updated in place; a warm-up pass of the same
+    tokens runs first).  One workgroup per head, so the step is set by
+    latency, not bandwidth; bytes per token are the 32 fp32 states read and
+    written."""
+    steps = [{k: v.to(dev) for k, v in st.items()} for st in tail]
+    state, cache = g["final_state"], g["cache_out"]
+    y = torch.empty(1, H, D, dtype=torch.float32, device=dev)
+
+    def run():
+        for st in steps:
+            kda.decode_step(st["q_raw"], st["k_raw"], st["v_raw"], g["conv_w"], cache, state, st["log_alpha"],
+                            st["beta_logit"], st["gate_logit"], out=y)
+
+    spin_up(torch, run)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    run()
+    b.record()
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) * 1e3 / len(steps)
+    # the same 128 launches replayed from a HIP graph (captured on torch's
+    # capture stream after a warm-up there): launch overhead mostly gone
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    spin_up(torch, graph.replay)
+    a.record()
+    graph.replay()
+    b.record()
+    torch.cuda.synchronize()
+    us_graph = a.elapsed_time(b) * 1e3 / len(steps)
+    return {"steps": len(steps), "us_per_token": us, "value": 1e6 / us, "unit": "tokens/s",
+            "us_per_token_graph": us_graph, "state_bytes_per_token": DECODE_B_PER_ROW,
+            "achieved_gbs": DECODE_B_PER_ROW / (us * 1e-6) / 1e9}
 
 
 def bench_decode(torch, kda, ki, args, dev):
