@@ -36,6 +36,8 @@
 //   log alpha = -exp(a_log[h]) * softplus(z + bias[h d + c]),
 // a mapping the pages leave open (this library's reading; a_log and bias may
 // be absent, giving -softplus(z)).
+#include <atomic>
+
 #include "kda_device.h"
 #include "kda_internal.h"
 
@@ -291,6 +293,19 @@ __global__ __launch_bounds__(512) void gemm_narrow_kernel(ProjParams p, const ui
     if (row < p.M && col < n_cols) out[(long)row * ldo + col] = f2bf(sum);
 }
 
+// CUs of the current device, looked up once per device ordinal (256 when
+// the query fails).  Racing first calls on one device store the same value.
+int cu_count() {
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n > 0) return n;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    cached[dev].store(n, std::memory_order_relaxed);
+    return n;
+}
+
 }  // namespace
 
 hipError_t launch_gemm(const ProjParams &p, hipStream_t s) {
@@ -305,10 +320,7 @@ hipError_t launch_gemm(const ProjParams &p, hipStream_t s) {
         } else {
             // the tile width whose rounds over the CUs, each as long as its
             // tile is wide, add up to less (ties: 256)
-            int dev = 0, cus = 0;
-            if (hipGetDevice(&dev) != hipSuccess ||
-                hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-                cus = 256;
+            const int cus = cu_count();
             auto cost = [&](int bn) { return (tiles(bn) + cus - 1) / cus * bn; };
             if (cost(224) < cost(256))
                 hipLaunchKernelGGL((gemm_kernel<0, 224>), dim3((unsigned)tiles(224)), dim3(512), 0, s, q);
