@@ -233,10 +233,17 @@ struct RowIn128 {
 };
 __device__ __forceinline__ float2 pair_f2(uint32_t u) { return make_float2(lo_bf(u), hi_bf(u)); }
 __device__ __forceinline__ float2 pair_f2(float2 v) { return v; }
+// The streaming kernel reads every row once: its loads carry the
+// non-temporal bit.
+typedef float ntf2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float2 nt2(const float *q) {
+    const ntf2 v = __builtin_nontemporal_load(reinterpret_cast<const ntf2 *>(q));
+    return make_float2(v[0], v[1]);
+}
 template <int DT>
 __device__ __forceinline__ typename RowIn128<DT>::Pair load_pair(const void *base, long idx) {
-    if constexpr (DT == 1) return *reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(base) + idx);
-    else return *reinterpret_cast<const float2 *>(static_cast<const float *>(base) + idx);
+    if constexpr (DT == 1) return __builtin_nontemporal_load(reinterpret_cast<const uint32_t *>(static_cast<const uint16_t *>(base) + idx));
+    else return nt2(static_cast<const float *>(base) + idx);
 }
 // Rows past the end load the last row (unused).  Without a gate, the gate
 // loads read dq instead (in bounds, unused), so no branch splits the loads.
@@ -244,11 +251,11 @@ template <int DT>
 __device__ __forceinline__ void load_row128(const PrologueBwdParams &p, long t, long C, long ch, RowIn128<DT> &r) {
     t = min(t, (long)p.T - 1);
     const long o = t * C + ch;
-    r.dy[0] = *reinterpret_cast<const float2 *>(p.dq + o);
-    r.dy[1] = *reinterpret_cast<const float2 *>(p.dk + o);
-    r.dy[2] = *reinterpret_cast<const float2 *>(p.dv + o);
+    r.dy[0] = nt2(p.dq + o);
+    r.dy[1] = nt2(p.dk + o);
+    r.dy[2] = nt2(p.dv + o);
     r.zg = load_pair<DT>(p.gate_logit ? p.gate_logit : static_cast<const void *>(p.dq), o);
-    r.dg = *reinterpret_cast<const float2 *>((p.gate_logit ? p.dgate : p.dq) + o);
+    r.dg = nt2((p.gate_logit ? p.dgate : p.dq) + o);
     r.xr[0] = load_pair<DT>(p.q_raw, o);
     r.xr[1] = load_pair<DT>(p.k_raw, o);
     r.xr[2] = load_pair<DT>(p.v_raw, o);
