@@ -103,10 +103,10 @@ def test_mla_production_like_split_edges():
 @pytest.mark.parametrize("H,H_kv,dqk,dv", [(8, 2, 128, 128), (6, 3, 64, 64), (4, 1, 256, 256), (4, 4, 100, 72),
                                            (2, 2, 16, 8), (16, 2, 192, 128), (24, 3, 64, 64), (32, 2, 64, 64)])
 def test_mla_shapes(H, H_kv, dqk, dv):
-    """Grouped heads (groups of 2, 4 and 8 take the grouped kernel, one block
-    per kv head; a group of 16 takes the per-head kernel), the other vector
-    instances, widths that are not whole chunks (the element-wise path at
-    100 / 72 channels)."""
+    """Grouped heads (groups of 2 to 16; 16, 24 and 32 heads take the
+    launch's XCD head order, H a multiple of 8), the other vector instances,
+    widths that are not whole chunks (the element-wise path at 100 / 72
+    channels)."""
     inp = ki.mla_inputs(42 + dqk, 3, H, H_kv, dqk, dv, 700, len_range=(0, 699))
     check(inp, f"mla H={H} H_kv={H_kv} {dqk}/{dv}")
 
