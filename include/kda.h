@@ -44,7 +44,9 @@
  *   - Layouts are row-major (last index fastest).  Tokens of all sequences
  *     are packed ("THD": [total_tokens, H, d]); sequence n owns tokens
  *     cu_seqlens[n] .. cu_seqlens[n+1]-1 (int32, cu_seqlens[0] = 0,
- *     non-decreasing; empty sequences are allowed).
+ *     non-decreasing; empty sequences are allowed).  A batch may hold no
+ *     token at all (total_tokens = 0): the per-token arrays ([T][...]) may
+ *     then be NULL, and the states and conv caches pass through unchanged.
  *   - Every tensor pointer must be 16-byte aligned.
  *   - dk = dv = d.  kda_prologue and kda_decode_step accept d in
  *     {4, 8, 16, 32, 64, 128}; the chunk path accepts d = 128 and bf16 only.

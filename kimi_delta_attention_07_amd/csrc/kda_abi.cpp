@@ -306,10 +306,12 @@ kda_status kda_prologue(const kda_geom *geom, int32_t n_seqs, int32_t total_toke
     KDA_TRY(check_geom(geom, false));
     KDA_TRY(check_seqlens(n_seqs, total_tokens, cu_seqlens_host, nullptr));
     KDA_TRY(check_dtype(in_dtype));
-    KDA_TRY(check_required({{cu_seqlens_dev, "cu_seqlens_dev"}, {q_raw, "q_raw"}, {k_raw, "k_raw"},
-                            {v_raw, "v_raw"}, {conv_w, "conv_w"}, {beta_logit, "beta_logit"},
-                            {q_out, "q_out"}, {k_out, "k_out"}, {v_out, "v_out"}, {beta_out, "beta_out"}}));
-    if (gate_logit && !gate_out) return fail(KDA_ERR_NULL, "gate_out is NULL while gate_logit is given");
+    KDA_TRY(check_required({{cu_seqlens_dev, "cu_seqlens_dev"}, {conv_w, "conv_w"}}));
+    if (total_tokens > 0) {   // per-token arrays: none is touched when every sequence is empty
+        KDA_TRY(check_required({{q_raw, "q_raw"}, {k_raw, "k_raw"}, {v_raw, "v_raw"}, {beta_logit, "beta_logit"},
+                                {q_out, "q_out"}, {k_out, "k_out"}, {v_out, "v_out"}, {beta_out, "beta_out"}}));
+        if (gate_logit && !gate_out) return fail(KDA_ERR_NULL, "gate_out is NULL while gate_logit is given");
+    }
     KDA_TRY(check_aligned({{q_raw, "q_raw"}, {k_raw, "k_raw"}, {v_raw, "v_raw"}, {conv_w, "conv_w"},
                            {conv_cache_in, "conv_cache_in"}, {conv_cache_out, "conv_cache_out"},
                            {beta_logit, "beta_logit"}, {gate_logit, "gate_logit"}, {q_out, "q_out"},
@@ -419,7 +421,8 @@ kda_status kda_chunk_prepare(const kda_geom *geom, int32_t n_seqs, int32_t total
     long n_chunks = 0;
     KDA_TRY(check_chunk_common(geom, n_seqs, total_tokens, cu_seqlens_dev, cu_seqlens_host, in_dtype, workspace,
                                workspace_bytes, &n_chunks));
-    KDA_TRY(check_required({{q, "q"}, {k, "k"}, {v, "v"}, {log_alpha, "log_alpha"}, {beta, "beta"}}));
+    if (total_tokens > 0)
+        KDA_TRY(check_required({{q, "q"}, {k, "k"}, {v, "v"}, {log_alpha, "log_alpha"}, {beta, "beta"}}));
     KDA_TRY(check_aligned({{q, "q"}, {k, "k"}, {v, "v"}, {log_alpha, "log_alpha"}, {beta, "beta"}}));
     KDA_TRY(check_device());
     kda::ChunkParams p = chunk_params(geom, n_seqs, total_tokens, n_chunks, cu_seqlens_dev, cu_seqlens_host, workspace);
@@ -460,7 +463,8 @@ kda_status kda_chunk_forward(const kda_geom *geom, int32_t n_seqs, int32_t total
     long n_chunks = 0;
     KDA_TRY(check_chunk_common(geom, n_seqs, total_tokens, cu_seqlens_dev, cu_seqlens_host, in_dtype, workspace,
                                workspace_bytes, &n_chunks));
-    KDA_TRY(check_required({{q, "q"}, {k, "k"}, {v, "v"}, {log_alpha, "log_alpha"}, {beta, "beta"}}));
+    if (total_tokens > 0)
+        KDA_TRY(check_required({{q, "q"}, {k, "k"}, {v, "v"}, {log_alpha, "log_alpha"}, {beta, "beta"}}));
     if (total_tokens > 0) KDA_TRY(check_required({{out, "out"}}));
     KDA_TRY(check_aligned({{q, "q"}, {k, "k"}, {v, "v"}, {log_alpha, "log_alpha"}, {beta, "beta"}, {gate, "gate"},
                            {initial_state, "initial_state"}, {final_state, "final_state"}, {out, "out"}}));
@@ -478,8 +482,10 @@ kda_status kda_prefill_prepare(const kda_geom *geom, int32_t n_seqs, int32_t tot
     long n_chunks = 0;
     KDA_TRY(check_chunk_common(geom, n_seqs, total_tokens, cu_seqlens_dev, cu_seqlens_host, in_dtype, workspace,
                                workspace_bytes, &n_chunks));
-    KDA_TRY(check_required({{q_raw, "q_raw"}, {k_raw, "k_raw"}, {v_raw, "v_raw"}, {conv_w, "conv_w"},
-                            {log_alpha, "log_alpha"}, {beta_logit, "beta_logit"}}));
+    KDA_TRY(check_required({{conv_w, "conv_w"}}));
+    if (total_tokens > 0)
+        KDA_TRY(check_required({{q_raw, "q_raw"}, {k_raw, "k_raw"}, {v_raw, "v_raw"}, {log_alpha, "log_alpha"},
+                                {beta_logit, "beta_logit"}}));
     KDA_TRY(check_aligned({{q_raw, "q_raw"}, {k_raw, "k_raw"}, {v_raw, "v_raw"}, {conv_w, "conv_w"},
                            {conv_cache_in, "conv_cache_in"}, {conv_cache_out, "conv_cache_out"},
                            {log_alpha, "log_alpha"}, {beta_logit, "beta_logit"}}));
@@ -560,8 +566,10 @@ kda_status kda_prefill(const kda_geom *geom, int32_t n_seqs, int32_t total_token
     long n_chunks = 0;
     KDA_TRY(check_chunk_common(geom, n_seqs, total_tokens, cu_seqlens_dev, cu_seqlens_host, in_dtype, workspace,
                                workspace_bytes, &n_chunks));
-    KDA_TRY(check_required({{q_raw, "q_raw"}, {k_raw, "k_raw"}, {v_raw, "v_raw"}, {conv_w, "conv_w"},
-                            {log_alpha, "log_alpha"}, {beta_logit, "beta_logit"}}));
+    KDA_TRY(check_required({{conv_w, "conv_w"}}));
+    if (total_tokens > 0)
+        KDA_TRY(check_required({{q_raw, "q_raw"}, {k_raw, "k_raw"}, {v_raw, "v_raw"}, {log_alpha, "log_alpha"},
+                                {beta_logit, "beta_logit"}}));
     if (total_tokens > 0) KDA_TRY(check_required({{out, "out"}}));
     KDA_TRY(check_aligned({{gate_logit, "gate_logit"}, {initial_state, "initial_state"},
                            {final_state, "final_state"}, {out, "out"}}));
@@ -788,10 +796,10 @@ kda_status kda_prefill_noalloc(const kda_geom *geom, int32_t n_seqs, int32_t tot
     // address lookup needs one).
     KDA_TRY(check_dtype(in_dtype));
     if (in_dtype != KDA_BF16) return fail(KDA_ERR_UNSUPPORTED, "the chunk path takes bf16 inputs only");
-    KDA_TRY(check_required({{cu_seqlens_dev, "cu_seqlens_dev"}, {q_raw, "q_raw"}, {k_raw, "k_raw"},
-                            {v_raw, "v_raw"}, {conv_w, "conv_w"}, {log_alpha, "log_alpha"},
-                            {beta_logit, "beta_logit"}}));
-    if (total_tokens > 0) KDA_TRY(check_required({{out, "out"}}));
+    KDA_TRY(check_required({{cu_seqlens_dev, "cu_seqlens_dev"}, {conv_w, "conv_w"}}));
+    if (total_tokens > 0)
+        KDA_TRY(check_required({{q_raw, "q_raw"}, {k_raw, "k_raw"}, {v_raw, "v_raw"}, {log_alpha, "log_alpha"},
+                                {beta_logit, "beta_logit"}, {out, "out"}}));
     KDA_TRY(check_aligned({{q_raw, "q_raw"}, {k_raw, "k_raw"}, {v_raw, "v_raw"}, {conv_w, "conv_w"},
                            {conv_cache_in, "conv_cache_in"}, {conv_cache_out, "conv_cache_out"},
                            {log_alpha, "log_alpha"}, {beta_logit, "beta_logit"}, {gate_logit, "gate_logit"},

@@ -247,6 +247,37 @@ def test_prefill_rejects(L):
     assert prefill(L, ptrs=p) == ALIGN
 
 
+def test_empty_batch_takes_null_token_arrays(L):
+    """A batch with no token (total_tokens = 0) may pass NULL for every
+    per-token array.  Each call gets past the pointer checks and is stopped
+    by a misaligned state or cache pointer instead, before any device work;
+    with tokens, the same NULLs are refused."""
+    mis = ctypes.c_void_p(0x10004)
+    cu = (0, 0, 0)
+    t, hp = _cu(list(cu))
+    p = [None] * 13
+    p[3], p[4] = FAKE[3], mis   # conv_w; conv_cache_in misaligned
+    assert prologue(L, cu_vals=cu, total=0, ptrs=p) == ALIGN
+    assert prologue(L, cu_vals=(0, 5, 9), total=9, ptrs=p) == NULL
+    p = [None] * 9
+    p[6] = mis   # initial_state
+    assert chunk_forward(L, cu_vals=cu, ptrs=p) == ALIGN
+    assert chunk_forward(L, ptrs=p) == NULL
+    p = [None] * 12
+    p[3], p[9] = FAKE[3], mis   # conv_w; initial_state misaligned
+    assert prefill(L, cu_vals=cu, ptrs=p) == ALIGN
+    assert prefill(L, ptrs=p) == NULL
+    t2, hp2 = _cu([0, 100, 228])
+    args = lambda T: (_geom(), 2, T, FAKE[15], hp if T == 0 else hp2, 1)
+    assert L.kda_chunk_prepare(*args(0), None, None, None, None, None, mis, 1 << 40, None) == ALIGN
+    assert L.kda_prefill_prepare(*args(0), None, None, None, FAKE[3], mis, None, None, None, FAKE[16], 1 << 40,
+                                 None) == ALIGN
+    assert L.kda_prefill_noalloc(*args(0), 64, None, None, None, FAKE[3], None, None, None, None, None, mis, None,
+                                 None, None) == ALIGN
+    assert L.kda_prefill_noalloc(*args(228), 64, None, None, None, FAKE[3], None, None, None, None, None, mis, None,
+                                 None, None) == NULL
+
+
 def backward(L, geom=None, dtype=1, ws=FAKE[16], ws_bytes=1 << 40, ptrs=None, cu_vals=(0, 100, 228)):
     t, hp = _cu(list(cu_vals))
     p = list(FAKE[:16]) if ptrs is None else ptrs

@@ -314,6 +314,30 @@ def test_prefill_fused_conv_cache_out(lens, alias):
     assert_fp32_close(res["conv_cache"], ref["conv_cache"], "conv cache", 0.0)
 
 
+def test_prefill_empty_batch_passes_states_through():
+    """Three empty sequences (total_tokens = 0: every per-token tensor is
+    empty and reaches the library as NULL).  The fused, no-alloc and
+    three-call paths leave each final state equal to its initial state and
+    each outgoing conv cache equal to the incoming one, bit for bit, as the
+    oracle does."""
+    inp = ki.prefill_inputs(90, [0, 0, 0], H=2, d=128, K=4, cache_std=1.0)
+    ref = ORC.prefill(inp)
+    g = to_dev(inp)
+    cu_h = inp["cu_seqlens"]
+    runs = {"fused": gpu_prefill_fused(inp), "unfused": gpu_prefill(inp)}
+    cache_out = torch.full_like(g["conv_cache"], float("nan"))
+    y, S = kda.prefill_noalloc(g["q_raw"], g["k_raw"], g["v_raw"], g["conv_w"], g["log_alpha"], g["beta_logit"],
+                               g["gate_logit"], g["cu_seqlens"], g["initial_state"], g["conv_cache"], cache_out,
+                               cu_seqlens_host=cu_h)
+    torch.cuda.synchronize()
+    runs["noalloc"] = dict(y=y, final_state=S, conv_cache=cache_out)
+    for name, res in runs.items():
+        assert res["y"].numel() == 0, name
+        assert np.array_equal(np64(res["final_state"]), ref["final_state"]), name
+        assert np.array_equal(np64(res["conv_cache"]), ref["conv_cache"]), name
+        print(f"empty batch {name}: states and conv caches passed through exactly")
+
+
 def test_prefill_many_sequences():
     """150 short sequences (0..90 tokens, empty ones included): more than the
     128 whose chunk table travels in the kernel arguments, so the table is
