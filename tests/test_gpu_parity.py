@@ -427,6 +427,42 @@ def test_prefill_fused_alias_nogate_scale_and_matches_unfused():
     assert torch.equal(a["y"], c["y"]) and torch.equal(a["final_state"], c["final_state"])
 
 
+def _random_prefill_config(i):
+    """Configuration i of the randomised prefill cases: batch shape, heads,
+    conv width, decay range, zero or drawn state and cache, gate, scale and
+    cache aliasing, all from one seeded generator."""
+    rng = np.random.default_rng(7000 + i)
+    n = int(rng.integers(1, 13))
+    lens = [int(x) for x in rng.integers(0, 300, n)]
+    if rng.random() < 0.3:
+        lens[int(rng.integers(0, n))] = 0
+    la = [(-5.0, 0.0), (-8.0, -2.0), (-1.0, 1.5)][int(rng.integers(0, 3))]
+    kw = dict(H=int(rng.integers(1, 6)), d=128, K=int(rng.integers(1, 5)), la_range=la,
+              state_std=None if rng.random() < 0.3 else 0.05, cache_std=None if rng.random() < 0.3 else 1.0)
+    opts = dict(gated=bool(rng.random() < 0.7), scale=float(rng.choice([1.0, 128 ** -0.5])),
+                alias=bool(rng.random() < 0.5))
+    return ki.prefill_inputs(7000 + i, lens, **kw), opts
+
+
+@pytest.mark.parametrize("i", range(8))
+def test_prefill_random_configs(i):
+    """Eight seeded random batches through the fused path (and, gated, the
+    three-call path) against the oracle: every element within the chunk
+    bar, the conv cache exact."""
+    inp, o = _random_prefill_config(i)
+    ref = ORC.prefill(inp if o["gated"] else dict(inp, gate_logit=None), scale=o["scale"])
+    res = gpu_prefill_fused(inp, scale=o["scale"], alias_cache=o["alias"], gated=o["gated"])
+    what = f"random {i} (lens {inp['lengths']}, H={inp['H']}, K={inp['K']}, {o})"
+    assert_chunk_close(res["y"], ref["y"], what + " fused y")
+    assert_chunk_close(res["final_state"], ref["final_state"], what + " fused final state")
+    assert_fp32_close(res["conv_cache"], ref["conv_cache"], what + " fused conv cache", 0.0)
+    if o["gated"]:
+        res = gpu_prefill(inp, scale=o["scale"])
+        assert_chunk_close(res["y"], ref["y"], what + " unfused y")
+        assert_chunk_close(res["final_state"], ref["final_state"], what + " unfused final state")
+        assert_fp32_close(res["conv_cache"], ref["conv_cache"], what + " unfused conv cache", 0.0)
+
+
 def test_prefill_fused_T4096_full():
     inp = ki.config_prefill(1)
     res = gpu_prefill_fused(inp)
