@@ -104,6 +104,16 @@ def test_backward_many_sequences_dealt_to_xcds():
     assert_grads_close(run_gpu(c), run_oracle(c), "136 sequences")
 
 
+@pytest.mark.parametrize("la_range", [(0.1823, 0.1823), (-1.0, 0.1823)])
+def test_backward_strong_decay_within_contract(la_range):
+    """Decays up to the documented bound: log alpha = -1.2 on every token
+    and channel (bf16: -1.203125, 77 per 64-token chunk, below the 80 the
+    chunk-start reference allows), and log alpha = -exp(U(-1, 0.18)), per
+    token in [-1.2, -0.37]."""
+    c = make_case(15, [130, 64, 200], 2, la_range=la_range)
+    assert_grads_close(run_gpu(c), run_oracle(c), f"strong decay {la_range}")
+
+
 def test_backward_slow_decay_long():
     """Decays near 1 (log alpha = -exp(U(-8, -2))) over 16 chunks."""
     c = make_case(5, [1024], 2, la_range=(-8.0, -2.0))
