@@ -110,6 +110,40 @@ def test_decode_out_of_range_slot_is_skipped():
     assert_fp32_close(gca, ca, "conv cache", 0.0)
 
 
+@pytest.mark.parametrize("i", range(8))
+def test_decode_random_configs(i):
+    """Eight seeded random decode batches: rows, heads, head dim, conv width,
+    step count, slot count and row-to-slot map, decay range, gate on or off.
+    Every output row, the states and the conv caches against the oracle, fp32
+    bar 1e-5."""
+    rng = np.random.default_rng(8000 + i)
+    batch, H = int(rng.integers(1, 41)), int(rng.integers(1, 7))
+    d, K = int(rng.choice([4, 8, 16, 32, 64, 128])), int(rng.integers(1, 5))
+    perm = bool(rng.random() < 0.6)
+    n_slots = batch + int(rng.integers(0, 8)) if perm else None
+    la = [(-5.0, 0.0), (-8.0, -2.0), (-1.0, 1.5)][int(rng.integers(0, 3))]
+    gated = bool(rng.random() < 0.7)
+    dec = ki.decode_inputs(8000 + i, batch, H=H, d=d, K=K, steps=int(rng.integers(1, 4)), la_range=la,
+                           n_slots=n_slots, slot_perm=perm, state_std=0.1)
+    what = f"random decode {i} (batch {batch}, H={H}, d={d}, K={K}, slots {n_slots}, la {la}, gated {gated})"
+    si = dec["slot_idx"]
+    st = dec["state"].double().numpy().copy()
+    ca = dec["conv_cache"].double().numpy().copy()
+    gst, gca, cw = dec["state"].cuda(), dec["conv_cache"].cuda(), dec["conv_w"].cuda()
+    gsi = si.cuda() if si is not None else None
+    for t, step in enumerate(dec["steps"]):
+        if not gated:
+            step = dict(step, gate_logit=None)
+        want = ORC.decode_step(st, ca, dec["conv_w"], step, slot_idx=si)
+        s = {k: (v.cuda() if v is not None else None) for k, v in step.items()}
+        got = kda.decode_step(s["q_raw"], s["k_raw"], s["v_raw"], cw, gca, gst, s["log_alpha"], s["beta_logit"],
+                              s["gate_logit"], gsi)
+        torch.cuda.synchronize()
+        assert_fp32_close(got, want, f"{what} y step {t}")
+    assert_fp32_close(gst, st, what + " state")
+    assert_fp32_close(gca, ca, what + " conv cache", 0.0)
+
+
 def test_decode_bf16_output_and_no_gate():
     dec = ki.decode_inputs(50, 4, H=2, d=128, K=4, steps=2)
     for s in dec["steps"]:
