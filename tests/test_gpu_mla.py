@@ -100,6 +100,26 @@ def test_mla_production_like_split_edges():
     check(inp, "mla 192/128 split edges")
 
 
+@pytest.mark.parametrize("i", range(6))
+def test_mla_random_configs(i):
+    """Six seeded random batches: sequences, kv heads and group size, q/k and
+    value widths anywhere in 1..256 (whole 16-byte chunks or not), cache
+    size, lengths (the last slot and 0 among them), gate on or off."""
+    rng = np.random.default_rng(9000 + i)
+    B, Hkv, G = int(rng.integers(1, 9)), int(rng.choice([1, 2, 3, 4, 8])), int(rng.choice([1, 2, 4, 8]))
+    vec = rng.random() < 0.5
+    dqk = int(rng.integers(1, 33)) * 8 if vec else int(rng.integers(1, 257))
+    dv = int(rng.integers(1, 33)) * 8 if vec else int(rng.integers(1, 257))
+    L = int(rng.integers(1, 1201))
+    lens = [int(x) for x in rng.integers(0, L, B)]
+    lens[0] = L - 1
+    if B > 1:
+        lens[1] = 0
+    gate = bool(rng.random() < 0.7)
+    inp = ki.mla_inputs(9000 + i, B, Hkv * G, Hkv, dqk, dv, L, lens=lens, gate=gate)
+    check(inp, f"mla random {i} (B={B}, H={Hkv * G}, H_kv={Hkv}, {dqk}/{dv}, L={L}, gate {gate})", gate=gate)
+
+
 @pytest.mark.parametrize("H,H_kv,dqk,dv", [(8, 2, 128, 128), (6, 3, 64, 64), (4, 1, 256, 256), (4, 4, 100, 72),
                                            (2, 2, 16, 8), (16, 2, 192, 128), (24, 3, 64, 64), (32, 2, 64, 64)])
 def test_mla_shapes(H, H_kv, dqk, dv):
