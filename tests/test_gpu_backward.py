@@ -83,6 +83,21 @@ def test_backward_varlen(seed, lengths, H, gate, s0, dsf, scale):
     assert_grads_close(run_gpu(c, scale), run_oracle(c, scale), f"seed {seed}")
 
 
+@pytest.mark.parametrize("i", range(4))
+def test_backward_random_configs(i):
+    """Four seeded random batches: sequence lengths, heads, gate, initial
+    state, gradient of the final state, scale and a decay range within the
+    backward's bound."""
+    rng = np.random.default_rng(9500 + i)
+    lens = [int(x) for x in rng.integers(0, 200, int(rng.integers(1, 5)))]
+    la = [(-5.0, 0.0), (-8.0, -2.0), (-1.0, 0.1823)][int(rng.integers(0, 3))]
+    gate, s0, dsf = (bool(rng.random() < 0.7) for _ in range(3))
+    scale = float(rng.choice([1.0, 128 ** -0.5]))
+    c = make_case(9500 + i, lens, int(rng.integers(1, 4)), gate, s0, dsf, la_range=la)
+    assert_grads_close(run_gpu(c, scale), run_oracle(c, scale),
+                       f"random {i} (lens {lens}, H={c['H']}, la {la}, gate {gate}, s0 {s0}, dsf {dsf}, scale {scale:.3f})")
+
+
 def test_backward_many_sequences():
     """150 short sequences (0..90 tokens): more than the 128 whose chunk table
     travels in the kernel arguments, so the backward reads the table the
