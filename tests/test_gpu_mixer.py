@@ -97,6 +97,43 @@ def test_out_projection(T, C, hidden):
     assert_gemm_close(out, ref, np.abs(np64(y)) @ np.abs(np64(w)).T, C, f"out projection {T}x{C}->{hidden}")
 
 
+@pytest.mark.parametrize("i", range(6))
+def test_projections_random_shapes(i):
+    """Six seeded random shapes for each projection: rows 1..700, inner
+    dimension any multiple of 8 up to 1280 (2048 for the output projection),
+    1..12 heads of 4..128 channels (any output width for the output
+    projection), decay parameters present or absent."""
+    rng = np.random.default_rng(9700 + i)
+    T, hidden = int(rng.integers(1, 701)), 8 * int(rng.integers(1, 161))
+    H, d = int(rng.integers(1, 13)), int(rng.choice([4, 8, 16, 32, 64, 128]))
+    inp = ki.mixer_inputs(9700 + i, [T], hidden, H, d, 4)
+    if rng.random() < 0.5:
+        res = kda.in_projection(inp["x"].cuda(), inp["w_in"].cuda(), H, d, inp["a_log"].cuda(),
+                                inp["dt_bias"].cuda())
+        torch.cuda.synchronize()
+        check_in_projection(inp, res)
+    else:
+        res = kda.in_projection(inp["x"].cuda(), inp["w_in"].cuda(), H, d)
+        torch.cuda.synchronize()
+        x, w = np64(inp["x"]), np64(inp["w_in"])
+        ref = ORC.in_projection(x, w, H, d)
+        S = np.abs(x) @ np.abs(w).T
+        C = H * d
+        for j, key in enumerate(("q_raw", "k_raw", "v_raw", "gate_logit", "log_alpha")):
+            assert_gemm_close(res[key], ref[key], S[:, j * C:(j + 1) * C].reshape(T, H, d), hidden,
+                              f"random {i} in projection {key} (no decay parameters)")
+        assert_gemm_close(res["beta_logit"], ref["beta_logit"], S[:, 5 * C:5 * C + H], hidden,
+                          f"random {i} in projection beta_logit")
+    C, N = 8 * int(rng.integers(1, 257)), int(rng.integers(1, 1501))
+    g = torch.Generator().manual_seed(9700 + i)
+    y = torch.randn(T, C, generator=g).to(torch.bfloat16)
+    w = (torch.randn(N, C, generator=g) * C ** -0.5).to(torch.bfloat16)
+    out = kda.out_projection(y.cuda(), w.cuda())
+    torch.cuda.synchronize()
+    ref = ORC.linear(np64(y), np64(w))
+    assert_gemm_close(out, ref, np.abs(np64(y)) @ np.abs(np64(w)).T, C, f"random {i} out projection {T}x{C}->{N}")
+
+
 def test_mixer_prefill():
     """The whole mixer on a packed batch (ragged, an empty sequence): equal to
     its three stages called one by one, and each stage against the oracle."""
